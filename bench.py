@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of the fused KDA token step on one MI355X.
+
+Headline (one JSON line on stdout): decode over 64 sequences x 32 heads,
+dk = dv = 128, fp32 state, one kda_token_step launch per token, K steps back
+to back with every step's inputs already resident in HBM.  value = total
+token.heads per second.  Alongside: the decode kernel's HBM roofline, the CPU
+oracle timed on this host on a bounded sample (its only use here; parity is
+checked by the GPU tests at these same sizes), a disclosed over-cache decode
+run, and the prefill workloads (kda_sequence) with their VALU roofline.
+
+  python bench.py [--gpus 1] [--steps 1000] [--warmup 10]
+                  [--prefill default|all|none] [--no-cpu-baseline] [--no-overcache]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA tokens·heads/sec (decode + prefill); achieved HBM GB/s vs peak"
+UNIT = "token·heads/s"
+HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published (packed FP32)
+DK = DV = 128
+STATE_BYTES = DK * DV * 4 * 2         # state read + write per (sequence, head) per decode token
+# per decode token.head: q, k, v (3 x 512) + window in/out (2 x 3 x 384 x 4) + f 512 + beta 4 + g 512 + y 512
+DECODE_OTHER_BYTES = 3 * 512 + 2 * 3 * 384 * 4 + 512 + 4 + 512 + 512
+RECUR_FLOPS = 7 * DK * DV             # u, p dot products (2 FMAs), decay multiply, rank-1 FMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def file_sha(path):
+    h = hashlib.sha256()
+    with open(path, "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_file, workload_key):
+    """HBM bytes per dispatch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload_key)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "linear_attention_recurrence_token_amd", "csrc", kernel_file)
+    if vals.get("kernel_source_sha256_16") != file_sha(src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def rocm_smi_snapshot():
+    try:
+        out = subprocess.run(["rocm-smi", "--showtemp", "--showpower", "--showclocks", "--json"],
+                             capture_output=True, text=True, timeout=20)
+        data = json.loads(out.stdout)
+        card = data[sorted(data)[0]]
+        keep = {}
+        for k, v in card.items():
+            kl = k.lower()
+            if any(s in kl for s in ("temperature (sensor junction)", "power", "sclk", "mclk")):
+                keep[k] = v
+        return keep
+    except Exception as e:  # the snapshot is informational only
+        return {"error": str(e)[:80]}
+
+
+class TokenStepRunner:
+    """Pre-marshalled kda_token_step calls, one per decode step."""
+
+    def __init__(self, kda, cfg, d, N, steps, stream):
+        self.L = kda.lib()
+        self.cfg = cfg.to_c()
+        self.N = N
+        self.sh = stream.cuda_stream
+        self.structs = []
+        H = cfg.num_heads
+        for s in range(steps):
+            off = s * N
+
+            def ptr(name, per_row):
+                t = d[name]
+                return t.data_ptr() + off * per_row * t.element_size()
+            vals = {}
+            for name in ("q", "k", "v", "f", "g", "y"):
+                vals[name] = ptr(name, H * DK)
+            vals["beta"] = ptr("beta", H)
+            for name in ("conv_w", "A_log", "dt_bias", "gamma", "state", "conv_win"):
+                vals[name] = d[name].data_ptr()
+            vals["o_raw"] = None
+            self.structs.append(kda.kda_tensors(*[vals[n] for n in kda.TENSOR_FIELDS]))
+
+    def run(self, s):
+        st = self.L.kda_token_step(ctypes.byref(self.cfg), ctypes.byref(self.structs[s]), self.N, self.sh)
+        if st != 0:
+            raise RuntimeError("kda_token_step returned %d" % st)
+
+
+def bench_decode(torch, kda, synth, dev, N, H, steps, warmup):
+    w = synth.workload(1, scale={"N": N, "H": H, "steps": steps})
+    d = synth.to_device(w, dev, with_o_raw=False)
+    state0, win0 = d["state"].clone(), d["conv_win"].clone()
+    cfg = kda.KdaConfig(num_heads=H)
+    stream = torch.cuda.current_stream()
+    runner = TokenStepRunner(kda, cfg, d, N, steps, stream)
+    for s in range(warmup):
+        runner.run(s % steps)
+    d["state"].copy_(state0)
+    d["conv_win"].copy_(win0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(steps):
+        runner.run(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    res = {"w": w, "ms_total": ms, "wall_s": wall}
+    del d, state0, win0
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_as_prefill(synth, w, steps=None):
+    import dataclasses
+    import numpy as np
+    steps = w.decode_steps if steps is None else steps
+    T = steps * w.N
+    ww = dataclasses.replace(w, decode_steps=steps, q=w.q[:T], k=w.k[:T], v=w.v[:T], f=w.f[:T],
+                             beta=w.beta[:T], g=w.g[:T])
+    re = {k: synth.decode_rows_as_sequences(ww, getattr(ww, k)) for k in ("q", "k", "v", "f", "beta", "g")}
+    cu = np.arange(w.N + 1, dtype=np.int64) * steps
+    return dataclasses.replace(ww, decode_steps=0, cu_seqlens=cu, **re)
+
+
+def cpu_baseline_decode(synth, w, target_s):
+    """The oracle as it stands, on this host, over all (sequence, head) pairs of
+    the decode workload for as many of its steps as fit in about target_s."""
+    import oracle
+
+    def run(steps):
+        sw = decode_as_prefill(synth, w, steps)
+        t = time.perf_counter()
+        oracle.kda_reference(sw.q, sw.k, sw.v, sw.f, sw.beta, sw.g, sw.conv_w, sw.A_log,
+                             sw.dt_bias, sw.gamma, sw.state0, sw.win0, sw.cu_seqlens,
+                             want_o_raw=False)
+        return time.perf_counter() - t
+    t1 = run(2) / 2.0
+    steps = int(max(1, min(w.decode_steps, target_s / max(t1, 1e-6))))
+    wall = run(steps)
+    th = w.N * w.H * steps
+    return {"value": th / wall, "unit": UNIT, "cores": oracle.omp_threads(), "kind": "oracle",
+            "sample": "all %d x %d (sequence, head) pairs, first %d decode steps, fp64 oracle, %.1f s"
+                      % (w.N, w.H, steps, wall)}
+
+
+def bench_prefill(torch, kda, synth, dev, idx, runs):
+    import numpy as np
+    w = synth.workload(idx)
+    d = synth.to_device(w, dev, with_o_raw=False)
+    state0, win0 = d["state"].clone(), d["conv_win"].clone()
+    cfg = kda.KdaConfig(num_heads=w.H, act_dtype=kda.KDA_BF16 if w.act_dtype == "bf16" else kda.KDA_F32)
+    stream = torch.cuda.current_stream()
+    L = kda.lib()
+    ccfg = cfg.to_c()
+    t = kda.kda_tensors(*[(d[n].data_ptr() if d.get(n) is not None else None) for n in kda.TENSOR_FIELDS])
+    cu = d["cu_seqlens"].data_ptr()
+    lens = w.lengths
+    order = torch.from_numpy(np.argsort(-lens, kind="stable").astype(np.int32)).to(dev)
+
+    def launch():
+        st = L.kda_sequence(ctypes.byref(ccfg), ctypes.byref(t), w.N, cu, order.data_ptr(),
+                            w.total_tokens, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError("kda_sequence returned %d" % st)
+    times = []
+    for r in range(runs + 1):
+        d["state"].copy_(state0)
+        d["conv_win"].copy_(win0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    th = int(lens.sum()) * w.H
+    flops = th * RECUR_FLOPS
+    out = {"workload": w.name, "token_heads": th, "ms": ms, "runs": runs,
+           "value": th / (ms * 1e-3), "unit": UNIT,
+           "ns_per_token_per_chain": ms * 1e6 / int(lens.max()),
+           "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
+                        "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, "traffic": None}}
+    del d, state0, win0
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill", choices=["none", "default", "all"], default="default")
+    ap.add_argument("--prefill-runs", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-overcache", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: the KDA step has no cross-GPU part in this "
+                  "library (every (sequence, head) pair is independent); run with --gpus 1",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from linear_attention_recurrence_token_amd import kda, synth
+
+    if not os.path.exists(kda.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if kda.device_check() != 0:
+        raise SystemExit("libkda: the current device is not a gfx950 part")
+    smi_before = rocm_smi_snapshot()
+
+    N, H = 64, 32
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
+    log("decode %dx%d: generating %d steps of inputs" % (N, H, steps))
+    dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup)
+    ms_step = dec["ms_total"] / steps
+    units = N * H
+    value = units * steps / (dec["ms_total"] * 1e-3)
+    bytes_launch = units * (STATE_BYTES + DECODE_OTHER_BYTES)
+    achieved = bytes_launch / (ms_step * 1e-3) / 1e9
+    traffic = committed_traffic("kda_decode.hip", "decode_64x32")
+    log("decode: %.2f us/step, %.3g token.heads/s, %.0f GB/s algorithmic" % (ms_step * 1e3, value, achieved))
+
+    result = {
+        "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded PCG64, K3-shaped KDA heads)",
+        "config": {"workload": "decode: 64 sequences x 32 heads, dk=dv=128, fp32 state ~N(0,0.02), "
+                               "conv window carried in, one kda_token_step launch per token",
+                   "num_seqs": N, "num_heads": H, "head_dim": DK, "act_dtype": "fp32",
+                   "gate": "bounded", "tokens_per_step": 1},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "state_only_GBps": units * STATE_BYTES / (ms_step * 1e-3) / 1e9,
+                     "bytes_per_launch": bytes_launch},
+    }
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on this host (~%.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_decode(synth, dec["w"], args.cpu_seconds)
+        log("cpu baseline: %s" % result["cpu_baseline"])
+    del dec
+
+    if not args.no_overcache:
+        log("over-cache decode 512x32 (1 GiB of state), 100 steps")
+        oc = bench_decode(torch, kda, synth, dev, 512, H, 100, 5)
+        oms = oc["ms_total"] / 100
+        result["overcache_decode"] = {
+            "workload": "decode 512 x 32 heads (1 GiB state, exceeds the 256 MB Infinity Cache); disclosed, not the baseline",
+            "us_per_step": oms * 1e3, "value": 512 * H * 100 / (oc["ms_total"] * 1e-3),
+            "achieved_GBps": 512 * H * (STATE_BYTES + DECODE_OTHER_BYTES) / (oms * 1e-3) / 1e9}
+        log("over-cache: %s" % result["overcache_decode"])
+        del oc
+
+    if args.prefill != "none":
+        idxs = [2, 3] if args.prefill == "default" else [2, 3, 4]
+        result["prefill"] = []
+        for idx in idxs:
+            log("prefill workload %d" % idx)
+            r = bench_prefill(torch, kda, synth, dev, idx, args.prefill_runs)
+            log("prefill: %s" % r)
+            result["prefill"].append(r)
+
+    result["device"] = {"name": torch.cuda.get_device_name(dev), "rocm_smi_before": smi_before,
+                        "rocm_smi_after": rocm_smi_snapshot()}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * kda.h -- C ABI of libkda, the fused KDA (Kimi Delta Attention) token step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One call runs, for every (sequence, head) pair and every token in order:
+ *
+ *   1. causal depthwise 4-tap conv + SiLU on the raw q | k | v channels, the
+ *      conv window carried in and out
+ *        ("Kimi K3 Metal Gap Analysis", §2 KDA Attention, row "Conv4 + SiLU";
+ *         "Metal (Apple GPU) backend for Kimi K3", Design notes, "Fused KDA
+ *         token": conv_silu for each of q, k, v);
+ *   2. per-head L2 normalisation of q and k
+ *        (Gap Analysis §2, row "L2 normalize q/k");
+ *   3. the per-key-channel decay alpha = exp(gk), gk from A_log, dt_bias and
+ *      the decay pre-activation f (Gap Analysis §2, row "Decay compute");
+ *   4. the gated delta-rule update of the fp32 dk x dv state
+ *        S <- (I - beta k k^T) Diag(alpha) S + beta k v^T
+ *        (Gap Analysis §2, row "Recurrence"; beta as in "Metal (Apple GPU)
+ *         backend for Kimi K3", Correctness, token-0 zero-state check);
+ *   5. the readout o = S^T q from the updated state;
+ *   6. y = sigmoid(g) * gamma * o / sqrt(mean(o^2) + rms_eps)
+ *        (Gap Analysis §2, row "O projection": the gate and the per-head
+ *         RMSNorm around St*q; the W_o and W_g matmuls are not part of it).
+ *
+ * Conventions (readings of the pages, stated once here):
+ *   - conv: tap 3 multiplies the current raw row, tap 0 the oldest; no bias;
+ *     the window holds the last 3 RAW rows, oldest first, channel order
+ *     q | k | v, in fp32;
+ *   - L2: x / sqrt(sum(x^2) + l2_eps); no scale on q;
+ *   - gate: see kda_gate_mode; gamma has shape [dv], shared by all heads.
+ *
+ * Layouts (all device memory, C-contiguous, row = token index * H + head):
+ *   q, k  [T, H, 128] act dtype     v, g  [T, H, 128] act dtype
+ *   f     [T, H, 128] fp32          beta  [T, H]      fp32
+ *   conv_w [H, 384, 4] fp32         A_log, dt_bias [H, 128] fp32
+ *   gamma [128] fp32                y     [T, H, 128] act dtype
+ *   state [N, H, 128, 128] fp32, row index = key channel, in/out
+ *   conv_win [N, H, 3, 384] fp32, in/out
+ *   o_raw [T, H, 128] fp32, optional (the pre-norm readout; test hook)
+ * Every pointer must be 16-byte aligned.  q, k, v, f, beta, g, conv_w, A_log,
+ * dt_bias and gamma must not overlap y, o_raw, state or conv_win.
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer after
+ * a call returns and allocates no device memory.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns at once.  A kernel fault surfaces at the
+ * caller's next synchronisation, as for any HIP launch.
+ *
+ * Errors: a status other than KDA_OK means nothing was enqueued and no
+ * buffer was touched, so the caller may run another implementation instead
+ * (the pages' fused dispatch checks the return value and falls back to its
+ * CPU path: "Metal (Apple GPU) backend for Kimi K3", CPU fallback).  The
+ * library itself never computes on the CPU.
+ *
+ * Thread safety: stateless apart from a per-device capability cache; calls
+ * on different streams with disjoint buffers may run concurrently.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or enum */
+    KDA_ERR_UNSUPPORTED = -2,   /* dims other than dk = dv = 128, 4 taps     */
+    KDA_ERR_DEVICE = -3,        /* no current HIP device, or not gfx950      */
+    KDA_ERR_LAUNCH = -4         /* the HIP runtime refused the launch        */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,                /* q, k, v, g, y in fp32                     */
+    KDA_BF16 = 1                /* q, k, v, g, y in bf16 (math stays fp32)  */
+} kda_dtype;
+
+/* Decay gate forms ("Kimi K3 Metal Gap Analysis", §2, row "Decay compute").
+ * The extracted text reads gk = -5 * (exp(A_log) * (f + dt_bias)), which is
+ * not a decay when f + dt_bias < 0; a squashing function was evidently lost.
+ * BOUNDED is the reading taken by default; the other two are exact forms. */
+typedef enum kda_gate_mode {
+    KDA_GATE_BOUNDED = 0,       /* gk = lb * sigmoid(exp(A_log) * (f + dt_bias)) */
+    KDA_GATE_LITERAL = 1,       /* gk = lb * exp(A_log) * (f + dt_bias)         */
+    KDA_GATE_RAW = 2            /* gk = f (the caller supplies the log-decay)   */
+} kda_gate_mode;
+
+typedef struct kda_config {
+    int32_t num_heads;          /* H >= 1                                    */
+    int32_t head_dim_k;         /* dk: must be 128                           */
+    int32_t head_dim_v;         /* dv: must be 128                           */
+    int32_t conv_taps;          /* must be 4                                 */
+    int32_t act_dtype;          /* kda_dtype                                 */
+    int32_t gate_mode;          /* kda_gate_mode                             */
+    float gate_lower_bound;     /* lb, -5 in the pages                       */
+    float l2_eps;               /* e.g. 1e-6                                 */
+    float rms_eps;              /* e.g. 1e-6                                 */
+} kda_config;
+
+typedef struct kda_tensors {
+    const void *q;              /* [T, H, 128] act dtype, raw (pre-conv)     */
+    const void *k;              /* [T, H, 128] act dtype, raw                */
+    const void *v;              /* [T, H, 128] act dtype, raw                */
+    const float *f;             /* [T, H, 128] decay pre-activation          */
+    const float *beta;          /* [T, H]                                    */
+    const void *g;              /* [T, H, 128] act dtype, output-gate input  */
+    const float *conv_w;        /* [H, 384, 4]                               */
+    const float *A_log;         /* [H, 128]                                  */
+    const float *dt_bias;       /* [H, 128]                                  */
+    const float *gamma;         /* [128]                                     */
+    float *state;               /* [N, H, 128, 128] in/out                   */
+    float *conv_win;            /* [N, H, 3, 384] in/out                     */
+    void *y;                    /* [T, H, 128] act dtype, out                */
+    float *o_raw;               /* [T, H, 128] fp32 out, or NULL             */
+} kda_tensors;
+
+/*
+ * Decode: one token for each of num_seqs sequences (T = num_seqs, token row
+ * n belongs to sequence n).  One kernel launch; each (sequence, head) state
+ * is read once and written once.  num_seqs == 0 is a no-op.
+ * Equivalent to kda_sequence with every sequence of length 1.
+ */
+kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
+                          int32_t num_seqs, void *stream);
+
+/*
+ * Prefill: num_seqs sequences packed along the token axis.
+ *   cu_seqlens  device int32 [num_seqs + 1] token offsets, or NULL for a
+ *               dense batch of num_seqs sequences of total_tokens / num_seqs
+ *               tokens each (total_tokens must divide evenly).
+ *               Precondition (not checkable without a sync): cu[0] = 0,
+ *               non-decreasing, cu[num_seqs] = total_tokens.  The kernel
+ *               clamps every range to [0, total_tokens), so a violation gives
+ *               wrong results but no out-of-bounds access.
+ *   seq_order   device int32 [num_seqs] or NULL: the order in which sequences
+ *               are scheduled (e.g. longest first).  Must be a permutation of
+ *               0..num_seqs-1; entries outside that range are skipped.
+ *   total_tokens  T, the number of token rows of q, k, v, f, beta, g, y.
+ * Sequences of length 0 leave their state and window unchanged.  State and
+ * window are carried in and out, so splitting a sequence across calls gives
+ * the same result as one call (up to fp32 rounding order).
+ */
+kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t,
+                        int32_t num_seqs, const int32_t *cu_seqlens,
+                        const int32_t *seq_order, int64_t total_tokens,
+                        void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *kda_status_string(int32_t status);
+
+/* KDA_VERSION of the built library. */
+int32_t kda_version(void);
+
+/*
+ * KDA_OK if the current HIP device is a gfx950 part the library was built
+ * for, else KDA_ERR_DEVICE.  Cheap after the first call on a device.
+ */
+kda_status kda_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,145 @@
+// kda_api.hip -- the C ABI of libkda: argument validation, device check and
+// kernel dispatch.  No compute happens here; a non-OK status means nothing
+// was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = something else
+std::atomic<int> g_dev_kind[kMaxDevices];
+
+kda_status device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return KDA_ERR_DEVICE;
+    }
+    if (dev >= kMaxDevices) return KDA_ERR_DEVICE;
+    int kind = g_dev_kind[dev].load(std::memory_order_relaxed);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return KDA_ERR_DEVICE;
+        }
+        kind = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_dev_kind[dev].store(kind, std::memory_order_relaxed);
+    }
+    return kind == 1 ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+kda_status check_common(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
+    if (!cfg || !t) return KDA_ERR_INVALID_ARG;
+    if (cfg->num_heads <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARG;
+    if (cfg->act_dtype != KDA_F32 && cfg->act_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (cfg->gate_mode < KDA_GATE_BOUNDED || cfg->gate_mode > KDA_GATE_RAW) return KDA_ERR_INVALID_ARG;
+    if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
+    if (cfg->gate_lower_bound != cfg->gate_lower_bound) return KDA_ERR_INVALID_ARG;
+    if (cfg->head_dim_k != kda::DK || cfg->head_dim_v != kda::DV || cfg->conv_taps != kda::TAPS)
+        return KDA_ERR_UNSUPPORTED;
+    const void *ins[] = {t->q, t->k, t->v, t->f, t->beta, t->g,
+                         t->conv_w, t->A_log, t->dt_bias, t->gamma};
+    const void *outs[] = {t->state, t->conv_win, t->y};
+    for (const void *ptr : ins)
+        if (!ptr || !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    for (const void *ptr : outs)
+        if (!ptr || !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    if (t->o_raw && !aligned16(t->o_raw)) return KDA_ERR_INVALID_ARG;
+    // no output may coincide with an input or with another output
+    const void *all_outs[] = {t->state, t->conv_win, t->y, t->o_raw};
+    for (int a = 0; a < 4; ++a) {
+        if (!all_outs[a]) continue;
+        for (const void *in : ins)
+            if (in == all_outs[a]) return KDA_ERR_INVALID_ARG;
+        for (int b = a + 1; b < 4; ++b)
+            if (all_outs[a] == all_outs[b]) return KDA_ERR_INVALID_ARG;
+    }
+    if ((int64_t)num_seqs * cfg->num_heads > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+kda::Params make_params(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
+    kda::Params p;
+    p.q = t->q; p.k = t->k; p.v = t->v;
+    p.f = t->f; p.beta = t->beta; p.g = t->g;
+    p.conv_w = t->conv_w; p.A_log = t->A_log; p.dt_bias = t->dt_bias; p.gamma = t->gamma;
+    p.state = t->state; p.win = t->conv_win; p.y = t->y; p.o_raw = t->o_raw;
+    p.cu_seqlens = nullptr; p.seq_order = nullptr;
+    p.total_tokens = 0; p.num_seqs = num_seqs; p.H = cfg->num_heads; p.dense_len = 0;
+    p.gate_mode = cfg->gate_mode;
+    p.lb = cfg->gate_lower_bound; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_device_check(void) { return device_ok(); }
+
+int32_t kda_version(void) { return KDA_VERSION; }
+
+const char *kda_status_string(int32_t status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or enum, aliasing)";
+        case KDA_ERR_UNSUPPORTED: return "unsupported shape (libkda needs dk = dv = 128 and 4 conv taps)";
+        case KDA_ERR_DEVICE: return "no usable device (no current HIP device, or it is not gfx950)";
+        case KDA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs, void *stream) {
+    kda_status st = check_common(cfg, t, num_seqs);
+    if (st != KDA_OK) return st;
+    st = device_ok();
+    if (st != KDA_OK) return st;
+    if (num_seqs == 0) return KDA_OK;
+    kda::Params p = make_params(cfg, t, num_seqs);
+    p.total_tokens = num_seqs;
+    p.dense_len = 1;
+    const hipError_t e = kda::launch_decode(p, cfg->act_dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
+                        const int32_t *cu_seqlens, const int32_t *seq_order,
+                        int64_t total_tokens, void *stream) {
+    kda_status st = check_common(cfg, t, num_seqs);
+    if (st != KDA_OK) return st;
+    if (total_tokens < 0) return KDA_ERR_INVALID_ARG;
+    if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARG;
+    if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) ||
+        (seq_order && (reinterpret_cast<uintptr_t>(seq_order) & 3u)))
+        return KDA_ERR_INVALID_ARG;
+    int32_t dense_len = 0;
+    if (!cu_seqlens && num_seqs > 0) {
+        if (total_tokens % num_seqs != 0) return KDA_ERR_INVALID_ARG;
+        if (total_tokens / num_seqs > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+        dense_len = (int32_t)(total_tokens / num_seqs);
+    }
+    // row offsets are formed in 64-bit arithmetic; keep them well inside it
+    if (total_tokens > (int64_t(1) << 40) / ((int64_t)cfg->num_heads * kda::DK)) return KDA_ERR_INVALID_ARG;
+    st = device_ok();
+    if (st != KDA_OK) return st;
+    if (num_seqs == 0 || total_tokens == 0) return KDA_OK;
+    kda::Params p = make_params(cfg, t, num_seqs);
+    p.cu_seqlens = cu_seqlens;
+    p.seq_order = seq_order;
+    p.total_tokens = total_tokens;
+    p.dense_len = dense_len;
+    const hipError_t e = kda::launch_prefill(p, cfg->act_dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// kda_decode.hip -- one decode token for each of N sequences, all heads, in
+// one launch.
+//
+// The step is HBM-bound: per (sequence, head) it must stream the 64 KiB fp32
+// state in and 64 KiB out, against ~115 K flops.  So the design is about the
+// memory stream:
+//   * one 256-thread workgroup per (sequence, head); the 128 x 128 state is
+//     held in registers, 64 floats per thread (16 rows x 4 columns), loaded
+//     with 16 coalesced 16-byte loads issued before any other work, so the
+//     whole 64 KiB is in flight while the pre-step runs;
+//   * the pre-step (conv4 + SiLU, window shift, L2 norms, decay) runs from
+//     the raw inputs while those loads are outstanding;
+//   * one pass over the registers gives both dot products the step needs,
+//     u = S^T (alpha * k) and p = S^T (alpha * q), because the readout of the
+//     updated state equals p + beta (q.k) (v - u)  (expand S_new^T q with
+//     S_new = Diag(alpha) S + beta k (v - u)^T, "Kimi K3 Metal Gap Analysis",
+//     §2, rows "Recurrence" and "O projection");
+//   * the update is written back in place with 16-byte stores; the RMSNorm +
+//     sigmoid gate epilogue needs only a 32-lane reduction.
+//
+// Thread layout: tid = 32 * rg + cg.  Thread (rg, cg) owns rows rg + 8 m
+// (m = 0..15) and columns 4 cg .. 4 cg + 3.  A wavefront covers two adjacent
+// rows per load instruction: 1 KiB contiguous.
+#include "kda_device.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int DEC_THREADS = 256;
+
+template <typename Act>
+__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(Params p) {
+    const int unit = blockIdx.x;           // n * H + h == token row of sequence n
+    const int h = unit % p.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cg = tid & 31, rg = tid >> 5;
+
+    __shared__ float s_act[CH];            // activated q | k | v of this token
+    __shared__ float s_alpha[DK];
+    __shared__ float s_red[4][4];          // per-wave partial sums (qq, kk, qk)
+    __shared__ float4 s_up[4][32][2];      // per-wave partial u, p per column group
+
+    float *S = p.state + (int64_t)unit * (DK * DV);
+
+    // ---- 1. put the whole state in flight
+    float4 s[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        s[m] = *reinterpret_cast<const float4 *>(S + (rg + 8 * m) * DV + 4 * cg);
+
+    // ---- 2. pre-step from the raw inputs
+    float *W = p.win + (int64_t)unit * (PAST * CH);
+    const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+    const int64_t row = (int64_t)unit * DK;   // DK == DV
+    if (tid < DK) {
+        // q channel i and k channel i
+        const int i = tid;
+        const float xq = Act::load1(p.q, row + i);
+        const float xk = Act::load1(p.k, row + i);
+        const float4 wq = *reinterpret_cast<const float4 *>(cw + i * TAPS);
+        const float4 wk = *reinterpret_cast<const float4 *>(cw + (DK + i) * TAPS);
+        const float q0 = W[i], q1 = W[CH + i], q2 = W[2 * CH + i];
+        const float k0 = W[DK + i], k1 = W[CH + DK + i], k2 = W[2 * CH + DK + i];
+        const float aq = silu(wq.x * q0 + wq.y * q1 + wq.z * q2 + wq.w * xq);
+        const float ak = silu(wk.x * k0 + wk.y * k1 + wk.z * k2 + wk.w * xk);
+        W[i] = q1; W[CH + i] = q2; W[2 * CH + i] = xq;
+        W[DK + i] = k1; W[CH + DK + i] = k2; W[2 * CH + DK + i] = xk;
+        s_act[i] = aq;
+        s_act[DK + i] = ak;
+        const float qq = sum64(aq * aq), kk = sum64(ak * ak), qk = sum64(aq * ak);
+        if (lane == 0) { s_red[wave][0] = qq; s_red[wave][1] = kk; s_red[wave][2] = qk; }
+    } else {
+        // v channel j, and the decay of key channel j
+        const int j = tid - DK;
+        const float xv = Act::load1(p.v, row + j);
+        const float4 wv = *reinterpret_cast<const float4 *>(cw + (2 * DK + j) * TAPS);
+        const float v0 = W[2 * DK + j], v1 = W[CH + 2 * DK + j], v2 = W[2 * CH + 2 * DK + j];
+        s_act[2 * DK + j] = silu(wv.x * v0 + wv.y * v1 + wv.z * v2 + wv.w * xv);
+        W[2 * DK + j] = v1; W[CH + 2 * DK + j] = v2; W[2 * CH + 2 * DK + j] = xv;
+        const float expA = __expf(p.A_log[h * DK + j]);
+        s_alpha[j] = decay(p.f[row + j], expA, p.dt_bias[h * DK + j], p.gate_mode, p.lb);
+    }
+    __syncthreads();
+
+    const float rq = rsqrtf(s_red[0][0] + s_red[1][0] + p.l2_eps);
+    const float rk = rsqrtf(s_red[0][1] + s_red[1][1] + p.l2_eps);
+    const float qk = (s_red[0][2] + s_red[1][2]) * rq * rk;
+    const float b = p.beta[unit];
+
+    // ---- 3. one pass: u = S^T (alpha k_hat), p = S^T (alpha q_hat)
+    float4 u = make_float4(0.f, 0.f, 0.f, 0.f), pq = u;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int i = rg + 8 * m;
+        const float al = s_alpha[i];
+        const float ak = al * s_act[DK + i] * rk;
+        const float aq = al * s_act[i] * rq;
+        u.x += s[m].x * ak; u.y += s[m].y * ak; u.z += s[m].z * ak; u.w += s[m].w * ak;
+        pq.x += s[m].x * aq; pq.y += s[m].y * aq; pq.z += s[m].z * aq; pq.w += s[m].w * aq;
+    }
+    // the two row groups of this wavefront, then the four wavefronts
+    u.x += __shfl_xor(u.x, 32); u.y += __shfl_xor(u.y, 32);
+    u.z += __shfl_xor(u.z, 32); u.w += __shfl_xor(u.w, 32);
+    pq.x += __shfl_xor(pq.x, 32); pq.y += __shfl_xor(pq.y, 32);
+    pq.z += __shfl_xor(pq.z, 32); pq.w += __shfl_xor(pq.w, 32);
+    if (lane < 32) { s_up[wave][cg][0] = u; s_up[wave][cg][1] = pq; }
+    __syncthreads();
+    u = s_up[0][cg][0]; pq = s_up[0][cg][1];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        const float4 a = s_up[w][cg][0], c = s_up[w][cg][1];
+        u.x += a.x; u.y += a.y; u.z += a.z; u.w += a.w;
+        pq.x += c.x; pq.y += c.y; pq.z += c.z; pq.w += c.w;
+    }
+
+    // ---- 4. delta, readout, in-place update
+    const float4 vv = *reinterpret_cast<const float4 *>(&s_act[2 * DK + 4 * cg]);
+    float4 d, o;
+    d.x = b * (vv.x - u.x); d.y = b * (vv.y - u.y); d.z = b * (vv.z - u.z); d.w = b * (vv.w - u.w);
+    o.x = pq.x + qk * d.x; o.y = pq.y + qk * d.y; o.z = pq.z + qk * d.z; o.w = pq.w + qk * d.w;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int i = rg + 8 * m;
+        const float al = s_alpha[i];
+        const float kh = s_act[DK + i] * rk;
+        float4 t;
+        t.x = al * s[m].x + kh * d.x; t.y = al * s[m].y + kh * d.y;
+        t.z = al * s[m].z + kh * d.z; t.w = al * s[m].w + kh * d.w;
+        *reinterpret_cast<float4 *>(S + i * DV + 4 * cg) = t;
+    }
+
+    // ---- 5. RMSNorm over the 128 outputs (32 lanes x 4), gamma, sigmoid gate
+    const float ss = sum32(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+    if (tid < 32) {
+        const float r = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
+        const float4 gm = *reinterpret_cast<const float4 *>(p.gamma + 4 * cg);
+        const int64_t orow = row + 4 * cg;
+        const float2 g01 = Act::load2(p.g, orow), g23 = Act::load2(p.g, orow + 2);
+        float4 y;
+        y.x = sigmoid(g01.x) * gm.x * o.x * r;
+        y.y = sigmoid(g01.y) * gm.y * o.y * r;
+        y.z = sigmoid(g23.x) * gm.z * o.z * r;
+        y.w = sigmoid(g23.y) * gm.w * o.w * r;
+        Act::store4(p.y, orow, y);
+        if (p.o_raw) *reinterpret_cast<float4 *>(p.o_raw + orow) = o;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Params &p, bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.num_seqs * p.H)), block(DEC_THREADS);
+    if (bf16)
+        hipLaunchKernelGGL(decode_kernel<BF16>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_kernel<F32>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,123 @@
+// kda_device.hpp -- device helpers shared by the libkda kernels: activation
+// I/O in fp32 or bf16, the pointwise functions of the pre-step, the decay
+// gate, and wavefront reductions built on DPP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_internal.hpp"
+
+namespace kda {
+
+// ---------------------------------------------------------------- activations
+
+struct F32 {
+    using storage = float;
+    static __device__ __forceinline__ float load1(const void *p, int64_t i) {
+        return static_cast<const float *>(p)[i];
+    }
+    // two consecutive elements; i must be even
+    static __device__ __forceinline__ float2 load2(const void *p, int64_t i) {
+        return *reinterpret_cast<const float2 *>(static_cast<const float *>(p) + i);
+    }
+    static __device__ __forceinline__ void store2(void *p, int64_t i, float2 x) {
+        *reinterpret_cast<float2 *>(static_cast<float *>(p) + i) = x;
+    }
+    static __device__ __forceinline__ void store4(void *p, int64_t i, float4 x) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(p) + i) = x;
+    }
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+struct BF16 {
+    using storage = uint16_t;
+    static __device__ __forceinline__ float load1(const void *p, int64_t i) {
+        return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    }
+    static __device__ __forceinline__ float2 load2(const void *p, int64_t i) {
+        uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p) + i);
+        return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    }
+    static __device__ __forceinline__ void store2(void *p, int64_t i, float2 x) {
+        uint32_t w = f32_to_bf16_bits(x.x) | (f32_to_bf16_bits(x.y) << 16);
+        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p) + i) = w;
+    }
+    static __device__ __forceinline__ void store4(void *p, int64_t i, float4 x) {
+        uint2 w;
+        w.x = f32_to_bf16_bits(x.x) | (f32_to_bf16_bits(x.y) << 16);
+        w.y = f32_to_bf16_bits(x.z) | (f32_to_bf16_bits(x.w) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p) + i) = w;
+    }
+};
+
+// ------------------------------------------------------------ pointwise math
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + __expf(-x)); }
+
+__device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
+
+// alpha = exp(gk) for one key channel; expA = exp(A_log) of that channel
+__device__ __forceinline__ float decay(float f, float expA, float dtb, int32_t mode, float lb) {
+    float gk;
+    if (mode == GATE_RAW) {
+        gk = f;
+    } else {
+        const float z = expA * (f + dtb);
+        gk = (mode == GATE_BOUNDED) ? lb * sigmoid(z) : lb * z;
+    }
+    return __expf(gk);
+}
+
+// --------------------------------------------------------- lane exchanges
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int DPP_ROW_MIRROR = 0x140;   // lane i <-> 15-i within 16 lanes
+
+// sum over each aligned group of 8 lanes, result in every lane of the group
+// (identical bits in all 8 lanes: every partial sum is formed symmetrically)
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp<DPP_QUAD_XOR1>(x);
+    x += dpp<DPP_QUAD_XOR2>(x);
+    x += dpp<DPP_HALF_MIRROR>(x);
+    return x;
+}
+
+__device__ __forceinline__ float sum16(float x) {
+    x = sum8(x);
+    x += dpp<DPP_ROW_MIRROR>(x);
+    return x;
+}
+
+__device__ __forceinline__ float sum32(float x) {
+    x = sum16(x);
+    x += __shfl_xor(x, 16);
+    return x;
+}
+
+__device__ __forceinline__ float sum64(float x) {
+    x = sum32(x);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+}  // namespace kda

@@ -1,0 +1,40 @@
+// kda_internal.hpp -- parameters shared by the host layer and the kernels of
+// libkda (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int DK = 128;        // key channels per head
+constexpr int DV = 128;        // value channels per head
+constexpr int TAPS = 4;        // causal conv taps
+constexpr int PAST = TAPS - 1; // raw rows kept in the conv window
+constexpr int CH = 2 * DK + DV; // conv channels per head (q | k | v)
+
+enum GateMode : int32_t { GATE_BOUNDED = 0, GATE_LITERAL = 1, GATE_RAW = 2 };
+
+struct Params {
+    const void *q, *k, *v;
+    const float *f, *beta;
+    const void *g;
+    const float *conv_w, *A_log, *dt_bias, *gamma;
+    float *state, *win;
+    void *y;
+    float *o_raw;
+    const int32_t *cu_seqlens;   // prefill only; nullptr = dense
+    const int32_t *seq_order;    // prefill only; nullptr = natural order
+    int64_t total_tokens;
+    int32_t num_seqs;
+    int32_t H;
+    int32_t dense_len;           // tokens per sequence when cu_seqlens is null
+    int32_t gate_mode;
+    float lb, l2_eps, rms_eps;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_decode(const Params &p, bool bf16, hipStream_t stream);
+hipError_t launch_prefill(const Params &p, bool bf16, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,297 @@
+// kda_prefill.hip -- multi-token KDA over dense or ragged (cu_seqlens) batches,
+// with state and conv window carried in and out.
+//
+// In the recurrent form every token costs 4 VALU operations per state element
+// (u and p dot products, decay multiply, rank-1 FMA) against almost no memory
+// traffic, so the kernel is built around keeping the state resident and the
+// VALU busy:
+//   * one 128-thread workgroup (two wavefronts) per (sequence, head); the
+//     128 x 128 fp32 state lives in registers for the whole token run,
+//     128 floats per lane: lane (rg, cg) holds rows 16 rg .. 16 rg + 15 and
+//     columns 8 cg .. 8 cg + 7, with rg in the low 3 lane bits so the
+//     reductions over rows are 3 DPP steps inside a group of 8 lanes;
+//   * tokens run in chunks of TC.  Per chunk, phase P computes the pre-step
+//     (conv4 + SiLU with a rolling window, L2 norms, decay, beta, q.k) for
+//     all TC tokens in parallel -- it depends only on inputs -- and writes
+//     per-row values (alpha k_hat, alpha q_hat) and (alpha, k_hat) and per-column
+//     v to LDS; phase R runs the serial recurrence over the chunk reading
+//     those values as LDS broadcasts; the RMSNorm + gate epilogue of a chunk
+//     runs token-parallel in the next phase P, off the serial chain;
+//   * the readout uses the pre-update state, o = S^T(alpha q) + beta (q.k)
+//     (v - u), so one read of the registers feeds both dot products
+//     ("Kimi K3 Metal Gap Analysis", §2, rows "Recurrence" and
+//     "O projection", expanded).
+#include "kda_device.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int PF_THREADS = 128;
+constexpr int TC = 8;              // tokens per chunk
+constexpr int HALF = TC / 2;       // chunk slots handled by each wavefront in phase P
+constexpr int RGS = 17;            // LDS slots per row group: 16 key rows + 1 pad (bank spread)
+
+struct Range {
+    int64_t lo, len;
+};
+
+__device__ __forceinline__ Range seq_range(const Params &p, int n) {
+    Range r;
+    if (p.cu_seqlens) {
+        int64_t a = p.cu_seqlens[n], b = p.cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+        b = b < a ? a : (b > p.total_tokens ? p.total_tokens : b);
+        r.lo = a;
+        r.len = b - a;
+    } else {
+        r.lo = (int64_t)n * p.dense_len;
+        r.len = p.dense_len;
+    }
+    return r;
+}
+
+template <typename Act>
+struct Ctx {
+    const void *q, *k, *v;
+    const float *W;   // carried-in window of this (sequence, head); read-only until the end
+    int64_t lo;       // first token row of the sequence
+    int H, h, lane;
+
+    // raw row j of the history (j < 0: window row j + PAST), channels 2 lane, 2 lane + 1
+    __device__ __forceinline__ void hist(int64_t j, float2 &xq, float2 &xk, float2 &xv) const {
+        if (j >= 0) {
+            const int64_t r = ((lo + j) * H + h) * DK + 2 * lane;
+            xq = Act::load2(q, r);
+            xk = Act::load2(k, r);
+            xv = Act::load2(v, r);
+        } else {
+            const float *wr = W + (j + PAST) * CH + 2 * lane;
+            xq = *reinterpret_cast<const float2 *>(wr);
+            xk = *reinterpret_cast<const float2 *>(wr + DK);
+            xv = *reinterpret_cast<const float2 *>(wr + 2 * DK);
+        }
+    }
+};
+
+__device__ __forceinline__ float conv4(float4 w, float a, float b, float c, float x) {
+    return w.x * a + w.y * b + w.z * c + w.w * x;
+}
+
+template <typename Act>
+__global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(Params p) {
+    const int slot_n = blockIdx.x / p.H;
+    const int h = blockIdx.x - slot_n * p.H;
+    int n = slot_n;
+    if (p.seq_order) {
+        n = p.seq_order[slot_n];
+        if (n < 0 || n >= p.num_seqs) return;
+    }
+    const Range rng = seq_range(p, n);
+    if (rng.len <= 0) return;
+    const int64_t L = rng.len;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int rg = lane & 7;                   // row group: rows 16 rg .. 16 rg + 15
+    const int cg = wave * 8 + (lane >> 3);     // column group: columns 8 cg .. 8 cg + 7
+    const int64_t unit = (int64_t)n * p.H + h;
+
+    __shared__ float2 s_dot[TC][8 * RGS];      // (alpha k_hat, alpha q_hat) per key row
+    __shared__ float2 s_upd[TC][8 * RGS];      // (alpha, k_hat) per key row
+    __shared__ float s_col[TC][DV];            // activated v, overwritten by the readout o
+    __shared__ float2 s_tok[TC];               // (beta, q_hat . k_hat)
+
+    float *S = p.state + unit * (DK * DV);
+    float *Wout = p.win + unit * (PAST * CH);
+    const Ctx<Act> cx{p.q, p.k, p.v, Wout, rng.lo, p.H, h, lane};
+
+    float4 s[16][2];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const float *src = S + (16 * rg + m) * DV + 8 * cg;
+        s[m][0] = *reinterpret_cast<const float4 *>(src);
+        s[m][1] = *reinterpret_cast<const float4 *>(src + 4);
+    }
+
+    const int s0 = wave * HALF;                // this wavefront's chunk slots in phase P
+
+    // token-parallel epilogue of slots [s0, s0 + HALF) of the chunk starting at c0
+    auto epilogue = [&](int64_t c0, int nvalid) {
+        const float2 gm = *reinterpret_cast<const float2 *>(p.gamma + 2 * lane);
+#pragma unroll 1
+        for (int sl = 0; sl < HALF; ++sl) {
+            const int slot = s0 + sl;
+            if (slot >= nvalid) break;
+            const float2 o = *reinterpret_cast<const float2 *>(&s_col[slot][2 * lane]);
+            const float ss = sum64(o.x * o.x + o.y * o.y);
+            const float r = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
+            const int64_t orow = ((rng.lo + c0 + slot) * p.H + h) * DV + 2 * lane;
+            const float2 gg = Act::load2(p.g, orow);
+            float2 y;
+            y.x = sigmoid(gg.x) * gm.x * o.x * r;
+            y.y = sigmoid(gg.y) * gm.y * o.y * r;
+            Act::store2(p.y, orow, y);
+            if (p.o_raw) *reinterpret_cast<float2 *>(p.o_raw + orow) = o;
+        }
+    };
+
+    // pre-step of slots [s0, s0 + HALF) of the chunk starting at c0
+    auto prestep = [&](int64_t c0) {
+        const int64_t j0 = c0 + s0;
+        if (j0 >= L) return;
+        const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+        const int c = 2 * lane;
+        const float4 wq0 = *reinterpret_cast<const float4 *>(cw + c * TAPS);
+        const float4 wq1 = *reinterpret_cast<const float4 *>(cw + (c + 1) * TAPS);
+        const float4 wk0 = *reinterpret_cast<const float4 *>(cw + (DK + c) * TAPS);
+        const float4 wk1 = *reinterpret_cast<const float4 *>(cw + (DK + c + 1) * TAPS);
+        const float4 wv0 = *reinterpret_cast<const float4 *>(cw + (2 * DK + c) * TAPS);
+        const float4 wv1 = *reinterpret_cast<const float4 *>(cw + (2 * DK + c + 1) * TAPS);
+        const float2 alog = *reinterpret_cast<const float2 *>(p.A_log + h * DK + c);
+        const float2 dtb = *reinterpret_cast<const float2 *>(p.dt_bias + h * DK + c);
+        const float eA0 = __expf(alog.x), eA1 = __expf(alog.y);
+
+        float2 hq[3], hk[3], hv[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) cx.hist(j0 - 3 + r, hq[r], hk[r], hv[r]);
+
+        const int grp = c >> 4, m0 = c & 15;   // LDS slot of key rows c, c + 1
+#pragma unroll 1
+        for (int sl = 0; sl < HALF; ++sl) {
+            const int64_t j = j0 + sl;
+            if (j >= L) break;
+            float2 xq, xk, xv;
+            cx.hist(j, xq, xk, xv);
+            const float aq0 = silu(conv4(wq0, hq[0].x, hq[1].x, hq[2].x, xq.x));
+            const float aq1 = silu(conv4(wq1, hq[0].y, hq[1].y, hq[2].y, xq.y));
+            const float ak0 = silu(conv4(wk0, hk[0].x, hk[1].x, hk[2].x, xk.x));
+            const float ak1 = silu(conv4(wk1, hk[0].y, hk[1].y, hk[2].y, xk.y));
+            const float av0 = silu(conv4(wv0, hv[0].x, hv[1].x, hv[2].x, xv.x));
+            const float av1 = silu(conv4(wv1, hv[0].y, hv[1].y, hv[2].y, xv.y));
+            hq[0] = hq[1]; hq[1] = hq[2]; hq[2] = xq;
+            hk[0] = hk[1]; hk[1] = hk[2]; hk[2] = xk;
+            hv[0] = hv[1]; hv[1] = hv[2]; hv[2] = xv;
+
+            const float qq = sum64(aq0 * aq0 + aq1 * aq1);
+            const float kk = sum64(ak0 * ak0 + ak1 * ak1);
+            const float qk = sum64(aq0 * ak0 + aq1 * ak1);
+            const float rq = rsqrtf(qq + p.l2_eps), rk = rsqrtf(kk + p.l2_eps);
+
+            const int64_t trow = (rng.lo + j) * p.H + h;
+            const float2 fv = *reinterpret_cast<const float2 *>(p.f + trow * DK + c);
+            const float al0 = decay(fv.x, eA0, dtb.x, p.gate_mode, p.lb);
+            const float al1 = decay(fv.y, eA1, dtb.y, p.gate_mode, p.lb);
+            const float kh0 = ak0 * rk, kh1 = ak1 * rk;
+            const float qh0 = aq0 * rq, qh1 = aq1 * rq;
+
+            const int slot = s0 + sl;
+            s_dot[slot][grp * RGS + m0] = make_float2(al0 * kh0, al0 * qh0);
+            s_dot[slot][grp * RGS + m0 + 1] = make_float2(al1 * kh1, al1 * qh1);
+            s_upd[slot][grp * RGS + m0] = make_float2(al0, kh0);
+            s_upd[slot][grp * RGS + m0 + 1] = make_float2(al1, kh1);
+            *reinterpret_cast<float2 *>(&s_col[slot][c]) = make_float2(av0, av1);
+            if (lane == 0) s_tok[slot] = make_float2(p.beta[trow], qk * rq * rk);
+        }
+    };
+
+#pragma unroll 1
+    for (int64_t c0 = 0; c0 < L; c0 += TC) {
+        const int nv = (int)((L - c0) < TC ? (L - c0) : TC);
+        if (c0 > 0) epilogue(c0 - TC, TC);
+        prestep(c0);
+        __syncthreads();
+
+#pragma unroll 1
+        for (int t = 0; t < nv; ++t) {
+            const float2 bt = s_tok[t];
+            float u[8], pq[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) { u[c] = 0.f; pq[c] = 0.f; }
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const float2 rd = s_dot[t][rg * RGS + m];   // (alpha k_hat, alpha q_hat)
+                u[0] += s[m][0].x * rd.x; u[1] += s[m][0].y * rd.x;
+                u[2] += s[m][0].z * rd.x; u[3] += s[m][0].w * rd.x;
+                u[4] += s[m][1].x * rd.x; u[5] += s[m][1].y * rd.x;
+                u[6] += s[m][1].z * rd.x; u[7] += s[m][1].w * rd.x;
+                pq[0] += s[m][0].x * rd.y; pq[1] += s[m][0].y * rd.y;
+                pq[2] += s[m][0].z * rd.y; pq[3] += s[m][0].w * rd.y;
+                pq[4] += s[m][1].x * rd.y; pq[5] += s[m][1].y * rd.y;
+                pq[6] += s[m][1].z * rd.y; pq[7] += s[m][1].w * rd.y;
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) { u[c] = sum8(u[c]); pq[c] = sum8(pq[c]); }
+
+            const float4 v0 = *reinterpret_cast<const float4 *>(&s_col[t][8 * cg]);
+            const float4 v1 = *reinterpret_cast<const float4 *>(&s_col[t][8 * cg + 4]);
+            const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            float d[8], o[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                d[c] = bt.x * (vv[c] - u[c]);
+                o[c] = pq[c] + bt.y * d[c];
+            }
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                // decay in place, then the rank-1 FMA into the same register (this
+                // order lets the state keep its registers across iterations)
+                const float2 rd = s_upd[t][rg * RGS + m];   // (alpha, k_hat)
+                s[m][0].x = __builtin_fmaf(rd.y, d[0], s[m][0].x * rd.x);
+                s[m][0].y = __builtin_fmaf(rd.y, d[1], s[m][0].y * rd.x);
+                s[m][0].z = __builtin_fmaf(rd.y, d[2], s[m][0].z * rd.x);
+                s[m][0].w = __builtin_fmaf(rd.y, d[3], s[m][0].w * rd.x);
+                s[m][1].x = __builtin_fmaf(rd.y, d[4], s[m][1].x * rd.x);
+                s[m][1].y = __builtin_fmaf(rd.y, d[5], s[m][1].y * rd.x);
+                s[m][1].z = __builtin_fmaf(rd.y, d[6], s[m][1].z * rd.x);
+                s[m][1].w = __builtin_fmaf(rd.y, d[7], s[m][1].w * rd.x);
+            }
+            if (rg == 0) {
+                *reinterpret_cast<float4 *>(&s_col[t][8 * cg]) = make_float4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<float4 *>(&s_col[t][8 * cg + 4]) = make_float4(o[4], o[5], o[6], o[7]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // epilogue of the last chunk
+    const int64_t last = ((L - 1) / TC) * TC;
+    epilogue(last, (int)(L - last));
+
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        float *dst = S + (16 * rg + m) * DV + 8 * cg;
+        *reinterpret_cast<float4 *>(dst) = s[m][0];
+        *reinterpret_cast<float4 *>(dst + 4) = s[m][1];
+    }
+
+    // window out: the last PAST raw rows (old window rows when L < PAST).
+    // Only wavefront 0 touches the window; it reads all three sources before
+    // writing, and wavefront 1 finished its last read of the window (phase P)
+    // before the final barrier of the loop.
+    if (wave == 0) {
+        float2 xq[3], xk[3], xv[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) cx.hist(L - 3 + r, xq[r], xk[r], xv[r]);
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            float *wr = Wout + r * CH + 2 * lane;
+            *reinterpret_cast<float2 *>(wr) = xq[r];
+            *reinterpret_cast<float2 *>(wr + DK) = xk[r];
+            *reinterpret_cast<float2 *>(wr + 2 * DK) = xv[r];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const Params &p, bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.H)), block(PF_THREADS);
+    if (bf16)
+        hipLaunchKernelGGL(prefill_kernel<BF16>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(prefill_kernel<F32>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,205 @@
+"""Python binding of libkda (ctypes).  Argument marshalling only: every step
+of the computation runs in the HIP kernels behind the C ABI in include/kda.h.
+
+``kda_token_step`` and ``kda_sequence`` take torch tensors that already live
+on the GPU, check their shapes and dtypes, and call the C entry points of the
+same names on the current (or given) torch stream.  A non-OK status raises
+``KdaError``; nothing computes on the CPU, and a missing ``libkda.so`` raises
+at import of the library rather than falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import threading
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE, KDA_ERR_LAUNCH = 0, -1, -2, -3, -4
+KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_BOUNDED, KDA_GATE_LITERAL, KDA_GATE_RAW = 0, 1, 2
+DK = DV = 128
+TAPS = 4
+CH = 2 * DK + DV
+
+
+class kda_config(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32), ("conv_taps", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+                ("gate_lower_bound", ctypes.c_float), ("l2_eps", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
+
+
+TENSOR_FIELDS = ("q", "k", "v", "f", "beta", "g", "conv_w", "A_log", "dt_bias", "gamma",
+                 "state", "conv_win", "y", "o_raw")
+
+
+class kda_tensors(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in TENSOR_FIELDS]
+
+
+EXPORTS = ("kda_token_step", "kda_sequence", "kda_status_string", "kda_version",
+           "kda_device_check")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError("libkda.so is not built (expected at %s); run "
+                                  "__graft_entry__.build() first" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            cfgp, tp = ctypes.POINTER(kda_config), ctypes.POINTER(kda_tensors)
+            L.kda_token_step.restype = ctypes.c_int32
+            L.kda_token_step.argtypes = [cfgp, tp, ctypes.c_int32, ctypes.c_void_p]
+            L.kda_sequence.restype = ctypes.c_int32
+            L.kda_sequence.argtypes = [cfgp, tp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p]
+            L.kda_status_string.restype = ctypes.c_char_p
+            L.kda_status_string.argtypes = [ctypes.c_int32]
+            L.kda_version.restype = ctypes.c_int32
+            L.kda_version.argtypes = []
+            L.kda_device_check.restype = ctypes.c_int32
+            L.kda_device_check.argtypes = []
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+@dataclasses.dataclass
+class KdaConfig:
+    num_heads: int
+    act_dtype: int = KDA_F32
+    gate_mode: int = KDA_GATE_BOUNDED
+    gate_lower_bound: float = -5.0
+    l2_eps: float = 1e-6
+    rms_eps: float = 1e-6
+    head_dim_k: int = DK
+    head_dim_v: int = DV
+    conv_taps: int = TAPS
+
+    def to_c(self) -> kda_config:
+        return kda_config(self.num_heads, self.head_dim_k, self.head_dim_v, self.conv_taps,
+                          self.act_dtype, self.gate_mode, self.gate_lower_bound,
+                          self.l2_eps, self.rms_eps)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensors(cfg: KdaConfig, T: int, N: int, ts: dict) -> None:
+    import torch
+    act = torch.bfloat16 if cfg.act_dtype == KDA_BF16 else torch.float32
+    H = cfg.num_heads
+    dk, dv = cfg.head_dim_k, cfg.head_dim_v
+    C = 2 * dk + dv
+    expect = {
+        "q": ((T, H, dk), act), "k": ((T, H, dk), act), "v": ((T, H, dv), act),
+        "f": ((T, H, dk), torch.float32), "beta": ((T, H), torch.float32),
+        "g": ((T, H, dv), act), "conv_w": ((H, C, cfg.conv_taps), torch.float32),
+        "A_log": ((H, dk), torch.float32), "dt_bias": ((H, dk), torch.float32),
+        "gamma": ((dv,), torch.float32), "state": ((N, H, dk, dv), torch.float32),
+        "conv_win": ((N, H, cfg.conv_taps - 1, C), torch.float32),
+        "y": ((T, H, dv), act), "o_raw": ((T, H, dv), torch.float32),
+    }
+    dev = None
+    for name, (shape, dtype) in expect.items():
+        t = ts.get(name)
+        if t is None:
+            if name == "o_raw":
+                continue
+            raise ValueError("missing tensor %r" % name)
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+        if t.dtype != dtype:
+            raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _tensors_struct(ts: dict) -> kda_tensors:
+    return kda_tensors(*[_ptr(ts.get(name)) for name in TENSOR_FIELDS])
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def kda_token_step(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bias, gamma,
+                   state, conv_win, y, o_raw=None, stream=None, check: bool = True) -> None:
+    """Decode one token for each of N = q.shape[0] sequences (C: kda_token_step)."""
+    ts = dict(q=q, k=k, v=v, f=f, beta=beta, g=g, conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
+              gamma=gamma, state=state, conv_win=conv_win, y=y, o_raw=o_raw)
+    N = int(q.shape[0])
+    if check:
+        _check_tensors(config, N, N, ts)
+    c = config.to_c()
+    t = _tensors_struct(ts)
+    st = lib().kda_token_step(ctypes.byref(c), ctypes.byref(t), N, _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_token_step")
+
+
+def kda_sequence(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bias, gamma,
+                 state, conv_win, y, o_raw=None, cu_seqlens=None, seq_order=None,
+                 num_seqs: Optional[int] = None, stream=None, check: bool = True) -> None:
+    """Prefill over packed sequences (C: kda_sequence).
+
+    cu_seqlens: int32 GPU tensor [N+1] of token offsets, or None for a dense
+    batch (N = state.shape[0] sequences of T / N tokens).  seq_order: optional
+    int32 GPU tensor [N], the scheduling order of the sequences."""
+    import torch
+    ts = dict(q=q, k=k, v=v, f=f, beta=beta, g=g, conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
+              gamma=gamma, state=state, conv_win=conv_win, y=y, o_raw=o_raw)
+    T = int(q.shape[0])
+    N = int(state.shape[0]) if num_seqs is None else int(num_seqs)
+    if check:
+        _check_tensors(config, T, N, ts)
+        for name, a, n in (("cu_seqlens", cu_seqlens, N + 1), ("seq_order", seq_order, N)):
+            if a is None:
+                continue
+            if not a.is_cuda or a.dtype != torch.int32 or tuple(a.shape) != (n,) or not a.is_contiguous():
+                raise ValueError("%s must be a contiguous int32 GPU tensor of shape (%d,)" % (name, n))
+    c = config.to_c()
+    t = _tensors_struct(ts)
+    st = lib().kda_sequence(ctypes.byref(c), ctypes.byref(t), N, _ptr(cu_seqlens), _ptr(seq_order),
+                            T, _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_sequence")
+
+
+def device_check() -> int:
+    return int(lib().kda_device_check())
+
+
+def version() -> int:
+    return int(lib().kda_version())

@@ -219,11 +219,14 @@ def make_workload(name: str, *, seed: int, N: int, H: int, lengths=None,
     beta = (1.0 / (1.0 + np.exp(-bl.astype(np.float64)))).astype(np.float32)
     d = _uniform(ss_decay, (T, H, dk), decay[0], decay[1])
     f = np.empty_like(d)
-    # invert the gate head by head (A_log, dt_bias broadcast over tokens)
-    step = max(1, _BLOCK // max(1, H * dk))
-    for lo in range(0, T, step):
+    # invert the gate over blocks of tokens (A_log, dt_bias broadcast over tokens)
+    step = max(1, (_BLOCK // 4) // max(1, H * dk))
+
+    def inv(lo):
         hi = min(T, lo + step)
         f[lo:hi] = _decay_to_f(d[lo:hi], A_log[None], dt_bias[None], gate_mode, lower_bound)
+    with _cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(inv, range(0, T, step)))
     del d
 
     if fresh_prob is not None:
@@ -310,3 +313,38 @@ def subset(w: Workload, seqs, heads) -> Workload:
         dt_bias=np.ascontiguousarray(w.dt_bias[heads]),
         state0=np.ascontiguousarray(w.state0[seqs][:, heads]),
         win0=np.ascontiguousarray(w.win0[seqs][:, heads]))
+
+
+def to_device(w: Workload, device="cuda:0", *, with_o_raw: bool = True, decode_step: Optional[int] = None):
+    """Device tensors for a workload (torch; plumbing only).
+
+    Returns a dict with the kda_sequence / kda_token_step keyword tensors plus
+    'cu_seqlens' (int32).  bf16 workloads get bf16 q, k, v, g and y.  For a
+    decode workload, decode_step=None uploads every step's rows ([steps*N, ...],
+    step-major); an integer uploads that step only."""
+    import torch
+    act = torch.bfloat16 if w.act_dtype == "bf16" else torch.float32
+
+    def tok(a):
+        if w.decode_steps and decode_step is not None:
+            a = a[decode_step * w.N:(decode_step + 1) * w.N]
+        return a
+
+    def up_act(a):
+        a = tok(a)
+        if w.act_dtype == "bf16":
+            return torch.from_numpy(bf16_bits(a)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    def up32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    q = up_act(w.q)
+    T = q.shape[0]
+    d = dict(q=q, k=up_act(w.k), v=up_act(w.v), f=up32(tok(w.f)), beta=up32(tok(w.beta)),
+             g=up_act(w.g), conv_w=up32(w.conv_w), A_log=up32(w.A_log), dt_bias=up32(w.dt_bias),
+             gamma=up32(w.gamma), state=up32(w.state0), conv_win=up32(w.win0),
+             y=torch.empty((T, w.H, w.dv), dtype=act, device=device),
+             o_raw=torch.empty((T, w.H, w.dv), dtype=torch.float32, device=device) if with_o_raw else None)
+    d["cu_seqlens"] = torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(device)
+    return d
