@@ -37,7 +37,8 @@
  *   state [N, H, 128, 128] fp32, row index = key channel, in/out
  *   conv_win [N, H, 3, 384] fp32, in/out
  *   o_raw [T, H, 128] fp32, optional (the pre-norm readout; test hook)
- * Every pointer must be 16-byte aligned.  q, k, v, f, beta, g, conv_w, A_log,
+ * Every pointer must be 16-byte aligned, except beta (4-byte aligned, so that
+ * one decode step's rows can be a slice of a longer run).  q, k, v, f, beta, g, conv_w, A_log,
  * dt_bias and gamma must not overlap y, o_raw, state or conv_win.
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer after
@@ -122,7 +123,8 @@ typedef struct kda_tensors {
 /*
  * Decode: one token for each of num_seqs sequences (T = num_seqs, token row
  * n belongs to sequence n).  One kernel launch; each (sequence, head) state
- * is read once and written once.  num_seqs == 0 is a no-op.
+ * is read once and written once.  num_seqs == 0 is a no-op that returns
+ * KDA_OK after checking cfg (the tensor pointers are not inspected).
  * Equivalent to kda_sequence with every sequence of length 1.
  */
 kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
@@ -141,7 +143,9 @@ kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
  *               are scheduled (e.g. longest first).  Must be a permutation of
  *               0..num_seqs-1; entries outside that range are skipped.
  *   total_tokens  T, the number of token rows of q, k, v, f, beta, g, y.
- * Sequences of length 0 leave their state and window unchanged.  State and
+ * Sequences of length 0 leave their state and window unchanged;
+ * total_tokens == 0 is a no-op that returns KDA_OK after checking cfg (the
+ * tensor pointers, which may then be NULL, are not inspected).  State and
  * window are carried in and out, so splitting a sequence across calls gives
  * the same result as one call (up to fp32 rounding order).
  */

@@ -37,7 +37,7 @@ kda_status device_ok() {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-kda_status check_common(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
+kda_status check_config(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
     if (!cfg || !t) return KDA_ERR_INVALID_ARG;
     if (cfg->num_heads <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARG;
     if (cfg->act_dtype != KDA_F32 && cfg->act_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
@@ -46,11 +46,17 @@ kda_status check_common(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (cfg->gate_lower_bound != cfg->gate_lower_bound) return KDA_ERR_INVALID_ARG;
     if (cfg->head_dim_k != kda::DK || cfg->head_dim_v != kda::DV || cfg->conv_taps != kda::TAPS)
         return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+kda_status check_tensors(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
     const void *ins[] = {t->q, t->k, t->v, t->f, t->beta, t->g,
                          t->conv_w, t->A_log, t->dt_bias, t->gamma};
     const void *outs[] = {t->state, t->conv_win, t->y};
+    // beta is read one float at a time: 4-byte alignment suffices for it
     for (const void *ptr : ins)
-        if (!ptr || !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+        if (!ptr || (ptr == t->beta ? (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0 : !aligned16(ptr)))
+            return KDA_ERR_INVALID_ARG;
     for (const void *ptr : outs)
         if (!ptr || !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
     if (t->o_raw && !aligned16(t->o_raw)) return KDA_ERR_INVALID_ARG;
@@ -100,11 +106,13 @@ const char *kda_status_string(int32_t status) {
 }
 
 kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs, void *stream) {
-    kda_status st = check_common(cfg, t, num_seqs);
+    kda_status st = check_config(cfg, t, num_seqs);
+    if (st != KDA_OK) return st;
+    if (num_seqs == 0) return KDA_OK;     // nothing to do; pointers are not inspected
+    st = check_tensors(cfg, t, num_seqs);
     if (st != KDA_OK) return st;
     st = device_ok();
     if (st != KDA_OK) return st;
-    if (num_seqs == 0) return KDA_OK;
     kda::Params p = make_params(cfg, t, num_seqs);
     p.total_tokens = num_seqs;
     p.dense_len = 1;
@@ -115,10 +123,13 @@ kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t, int32_t n
 kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
                         const int32_t *cu_seqlens, const int32_t *seq_order,
                         int64_t total_tokens, void *stream) {
-    kda_status st = check_common(cfg, t, num_seqs);
+    kda_status st = check_config(cfg, t, num_seqs);
     if (st != KDA_OK) return st;
     if (total_tokens < 0) return KDA_ERR_INVALID_ARG;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARG;
+    if (total_tokens == 0) return KDA_OK; // every sequence is empty; pointers are not inspected
+    st = check_tensors(cfg, t, num_seqs);
+    if (st != KDA_OK) return st;
     if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) ||
         (seq_order && (reinterpret_cast<uintptr_t>(seq_order) & 3u)))
         return KDA_ERR_INVALID_ARG;
@@ -132,7 +143,6 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (total_tokens > (int64_t(1) << 40) / ((int64_t)cfg->num_heads * kda::DK)) return KDA_ERR_INVALID_ARG;
     st = device_ok();
     if (st != KDA_OK) return st;
-    if (num_seqs == 0 || total_tokens == 0) return KDA_OK;
     kda::Params p = make_params(cfg, t, num_seqs);
     p.cu_seqlens = cu_seqlens;
     p.seq_order = seq_order;
