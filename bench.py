@@ -227,6 +227,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-overcache", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="profiling runs: 'decode' or 'prefill:<workload index>' alone, no baselines")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times (torch copy "
+                         "kernel of known size, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,6 +257,28 @@ def main():
 
     N, H = 64, 32
     steps, warmup = max(1, args.steps), max(0, args.warmup)
+
+    if args.only:
+        out = {"only": args.only}
+        if args.only == "decode":
+            dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup)
+            out["us_per_step"] = dec["ms_total"] / steps * 1e3
+        elif args.only.startswith("prefill:"):
+            r = bench_prefill(torch, kda, synth, dev, int(args.only.split(":")[1]), args.prefill_runs)
+            out.update(r)
+        else:
+            raise SystemExit("unknown --only %r" % args.only)
+        if args.copy_calibration_mib:
+            nbytes = args.copy_calibration_mib << 20
+            src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            out["copy_calibration_bytes_each_way"] = nbytes
+        print(json.dumps(out), flush=True)
+        return
     log("decode %dx%d: generating %d steps of inputs" % (N, H, steps))
     dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup)
     ms_step = dec["ms_total"] / steps

@@ -4,10 +4,10 @@
 // The step is HBM-bound: per (sequence, head) it must stream the 64 KiB fp32
 // state in and 64 KiB out, against ~115 K flops.  So the design is about the
 // memory stream:
-//   * one 256-thread workgroup per (sequence, head); the 128 x 128 state is
-//     held in registers, 64 floats per thread (16 rows x 4 columns), loaded
-//     with 16 coalesced 16-byte loads issued before any other work, so the
-//     whole 64 KiB is in flight while the pre-step runs;
+//   * one workgroup of NT threads per (sequence, head); the 128 x 128 state is
+//     held in registers (16384 / NT floats per thread), loaded with coalesced
+//     16-byte loads issued before any other work, so the whole 64 KiB is in
+//     flight while the pre-step runs;
 //   * the pre-step (conv4 + SiLU, window shift, L2 norms, decay) runs from
 //     the raw inputs while those loads are outstanding;
 //   * one pass over the registers gives both dot products the step needs,
@@ -18,19 +18,58 @@
 //   * the update is written back in place with 16-byte stores; the RMSNorm +
 //     sigmoid gate epilogue needs only a 32-lane reduction.
 //
-// Thread layout: tid = 32 * rg + cg.  Thread (rg, cg) owns rows rg + 8 m
-// (m = 0..15) and columns 4 cg .. 4 cg + 3.  A wavefront covers two adjacent
-// rows per load instruction: 1 KiB contiguous.
+// Thread layout: tid = 32 * rg + cg.  Thread (rg, cg) owns rows rg + NRG m
+// (m = 0 .. 128 / NRG - 1, NRG = NT / 32 row groups) and columns 4 cg ..
+// 4 cg + 3.  A wavefront covers two adjacent rows per load instruction: 1 KiB
+// contiguous.
 #include "kda_device.hpp"
 
 namespace kda {
 
 namespace {
 
-constexpr int DEC_THREADS = 256;
+template <int NT>
+struct DecodeShape {
+    static constexpr int NW = NT / 64;        // wavefronts
+    static constexpr int NRG = NT / 32;       // row groups
+    static constexpr int RPT = DK / NRG;      // rows per thread
+    static_assert(NT == 128 || NT == 256 || NT == 512, "decode workgroup size");
+};
 
-template <typename Act>
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(Params p) {
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NTMP>
+__device__ __forceinline__ float4 ld_state(const float *p) {
+    if constexpr (NTMP) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+}
+
+template <bool NTMP>
+__device__ __forceinline__ void st_state(float *p, float4 v) {
+    if constexpr (NTMP) {
+        const f32x4 w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p));
+    } else {
+        *reinterpret_cast<float4 *>(p) = v;
+    }
+}
+
+// Row owned by row group rg at step m: interleaved (rg + NRG m: one load
+// instruction of a wavefront covers two adjacent rows) or blocked (RPT rg + m:
+// a wavefront's loads cover one contiguous 2 * RPT-row region).
+template <int NT, bool BLOCKED>
+__device__ __forceinline__ int dec_row(int rg, int m) {
+    using Sh = DecodeShape<NT>;
+    return BLOCKED ? Sh::RPT * rg + m : rg + Sh::NRG * m;
+}
+
+template <typename Act, int NT, bool NT_LOAD, bool NT_STORE, bool BLOCKED = false>
+__global__ __launch_bounds__(NT) void decode_kernel(Params p) {
+    using Sh = DecodeShape<NT>;
     const int unit = blockIdx.x;           // n * H + h == token row of sequence n
     const int h = unit % p.H;
     const int tid = threadIdx.x;
@@ -39,68 +78,75 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(Params p) {
 
     __shared__ float s_act[CH];            // activated q | k | v of this token
     __shared__ float s_alpha[DK];
-    __shared__ float s_red[4][4];          // per-wave partial sums (qq, kk, qk)
-    __shared__ float4 s_up[4][32][2];      // per-wave partial u, p per column group
+    __shared__ float s_red[Sh::NW][4];     // per-wave partial sums (qq, kk, qk)
+    __shared__ float4 s_up[Sh::NW][32][2]; // per-wave partial u, p per column group
 
     float *S = p.state + (int64_t)unit * (DK * DV);
 
     // ---- 1. put the whole state in flight
-    float4 s[16];
+    float4 s[Sh::RPT];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        s[m] = *reinterpret_cast<const float4 *>(S + (rg + 8 * m) * DV + 4 * cg);
+    for (int m = 0; m < Sh::RPT; ++m)
+        s[m] = ld_state<NT_LOAD>(S + dec_row<NT, BLOCKED>(rg, m) * DV + 4 * cg);
 
-    // ---- 2. pre-step from the raw inputs
+    // ---- 2. pre-step from the raw inputs: task i < 128 is the (q_i, k_i)
+    // channel pair, task 128 + j the v channel j and the decay of key channel j
     float *W = p.win + (int64_t)unit * (PAST * CH);
     const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
     const int64_t row = (int64_t)unit * DK;   // DK == DV
-    if (tid < DK) {
-        // q channel i and k channel i
-        const int i = tid;
-        const float xq = Act::load1(p.q, row + i);
-        const float xk = Act::load1(p.k, row + i);
-        const float4 wq = *reinterpret_cast<const float4 *>(cw + i * TAPS);
-        const float4 wk = *reinterpret_cast<const float4 *>(cw + (DK + i) * TAPS);
-        const float q0 = W[i], q1 = W[CH + i], q2 = W[2 * CH + i];
-        const float k0 = W[DK + i], k1 = W[CH + DK + i], k2 = W[2 * CH + DK + i];
-        const float aq = silu(wq.x * q0 + wq.y * q1 + wq.z * q2 + wq.w * xq);
-        const float ak = silu(wk.x * k0 + wk.y * k1 + wk.z * k2 + wk.w * xk);
-        W[i] = q1; W[CH + i] = q2; W[2 * CH + i] = xq;
-        W[DK + i] = k1; W[CH + DK + i] = k2; W[2 * CH + DK + i] = xk;
-        s_act[i] = aq;
-        s_act[DK + i] = ak;
-        const float qq = sum64(aq * aq), kk = sum64(ak * ak), qk = sum64(aq * ak);
-        if (lane == 0) { s_red[wave][0] = qq; s_red[wave][1] = kk; s_red[wave][2] = qk; }
-    } else {
-        // v channel j, and the decay of key channel j
-        const int j = tid - DK;
-        const float xv = Act::load1(p.v, row + j);
-        const float4 wv = *reinterpret_cast<const float4 *>(cw + (2 * DK + j) * TAPS);
-        const float v0 = W[2 * DK + j], v1 = W[CH + 2 * DK + j], v2 = W[2 * CH + 2 * DK + j];
-        s_act[2 * DK + j] = silu(wv.x * v0 + wv.y * v1 + wv.z * v2 + wv.w * xv);
-        W[2 * DK + j] = v1; W[CH + 2 * DK + j] = v2; W[2 * CH + 2 * DK + j] = xv;
-        const float expA = __expf(p.A_log[h * DK + j]);
-        s_alpha[j] = decay(p.f[row + j], expA, p.dt_bias[h * DK + j], p.gate_mode, p.lb);
+    float qq = 0.f, kk = 0.f, qk = 0.f;
+#pragma unroll
+    for (int task = tid; task < 2 * DK; task += NT) {
+        if (task < DK) {
+            const int i = task;
+            const float xq = Act::load1(p.q, row + i);
+            const float xk = Act::load1(p.k, row + i);
+            const float4 wq = *reinterpret_cast<const float4 *>(cw + i * TAPS);
+            const float4 wk = *reinterpret_cast<const float4 *>(cw + (DK + i) * TAPS);
+            const float q0 = W[i], q1 = W[CH + i], q2 = W[2 * CH + i];
+            const float k0 = W[DK + i], k1 = W[CH + DK + i], k2 = W[2 * CH + DK + i];
+            const float aq = silu(wq.x * q0 + wq.y * q1 + wq.z * q2 + wq.w * xq);
+            const float ak = silu(wk.x * k0 + wk.y * k1 + wk.z * k2 + wk.w * xk);
+            W[i] = q1; W[CH + i] = q2; W[2 * CH + i] = xq;
+            W[DK + i] = k1; W[CH + DK + i] = k2; W[2 * CH + DK + i] = xk;
+            s_act[i] = aq;
+            s_act[DK + i] = ak;
+            qq += aq * aq; kk += ak * ak; qk += aq * ak;
+        } else {
+            const int j = task - DK;
+            const float xv = Act::load1(p.v, row + j);
+            const float4 wv = *reinterpret_cast<const float4 *>(cw + (2 * DK + j) * TAPS);
+            const float v0 = W[2 * DK + j], v1 = W[CH + 2 * DK + j], v2 = W[2 * CH + 2 * DK + j];
+            s_act[2 * DK + j] = silu(wv.x * v0 + wv.y * v1 + wv.z * v2 + wv.w * xv);
+            W[2 * DK + j] = v1; W[CH + 2 * DK + j] = v2; W[2 * CH + 2 * DK + j] = xv;
+            const float expA = __expf(p.A_log[h * DK + j]);
+            s_alpha[j] = decay(p.f[row + j], expA, p.dt_bias[h * DK + j], p.gate_mode, p.lb);
+        }
     }
+    qq = sum64(qq); kk = sum64(kk); qk = sum64(qk);
+    if (lane == 0) { s_red[wave][0] = qq; s_red[wave][1] = kk; s_red[wave][2] = qk; }
     __syncthreads();
 
-    const float rq = rsqrtf(s_red[0][0] + s_red[1][0] + p.l2_eps);
-    const float rk = rsqrtf(s_red[0][1] + s_red[1][1] + p.l2_eps);
-    const float qk = (s_red[0][2] + s_red[1][2]) * rq * rk;
+    qq = 0.f; kk = 0.f; qk = 0.f;
+#pragma unroll
+    for (int w = 0; w < Sh::NW; ++w) { qq += s_red[w][0]; kk += s_red[w][1]; qk += s_red[w][2]; }
+    const float rq = rsqrtf(qq + p.l2_eps);
+    const float rk = rsqrtf(kk + p.l2_eps);
+    qk *= rq * rk;
     const float b = p.beta[unit];
 
     // ---- 3. one pass: u = S^T (alpha k_hat), p = S^T (alpha q_hat)
     float4 u = make_float4(0.f, 0.f, 0.f, 0.f), pq = u;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int i = rg + 8 * m;
+    for (int m = 0; m < Sh::RPT; ++m) {
+        const int i = dec_row<NT, BLOCKED>(rg, m);
         const float al = s_alpha[i];
         const float ak = al * s_act[DK + i] * rk;
         const float aq = al * s_act[i] * rq;
         u.x += s[m].x * ak; u.y += s[m].y * ak; u.z += s[m].z * ak; u.w += s[m].w * ak;
         pq.x += s[m].x * aq; pq.y += s[m].y * aq; pq.z += s[m].z * aq; pq.w += s[m].w * aq;
     }
-    // the two row groups of this wavefront, then the four wavefronts
+    // the two row groups of this wavefront, then the wavefronts
     u.x += __shfl_xor(u.x, 32); u.y += __shfl_xor(u.y, 32);
     u.z += __shfl_xor(u.z, 32); u.w += __shfl_xor(u.w, 32);
     pq.x += __shfl_xor(pq.x, 32); pq.y += __shfl_xor(pq.y, 32);
@@ -109,7 +155,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(Params p) {
     __syncthreads();
     u = s_up[0][cg][0]; pq = s_up[0][cg][1];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < Sh::NW; ++w) {
         const float4 a = s_up[w][cg][0], c = s_up[w][cg][1];
         u.x += a.x; u.y += a.y; u.z += a.z; u.w += a.w;
         pq.x += c.x; pq.y += c.y; pq.z += c.z; pq.w += c.w;
@@ -121,14 +167,14 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(Params p) {
     d.x = b * (vv.x - u.x); d.y = b * (vv.y - u.y); d.z = b * (vv.z - u.z); d.w = b * (vv.w - u.w);
     o.x = pq.x + qk * d.x; o.y = pq.y + qk * d.y; o.z = pq.z + qk * d.z; o.w = pq.w + qk * d.w;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int i = rg + 8 * m;
+    for (int m = 0; m < Sh::RPT; ++m) {
+        const int i = dec_row<NT, BLOCKED>(rg, m);
         const float al = s_alpha[i];
         const float kh = s_act[DK + i] * rk;
         float4 t;
         t.x = al * s[m].x + kh * d.x; t.y = al * s[m].y + kh * d.y;
         t.z = al * s[m].z + kh * d.z; t.w = al * s[m].w + kh * d.w;
-        *reinterpret_cast<float4 *>(S + i * DV + 4 * cg) = t;
+        st_state<NT_STORE>(S + i * DV + 4 * cg, t);
     }
 
     // ---- 5. RMSNorm over the 128 outputs (32 lanes x 4), gamma, sigmoid gate
@@ -148,15 +194,26 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(Params p) {
     }
 }
 
+template <int NT, bool NT_LOAD, bool NT_STORE, bool BLOCKED = false>
+hipError_t launch_decode_as(const Params &p, bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.num_seqs * p.H)), block(NT);
+    if (bf16)
+        hipLaunchKernelGGL((decode_kernel<BF16, NT, NT_LOAD, NT_STORE, BLOCKED>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<F32, NT, NT_LOAD, NT_STORE, BLOCKED>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
+// Nontemporal state traffic wins at every size measured on MI355X.  Up to
+// the Infinity Cache size the interleaved row order is slightly faster; above
+// it the blocked order streams better (6.3 vs 6.0 TB/s at 1 GiB of state).
 hipError_t launch_decode(const Params &p, bool bf16, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.num_seqs * p.H)), block(DEC_THREADS);
-    if (bf16)
-        hipLaunchKernelGGL(decode_kernel<BF16>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(decode_kernel<F32>, grid, block, 0, stream, p);
-    return hipGetLastError();
+    const int64_t state_bytes = (int64_t)p.num_seqs * p.H * (DK * DV * 4);
+    if (state_bytes > (int64_t(256) << 20))
+        return launch_decode_as<256, true, true, true>(p, bf16, stream);
+    return launch_decode_as<256, true, true, false>(p, bf16, stream);
 }
 
 }  // namespace kda

@@ -1,26 +1,37 @@
 // kda_prefill.hip -- multi-token KDA over dense or ragged (cu_seqlens) batches,
 // with state and conv window carried in and out.
 //
-// In the recurrent form every token costs 4 VALU operations per state element
-// (u and p dot products, decay multiply, rank-1 FMA) against almost no memory
-// traffic, so the kernel is built around keeping the state resident and the
-// VALU busy:
+// In the recurrent form every token touches every state element a few times
+// (two dot products and the update) against almost no memory traffic, so the
+// kernel is built around keeping the state resident and the VALU busy:
 //   * one 128-thread workgroup (two wavefronts) per (sequence, head); the
 //     128 x 128 fp32 state lives in registers for the whole token run,
 //     128 floats per lane: lane (rg, cg) holds rows 16 rg .. 16 rg + 15 and
 //     columns 8 cg .. 8 cg + 7, with rg in the low 3 lane bits so the
 //     reductions over rows are 3 DPP steps inside a group of 8 lanes;
-//   * tokens run in chunks of TC.  Per chunk, phase P computes the pre-step
-//     (conv4 + SiLU with a rolling window, L2 norms, decay, beta, q.k) for
-//     all TC tokens in parallel -- it depends only on inputs -- and writes
-//     per-row values (alpha k_hat, alpha q_hat) and (alpha, k_hat) and per-column
-//     v to LDS; phase R runs the serial recurrence over the chunk reading
-//     those values as LDS broadcasts; the RMSNorm + gate epilogue of a chunk
-//     runs token-parallel in the next phase P, off the serial chain;
+//   * tokens run in chunks of TC.  Per chunk, phase P computes everything
+//     that depends only on inputs, in parallel over the chunk: the conv4 +
+//     SiLU pre-step and L2 norms token by token (one wavefront per token),
+//     and the decays key row by key row (one thread per row); phase Q
+//     combines them into per-row coefficients in LDS; phase R runs the serial
+//     recurrence reading those as LDS broadcasts; the RMSNorm + gate epilogue
+//     of a chunk runs token-parallel in the next phase P, off the serial chain;
 //   * the readout uses the pre-update state, o = S^T(alpha q) + beta (q.k)
 //     (v - u), so one read of the registers feeds both dot products
 //     ("Kimi K3 Metal Gap Analysis", §2, rows "Recurrence" and
 //     "O projection", expanded).
+//
+// Decay folding (FOLD = true).  Inside a chunk the registers hold
+// X_t = D_t^{-1} S_t, with D_t = Diag(alpha_1 ... alpha_t) the decay
+// accumulated since the chunk start.  Then
+//     u_t = X_{t-1}^T (D_t k),  p_t = X_{t-1}^T (D_t q),
+//     X_t = X_{t-1} + (D_t^{-1} k) delta_t^T,
+// so each state element costs 3 FMAs per token instead of 4 operations, and
+// S = D X is restored once per chunk.  Rounding is of the same size as in the
+// direct form (every product has the same magnitude once the D factors are
+// applied).  It needs D_t to stay well inside fp32 range, which holds when
+// the decay is bounded below: the bounded gate with lb * TC >= -60.  Other
+// gate forms (unbounded log-decay) take the direct form.
 #include "kda_device.hpp"
 
 namespace kda {
@@ -31,6 +42,7 @@ constexpr int PF_THREADS = 128;
 constexpr int TC = 8;              // tokens per chunk
 constexpr int HALF = TC / 2;       // chunk slots handled by each wavefront in phase P
 constexpr int RGS = 17;            // LDS slots per row group: 16 key rows + 1 pad (bank spread)
+constexpr float FOLD_MIN_LOG_DECAY = -60.0f;   // lowest chunk log-decay the folded form accepts
 
 struct Range {
     int64_t lo, len;
@@ -78,8 +90,12 @@ __device__ __forceinline__ float conv4(float4 w, float a, float b, float c, floa
     return w.x * a + w.y * b + w.z * c + w.w * x;
 }
 
-template <typename Act>
-__global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(Params p) {
+// LDS slot of key row i in the padded row-group layout
+__device__ __forceinline__ int row_slot(int i) { return (i >> 4) * RGS + (i & 15); }
+
+template <typename Act, bool FOLD>
+__global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(Params p) {
     const int slot_n = blockIdx.x / p.H;
     const int h = blockIdx.x - slot_n * p.H;
     int n = slot_n;
@@ -97,10 +113,15 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     const int cg = wave * 8 + (lane >> 3);     // column group: columns 8 cg .. 8 cg + 7
     const int64_t unit = (int64_t)n * p.H + h;
 
-    __shared__ float2 s_dot[TC][8 * RGS];      // (alpha k_hat, alpha q_hat) per key row
-    __shared__ float2 s_upd[TC][8 * RGS];      // (alpha, k_hat) per key row
+    // per-row coefficients for the dot products: FOLD (D k, D q), else (alpha k, alpha q)
+    __shared__ float2 s_dot[TC][8 * RGS];
+    // per-row coefficients for the update: FOLD (k / D, -), else (alpha, k)
+    __shared__ float2 s_upd[TC][8 * RGS];
     __shared__ float s_col[TC][DV];            // activated v, overwritten by the readout o
     __shared__ float2 s_tok[TC];               // (beta, q_hat . k_hat)
+    __shared__ float s_kh[TC][DK];             // k_hat of each chunk token
+    __shared__ float s_qh[TC][DK];             // q_hat of each chunk token
+    __shared__ float s_dec[TC][DK];            // FOLD: D_t (decay since chunk start); else alpha_t
 
     float *S = p.state + unit * (DK * DV);
     float *Wout = p.win + unit * (PAST * CH);
@@ -136,8 +157,9 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
         }
     };
 
-    // pre-step of slots [s0, s0 + HALF) of the chunk starting at c0
-    auto prestep = [&](int64_t c0) {
+    // token pre-step of slots [s0, s0 + HALF) of the chunk starting at c0:
+    // conv4 + SiLU with a rolling window, L2 norms, beta, q.k
+    auto prestep_tokens = [&](int64_t c0) {
         const int64_t j0 = c0 + s0;
         if (j0 >= L) return;
         const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
@@ -148,15 +170,11 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
         const float4 wk1 = *reinterpret_cast<const float4 *>(cw + (DK + c + 1) * TAPS);
         const float4 wv0 = *reinterpret_cast<const float4 *>(cw + (2 * DK + c) * TAPS);
         const float4 wv1 = *reinterpret_cast<const float4 *>(cw + (2 * DK + c + 1) * TAPS);
-        const float2 alog = *reinterpret_cast<const float2 *>(p.A_log + h * DK + c);
-        const float2 dtb = *reinterpret_cast<const float2 *>(p.dt_bias + h * DK + c);
-        const float eA0 = __expf(alog.x), eA1 = __expf(alog.y);
 
         float2 hq[3], hk[3], hv[3];
 #pragma unroll
         for (int r = 0; r < 3; ++r) cx.hist(j0 - 3 + r, hq[r], hk[r], hv[r]);
 
-        const int grp = c >> 4, m0 = c & 15;   // LDS slot of key rows c, c + 1
 #pragma unroll 1
         for (int sl = 0; sl < HALF; ++sl) {
             const int64_t j = j0 + sl;
@@ -178,20 +196,47 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
             const float qk = sum64(aq0 * ak0 + aq1 * ak1);
             const float rq = rsqrtf(qq + p.l2_eps), rk = rsqrtf(kk + p.l2_eps);
 
-            const int64_t trow = (rng.lo + j) * p.H + h;
-            const float2 fv = *reinterpret_cast<const float2 *>(p.f + trow * DK + c);
-            const float al0 = decay(fv.x, eA0, dtb.x, p.gate_mode, p.lb);
-            const float al1 = decay(fv.y, eA1, dtb.y, p.gate_mode, p.lb);
-            const float kh0 = ak0 * rk, kh1 = ak1 * rk;
-            const float qh0 = aq0 * rq, qh1 = aq1 * rq;
-
             const int slot = s0 + sl;
-            s_dot[slot][grp * RGS + m0] = make_float2(al0 * kh0, al0 * qh0);
-            s_dot[slot][grp * RGS + m0 + 1] = make_float2(al1 * kh1, al1 * qh1);
-            s_upd[slot][grp * RGS + m0] = make_float2(al0, kh0);
-            s_upd[slot][grp * RGS + m0 + 1] = make_float2(al1, kh1);
+            *reinterpret_cast<float2 *>(&s_qh[slot][c]) = make_float2(aq0 * rq, aq1 * rq);
+            *reinterpret_cast<float2 *>(&s_kh[slot][c]) = make_float2(ak0 * rk, ak1 * rk);
             *reinterpret_cast<float2 *>(&s_col[slot][c]) = make_float2(av0, av1);
-            if (lane == 0) s_tok[slot] = make_float2(p.beta[trow], qk * rq * rk);
+            if (lane == 0) {
+                const int64_t trow = (rng.lo + j) * p.H + h;
+                s_tok[slot] = make_float2(p.beta[trow], qk * rq * rk);
+            }
+        }
+    };
+
+    // row pre-step of the chunk starting at c0 (thread tid = key row): the
+    // decays of its nv tokens, accumulated from the chunk start when folding
+    const float eA = __expf(p.A_log[h * DK + tid]);
+    const float dtb = p.dt_bias[h * DK + tid];
+    auto prestep_rows = [&](int64_t c0, int nv) {
+        float D = 1.0f;
+#pragma unroll 1
+        for (int t = 0; t < nv; ++t) {
+            const int64_t trow = (rng.lo + c0 + t) * p.H + h;
+            const float al = decay(p.f[trow * DK + tid], eA, dtb, p.gate_mode, p.lb);
+            if constexpr (FOLD) {
+                D *= al;
+                s_dec[t][tid] = D;
+            } else {
+                s_dec[t][tid] = al;
+            }
+        }
+    };
+
+    // phase Q (thread tid = key row): per-row coefficients of the chunk's tokens
+    auto combine_rows = [&](int nv) {
+        const int slot = row_slot(tid);
+#pragma unroll 1
+        for (int t = 0; t < nv; ++t) {
+            const float kh = s_kh[t][tid], qh = s_qh[t][tid], dd = s_dec[t][tid];
+            s_dot[t][slot] = make_float2(dd * kh, dd * qh);
+            if constexpr (FOLD)
+                s_upd[t][slot] = make_float2(kh * fast_rcp(dd), 0.0f);
+            else
+                s_upd[t][slot] = make_float2(dd, kh);
         }
     };
 
@@ -199,7 +244,10 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     for (int64_t c0 = 0; c0 < L; c0 += TC) {
         const int nv = (int)((L - c0) < TC ? (L - c0) : TC);
         if (c0 > 0) epilogue(c0 - TC, TC);
-        prestep(c0);
+        prestep_tokens(c0);
+        prestep_rows(c0, nv);
+        __syncthreads();
+        combine_rows(nv);
         __syncthreads();
 
 #pragma unroll 1
@@ -210,7 +258,7 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
             for (int c = 0; c < 8; ++c) { u[c] = 0.f; pq[c] = 0.f; }
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
-                const float2 rd = s_dot[t][rg * RGS + m];   // (alpha k_hat, alpha q_hat)
+                const float2 rd = s_dot[t][rg * RGS + m];
                 u[0] += s[m][0].x * rd.x; u[1] += s[m][0].y * rd.x;
                 u[2] += s[m][0].z * rd.x; u[3] += s[m][0].w * rd.x;
                 u[4] += s[m][1].x * rd.x; u[5] += s[m][1].y * rd.x;
@@ -232,23 +280,43 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
                 d[c] = bt.x * (vv[c] - u[c]);
                 o[c] = pq[c] + bt.y * d[c];
             }
+            if constexpr (FOLD) {
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
+                for (int m = 0; m < 16; ++m) {
+                    const float ck = s_upd[t][rg * RGS + m].x;   // k_hat / D_t
+                    s[m][0].x += ck * d[0]; s[m][0].y += ck * d[1];
+                    s[m][0].z += ck * d[2]; s[m][0].w += ck * d[3];
+                    s[m][1].x += ck * d[4]; s[m][1].y += ck * d[5];
+                    s[m][1].z += ck * d[6]; s[m][1].w += ck * d[7];
+                }
+            } else {
                 // decay in place, then the rank-1 FMA into the same register (this
                 // order lets the state keep its registers across iterations)
-                const float2 rd = s_upd[t][rg * RGS + m];   // (alpha, k_hat)
-                s[m][0].x = __builtin_fmaf(rd.y, d[0], s[m][0].x * rd.x);
-                s[m][0].y = __builtin_fmaf(rd.y, d[1], s[m][0].y * rd.x);
-                s[m][0].z = __builtin_fmaf(rd.y, d[2], s[m][0].z * rd.x);
-                s[m][0].w = __builtin_fmaf(rd.y, d[3], s[m][0].w * rd.x);
-                s[m][1].x = __builtin_fmaf(rd.y, d[4], s[m][1].x * rd.x);
-                s[m][1].y = __builtin_fmaf(rd.y, d[5], s[m][1].y * rd.x);
-                s[m][1].z = __builtin_fmaf(rd.y, d[6], s[m][1].z * rd.x);
-                s[m][1].w = __builtin_fmaf(rd.y, d[7], s[m][1].w * rd.x);
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const float2 rd = s_upd[t][rg * RGS + m];   // (alpha, k_hat)
+                    s[m][0].x = __builtin_fmaf(rd.y, d[0], s[m][0].x * rd.x);
+                    s[m][0].y = __builtin_fmaf(rd.y, d[1], s[m][0].y * rd.x);
+                    s[m][0].z = __builtin_fmaf(rd.y, d[2], s[m][0].z * rd.x);
+                    s[m][0].w = __builtin_fmaf(rd.y, d[3], s[m][0].w * rd.x);
+                    s[m][1].x = __builtin_fmaf(rd.y, d[4], s[m][1].x * rd.x);
+                    s[m][1].y = __builtin_fmaf(rd.y, d[5], s[m][1].y * rd.x);
+                    s[m][1].z = __builtin_fmaf(rd.y, d[6], s[m][1].z * rd.x);
+                    s[m][1].w = __builtin_fmaf(rd.y, d[7], s[m][1].w * rd.x);
+                }
             }
             if (rg == 0) {
                 *reinterpret_cast<float4 *>(&s_col[t][8 * cg]) = make_float4(o[0], o[1], o[2], o[3]);
                 *reinterpret_cast<float4 *>(&s_col[t][8 * cg + 4]) = make_float4(o[4], o[5], o[6], o[7]);
+            }
+        }
+        if constexpr (FOLD) {
+            // back to the true state: S = D X with the decay of the whole chunk
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const float dd = s_dec[nv - 1][16 * rg + m];
+                s[m][0].x *= dd; s[m][0].y *= dd; s[m][0].z *= dd; s[m][0].w *= dd;
+                s[m][1].x *= dd; s[m][1].y *= dd; s[m][1].z *= dd; s[m][1].w *= dd;
             }
         }
         __syncthreads();
@@ -283,15 +351,21 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     }
 }
 
+template <bool FOLD>
+hipError_t launch_prefill_as(const Params &p, bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.H)), block(PF_THREADS);
+    if (bf16)
+        hipLaunchKernelGGL((prefill_kernel<BF16, FOLD>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<F32, FOLD>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const Params &p, bool bf16, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.H)), block(PF_THREADS);
-    if (bf16)
-        hipLaunchKernelGGL(prefill_kernel<BF16>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(prefill_kernel<F32>, grid, block, 0, stream, p);
-    return hipGetLastError();
+    const bool fold = p.gate_mode == GATE_BOUNDED && p.lb <= 0.0f && p.lb * TC >= FOLD_MIN_LOG_DECAY;
+    return fold ? launch_prefill_as<true>(p, bf16, stream) : launch_prefill_as<false>(p, bf16, stream);
 }
 
 }  // namespace kda

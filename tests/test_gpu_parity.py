@@ -100,6 +100,41 @@ def test_other_gate_modes(gpu, mode):
     _gpu.assert_parity(_gpu.run_decode(wd, gpu), _gpu.oracle_decode(wd), label="gate %d dec" % mode)
 
 
+@pytest.mark.parametrize("lb", [-1.0, -9.0])
+def test_bounded_gate_other_bounds(gpu, lb):
+    # -9 * 8 tokens < -60: outside the range of the folded prefill form, so this
+    # also runs the direct form with the bounded gate
+    lo = 0.4 if lb > -2 else 0.2      # decays the bound can reach: exp(lb) < d < 1
+    w = synth.make_workload("lb", seed=70, N=2, H=2, lengths=[29, 12], lower_bound=lb,
+                            decay=(lo, 0.999), state_std=0.02, win_std=1.0)
+    assert np.all(np.isfinite(w.f))
+    note("bounded gate lb=%g" % lb)
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), label="lb %g" % lb)
+
+
+def test_strong_decay_chunks(gpu):
+    # decays down to exp(-5) every token: the folded form's per-chunk scaling
+    # reaches exp(-40); results must still hold the fp32 bar
+    w = synth.make_workload("strong decay", seed=71, N=1, H=4, lengths=[203], decay=(0.0068, 0.05),
+                            state_std=0.02, win_std=1.0)
+    note("strong decay")
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), label="strong decay")
+
+
+def test_decode_large_state(gpu):
+    # 320 x 32 x 64 KiB = 640 MiB of state: the row order used above the cache size
+    w = synth.workload(1, scale={"N": 320, "H": 32, "steps": 2})
+    note("decode 320x32 (640 MiB state), 2 steps, sampled")
+    full = _gpu.run_decode(w, gpu)
+    sw, ww = _gpu.decode_as_prefill(w)
+    seqs, heads = [0, 199, 319], [1, 30]
+    ref = _gpu.oracle_sequence(synth.subset(sw, seqs, heads))
+    y = full["y"].reshape(2, 320, 32, 128)[:, seqs][:, :, heads]
+    got = {"y": np.ascontiguousarray(y.swapaxes(0, 1)).reshape(-1, len(heads), 128),
+           "state": full["state"][seqs][:, heads], "win": full["win"][seqs][:, heads]}
+    _gpu.assert_parity(got, ref, keys=("y", "state"), label="decode large")
+
+
 # ---------------------------------------------------------------- invariances
 
 def test_split_sequence_and_token_steps_agree(gpu):
