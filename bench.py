@@ -186,10 +186,13 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
     cu = d["cu_seqlens"].data_ptr()
     lens = w.lengths
     order = torch.from_numpy(np.argsort(-lens, kind="stable").astype(np.int32)).to(dev)
+    ws_bytes = kda.sequence_workspace_size(cfg, w.N, w.total_tokens)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_ptr = ws.data_ptr() if ws_bytes > 0 else None
 
     def launch():
         st = L.kda_sequence(ctypes.byref(ccfg), ctypes.byref(t), w.N, cu, order.data_ptr(),
-                            w.total_tokens, stream.cuda_stream)
+                            w.total_tokens, ws_ptr, ws_bytes, stream.cuda_stream)
         if st != 0:
             raise RuntimeError("kda_sequence returned %d" % st)
     times = []

@@ -48,11 +48,13 @@
  * stream) and the call returns at once.  A kernel fault surfaces at the
  * caller's next synchronisation, as for any HIP launch.
  *
- * Errors: a status other than KDA_OK means nothing was enqueued and no
- * buffer was touched, so the caller may run another implementation instead
- * (the pages' fused dispatch checks the return value and falls back to its
- * CPU path: "Metal (Apple GPU) backend for Kimi K3", CPU fallback).  The
- * library itself never computes on the CPU.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED and KDA_ERR_DEVICE mean
+ * nothing was enqueued and no buffer was touched, so the caller may run
+ * another implementation instead (the pages' fused dispatch checks the return
+ * value and falls back to its CPU path: "Metal (Apple GPU) backend for Kimi
+ * K3", CPU fallback).  KDA_ERR_LAUNCH means the HIP runtime refused a launch;
+ * for a call that enqueues several kernels, the ones before it stay enqueued.
+ * The library itself never computes on the CPU.
  *
  * Thread safety: stateless apart from a per-device capability cache; calls
  * on different streams with disjoint buffers may run concurrently.
@@ -91,6 +93,18 @@ typedef enum kda_gate_mode {
     KDA_GATE_RAW = 2            /* gk = f (the caller supplies the log-decay)   */
 } kda_gate_mode;
 
+/* Which prefill kernel kda_sequence runs.  Both compute the same function
+ * (up to fp32 rounding order); AUTO picks by the number of (sequence, head)
+ * pairs.  SPLIT spreads each pair's state columns over several workgroups
+ * (for few pairs, e.g. one long sequence) and needs an fp32 buffer for the
+ * pre-norm readout: o_raw, or else a workspace of the size
+ * kda_sequence_workspace_size reports. */
+typedef enum kda_prefill_path {
+    KDA_PREFILL_AUTO = 0,
+    KDA_PREFILL_FUSED = 1,      /* one workgroup per (sequence, head)        */
+    KDA_PREFILL_SPLIT = 2       /* state columns split across workgroups    */
+} kda_prefill_path;
+
 typedef struct kda_config {
     int32_t num_heads;          /* H >= 1                                    */
     int32_t head_dim_k;         /* dk: must be 128                           */
@@ -101,6 +115,7 @@ typedef struct kda_config {
     float gate_lower_bound;     /* lb, -5 in the pages                       */
     float l2_eps;               /* e.g. 1e-6                                 */
     float rms_eps;              /* e.g. 1e-6                                 */
+    int32_t prefill_path;       /* kda_prefill_path (kda_sequence only)      */
 } kda_config;
 
 typedef struct kda_tensors {
@@ -143,6 +158,8 @@ kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
  *               are scheduled (e.g. longest first).  Must be a permutation of
  *               0..num_seqs-1; entries outside that range are skipped.
  *   total_tokens  T, the number of token rows of q, k, v, f, beta, g, y.
+ *   workspace, workspace_bytes  optional device scratch (see
+ *               kda_sequence_workspace_size); NULL / 0 is always allowed.
  * Sequences of length 0 leave their state and window unchanged;
  * total_tokens == 0 is a no-op that returns KDA_OK after checking cfg (the
  * tensor pointers, which may then be NULL, are not inspected).  State and
@@ -152,7 +169,21 @@ kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
 kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t,
                         int32_t num_seqs, const int32_t *cu_seqlens,
                         const int32_t *seq_order, int64_t total_tokens,
+                        void *workspace, int64_t workspace_bytes,
                         void *stream);
+
+/*
+ * Bytes of device workspace with which kda_sequence runs its faster path for
+ * this shape (num_seqs sequences, total_tokens token rows, cfg->num_heads
+ * heads, cfg->prefill_path); 0 if that path needs none.  A negative value is
+ * a kda_status for bad arguments.  The workspace is needed only when o_raw is
+ * NULL; with a smaller or NULL workspace kda_sequence falls back to the fused
+ * kernel under KDA_PREFILL_AUTO and fails with KDA_ERR_INVALID_ARG under
+ * KDA_PREFILL_SPLIT.  Caller-owned, 16-byte aligned, no initialisation
+ * needed, not kept after the call; its contents are scratch.
+ */
+int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs,
+                                    int64_t total_tokens);
 
 /* Static description of a status code (never NULL). */
 const char *kda_status_string(int32_t status);

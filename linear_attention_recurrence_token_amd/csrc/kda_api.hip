@@ -44,9 +44,20 @@ kda_status check_config(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (cfg->gate_mode < KDA_GATE_BOUNDED || cfg->gate_mode > KDA_GATE_RAW) return KDA_ERR_INVALID_ARG;
     if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
     if (cfg->gate_lower_bound != cfg->gate_lower_bound) return KDA_ERR_INVALID_ARG;
+    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_SPLIT)
+        return KDA_ERR_INVALID_ARG;
     if (cfg->head_dim_k != kda::DK || cfg->head_dim_v != kda::DV || cfg->conv_taps != kda::TAPS)
         return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
+}
+
+// columns per lane of the split prefill for this shape, 0 = fused kernel
+int split_cols_for(const kda_config *cfg, int32_t num_seqs) {
+    const int64_t units = (int64_t)num_seqs * cfg->num_heads;
+    if (cfg->prefill_path == KDA_PREFILL_FUSED) return 0;
+    const int c = kda::prefill_split_cols(units);
+    if (cfg->prefill_path == KDA_PREFILL_SPLIT) return c ? c : 4;
+    return c;
 }
 
 kda_status check_tensors(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
@@ -120,9 +131,20 @@ kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t, int32_t n
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    kda_tensors dummy;
+    std::memset(&dummy, 0, sizeof(dummy));
+    const kda_status st = check_config(cfg, &dummy, num_seqs);
+    if (st != KDA_OK) return st;
+    if (total_tokens < 0) return KDA_ERR_INVALID_ARG;
+    if (num_seqs == 0 || total_tokens == 0 || split_cols_for(cfg, num_seqs) == 0) return 0;
+    return total_tokens * cfg->num_heads * kda::DV * (int64_t)sizeof(float);
+}
+
 kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
                         const int32_t *cu_seqlens, const int32_t *seq_order,
-                        int64_t total_tokens, void *stream) {
+                        int64_t total_tokens, void *workspace, int64_t workspace_bytes,
+                        void *stream) {
     kda_status st = check_config(cfg, t, num_seqs);
     if (st != KDA_OK) return st;
     if (total_tokens < 0) return KDA_ERR_INVALID_ARG;
@@ -141,6 +163,19 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     }
     // row offsets are formed in 64-bit arithmetic; keep them well inside it
     if (total_tokens > (int64_t(1) << 40) / ((int64_t)cfg->num_heads * kda::DK)) return KDA_ERR_INVALID_ARG;
+    if (workspace_bytes < 0 || (workspace && !aligned16(workspace))) return KDA_ERR_INVALID_ARG;
+    // the readout buffer of the split path: o_raw, else a large enough workspace
+    const int cols = split_cols_for(cfg, num_seqs);
+    float *obuf = nullptr;
+    if (cols) {
+        const int64_t need = total_tokens * cfg->num_heads * kda::DV * (int64_t)sizeof(float);
+        if (t->o_raw)
+            obuf = t->o_raw;
+        else if (workspace && workspace_bytes >= need)
+            obuf = static_cast<float *>(workspace);
+        else if (cfg->prefill_path == KDA_PREFILL_SPLIT)
+            return KDA_ERR_INVALID_ARG;
+    }
     st = device_ok();
     if (st != KDA_OK) return st;
     kda::Params p = make_params(cfg, t, num_seqs);
@@ -148,7 +183,10 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     p.seq_order = seq_order;
     p.total_tokens = total_tokens;
     p.dense_len = dense_len;
-    const hipError_t e = kda::launch_prefill(p, cfg->act_dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    const bool bf16 = cfg->act_dtype == KDA_BF16;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = obuf ? kda::launch_prefill_split(p, bf16, obuf, cols, s)
+                              : kda::launch_prefill(p, bf16, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -120,4 +120,27 @@ __device__ __forceinline__ float sum64(float x) {
     return x;
 }
 
+// ------------------------------------------------------------ sequences
+
+struct Range {
+    int64_t lo, len;
+};
+
+// token range of sequence n: from cu_seqlens (clamped to [0, total_tokens)),
+// or the dense layout when cu_seqlens is null
+__device__ __forceinline__ Range seq_range(const Params &p, int n) {
+    Range r;
+    if (p.cu_seqlens) {
+        int64_t a = p.cu_seqlens[n], b = p.cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+        b = b < a ? a : (b > p.total_tokens ? p.total_tokens : b);
+        r.lo = a;
+        r.len = b - a;
+    } else {
+        r.lo = (int64_t)n * p.dense_len;
+        r.len = p.dense_len;
+    }
+    return r;
+}
+
 }  // namespace kda

@@ -37,4 +37,14 @@ struct Params {
 hipError_t launch_decode(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill(const Params &p, bool bf16, hipStream_t stream);
 
+// Column-split prefill for workloads with few (sequence, head) pairs, where
+// one workgroup per pair would leave most of the GPU idle: each pair's state
+// columns are spread over several workgroups, the pre-norm readout goes to
+// obuf ([T, H, 128] fp32), and an epilogue kernel applies RMSNorm + gate and
+// writes the window.  prefill_split_cols returns the columns per lane (1, 2
+// or 4) to use for `units` pairs, or 0 when the fused kernel is the better one.
+int prefill_split_cols(int64_t units);
+hipError_t launch_prefill_split(const Params &p, bool bf16, float *obuf, int cols_per_lane,
+                                hipStream_t stream);
+
 }  // namespace kda

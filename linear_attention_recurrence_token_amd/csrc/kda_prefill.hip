@@ -44,25 +44,6 @@ constexpr int HALF = TC / 2;       // chunk slots handled by each wavefront in p
 constexpr int RGS = 17;            // LDS slots per row group: 16 key rows + 1 pad (bank spread)
 constexpr float FOLD_MIN_LOG_DECAY = -60.0f;   // lowest chunk log-decay the folded form accepts
 
-struct Range {
-    int64_t lo, len;
-};
-
-__device__ __forceinline__ Range seq_range(const Params &p, int n) {
-    Range r;
-    if (p.cu_seqlens) {
-        int64_t a = p.cu_seqlens[n], b = p.cu_seqlens[n + 1];
-        a = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
-        b = b < a ? a : (b > p.total_tokens ? p.total_tokens : b);
-        r.lo = a;
-        r.len = b - a;
-    } else {
-        r.lo = (int64_t)n * p.dense_len;
-        r.len = p.dense_len;
-    }
-    return r;
-}
-
 template <typename Act>
 struct Ctx {
     const void *q, *k, *v;
@@ -137,10 +118,21 @@ void prefill_kernel(Params p) {
 
     const int s0 = wave * HALF;                // this wavefront's chunk slots in phase P
 
+    // Phase P issues every global load of a helper before the first use, so a
+    // chunk pays one memory latency per helper rather than one per token.
+
     // token-parallel epilogue of slots [s0, s0 + HALF) of the chunk starting at c0
     auto epilogue = [&](int64_t c0, int nvalid) {
         const float2 gm = *reinterpret_cast<const float2 *>(p.gamma + 2 * lane);
-#pragma unroll 1
+        float2 gg[HALF];
+#pragma unroll
+        for (int sl = 0; sl < HALF; ++sl) {
+            const int slot = s0 + sl;
+            gg[sl] = slot < nvalid
+                ? Act::load2(p.g, ((rng.lo + c0 + slot) * p.H + h) * DV + 2 * lane)
+                : make_float2(0.f, 0.f);
+        }
+#pragma unroll
         for (int sl = 0; sl < HALF; ++sl) {
             const int slot = s0 + sl;
             if (slot >= nvalid) break;
@@ -148,17 +140,16 @@ void prefill_kernel(Params p) {
             const float ss = sum64(o.x * o.x + o.y * o.y);
             const float r = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
             const int64_t orow = ((rng.lo + c0 + slot) * p.H + h) * DV + 2 * lane;
-            const float2 gg = Act::load2(p.g, orow);
             float2 y;
-            y.x = sigmoid(gg.x) * gm.x * o.x * r;
-            y.y = sigmoid(gg.y) * gm.y * o.y * r;
+            y.x = sigmoid(gg[sl].x) * gm.x * o.x * r;
+            y.y = sigmoid(gg[sl].y) * gm.y * o.y * r;
             Act::store2(p.y, orow, y);
             if (p.o_raw) *reinterpret_cast<float2 *>(p.o_raw + orow) = o;
         }
     };
 
     // token pre-step of slots [s0, s0 + HALF) of the chunk starting at c0:
-    // conv4 + SiLU with a rolling window, L2 norms, beta, q.k
+    // conv4 + SiLU over the raw rows j0 - 3 .. j0 + HALF - 1, L2 norms, beta, q.k
     auto prestep_tokens = [&](int64_t c0) {
         const int64_t j0 = c0 + s0;
         if (j0 >= L) return;
@@ -171,25 +162,30 @@ void prefill_kernel(Params p) {
         const float4 wv0 = *reinterpret_cast<const float4 *>(cw + (2 * DK + c) * TAPS);
         const float4 wv1 = *reinterpret_cast<const float4 *>(cw + (2 * DK + c + 1) * TAPS);
 
-        float2 hq[3], hk[3], hv[3];
+        float2 xq[PAST + HALF], xk[PAST + HALF], xv[PAST + HALF];
+        float bta[HALF];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) cx.hist(j0 - 3 + r, hq[r], hk[r], hv[r]);
+        for (int r = 0; r < PAST + HALF; ++r) {
+            const int64_t j = j0 - PAST + r;
+            if (j < L) {
+                cx.hist(j, xq[r], xk[r], xv[r]);
+            } else {
+                xq[r] = xk[r] = xv[r] = make_float2(0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < HALF; ++sl)
+            bta[sl] = (lane == 0 && j0 + sl < L) ? p.beta[(rng.lo + j0 + sl) * p.H + h] : 0.f;
 
-#pragma unroll 1
+#pragma unroll
         for (int sl = 0; sl < HALF; ++sl) {
-            const int64_t j = j0 + sl;
-            if (j >= L) break;
-            float2 xq, xk, xv;
-            cx.hist(j, xq, xk, xv);
-            const float aq0 = silu(conv4(wq0, hq[0].x, hq[1].x, hq[2].x, xq.x));
-            const float aq1 = silu(conv4(wq1, hq[0].y, hq[1].y, hq[2].y, xq.y));
-            const float ak0 = silu(conv4(wk0, hk[0].x, hk[1].x, hk[2].x, xk.x));
-            const float ak1 = silu(conv4(wk1, hk[0].y, hk[1].y, hk[2].y, xk.y));
-            const float av0 = silu(conv4(wv0, hv[0].x, hv[1].x, hv[2].x, xv.x));
-            const float av1 = silu(conv4(wv1, hv[0].y, hv[1].y, hv[2].y, xv.y));
-            hq[0] = hq[1]; hq[1] = hq[2]; hq[2] = xq;
-            hk[0] = hk[1]; hk[1] = hk[2]; hk[2] = xk;
-            hv[0] = hv[1]; hv[1] = hv[2]; hv[2] = xv;
+            if (j0 + sl >= L) break;
+            const float aq0 = silu(conv4(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
+            const float aq1 = silu(conv4(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
+            const float ak0 = silu(conv4(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
+            const float ak1 = silu(conv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
+            const float av0 = silu(conv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
+            const float av1 = silu(conv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
 
             const float qq = sum64(aq0 * aq0 + aq1 * aq1);
             const float kk = sum64(ak0 * ak0 + ak1 * ak1);
@@ -200,10 +196,7 @@ void prefill_kernel(Params p) {
             *reinterpret_cast<float2 *>(&s_qh[slot][c]) = make_float2(aq0 * rq, aq1 * rq);
             *reinterpret_cast<float2 *>(&s_kh[slot][c]) = make_float2(ak0 * rk, ak1 * rk);
             *reinterpret_cast<float2 *>(&s_col[slot][c]) = make_float2(av0, av1);
-            if (lane == 0) {
-                const int64_t trow = (rng.lo + j) * p.H + h;
-                s_tok[slot] = make_float2(p.beta[trow], qk * rq * rk);
-            }
+            if (lane == 0) s_tok[slot] = make_float2(bta[sl], qk * rq * rk);
         }
     };
 
@@ -212,11 +205,15 @@ void prefill_kernel(Params p) {
     const float eA = __expf(p.A_log[h * DK + tid]);
     const float dtb = p.dt_bias[h * DK + tid];
     auto prestep_rows = [&](int64_t c0, int nv) {
+        float fv[TC];
+#pragma unroll
+        for (int t = 0; t < TC; ++t)
+            fv[t] = t < nv ? p.f[((rng.lo + c0 + t) * p.H + h) * DK + tid] : 0.f;
         float D = 1.0f;
-#pragma unroll 1
-        for (int t = 0; t < nv; ++t) {
-            const int64_t trow = (rng.lo + c0 + t) * p.H + h;
-            const float al = decay(p.f[trow * DK + tid], eA, dtb, p.gate_mode, p.lb);
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+            if (t >= nv) break;
+            const float al = decay(fv[t], eA, dtb, p.gate_mode, p.lb);
             if constexpr (FOLD) {
                 D *= al;
                 s_dec[t][tid] = D;

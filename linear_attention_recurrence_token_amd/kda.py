@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE, KDA_ERR_LAUNCH = 0, -1, -2, -3, -4
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_BOUNDED, KDA_GATE_LITERAL, KDA_GATE_RAW = 0, 1, 2
+KDA_PREFILL_AUTO, KDA_PREFILL_FUSED, KDA_PREFILL_SPLIT = 0, 1, 2
 DK = DV = 128
 TAPS = 4
 CH = 2 * DK + DV
@@ -31,7 +32,7 @@ class kda_config(ctypes.Structure):
                 ("head_dim_v", ctypes.c_int32), ("conv_taps", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
                 ("gate_lower_bound", ctypes.c_float), ("l2_eps", ctypes.c_float),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("prefill_path", ctypes.c_int32)]
 
 
 TENSOR_FIELDS = ("q", "k", "v", "f", "beta", "g", "conv_w", "A_log", "dt_bias", "gamma",
@@ -42,8 +43,8 @@ class kda_tensors(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in TENSOR_FIELDS]
 
 
-EXPORTS = ("kda_token_step", "kda_sequence", "kda_status_string", "kda_version",
-           "kda_device_check")
+EXPORTS = ("kda_token_step", "kda_sequence", "kda_sequence_workspace_size",
+           "kda_status_string", "kda_version", "kda_device_check")
 
 
 class KdaError(RuntimeError):
@@ -70,7 +71,10 @@ def lib() -> ctypes.CDLL:
             L.kda_token_step.argtypes = [cfgp, tp, ctypes.c_int32, ctypes.c_void_p]
             L.kda_sequence.restype = ctypes.c_int32
             L.kda_sequence.argtypes = [cfgp, tp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_int64, ctypes.c_void_p]
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p]
+            L.kda_sequence_workspace_size.restype = ctypes.c_int64
+            L.kda_sequence_workspace_size.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int64]
             L.kda_status_string.restype = ctypes.c_char_p
             L.kda_status_string.argtypes = [ctypes.c_int32]
             L.kda_version.restype = ctypes.c_int32
@@ -96,11 +100,12 @@ class KdaConfig:
     head_dim_k: int = DK
     head_dim_v: int = DV
     conv_taps: int = TAPS
+    prefill_path: int = KDA_PREFILL_AUTO
 
     def to_c(self) -> kda_config:
         return kda_config(self.num_heads, self.head_dim_k, self.head_dim_v, self.conv_taps,
                           self.act_dtype, self.gate_mode, self.gate_lower_bound,
-                          self.l2_eps, self.rms_eps)
+                          self.l2_eps, self.rms_eps, self.prefill_path)
 
 
 def _ptr(t) -> Optional[int]:
@@ -171,12 +176,15 @@ def kda_token_step(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_
 
 def kda_sequence(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bias, gamma,
                  state, conv_win, y, o_raw=None, cu_seqlens=None, seq_order=None,
-                 num_seqs: Optional[int] = None, stream=None, check: bool = True) -> None:
+                 num_seqs: Optional[int] = None, workspace="auto", stream=None,
+                 check: bool = True) -> None:
     """Prefill over packed sequences (C: kda_sequence).
 
     cu_seqlens: int32 GPU tensor [N+1] of token offsets, or None for a dense
     batch (N = state.shape[0] sequences of T / N tokens).  seq_order: optional
-    int32 GPU tensor [N], the scheduling order of the sequences."""
+    int32 GPU tensor [N], the scheduling order of the sequences.  workspace:
+    "auto" allocates (through torch) the scratch the faster path can use, as
+    kda_sequence_workspace_size reports; None passes none; or a GPU tensor."""
     import torch
     ts = dict(q=q, k=k, v=v, f=f, beta=beta, g=g, conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
               gamma=gamma, state=state, conv_win=conv_win, y=y, o_raw=o_raw)
@@ -191,10 +199,28 @@ def kda_sequence(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bi
                 raise ValueError("%s must be a contiguous int32 GPU tensor of shape (%d,)" % (name, n))
     c = config.to_c()
     t = _tensors_struct(ts)
+    ws_ptr, ws_bytes = None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a GPU tensor")
+        need = int(lib().kda_sequence_workspace_size(ctypes.byref(c), N, T)) if o_raw is None else 0
+        if need < 0:
+            raise KdaError(need, "kda_sequence_workspace_size")
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        else:
+            workspace = None
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = lib().kda_sequence(ctypes.byref(c), ctypes.byref(t), N, _ptr(cu_seqlens), _ptr(seq_order),
-                            T, _stream_handle(stream))
+                            T, ws_ptr, ws_bytes, _stream_handle(stream))
     if st != KDA_OK:
         raise KdaError(st, "kda_sequence")
+
+
+def sequence_workspace_size(config: KdaConfig, num_seqs: int, total_tokens: int) -> int:
+    c = config.to_c()
+    return int(lib().kda_sequence_workspace_size(ctypes.byref(c), int(num_seqs), int(total_tokens)))
 
 
 def device_check() -> int:

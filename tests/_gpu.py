@@ -28,12 +28,15 @@ def tensors(d):
     return {k: d[k] for k in kda.TENSOR_FIELDS}
 
 
-def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, check_twice=False):
+PATHS = {"fused": kda.KDA_PREFILL_FUSED, "split": kda.KDA_PREFILL_SPLIT, "auto": kda.KDA_PREFILL_AUTO}
+
+
+def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, path="auto"):
     import torch
     d = synth.to_device(w, dev, with_o_raw=with_o_raw)
     order = None if seq_order is None else torch.as_tensor(np.asarray(seq_order, np.int32), device=dev)
-    kda.kda_sequence(cfg_of(w), **tensors(d), cu_seqlens=None if dense else d["cu_seqlens"],
-                     seq_order=order, num_seqs=w.N)
+    kda.kda_sequence(cfg_of(w, prefill_path=PATHS[path]), **tensors(d),
+                     cu_seqlens=None if dense else d["cu_seqlens"], seq_order=order, num_seqs=w.N)
     torch.cuda.synchronize()
     out = {"y": _np(d["y"]), "state": _np(d["state"]), "win": d["conv_win"].cpu().numpy()}
     out["o_raw"] = _np(d["o_raw"]) if with_o_raw else None

@@ -45,8 +45,8 @@ def test_version_and_status_strings(lib):
 
 
 def test_struct_layout_matches_header():
-    # 6 int32 + 3 float, no padding; 14 pointers
-    assert ctypes.sizeof(kda.kda_config) == 36
+    # 6 int32 + 3 float + 1 int32, no padding; 14 pointers
+    assert ctypes.sizeof(kda.kda_config) == 40
     assert ctypes.sizeof(kda.kda_tensors) == 14 * ctypes.sizeof(ctypes.c_void_p)
 
 
@@ -70,8 +70,8 @@ def _step(lib, cfg, t, n=2):
     return lib.kda_token_step(ctypes.byref(cfg), ctypes.byref(t), n, None)
 
 
-def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8):
-    return lib.kda_sequence(ctypes.byref(cfg), ctypes.byref(t), n, cu, order, total, None)
+def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8, ws=None, ws_bytes=0):
+    return lib.kda_sequence(ctypes.byref(cfg), ctypes.byref(t), n, cu, order, total, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -85,6 +85,7 @@ def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8):
     ({"l2_eps": -1.0}, kda.KDA_ERR_INVALID_ARG),
     ({"rms_eps": float("nan")}, kda.KDA_ERR_INVALID_ARG),
     ({"gate_lower_bound": float("nan")}, kda.KDA_ERR_INVALID_ARG),
+    ({"prefill_path": 3}, kda.KDA_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected(lib, over, status):
     t = _fake_tensors()
@@ -127,6 +128,24 @@ def test_beta_needs_only_word_alignment(lib):
     except ImportError:
         pass
     assert _step(lib, _cfg(), _fake_tensors(beta=(1 << 40) + 4)) == kda.KDA_ERR_DEVICE
+
+
+def test_workspace_size_and_checks(lib):
+    # few (sequence, head) pairs: the split path wants one fp32 readout row per token.head
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 100) == 100 * 4 * 128 * 4
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=1)), 2, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 16, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, prefill_path=2)), 16, 100) \
+        == 100 * 64 * 128 * 4
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 0) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, -1) == kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(head_dim_k=64)), 2, 5) == kda.KDA_ERR_UNSUPPORTED
+    t = _fake_tensors()
+    assert _seq(lib, _cfg(), t, ws=(1 << 41) + 4, ws_bytes=1 << 20) == kda.KDA_ERR_INVALID_ARG
+    assert _seq(lib, _cfg(), t, ws=1 << 41, ws_bytes=-1) == kda.KDA_ERR_INVALID_ARG
+    # forced split without o_raw or a big enough workspace
+    assert _seq(lib, _cfg(prefill_path=2), t) == kda.KDA_ERR_INVALID_ARG
+    assert _seq(lib, _cfg(prefill_path=2), t, ws=1 << 41, ws_bytes=64) == kda.KDA_ERR_INVALID_ARG
 
 
 def test_bad_sizes_rejected(lib):

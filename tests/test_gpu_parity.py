@@ -26,10 +26,14 @@ def note(msg):
 
 # ---------------------------------------------------------------- small sizes
 
-def test_cfg0_sequence(gpu):
+PATHS = pytest.mark.parametrize("path", ["fused", "split"])
+
+
+@PATHS
+def test_cfg0_sequence(gpu, path):
     w = synth.workload(0)
-    note("cfg0 1x1x64 fp32 via kda_sequence")
-    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), label="cfg0")
+    note("cfg0 1x1x64 fp32 via kda_sequence, %s" % path)
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label="cfg0")
 
 
 def test_cfg0_as_token_steps(gpu):
@@ -54,71 +58,79 @@ def test_decode_bf16(gpu):
     _gpu.assert_parity(_gpu.run_decode(w, gpu), _gpu.oracle_decode(w), bf16=True, label="decode bf16")
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 9, 300])
-def test_prefill_fp32_lengths(gpu, T):
+@PATHS
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 9, 15, 16, 17, 300])
+def test_prefill_fp32_lengths(gpu, T, path):
     w = synth.workload(2, scale={"H": 3, "T": T}, seed=200 + T)
     w.state0[...] = synth.make_workload("s", seed=1, N=1, H=3, lengths=[1], state_std=0.02).state0
     w.win0[...] = synth.make_workload("w", seed=2, N=1, H=3, lengths=[1], win_std=1.0).win0
-    note("prefill fp32 1x3 T=%d" % T)
-    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), label="T=%d" % T)
+    note("prefill fp32 1x3 T=%d %s" % (T, path))
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label="T=%d" % T)
 
 
-def test_prefill_cfg3_small_bf16(gpu):
+@PATHS
+def test_prefill_cfg3_small_bf16(gpu, path):
     w = synth.workload(3, scale={"N": 2, "H": 4, "T": 300})
-    note("cfg3-shaped bf16 2x4x300")
-    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), bf16=True, label="cfg3s")
+    note("cfg3-shaped bf16 2x4x300 %s" % path)
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), bf16=True,
+                       label="cfg3s")
 
 
-def test_prefill_dense_mode_matches_packed(gpu):
+@PATHS
+def test_prefill_dense_mode_matches_packed(gpu, path):
     w = synth.workload(3, scale={"N": 3, "H": 2, "T": 40})
-    note("dense (cu_seqlens=NULL) vs packed")
-    a = _gpu.run_sequence(w, gpu, dense=True)
-    b = _gpu.run_sequence(w, gpu)
+    note("dense (cu_seqlens=NULL) vs packed %s" % path)
+    a = _gpu.run_sequence(w, gpu, dense=True, path=path)
+    b = _gpu.run_sequence(w, gpu, path=path)
     for k in ("y", "o_raw", "state", "win"):
         np.testing.assert_array_equal(a[k], b[k])
 
 
+@PATHS
 @pytest.mark.parametrize("act", ["bf16", "f32"])
-def test_ragged_edges(gpu, act):
+def test_ragged_edges(gpu, act, path):
     lengths = [0, 1, 2, 3, 4, 5, 17, 64, 0, 300, 1000]
     w = synth.make_workload("ragged edges", seed=41, N=len(lengths), H=4, lengths=lengths,
                             act_dtype=act, state_std=0.02, win_std=1.0, gamma_range=(0.5, 1.5),
                             fresh_prob=0.5)
-    note("ragged %s lengths=%s H=4" % (act, lengths))
-    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), bf16=(act == "bf16"),
-                       label="ragged")
+    note("ragged %s lengths=%s H=4 %s" % (act, lengths, path))
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w),
+                       bf16=(act == "bf16"), label="ragged")
 
 
+@PATHS
 @pytest.mark.parametrize("mode", [synth.GATE_LITERAL, synth.GATE_RAW])
-def test_other_gate_modes(gpu, mode):
+def test_other_gate_modes(gpu, mode, path):
     w = synth.make_workload("gate", seed=50 + mode, N=2, H=3, lengths=[33, 10], gate_mode=mode,
                             state_std=0.02, win_std=1.0)
-    note("gate mode %d prefill + decode" % mode)
-    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), label="gate %d" % mode)
+    note("gate mode %d prefill + decode %s" % (mode, path))
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label="gate %d" % mode)
     wd = synth.make_workload("gate d", seed=60 + mode, N=4, H=2, decode_steps=5, gate_mode=mode,
                              state_std=0.02, win_std=1.0)
     _gpu.assert_parity(_gpu.run_decode(wd, gpu), _gpu.oracle_decode(wd), label="gate %d dec" % mode)
 
 
+@PATHS
 @pytest.mark.parametrize("lb", [-1.0, -9.0])
-def test_bounded_gate_other_bounds(gpu, lb):
+def test_bounded_gate_other_bounds(gpu, lb, path):
     # -9 * 8 tokens < -60: outside the range of the folded prefill form, so this
     # also runs the direct form with the bounded gate
     lo = 0.4 if lb > -2 else 0.2      # decays the bound can reach: exp(lb) < d < 1
     w = synth.make_workload("lb", seed=70, N=2, H=2, lengths=[29, 12], lower_bound=lb,
                             decay=(lo, 0.999), state_std=0.02, win_std=1.0)
     assert np.all(np.isfinite(w.f))
-    note("bounded gate lb=%g" % lb)
-    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), label="lb %g" % lb)
+    note("bounded gate lb=%g %s" % (lb, path))
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label="lb %g" % lb)
 
 
-def test_strong_decay_chunks(gpu):
+@PATHS
+def test_strong_decay_chunks(gpu, path):
     # decays down to exp(-5) every token: the folded form's per-chunk scaling
     # reaches exp(-40); results must still hold the fp32 bar
     w = synth.make_workload("strong decay", seed=71, N=1, H=4, lengths=[203], decay=(0.0068, 0.05),
                             state_std=0.02, win_std=1.0)
-    note("strong decay")
-    _gpu.assert_parity(_gpu.run_sequence(w, gpu), _gpu.oracle_sequence(w), label="strong decay")
+    note("strong decay %s" % path)
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label="strong decay")
 
 
 def test_decode_large_state(gpu):
@@ -136,6 +148,17 @@ def test_decode_large_state(gpu):
 
 
 # ---------------------------------------------------------------- invariances
+
+def test_split_and_fused_paths_agree(gpu):
+    w = synth.workload(3, scale={"N": 3, "H": 5, "T": 131})
+    note("split vs fused prefill")
+    a = _gpu.run_sequence(w, gpu, path="fused")
+    b = _gpu.run_sequence(w, gpu, path="split")
+    for k in ("o_raw", "state"):
+        assert _gpu.rel_err(a[k], b[k]) <= 1e-5, k
+    assert _gpu.rel_err(a["y"], b["y"]) <= 1e-2
+    np.testing.assert_array_equal(a["win"], b["win"])
+
 
 def test_split_sequence_and_token_steps_agree(gpu):
     import torch
@@ -158,27 +181,29 @@ def test_split_sequence_and_token_steps_agree(gpu):
     assert _gpu.rel_err(steps["y"], whole["y"]) <= 1e-5
 
 
-def test_ragged_equals_each_sequence_alone_and_order(gpu):
+@PATHS
+def test_ragged_equals_each_sequence_alone_and_order(gpu, path):
     lengths = [5, 0, 40, 9]
     w = synth.make_workload("r", seed=91, N=4, H=3, lengths=lengths, act_dtype="bf16",
                             state_std=0.02, win_std=1.0)
-    note("ragged vs individual vs seq_order")
-    full = _gpu.run_sequence(w, gpu)
-    ordered = _gpu.run_sequence(w, gpu, seq_order=[2, 0, 3, 1])
+    note("ragged vs individual vs seq_order %s" % path)
+    full = _gpu.run_sequence(w, gpu, path=path)
+    ordered = _gpu.run_sequence(w, gpu, seq_order=[2, 0, 3, 1], path=path)
     for k in ("y", "o_raw", "state", "win"):
         np.testing.assert_array_equal(ordered[k], full[k])
     sub = synth.subset(w, [2], [0, 1, 2])
-    alone = _gpu.run_sequence(sub, gpu)
+    alone = _gpu.run_sequence(sub, gpu, path=path)
     lo, hi = w.cu_seqlens[2], w.cu_seqlens[3]
     np.testing.assert_array_equal(alone["y"], full["y"][lo:hi])
     np.testing.assert_array_equal(alone["state"][0], full["state"][2])
 
 
-def test_repeat_runs_bitwise_and_o_raw_optional(gpu):
+@PATHS
+def test_repeat_runs_bitwise_and_o_raw_optional(gpu, path):
     w = synth.workload(3, scale={"N": 2, "H": 2, "T": 70})
-    note("determinism and o_raw=NULL")
-    a = _gpu.run_sequence(w, gpu)
-    b = _gpu.run_sequence(w, gpu, with_o_raw=False)
+    note("determinism and o_raw=NULL (workspace) %s" % path)
+    a = _gpu.run_sequence(w, gpu, path=path)
+    b = _gpu.run_sequence(w, gpu, with_o_raw=False, path=path)
     for k in ("y", "state", "win"):
         np.testing.assert_array_equal(a[k], b[k])
     wd = synth.workload(1, scale={"N": 4, "H": 2, "steps": 3})
@@ -226,7 +251,7 @@ def test_full_decode_64x32(gpu):
 
 def test_full_prefill_1x32x8192(gpu):
     w = synth.workload(2)
-    note("full prefill 1x32x8192 fp32, sampled heads 0, 19")
+    note("full prefill 1x32x8192 fp32, sampled heads 0, 19 (auto path: split)")
     full = _gpu.run_sequence(w, gpu)
     _sampled(w, full, [0], [0, 19], bf16=False)
 
