@@ -208,13 +208,19 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
             times.append(e0.elapsed_time(e1))
     ms = float(np.median(times))
     th = int(lens.sum()) * w.H
+    # HBM traffic from the committed rocprofv3 summary of this workload, if it
+    # was taken on the current source of the kernel that runs it
+    traffic = None
+    if idx == 3 and kda.sequence_workspace_size(cfg, w.N, w.total_tokens) == 0:
+        traffic = committed_traffic("kda_prefill.hip", "prefill_16x64x2048")
     flops = th * RECUR_FLOPS
     out = {"workload": w.name, "token_heads": th, "ms": ms, "runs": runs,
            "value": th / (ms * 1e-3), "unit": UNIT,
            "ns_per_token_per_chain": ms * 1e6 / int(lens.max()),
            "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, "traffic": None}}
+                        "frac": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                        "traffic": traffic}}
     del d, state0, win0
     torch.cuda.empty_cache()
     return out
