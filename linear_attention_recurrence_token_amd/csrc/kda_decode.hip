@@ -6,8 +6,8 @@
 // memory stream:
 //   * one workgroup of NT threads per (sequence, head); the 128 x 128 state is
 //     held in registers (16384 / NT floats per thread), loaded with coalesced
-//     16-byte loads issued before any other work, so the whole 64 KiB is in
-//     flight while the pre-step runs;
+//     16-byte loads issued right after the pre-step's few input loads, so the
+//     whole 64 KiB is in flight while the pre-step runs;
 //   * the pre-step (conv4 + SiLU, window shift, L2 norms, decay) runs from
 //     the raw inputs while those loads are outstanding;
 //   * one pass over the registers gives both dot products the step needs,
@@ -67,8 +67,9 @@ __device__ __forceinline__ int dec_row(int rg, int m) {
     return BLOCKED ? Sh::RPT * rg + m : rg + Sh::NRG * m;
 }
 
-template <typename Act, int NT, bool NT_LOAD, bool NT_STORE, bool BLOCKED = false>
-__global__ __launch_bounds__(NT) void decode_kernel(Params p) {
+template <typename Act, int NT, bool NT_LOAD, bool NT_STORE, bool BLOCKED = false, int WPE = 1>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+void decode_kernel(Params p) {
     using Sh = DecodeShape<NT>;
     const int unit = blockIdx.x;           // n * H + h == token row of sequence n
     const int h = unit % p.H;
@@ -82,45 +83,66 @@ __global__ __launch_bounds__(NT) void decode_kernel(Params p) {
     __shared__ float4 s_up[Sh::NW][32][2]; // per-wave partial u, p per column group
 
     float *S = p.state + (int64_t)unit * (DK * DV);
+    float *W = p.win + (int64_t)unit * (PAST * CH);
+    const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+    const int64_t row = (int64_t)unit * DK;   // DK == DV
 
-    // ---- 1. put the whole state in flight
+    // ---- 1. the pre-step's inputs first: loads return in issue order, so
+    // issuing these few before the state lets the pre-step run while the
+    // 64 KiB of state is still arriving.  Task i < 128 is the (q_i, k_i)
+    // channel pair, task 128 + j the v channel j and the decay of key channel j.
+    constexpr int TPT = (2 * DK + NT - 1) / NT;   // pre-step tasks per thread
+    float x0[TPT], x1[TPT], w0[TPT][PAST], w1[TPT][PAST], fa[TPT], fb[TPT], fc[TPT];
+    float4 c0[TPT], c1[TPT];
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+        const int task = tid + r * NT;
+        if (task < DK) {
+            const int i = task;
+            x0[r] = Act::load1(p.q, row + i);
+            x1[r] = Act::load1(p.k, row + i);
+            c0[r] = *reinterpret_cast<const float4 *>(cw + i * TAPS);
+            c1[r] = *reinterpret_cast<const float4 *>(cw + (DK + i) * TAPS);
+#pragma unroll
+            for (int j = 0; j < PAST; ++j) { w0[r][j] = W[j * CH + i]; w1[r][j] = W[j * CH + DK + i]; }
+        } else if (task < 2 * DK) {
+            const int j = task - DK;
+            x0[r] = Act::load1(p.v, row + j);
+            c0[r] = *reinterpret_cast<const float4 *>(cw + (2 * DK + j) * TAPS);
+#pragma unroll
+            for (int jj = 0; jj < PAST; ++jj) w0[r][jj] = W[jj * CH + 2 * DK + j];
+            fa[r] = p.f[row + j];
+            fb[r] = p.A_log[h * DK + j];
+            fc[r] = p.dt_bias[h * DK + j];
+        }
+    }
+    const float b = p.beta[unit];
+
+    // ---- 2. put the whole state in flight
     float4 s[Sh::RPT];
 #pragma unroll
     for (int m = 0; m < Sh::RPT; ++m)
         s[m] = ld_state<NT_LOAD>(S + dec_row<NT, BLOCKED>(rg, m) * DV + 4 * cg);
 
-    // ---- 2. pre-step from the raw inputs: task i < 128 is the (q_i, k_i)
-    // channel pair, task 128 + j the v channel j and the decay of key channel j
-    float *W = p.win + (int64_t)unit * (PAST * CH);
-    const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
-    const int64_t row = (int64_t)unit * DK;   // DK == DV
+    // ---- 3. pre-step: conv4 + SiLU, window shift, L2 partial sums, decay
     float qq = 0.f, kk = 0.f, qk = 0.f;
 #pragma unroll
-    for (int task = tid; task < 2 * DK; task += NT) {
+    for (int r = 0; r < TPT; ++r) {
+        const int task = tid + r * NT;
         if (task < DK) {
             const int i = task;
-            const float xq = Act::load1(p.q, row + i);
-            const float xk = Act::load1(p.k, row + i);
-            const float4 wq = *reinterpret_cast<const float4 *>(cw + i * TAPS);
-            const float4 wk = *reinterpret_cast<const float4 *>(cw + (DK + i) * TAPS);
-            const float q0 = W[i], q1 = W[CH + i], q2 = W[2 * CH + i];
-            const float k0 = W[DK + i], k1 = W[CH + DK + i], k2 = W[2 * CH + DK + i];
-            const float aq = silu(wq.x * q0 + wq.y * q1 + wq.z * q2 + wq.w * xq);
-            const float ak = silu(wk.x * k0 + wk.y * k1 + wk.z * k2 + wk.w * xk);
-            W[i] = q1; W[CH + i] = q2; W[2 * CH + i] = xq;
-            W[DK + i] = k1; W[CH + DK + i] = k2; W[2 * CH + DK + i] = xk;
+            const float aq = silu(c0[r].x * w0[r][0] + c0[r].y * w0[r][1] + c0[r].z * w0[r][2] + c0[r].w * x0[r]);
+            const float ak = silu(c1[r].x * w1[r][0] + c1[r].y * w1[r][1] + c1[r].z * w1[r][2] + c1[r].w * x1[r]);
+            W[i] = w0[r][1]; W[CH + i] = w0[r][2]; W[2 * CH + i] = x0[r];
+            W[DK + i] = w1[r][1]; W[CH + DK + i] = w1[r][2]; W[2 * CH + DK + i] = x1[r];
             s_act[i] = aq;
             s_act[DK + i] = ak;
             qq += aq * aq; kk += ak * ak; qk += aq * ak;
-        } else {
+        } else if (task < 2 * DK) {
             const int j = task - DK;
-            const float xv = Act::load1(p.v, row + j);
-            const float4 wv = *reinterpret_cast<const float4 *>(cw + (2 * DK + j) * TAPS);
-            const float v0 = W[2 * DK + j], v1 = W[CH + 2 * DK + j], v2 = W[2 * CH + 2 * DK + j];
-            s_act[2 * DK + j] = silu(wv.x * v0 + wv.y * v1 + wv.z * v2 + wv.w * xv);
-            W[2 * DK + j] = v1; W[CH + 2 * DK + j] = v2; W[2 * CH + 2 * DK + j] = xv;
-            const float expA = __expf(p.A_log[h * DK + j]);
-            s_alpha[j] = decay(p.f[row + j], expA, p.dt_bias[h * DK + j], p.gate_mode, p.lb);
+            s_act[2 * DK + j] = silu(c0[r].x * w0[r][0] + c0[r].y * w0[r][1] + c0[r].z * w0[r][2] + c0[r].w * x0[r]);
+            W[2 * DK + j] = w0[r][1]; W[CH + 2 * DK + j] = w0[r][2]; W[2 * CH + 2 * DK + j] = x0[r];
+            s_alpha[j] = decay(fa[r], __expf(fb[r]), fc[r], p.gate_mode, p.lb);
         }
     }
     qq = sum64(qq); kk = sum64(kk); qk = sum64(qk);
@@ -133,7 +155,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(Params p) {
     const float rq = rsqrtf(qq + p.l2_eps);
     const float rk = rsqrtf(kk + p.l2_eps);
     qk *= rq * rk;
-    const float b = p.beta[unit];
 
     // ---- 3. one pass: u = S^T (alpha k_hat), p = S^T (alpha q_hat)
     float4 u = make_float4(0.f, 0.f, 0.f, 0.f), pq = u;
@@ -194,13 +215,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(Params p) {
     }
 }
 
-template <int NT, bool NT_LOAD, bool NT_STORE, bool BLOCKED = false>
+template <int NT, bool NT_LOAD, bool NT_STORE, bool BLOCKED = false, int WPE = 1>
 hipError_t launch_decode_as(const Params &p, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)(p.num_seqs * p.H)), block(NT);
     if (bf16)
-        hipLaunchKernelGGL((decode_kernel<BF16, NT, NT_LOAD, NT_STORE, BLOCKED>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_kernel<BF16, NT, NT_LOAD, NT_STORE, BLOCKED, WPE>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_kernel<F32, NT, NT_LOAD, NT_STORE, BLOCKED>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_kernel<F32, NT, NT_LOAD, NT_STORE, BLOCKED, WPE>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -99,41 +99,58 @@ __global__ __launch_bounds__(SP_THREADS) void prefill_split_kernel(Params p, flo
     const bool has_v = 2 * lane < CW;
     const int chq = 2 * lane, chk = DK + 2 * lane, chv = 2 * DK + g * CW + (has_v ? 2 * lane : 0);
 
+    // All global inputs of a chunk's phase P.  The next chunk's are loaded
+    // while the current chunk runs its serial phase R, so phase P never
+    // waits on memory.
+    struct ChunkIn {
+        float2 xq[PAST + SQ], xk[PAST + SQ], xv[PAST + SQ];   // raw rows j0 - 3 .. j0 + SQ - 1
+        float bta[SQ];
+        float fv[SFP];                                          // decay inputs of one key row
+    };
+    const int drow = tid & (DK - 1);           // key row of this thread's decay pre-step
+    const int dt0 = (tid >> 7) * SFP;          // its folding period in the chunk
+    auto load_chunk = [&](int64_t c0, ChunkIn &in) {
+        const int64_t j0 = c0 + wave * SQ;
+#pragma unroll
+        for (int r = 0; r < PAST + SQ; ++r) {
+            const int64_t j = j0 - PAST + r;
+            const bool ok = j < L;
+            in.xq[r] = ok ? hist2(j, chq) : make_float2(0.f, 0.f);
+            in.xk[r] = ok ? hist2(j, chk) : make_float2(0.f, 0.f);
+            in.xv[r] = (ok && has_v) ? hist2(j, chv) : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int sl = 0; sl < SQ; ++sl)
+            in.bta[sl] = (lane == 0 && j0 + sl < L) ? p.beta[(rng.lo + j0 + sl) * p.H + h] : 0.f;
+#pragma unroll
+        for (int t = 0; t < SFP; ++t)
+            in.fv[t] = (c0 + dt0 + t < L) ? p.f[((rng.lo + c0 + dt0 + t) * p.H + h) * DK + drow] : 0.f;
+    };
+    const float4 wq0 = *reinterpret_cast<const float4 *>(cw + chq * TAPS);
+    const float4 wq1 = *reinterpret_cast<const float4 *>(cw + (chq + 1) * TAPS);
+    const float4 wk0 = *reinterpret_cast<const float4 *>(cw + chk * TAPS);
+    const float4 wk1 = *reinterpret_cast<const float4 *>(cw + (chk + 1) * TAPS);
+    const float4 wv0 = *reinterpret_cast<const float4 *>(cw + chv * TAPS);
+    const float4 wv1 = *reinterpret_cast<const float4 *>(cw + (chv + 1) * TAPS);
+
+    ChunkIn cur;
+    load_chunk(0, cur);
+
 #pragma unroll 1
     for (int64_t c0 = 0; c0 < L; c0 += STC) {
         const int nv = (int)((L - c0) < STC ? (L - c0) : STC);
 
-        // ---- phase P: token pre-step (wavefront w: slots SQ w .. SQ w + SQ - 1).
-        // Every global load is issued before the first use: one memory latency
-        // per chunk instead of one per token.
+        // ---- phase P: token pre-step (wavefront w: slots SQ w .. SQ w + SQ - 1)
         const int64_t j0 = c0 + wave * SQ;
         if (j0 < L) {
-            const float4 wq0 = *reinterpret_cast<const float4 *>(cw + chq * TAPS);
-            const float4 wq1 = *reinterpret_cast<const float4 *>(cw + (chq + 1) * TAPS);
-            const float4 wk0 = *reinterpret_cast<const float4 *>(cw + chk * TAPS);
-            const float4 wk1 = *reinterpret_cast<const float4 *>(cw + (chk + 1) * TAPS);
-            const float4 wv0 = *reinterpret_cast<const float4 *>(cw + chv * TAPS);
-            const float4 wv1 = *reinterpret_cast<const float4 *>(cw + (chv + 1) * TAPS);
-            float2 xq[PAST + SQ], xk[PAST + SQ], xv[PAST + SQ];
-            float bta[SQ];
-#pragma unroll
-            for (int r = 0; r < PAST + SQ; ++r) {
-                const int64_t j = j0 - PAST + r;
-                const bool ok = j < L;
-                xq[r] = ok ? hist2(j, chq) : make_float2(0.f, 0.f);
-                xk[r] = ok ? hist2(j, chk) : make_float2(0.f, 0.f);
-                xv[r] = (ok && has_v) ? hist2(j, chv) : make_float2(0.f, 0.f);
-            }
-#pragma unroll
-            for (int sl = 0; sl < SQ; ++sl)
-                bta[sl] = (lane == 0 && j0 + sl < L) ? p.beta[(rng.lo + j0 + sl) * p.H + h] : 0.f;
 #pragma unroll
             for (int sl = 0; sl < SQ; ++sl) {
                 if (j0 + sl >= L) break;
-                const float aq0 = silu(conv4s(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
-                const float aq1 = silu(conv4s(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
-                const float ak0 = silu(conv4s(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
-                const float ak1 = silu(conv4s(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
+                const float2 *xq = cur.xq + sl, *xk = cur.xk + sl, *xv = cur.xv + sl;
+                const float aq0 = silu(conv4s(wq0, xq[0].x, xq[1].x, xq[2].x, xq[3].x));
+                const float aq1 = silu(conv4s(wq1, xq[0].y, xq[1].y, xq[2].y, xq[3].y));
+                const float ak0 = silu(conv4s(wk0, xk[0].x, xk[1].x, xk[2].x, xk[3].x));
+                const float ak1 = silu(conv4s(wk1, xk[0].y, xk[1].y, xk[2].y, xk[3].y));
                 const float qq = sum64(aq0 * aq0 + aq1 * aq1);
                 const float kk = sum64(ak0 * ak0 + ak1 * ak1);
                 const float qk = sum64(aq0 * ak0 + aq1 * ak1);
@@ -142,33 +159,27 @@ __global__ __launch_bounds__(SP_THREADS) void prefill_split_kernel(Params p, flo
                 *reinterpret_cast<float2 *>(&s_qh[slot][chq]) = make_float2(aq0 * rq, aq1 * rq);
                 *reinterpret_cast<float2 *>(&s_kh[slot][chq]) = make_float2(ak0 * rk, ak1 * rk);
                 if (has_v) {
-                    const float av0 = silu(conv4s(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
-                    const float av1 = silu(conv4s(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
+                    const float av0 = silu(conv4s(wv0, xv[0].x, xv[1].x, xv[2].x, xv[3].x));
+                    const float av1 = silu(conv4s(wv1, xv[0].y, xv[1].y, xv[2].y, xv[3].y));
                     *reinterpret_cast<float2 *>(&s_v[slot][2 * lane]) = make_float2(av0, av1);
                 }
-                if (lane == 0) s_tok[slot] = make_float2(bta[sl], qk * rq * rk);
+                if (lane == 0) s_tok[slot] = make_float2(cur.bta[sl], qk * rq * rk);
             }
         }
-        // ---- phase P: decays of key row tid & 127 over the folding period
-        // (tid >> 7) of the chunk -- each period's decay accumulates from its
-        // own start, so the two halves of the workgroup work independently
+        // ---- phase P: decays of key row drow over the folding period of this
+        // half of the workgroup -- each period's decay accumulates from its own
+        // start, so the two halves work independently
         {
-            const int i = tid & (DK - 1);
-            const int t0 = (tid >> 7) * SFP;
-            float fv[SFP];
-#pragma unroll
-            for (int t = 0; t < SFP; ++t)
-                fv[t] = (t0 + t < nv) ? p.f[((rng.lo + c0 + t0 + t) * p.H + h) * DK + i] : 0.f;
             float D = 1.0f;
 #pragma unroll
             for (int t = 0; t < SFP; ++t) {
-                if (t0 + t >= nv) break;
-                const float al = decay(fv[t], eA, dtb, p.gate_mode, p.lb);
+                if (dt0 + t >= nv) break;
+                const float al = decay(cur.fv[t], eA, dtb, p.gate_mode, p.lb);
                 if constexpr (FOLD) {
                     D *= al;
-                    s_dec[t0 + t][i] = D;
+                    s_dec[dt0 + t][drow] = D;
                 } else {
-                    s_dec[t0 + t][i] = al;
+                    s_dec[dt0 + t][drow] = al;
                 }
             }
         }
@@ -189,35 +200,48 @@ __global__ __launch_bounds__(SP_THREADS) void prefill_split_kernel(Params p, flo
         }
         __syncthreads();
 
-        // ---- phase R: the serial recurrence over the chunk; the row
-        // coefficients of token t + 1 are read while token t reduces
+        if (c0 + STC < L) load_chunk(c0 + STC, cur);   // phase P's inputs are consumed
+
+        // ---- phase R: the serial recurrence over the chunk.  Everything token
+        // t + 1 reads from LDS (beta, q.k, v, row coefficients) is loaded while
+        // token t computes, scalars first, so no LDS latency sits on the chain.
         float4 rd[8];
+        float2 bt = s_tok[0];
+        float vv[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) vv[c] = s_v[0][cl * C + c];
 #pragma unroll
         for (int m = 0; m < 8; ++m) rd[m] = s_row[0][rg * SRG + m];
 #pragma unroll 1
         for (int t = 0; t < nv; ++t) {
-            const float2 bt = s_tok[t];
-            float u[C], pq[C];
-#pragma unroll
-            for (int c = 0; c < C; ++c) { u[c] = 0.f; pq[c] = 0.f; }
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    u[c] += s[m][c] * rd[m].x;
-                    pq[c] += s[m][c] * rd[m].y;
-                }
-            float4 rn[8];
             const int tn = t + 1 < nv ? t + 1 : t;
+            const float2 btn = s_tok[tn];
+            float vn[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) vn[c] = s_v[tn][cl * C + c];
+            float4 rn[8];
 #pragma unroll
             for (int m = 0; m < 8; ++m) rn[m] = s_row[tn][rg * SRG + m];
+            // two partial sums per dot product halve the FMA chain
+            float u0[C], u1[C], p0[C], p1[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) { u0[c] = u1[c] = p0[c] = p1[c] = 0.f; }
+#pragma unroll
+            for (int m = 0; m < 8; m += 2)
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    u0[c] += s[m][c] * rd[m].x;
+                    p0[c] += s[m][c] * rd[m].y;
+                    u1[c] += s[m + 1][c] * rd[m + 1].x;
+                    p1[c] += s[m + 1][c] * rd[m + 1].y;
+                }
             float d[C], o[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                u[c] = sum16(u[c]);
-                pq[c] = sum16(pq[c]);
-                d[c] = bt.x * (s_v[t][cl * C + c] - u[c]);
-                o[c] = pq[c] + bt.y * d[c];
+                const float u = sum16(u0[c] + u1[c]);
+                const float pq = sum16(p0[c] + p1[c]);
+                d[c] = bt.x * (vv[c] - u);
+                o[c] = pq + bt.y * d[c];
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m)
@@ -235,6 +259,9 @@ __global__ __launch_bounds__(SP_THREADS) void prefill_split_kernel(Params p, flo
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) rd[m] = rn[m];
+            bt = btn;
+#pragma unroll
+            for (int c = 0; c < C; ++c) vv[c] = vn[c];
             if constexpr (FOLD) {
                 if (t % SFP == SFP - 1 || t == nv - 1) {
                     // end of a folding period: back to the true state, S = D X
