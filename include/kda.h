@@ -93,7 +93,7 @@ typedef enum kda_gate_mode {
     KDA_GATE_RAW = 2            /* gk = f (the caller supplies the log-decay)   */
 } kda_gate_mode;
 
-/* Which prefill kernel kda_sequence runs.  Both compute the same function
+/* Which prefill kernel kda_sequence runs.  All compute the same function
  * (up to fp32 rounding order); AUTO picks by the number of (sequence, head)
  * pairs.  SPLIT spreads each pair's state columns over several workgroups
  * (for few pairs, e.g. one long sequence) and needs an fp32 buffer for the
@@ -102,7 +102,10 @@ typedef enum kda_gate_mode {
 typedef enum kda_prefill_path {
     KDA_PREFILL_AUTO = 0,
     KDA_PREFILL_FUSED = 1,      /* one workgroup per (sequence, head)        */
-    KDA_PREFILL_SPLIT = 2       /* state columns split across workgroups    */
+    KDA_PREFILL_SPLIT = 2,      /* state columns split across workgroups    */
+    KDA_PREFILL_CHUNK = 3       /* 16-token chunks on the matrix cores; needs
+                                   KDA_GATE_BOUNDED with |lb| <= 7.5, else
+                                   KDA_ERR_UNSUPPORTED                       */
 } kda_prefill_path;
 
 typedef struct kda_config {

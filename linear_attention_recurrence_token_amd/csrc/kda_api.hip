@@ -44,17 +44,17 @@ kda_status check_config(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (cfg->gate_mode < KDA_GATE_BOUNDED || cfg->gate_mode > KDA_GATE_RAW) return KDA_ERR_INVALID_ARG;
     if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
     if (cfg->gate_lower_bound != cfg->gate_lower_bound) return KDA_ERR_INVALID_ARG;
-    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_SPLIT)
+    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_CHUNK)
         return KDA_ERR_INVALID_ARG;
     if (cfg->head_dim_k != kda::DK || cfg->head_dim_v != kda::DV || cfg->conv_taps != kda::TAPS)
         return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }
 
-// columns per lane of the split prefill for this shape, 0 = fused kernel
+// columns per lane of the split prefill for this shape, 0 = another kernel
 int split_cols_for(const kda_config *cfg, int32_t num_seqs) {
     const int64_t units = (int64_t)num_seqs * cfg->num_heads;
-    if (cfg->prefill_path == KDA_PREFILL_FUSED) return 0;
+    if (cfg->prefill_path == KDA_PREFILL_FUSED || cfg->prefill_path == KDA_PREFILL_CHUNK) return 0;
     const int c = kda::prefill_split_cols(units);
     if (cfg->prefill_path == KDA_PREFILL_SPLIT) return c ? c : 4;
     return c;
@@ -185,8 +185,15 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     p.dense_len = dense_len;
     const bool bf16 = cfg->act_dtype == KDA_BF16;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = obuf ? kda::launch_prefill_split(p, bf16, obuf, cols, s)
-                              : kda::launch_prefill(p, bf16, s);
+    const bool chunk_ok = kda::prefill_chunk_supported(p);
+    if (cfg->prefill_path == KDA_PREFILL_CHUNK && !chunk_ok) return KDA_ERR_UNSUPPORTED;
+    hipError_t e;
+    if (obuf)
+        e = kda::launch_prefill_split(p, bf16, obuf, cols, s);
+    else if (cfg->prefill_path == KDA_PREFILL_CHUNK || (cfg->prefill_path == KDA_PREFILL_AUTO && chunk_ok))
+        e = kda::launch_prefill_chunk(p, bf16, s);
+    else
+        e = kda::launch_prefill(p, bf16, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -120,6 +120,52 @@ __device__ __forceinline__ float sum64(float x) {
     return x;
 }
 
+// ---------------------------------------------------------- buffer accesses
+// A raw buffer resource lives in scalar registers; each access then needs
+// only a 32-bit per-lane byte offset (plus a scalar offset), instead of a
+// 64-bit address per load, and reads past num_records return 0.
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int RAW_BUFFER_FLAGS = 0x00020000;   // untyped buffer, word 3 of the descriptor
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             RAW_BUFFER_FLAGS);
+}
+__device__ __forceinline__ float bld_f32(Rsrc r, uint32_t voff, uint32_t soff = 0) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ float2 bld_f32x2(Rsrc r, uint32_t voff, uint32_t soff = 0) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+}
+__device__ __forceinline__ void bst_f32(Rsrc r, float v, uint32_t voff, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void bst_f32x2(Rsrc r, float2 v, uint32_t voff, uint32_t soff = 0) {
+    const u32x2 w = {__float_as_uint(v.x), __float_as_uint(v.y)};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
+}
+// two consecutive activations (element index i, even) through a buffer
+template <typename Act> struct BufAct;
+template <> struct BufAct<F32> {
+    static constexpr uint32_t ELEM = 4;
+    static __device__ __forceinline__ float2 load2(Rsrc r, uint32_t i) { return bld_f32x2(r, i * 4); }
+    static __device__ __forceinline__ void store2(Rsrc r, uint32_t i, float2 x) { bst_f32x2(r, x, i * 4); }
+};
+template <> struct BufAct<BF16> {
+    static constexpr uint32_t ELEM = 2;
+    static __device__ __forceinline__ float2 load2(Rsrc r, uint32_t i) {
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, i * 2, 0, 0);
+        return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    }
+    static __device__ __forceinline__ void store2(Rsrc r, uint32_t i, float2 x) {
+        const uint32_t w = f32_to_bf16_bits(x.x) | (f32_to_bf16_bits(x.y) << 16);
+        __builtin_amdgcn_raw_buffer_store_b32(w, r, i * 2, 0, 0);
+    }
+};
+
 // ------------------------------------------------------------ sequences
 
 struct Range {

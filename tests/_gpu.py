@@ -28,7 +28,8 @@ def tensors(d):
     return {k: d[k] for k in kda.TENSOR_FIELDS}
 
 
-PATHS = {"fused": kda.KDA_PREFILL_FUSED, "split": kda.KDA_PREFILL_SPLIT, "auto": kda.KDA_PREFILL_AUTO}
+PATHS = {"fused": kda.KDA_PREFILL_FUSED, "split": kda.KDA_PREFILL_SPLIT, "auto": kda.KDA_PREFILL_AUTO,
+         "chunk": kda.KDA_PREFILL_CHUNK}
 
 
 def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, path="auto"):

@@ -85,7 +85,7 @@ def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8, ws=None, ws_bytes=0):
     ({"l2_eps": -1.0}, kda.KDA_ERR_INVALID_ARG),
     ({"rms_eps": float("nan")}, kda.KDA_ERR_INVALID_ARG),
     ({"gate_lower_bound": float("nan")}, kda.KDA_ERR_INVALID_ARG),
-    ({"prefill_path": 3}, kda.KDA_ERR_INVALID_ARG),
+    ({"prefill_path": 4}, kda.KDA_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected(lib, over, status):
     t = _fake_tensors()

@@ -26,7 +26,8 @@ def note(msg):
 
 # ---------------------------------------------------------------- small sizes
 
-PATHS = pytest.mark.parametrize("path", ["fused", "split"])
+PATHS = pytest.mark.parametrize("path", ["fused", "split", "chunk"])
+PATHS_ANY_GATE = pytest.mark.parametrize("path", ["fused", "split"])
 
 
 @PATHS
@@ -98,7 +99,7 @@ def test_ragged_edges(gpu, act, path):
                        bf16=(act == "bf16"), label="ragged")
 
 
-@PATHS
+@PATHS_ANY_GATE
 @pytest.mark.parametrize("mode", [synth.GATE_LITERAL, synth.GATE_RAW])
 def test_other_gate_modes(gpu, mode, path):
     w = synth.make_workload("gate", seed=50 + mode, N=2, H=3, lengths=[33, 10], gate_mode=mode,
@@ -119,6 +120,12 @@ def test_bounded_gate_other_bounds(gpu, lb, path):
     w = synth.make_workload("lb", seed=70, N=2, H=2, lengths=[29, 12], lower_bound=lb,
                             decay=(lo, 0.999), state_std=0.02, win_std=1.0)
     assert np.all(np.isfinite(w.f))
+    if path == "chunk" and lb < -7.5:
+        # the chunkwise form needs |lb| <= 7.5 and says so
+        with pytest.raises(kda.KdaError) as ei:
+            _gpu.run_sequence(w, gpu, path=path)
+        assert ei.value.status == kda.KDA_ERR_UNSUPPORTED
+        return
     note("bounded gate lb=%g %s" % (lb, path))
     _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label="lb %g" % lb)
 
@@ -149,15 +156,23 @@ def test_decode_large_state(gpu):
 
 # ---------------------------------------------------------------- invariances
 
-def test_split_and_fused_paths_agree(gpu):
+@pytest.mark.parametrize("other", ["split", "chunk"])
+def test_prefill_paths_agree(gpu, other):
     w = synth.workload(3, scale={"N": 3, "H": 5, "T": 131})
-    note("split vs fused prefill")
+    note("%s vs fused prefill" % other)
     a = _gpu.run_sequence(w, gpu, path="fused")
-    b = _gpu.run_sequence(w, gpu, path="split")
+    b = _gpu.run_sequence(w, gpu, path=other)
     for k in ("o_raw", "state"):
-        assert _gpu.rel_err(a[k], b[k]) <= 1e-5, k
+        assert _gpu.rel_err(a[k], b[k]) <= 2e-5, k
     assert _gpu.rel_err(a["y"], b["y"]) <= 1e-2
     np.testing.assert_array_equal(a["win"], b["win"])
+
+
+def test_chunk_path_rejects_unbounded_gates(gpu):
+    w = synth.make_workload("raw", seed=5, N=1, H=2, lengths=[20], gate_mode=synth.GATE_RAW)
+    with pytest.raises(kda.KdaError) as ei:
+        _gpu.run_sequence(w, gpu, path="chunk")
+    assert ei.value.status == kda.KDA_ERR_UNSUPPORTED
 
 
 def test_split_sequence_and_token_steps_agree(gpu):
