@@ -208,13 +208,17 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
             times.append(e0.elapsed_time(e1))
     ms = float(np.median(times))
     th = int(lens.sum()) * w.H
+    # the kernel the automatic choice runs (the library's rule: chunkwise for
+    # the bounded gate with |lower bound| <= 7.5, else split / fused)
+    chunk = cfg.gate_mode == kda.KDA_GATE_BOUNDED and -7.5 <= cfg.gate_lower_bound <= 0.0
+    path = "chunk" if chunk else ("split" if ws_bytes > 0 else "fused")
     # HBM traffic from the committed rocprofv3 summary of this workload, if it
     # was taken on the current source of the kernel that runs it
     traffic = None
-    if idx == 3 and kda.sequence_workspace_size(cfg, w.N, w.total_tokens) == 0:
-        traffic = committed_traffic("kda_prefill.hip", "prefill_16x64x2048")
+    if idx == 3 and path == "chunk":
+        traffic = committed_traffic("kda_prefill_chunk.hip", "prefill_16x64x2048")
     flops = th * RECUR_FLOPS
-    out = {"workload": w.name, "token_heads": th, "ms": ms, "runs": runs,
+    out = {"workload": w.name, "path": path, "token_heads": th, "ms": ms, "runs": runs,
            "value": th / (ms * 1e-3), "unit": UNIT,
            "ns_per_token_per_chain": ms * 1e6 / int(lens.max()),
            "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,

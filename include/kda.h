@@ -94,11 +94,14 @@ typedef enum kda_gate_mode {
 } kda_gate_mode;
 
 /* Which prefill kernel kda_sequence runs.  All compute the same function
- * (up to fp32 rounding order); AUTO picks by the number of (sequence, head)
- * pairs.  SPLIT spreads each pair's state columns over several workgroups
- * (for few pairs, e.g. one long sequence) and needs an fp32 buffer for the
- * pre-norm readout: o_raw, or else a workspace of the size
- * kda_sequence_workspace_size reports. */
+ * within the fp32 tolerance; AUTO takes CHUNK wherever the gate allows it,
+ * otherwise SPLIT for few (sequence, head) pairs and FUSED for many.  SPLIT
+ * spreads each pair's state columns over several workgroups (for few pairs,
+ * e.g. one long sequence) and needs an fp32 buffer for the pre-norm readout:
+ * o_raw, or else a workspace of the size kda_sequence_workspace_size reports.
+ * CHUNK applies the recurrence 16 tokens at a time as small matrix products
+ * on the matrix cores (bf16 operands split into high and low parts, about
+ * 2^-16 relative error per product, fp32 accumulation and state). */
 typedef enum kda_prefill_path {
     KDA_PREFILL_AUTO = 0,
     KDA_PREFILL_FUSED = 1,      /* one workgroup per (sequence, head)        */

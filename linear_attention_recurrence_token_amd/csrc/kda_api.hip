@@ -51,13 +51,20 @@ kda_status check_config(const kda_config *cfg, const kda_tensors *t, int32_t num
     return KDA_OK;
 }
 
-// columns per lane of the split prefill for this shape, 0 = another kernel
+bool chunk_supported(const kda_config *cfg) {
+    return kda::prefill_chunk_supported(cfg->gate_mode, cfg->gate_lower_bound, cfg->num_heads);
+}
+
+// columns per lane of the split prefill for this shape, 0 = another kernel.
+// Automatic choice: the chunkwise kernel wherever the gate allows it (it is
+// the fastest at every batch size), else the split kernel for few
+// (sequence, head) pairs, else the fused kernel.
 int split_cols_for(const kda_config *cfg, int32_t num_seqs) {
     const int64_t units = (int64_t)num_seqs * cfg->num_heads;
     if (cfg->prefill_path == KDA_PREFILL_FUSED || cfg->prefill_path == KDA_PREFILL_CHUNK) return 0;
     const int c = kda::prefill_split_cols(units);
     if (cfg->prefill_path == KDA_PREFILL_SPLIT) return c ? c : 4;
-    return c;
+    return chunk_supported(cfg) ? 0 : c;
 }
 
 kda_status check_tensors(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
@@ -185,7 +192,7 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     p.dense_len = dense_len;
     const bool bf16 = cfg->act_dtype == KDA_BF16;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool chunk_ok = kda::prefill_chunk_supported(p);
+    const bool chunk_ok = chunk_supported(cfg);
     if (cfg->prefill_path == KDA_PREFILL_CHUNK && !chunk_ok) return KDA_ERR_UNSUPPORTED;
     hipError_t e;
     if (obuf)

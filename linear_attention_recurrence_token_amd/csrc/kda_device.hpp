@@ -149,13 +149,25 @@ __device__ __forceinline__ void bst_f32x2(Rsrc r, float2 v, uint32_t voff, uint3
 }
 // two consecutive activations (element index i, even) through a buffer
 template <typename Act> struct BufAct;
+// Raw2 / load_raw2 / unpack2 split a load from its conversion, so that a load
+// issued ahead of time is not waited for until the value is unpacked.
 template <> struct BufAct<F32> {
     static constexpr uint32_t ELEM = 4;
+    typedef float2 Raw2;
     static __device__ __forceinline__ float2 load2(Rsrc r, uint32_t i) { return bld_f32x2(r, i * 4); }
     static __device__ __forceinline__ void store2(Rsrc r, uint32_t i, float2 x) { bst_f32x2(r, x, i * 4); }
+    static __device__ __forceinline__ Raw2 load_raw2(Rsrc r, uint32_t i) { return bld_f32x2(r, i * 4); }
+    static __device__ __forceinline__ float2 unpack2(Raw2 x) { return x; }
 };
 template <> struct BufAct<BF16> {
     static constexpr uint32_t ELEM = 2;
+    typedef uint32_t Raw2;
+    static __device__ __forceinline__ Raw2 load_raw2(Rsrc r, uint32_t i) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, i * 2, 0, 0);
+    }
+    static __device__ __forceinline__ float2 unpack2(Raw2 w) {
+        return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    }
     static __device__ __forceinline__ float2 load2(Rsrc r, uint32_t i) {
         const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, i * 2, 0, 0);
         return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));

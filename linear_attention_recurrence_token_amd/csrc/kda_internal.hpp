@@ -45,10 +45,10 @@ hipError_t launch_prefill(const Params &p, bool bf16, hipStream_t stream);
 // or 4) to use for `units` pairs, or 0 when the fused kernel is the better one.
 int prefill_split_cols(int64_t units);
 
-// Chunkwise prefill on fp32 MFMA (16-token chunks); needs the bounded gate
-// with a lower bound of magnitude at most 7.5 so that the in-chunk decay
+// Chunkwise prefill on the matrix cores (16-token chunks); needs the bounded
+// gate with a lower bound of magnitude at most 7.5 so that the in-chunk decay
 // factors stay inside fp32 range.
-bool prefill_chunk_supported(const Params &p);
+bool prefill_chunk_supported(int32_t gate_mode, float lb, int32_t num_heads);
 hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_split(const Params &p, bool bf16, float *obuf, int cols_per_lane,
                                 hipStream_t stream);

@@ -1,4 +1,4 @@
-// kda_prefill_chunk.hip -- chunkwise KDA prefill on fp32 MFMA.
+// kda_prefill_chunk.hip -- chunkwise KDA prefill on the matrix cores.
 //
 // The recurrence of "Kimi K3 Metal Gap Analysis" (§2, row "Recurrence"),
 // S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T, is applied to a
@@ -15,23 +15,36 @@
 // so with P = (e^G . K) S_0 and R = (e^G . Q) S_0 (C x 128 each):
 //     (I + Diag(b) L) Delta = Diag(b) (V - P),  O = R + M Delta,
 //     S_C = Diag(e^{G_C}) S_0 + E^T Delta,  E_s = e^{G_C - G_s} . k_s.
-// Every product is a small dense GEMM, done with v_mfma_f32_16x16x4_f32:
-// the work per token is the same ~7 dk dv flops as the recurrent form, but on
-// the matrix cores, which run fp32 at twice the rate of the (unpacked) VALU.
+//
+// Arithmetic.  On gfx950 fp32 MFMA holds the SIMD's vector ALU for its whole
+// duration, while bf16 MFMA runs beside it at 16x the rate.  The products with
+// the state (P, R, the update) and Delta, O therefore run on bf16 MFMA with
+// every operand split as x = hi + lo, hi = bf16(x), lo = bf16(x - hi), and
+// a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi: relative error about 2^-16 per
+// product, accumulated in fp32, the state itself kept in fp32.  L and M (two
+// 16x16 products per chunk) stay on fp32 MFMA; T = (I + Diag(b) L)^{-1} is
+// solved by forward substitution in fp32.
 //
 // Exponent ranges: L and M use factors e^{G_t - r} and e^{r - G_s} with r the
 // log-decay at the chunk middle, so every factor lies within e^{+-|lb| C / 2};
-// with the bounded gate and |lb| <= 7.5 that is at most e^{60}, far inside
-// fp32.  (Products above the diagonal can reach e^{|lb| C}; they are masked
-// by selection, never multiplied.)  Other gate forms take the recurrent path.
+// with the bounded gate and |lb| <= 7.5 that is at most e^{60}, inside fp32.
+// (Products above the diagonal can reach e^{|lb| C}; they are masked by
+// selection, never multiplied.)  Other gate forms take the recurrent path.
 //
-// Layout.  One 256-thread workgroup (4 wavefronts) per (sequence, head).
-// Wavefront w owns state columns 32 w .. 32 w + 31 as 8 x 2 MFMA accumulator
-// tiles: lane l holds S[16 rt + 4 (l / 16) + r][32 w + 16 j + l % 16] in
-// element r of tile (rt, j).  The state never leaves the accumulators between
-// chunks: it feeds P and R as the B operand directly, by ordering the sum over
-// key channels so that MFMA step (rt, r) takes channel 16 rt + 4 (l / 16) + r
-// in lane l (the A operand is read from LDS in the matching order).
+// Layout and schedule.  One 512-thread workgroup (8 wavefronts) per
+// (sequence, head).  Wavefront w owns state columns 16 w .. 16 w + 15 as 8
+// MFMA accumulator tiles (lane l holds S[16 rt + 4 (l / 16) + r][16 w + l % 16]
+// in element r of tile rt) and takes tokens 2 w, 2 w + 1 of every chunk in the
+// token-wise work.  Each chunk i takes two workgroup barriers:
+//   half 1: P, R of chunk i; T and M of chunk i (wavefronts 0 and 1); conv,
+//           SiLU, L2 norm and decay of chunk i + 1 from registers loaded a
+//           chunk earlier; loads for chunk i + 2; RMSNorm and gate of chunk i - 1
+//   half 2: Delta, O and the state update of chunk i; the split operands and
+//           partial L, M of chunk i + 1
+// The state never leaves the accumulators between chunks: it feeds P and R
+// as the B operand of 16x16x32 steps directly, by ordering the sum over key
+// channels so that step m takes, in lane l, the rows the lane holds of tiles
+// 2 m and 2 m + 1; the A operands are stored in LDS in that order.
 #include "kda_device.hpp"
 
 namespace kda {
@@ -39,24 +52,75 @@ namespace kda {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int CK_THREADS = 256;
+constexpr int CK_THREADS = 512;    // 8 wavefronts
 constexpr int CC = 16;             // tokens per chunk
-constexpr int CQ = CC / 4;         // tokens per wavefront in the token pre-step
-constexpr int KP = DK + 4;         // padded LDS row
+constexpr int TW = CC / 8;         // tokens per wavefront in the token-wise work
+constexpr int RAWR = PAST + TW;    // raw rows behind those tokens
+constexpr int KP = DK + 4;         // padded fp32 LDS rows (rows read as float4 hit distinct banks)
+constexpr int TP = CC + 4;
+constexpr int OPR = 17;            // 16-byte slots per token row of the P / R operands (one pad slot)
+constexpr int ER = (CC + 4) / 2;   // u32 per channel row of E (16 tokens as bf16, padded)
+constexpr int TR = (CC + 4) / 2;   // u32 per row of T and M (bf16, padded)
+constexpr int NPART = 8;           // partial L, M over channel eighths
 constexpr float CHUNK_MAX_HALF_LOG_DECAY = 60.0f;
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+struct Split2 {
+    uint32_t hi, lo;   // bf16 pairs, first value in the low half
+};
+__device__ __forceinline__ Split2 split2(float x0, float x1) {
+    const f32x2 x = {x0, x1};
+    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    const f32x2 r = {x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u)};
+    return {hb, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
+}
+// c + a b with both operands split (16x16x32 and 16x16x16 bf16 steps)
+__device__ __forceinline__ f32x4 mma32(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+    typedef bf16x8 B8;
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(B8, al), __builtin_bit_cast(B8, bh), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(B8, ah), __builtin_bit_cast(B8, bl), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(B8, ah), __builtin_bit_cast(B8, bh), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(u32x2 ah, u32x2 al, u32x2 bh, u32x2 bl, f32x4 c) {
+    typedef bf16x4 B4;
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, al), __builtin_bit_cast(B4, bh), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, ah), __builtin_bit_cast(B4, bl), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, ah), __builtin_bit_cast(B4, bh), c, 0, 0, 0);
+}
+// the four rows 4 g + r of an accumulator tile as the split B operand of a 16x16x16 step
+__device__ __forceinline__ void split4(f32x4 d, u32x2 &h, u32x2 &l) {
+    const Split2 a = split2(d[0], d[1]), b = split2(d[2], d[3]);
+    h = u32x2{a.hi, b.hi};
+    l = u32x2{a.lo, b.lo};
+}
+
 __device__ __forceinline__ float cconv4(float4 w, float a, float b, float c, float x) {
     return w.x * a + w.y * b + w.z * c + w.w * x;
 }
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+__device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
+
+// LDS writes of this wavefront visible to its other lanes (no other wavefront)
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 template <typename Act>
-__global__ __launch_bounds__(CK_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_chunk_kernel(Params p) {
+__global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
+    typedef BufAct<Act> BA;
+    typedef typename BA::Raw2 Raw2;
     const int slot_n = blockIdx.x / p.H;
     const int h = blockIdx.x - slot_n * p.H;
     int n = slot_n;
@@ -67,311 +131,410 @@ void prefill_chunk_kernel(Params p) {
     const Range rng = seq_range(p, n);
     if (rng.len <= 0) return;
     const int64_t L = rng.len;
+    const int64_t NC = (L + CC - 1) / CC;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, g4 = lane >> 4;
     const int64_t unit = (int64_t)n * p.H + h;
-    const int col0 = 32 * wave;
+    const int64_t rowsz = (int64_t)p.H * DK;       // elements per token row of q, k, v, f, g, y
+    const int t0 = TW * wave;                       // this wavefront's tokens in the token-wise work
 
-    // LDS, [token][channel] unless noted.  Rows read as 16 tokens x float4 by
-    // one wavefront are padded to 132 floats so the 16 rows hit distinct banks.
-    __shared__ float s_ka[CC][KP];     // k_hat, then e^G . k_hat            (A operand of P)
-    __shared__ float s_qa[CC][KP];     // q_hat, then e^G . q_hat            (A operand of R)
-    __shared__ float s_v[CC][DV];      // activated v
-    __shared__ float s_G[CC][DK];      // log-decay accumulated from the chunk start
-    __shared__ float s_kt[CC][KP];     // e^{G - r} . k_hat, then the readout o of the chunk
-    __shared__ float s_qt[CC][KP];     // e^{G - r} . q_hat
-    __shared__ float s_kb[CC][KP];     // e^{r - G} . k_hat
-    __shared__ float s_E[DK][CC + 4];  // [channel][token]: e^{G_C - G} . k_hat (padded rows)
-    __shared__ float s_gC[DK];         // e^{G_C}: decay of the whole chunk
-    __shared__ float s_beta[CC];
-    __shared__ float s_Lp[4][CC][CC];  // per-wavefront partial L (channel quarters)
-    __shared__ float s_Mp[4][CC][CC];
-    __shared__ float s_T[CC][CC + 4];  // (I + Diag(b) L)^{-1}
-    __shared__ float s_M[CC][CC + 4];
+    __shared__ float s_kh[CC][KP];         // k_hat of the chunk being prepared
+    __shared__ float s_qh[CC][KP];         // q_hat of the chunk being prepared
+    __shared__ float s_Gq[CC][KP];         // log-decay summed from the start of the token's quarter
+    __shared__ float s_Gt[4][DK];          // log-decay summed over each quarter
+    __shared__ float s_v[2][CC][DV + 4];   // activated v            (by chunk parity)
+    __shared__ float s_beta[2][CC];        //                        (by chunk parity)
+    // split bf16 operands e^G . k_hat, e^G . q_hat of P and R: slot (t, m, g)
+    // holds channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3} of token t
+    __shared__ __attribute__((aligned(16))) uint32_t s_kah[CC * OPR * 4], s_kal[CC * OPR * 4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_qah[CC * OPR * 4], s_qal[CC * OPR * 4];
+    // [channel][token] split e^{G_C - G} . k_hat of the update (by chunk parity)
+    __shared__ __attribute__((aligned(16))) uint32_t s_Eh[2][DK][ER], s_El[2][DK][ER];
+    __shared__ float s_gC[2][DK];          // e^{G_C}, decay of the whole chunk (by chunk parity)
+    __shared__ float s_Lp[NPART][CC][CC];  // L, M summed over one channel eighth each
+    __shared__ float s_Mp[NPART][CC][CC];
+    __shared__ float s_A[CC][TP];          // Diag(b) L, strictly lower
+    // (I + Diag(b) L)^{-1} and M (lower triangle with the diagonal), [row][column] split bf16
+    __shared__ __attribute__((aligned(16))) uint32_t s_Th[CC][TR], s_Tl[CC][TR], s_Mh[CC][TR], s_Ml[CC][TR];
+    __shared__ float s_o[CC][DV + 4];      // readout of the chunk, before RMSNorm
+    __shared__ float s_cw[CH][TAPS];       // conv taps of this head
 
-    const float *W = p.win + unit * (PAST * CH);   // read-only; the window kernel writes it
+    {
+        const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+        for (int c = tid; c < CH; c += CK_THREADS) st4(s_cw[c], ld4(cw + c * TAPS));
+    }
 
-    // ---- state into the accumulator tiles.  Buffer accesses: lane offset
-    // (row 4 g4 + r, column col0 + 16 j + n16), row tile rt as the scalar offset.
-    const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
-    f32x4 st[8][2];
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                st[rt][j][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + 16 * j + n16) * 4,
-                                       rt * 16 * DV * 4);
-
-    // Per-chunk buffer resources over token rows [lo + base, lo + end): inputs
-    // of the pre-step (from PAST rows before the chunk) and of the epilogue.
-    const int64_t rowsz = (int64_t)p.H * DK;       // elements per token row
     auto tok_rsrc = [&](const void *t, uint32_t elem, int64_t base, int64_t end) -> Rsrc {
         return make_rsrc(static_cast<const char *>(t) + (rng.lo + base) * rowsz * elem,
                          (uint32_t)((end - base) * rowsz * elem));
     };
-    const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+    auto chunk_end = [&](int64_t c0) -> int64_t { return (c0 + CC < L) ? c0 + CC : L; };
+
+    // lane: conv channels chq, chq + 1 of q, k, v and value channels chq, chq + 1;
+    // decay: key channel dch over the tokens of quarter dq
     const int chq = 2 * lane, chk = DK + 2 * lane, chv = 2 * DK + 2 * lane;
-    const float4 wq0 = *reinterpret_cast<const float4 *>(cw + chq * TAPS);
-    const float4 wq1 = *reinterpret_cast<const float4 *>(cw + (chq + 1) * TAPS);
-    const float4 wk0 = *reinterpret_cast<const float4 *>(cw + chk * TAPS);
-    const float4 wk1 = *reinterpret_cast<const float4 *>(cw + (chk + 1) * TAPS);
-    const float4 wv0 = *reinterpret_cast<const float4 *>(cw + chv * TAPS);
-    const float4 wv1 = *reinterpret_cast<const float4 *>(cw + (chv + 1) * TAPS);
-    const int dch = tid & (DK - 1);    // key channel of this thread's decay / combine work
+    const int dch = tid & (DK - 1), dq = tid >> 7;
+    const uint32_t foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
     const float eA = __expf(p.A_log[h * DK + dch]);
     const float dtb = p.dt_bias[h * DK + dch];
-    const float2 gm = *reinterpret_cast<const float2 *>(p.gamma + 2 * lane);
+    const float2 gm = ld2(p.gamma + 2 * lane);
 
-    // RMSNorm + gate of the chunk starting at c0 (readout in s_kt), tokens CQ w ..
-    auto epilogue = [&](int64_t c0, int nvalid) {
-        const Rsrc rs_g = tok_rsrc(p.g, BufAct<Act>::ELEM, c0, c0 + nvalid);
-        const Rsrc rs_y = tok_rsrc(p.y, BufAct<Act>::ELEM, c0, c0 + nvalid);
-        const Rsrc rs_o = tok_rsrc(p.o_raw, 4, c0, c0 + nvalid);
+    // registers loaded a chunk ahead: raw inputs of the next chunk to pre-step,
+    // and the gate pre-activations of the chunk whose epilogue comes next
+    Raw2 rq[RAWR], rk[RAWR], rv[RAWR], rg[TW];
+    float rf[4], rb;
+
+    // loads of a chunk at c0 >= CC (its past rows are tokens, not the window);
+    // rows past the sequence end read as 0
+    auto issue_inputs = [&](int64_t c0) {
+        const int64_t base = c0 - PAST, end = chunk_end(c0);
+        const Rsrc aq = tok_rsrc(p.q, BA::ELEM, base, end);
+        const Rsrc ak = tok_rsrc(p.k, BA::ELEM, base, end);
+        const Rsrc av = tok_rsrc(p.v, BA::ELEM, base, end);
 #pragma unroll
-        for (int sl = 0; sl < CQ; ++sl) {
-            const int t = wave * CQ + sl;
-            if (t >= nvalid) break;
-            const float2 o = *reinterpret_cast<const float2 *>(&s_kt[t][2 * lane]);
-            const float ss = sum64(o.x * o.x + o.y * o.y);
-            const float r = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
-            const uint32_t e = (uint32_t)(t * rowsz + h * DV + 2 * lane);
-            const float2 gg = BufAct<Act>::load2(rs_g, e);
-            float2 y;
-            y.x = sigmoid(gg.x) * gm.x * o.x * r;
-            y.y = sigmoid(gg.y) * gm.y * o.y * r;
-            BufAct<Act>::store2(rs_y, e, y);
-            if (p.o_raw) bst_f32x2(rs_o, o, e * 4);
+        for (int r = 0; r < RAWR; ++r) {
+            const uint32_t e = (uint32_t)((t0 + r) * rowsz + h * DK + 2 * lane);
+            rq[r] = BA::load_raw2(aq, e);
+            rk[r] = BA::load_raw2(ak, e);
+            rv[r] = BA::load_raw2(av, e);
+        }
+        const Rsrc af = tok_rsrc(p.f, 4, c0, end);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
+        const Rsrc ab = make_rsrc(p.beta + (rng.lo + c0) * p.H, (uint32_t)((end - c0) * p.H * 4));
+        rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
+    };
+    auto issue_gate = [&](int64_t c0) {
+        const Rsrc ag = tok_rsrc(p.g, BA::ELEM, c0, chunk_end(c0));
+#pragma unroll
+        for (int sl = 0; sl < TW; ++sl)
+            rg[sl] = BA::load_raw2(ag, (uint32_t)((t0 + sl) * rowsz + h * DV + 2 * lane));
+    };
+
+    // conv + SiLU + L2 norm of this wavefront's tokens of the chunk at c0 (zeros
+    // past the end), decay sums of (dch, quarter dq); v, beta to buffer buf
+    auto prestep = [&](const float2 (&xq)[RAWR], const float2 (&xk)[RAWR], const float2 (&xv)[RAWR],
+                       int64_t c0, int buf) {
+        const int nv = (int)(L - c0 < CC ? L - c0 : CC);
+        const float4 wq0 = ld4(s_cw[chq]), wq1 = ld4(s_cw[chq + 1]);
+        const float4 wk0 = ld4(s_cw[chk]), wk1 = ld4(s_cw[chk + 1]);
+        const float4 wv0 = ld4(s_cw[chv]), wv1 = ld4(s_cw[chv + 1]);
+#pragma unroll
+        for (int sl = 0; sl < TW; ++sl) {
+            const int t = t0 + sl;
+            float2 qh = make_float2(0.f, 0.f), kh = qh, vh = qh;
+            if (t < nv) {                          // wavefront-uniform
+                const float aq0 = silu(cconv4(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
+                const float aq1 = silu(cconv4(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
+                const float ak0 = silu(cconv4(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
+                const float ak1 = silu(cconv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
+                vh.x = silu(cconv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
+                vh.y = silu(cconv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
+                const float nq = rsqrtf(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
+                const float nk = rsqrtf(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
+                qh = make_float2(aq0 * nq, aq1 * nq);
+                kh = make_float2(ak0 * nk, ak1 * nk);
+            }
+            *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
+            *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
+            *reinterpret_cast<float2 *>(&s_v[buf][t][chq]) = vh;
+        }
+        if (lane < TW) s_beta[buf][t0 + lane] = (t0 + lane < nv) ? rb : 0.f;
+        float G = 0.f;                             // held constant past the last token
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = 4 * dq + u;
+            if (t < nv) G += p.lb * sigmoid(eA * (rf[u] + dtb));
+            s_Gq[t][dch] = G;
+        }
+        s_Gt[dq][dch] = G;
+    };
+
+    // split operands of the prepared chunk (into buffer buf) and the partial
+    // L, M over channel eighth `wave`
+    auto operands = [&](int buf) {
+        {
+            // lane: channels chq, chq + 1 of this wavefront's tokens (quarter wave / 2)
+            const int qt = t0 >> 2;
+            const float2 gt0 = ld2(&s_Gt[0][chq]), gt1 = ld2(&s_Gt[1][chq]);
+            const float2 gt2 = ld2(&s_Gt[2][chq]), gt3 = ld2(&s_Gt[3][chq]);
+            // sums of the quarters before and after this one
+            float2 before = make_float2(0.f, 0.f), after = make_float2(0.f, 0.f);
+            if (qt > 0) { before.x += gt0.x; before.y += gt0.y; }
+            if (qt > 1) { before.x += gt1.x; before.y += gt1.y; }
+            if (qt > 2) { before.x += gt2.x; before.y += gt2.y; }
+            if (qt < 1) { after.x += gt1.x; after.y += gt1.y; }
+            if (qt < 2) { after.x += gt2.x; after.y += gt2.y; }
+            if (qt < 3) { after.x += gt3.x; after.y += gt3.y; }
+            const float2 gq_end = ld2(&s_Gt[qt][chq]);
+            const int m = chq >> 5, gg = (chq & 15) >> 2, e = ((chq & 31) >> 4) * 4 + (chq & 3);
+            float E0[TW], E1[TW];
+#pragma unroll
+            for (int sl = 0; sl < TW; ++sl) {
+                const int t = t0 + sl;
+                const float2 gq = ld2(&s_Gq[t][chq]);
+                const float2 kh = ld2(&s_kh[t][chq]);
+                const float2 qh = ld2(&s_qh[t][chq]);
+                const float eg0 = __expf(before.x + gq.x), eg1 = __expf(before.y + gq.y);
+                const Split2 ka = split2(eg0 * kh.x, eg1 * kh.y);
+                const Split2 qa = split2(eg0 * qh.x, eg1 * qh.y);
+                const int w = (t * OPR + m * 4 + gg) * 4 + e / 2;
+                s_kah[w] = ka.hi; s_kal[w] = ka.lo;
+                s_qah[w] = qa.hi; s_qal[w] = qa.lo;
+                // G_C - G_t = (rest of this quarter) + (later quarters)
+                E0[sl] = __expf(gq_end.x - gq.x + after.x) * kh.x;
+                E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
+            }
+            const Split2 a0 = split2(E0[0], E0[1]), a1 = split2(E1[0], E1[1]);
+            reinterpret_cast<uint32_t *>(s_Eh[buf][chq])[wave] = a0.hi;
+            reinterpret_cast<uint32_t *>(s_El[buf][chq])[wave] = a0.lo;
+            reinterpret_cast<uint32_t *>(s_Eh[buf][chq + 1])[wave] = a1.hi;
+            reinterpret_cast<uint32_t *>(s_El[buf][chq + 1])[wave] = a1.lo;
+            if (wave == 0) {
+                const float gc0 = gt0.x + gt1.x + gt2.x + gt3.x, gc1 = gt0.y + gt1.y + gt2.y + gt3.y;
+                *reinterpret_cast<float2 *>(&s_gC[buf][chq]) = make_float2(__expf(gc0), __expf(gc1));
+            }
+        }
+        // L_ts = sum_i (e^{G_ti - r_i} k_ti)(e^{r_i - G_si} k_si), M likewise with q_t,
+        // r = G at the chunk middle (token 7), on fp32 MFMA; lane l: token l % 16,
+        // channels 16 wave + 4 (l / 16) + s
+        const int cb = 16 * wave + 4 * g4;
+        const int tq = n16 >> 2;
+        const float4 k4 = ld4(&s_kh[n16][cb]);
+        const float4 q4 = ld4(&s_qh[n16][cb]);
+        const float4 gq = ld4(&s_Gq[n16][cb]);
+        const float4 g7 = ld4(&s_Gq[CC / 2 - 1][cb]);   // quarter 1 up to token 7
+        const float4 c0 = ld4(&s_Gt[0][cb]);
+        const float4 c2 = ld4(&s_Gt[2][cb]);
+        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+        const float gv[4] = {gq.x, gq.y, gq.z, gq.w};
+        const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
+        const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
+        const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
+        f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // G_t - r from sums that start as close to both tokens as possible
+            const float d = tq == 0 ? gv[s] - c0v[s] - g7v[s]
+                          : tq == 1 ? gv[s] - g7v[s]
+                          : tq == 2 ? gv[s] : gv[s] + c2v[s];
+            const float ef = __expf(d), eb = __expf(-d);
+            const float b = eb * kv[s];
+            Lt = mfma4(ef * kv[s], b, Lt);
+            Mt = mfma4(ef * qv[s], b, Mt);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s_Lp[wave][4 * g4 + r][n16] = Lt[r];
+            s_Mp[wave][4 * g4 + r][n16] = Mt[r];
         }
     };
 
-#pragma unroll 1
-    for (int64_t c0 = 0; c0 < L; c0 += CC) {
-        const int nv = (int)((L - c0) < CC ? (L - c0) : CC);
-
-        // ================= phase P: everything that depends on inputs only
-        if (c0 > 0) epilogue(c0 - CC, CC);
+    // T = (I + Diag(b) L)^{-1} by forward substitution (one wavefront)
+    auto solve_T = [&](int buf) {
         {
-            // token pre-step: wavefront w, tokens CQ w .. CQ w + CQ - 1 (zeros past the end)
-            const int64_t j0 = c0 + wave * CQ;
-            const int64_t base = c0 >= PAST ? c0 - PAST : 0;
-            const int64_t end = (c0 + CC < L) ? c0 + CC : L;
-            const Rsrc rq = tok_rsrc(p.q, BufAct<Act>::ELEM, base, end);
-            const Rsrc rk = tok_rsrc(p.k, BufAct<Act>::ELEM, base, end);
-            const Rsrc rv = tok_rsrc(p.v, BufAct<Act>::ELEM, base, end);
-            float2 xq[PAST + CQ], xk[PAST + CQ], xv[PAST + CQ];
-            float bta[CQ];
+            const int t = lane >> 2, s0 = 4 * (lane & 3);
+            float4 a = ld4(&s_Lp[0][t][s0]);
 #pragma unroll
-            for (int r = 0; r < PAST + CQ; ++r) {
-                const int64_t jj = j0 - PAST + r;
-                if (jj < 0) {            // from the carried-in window
-                    const float *wr = W + (jj + PAST) * CH;
-                    xq[r] = *reinterpret_cast<const float2 *>(wr + chq);
-                    xk[r] = *reinterpret_cast<const float2 *>(wr + chk);
-                    xv[r] = *reinterpret_cast<const float2 *>(wr + chv);
-                } else {                 // rows at or past the end read as 0
-                    const uint32_t e = (uint32_t)((jj - base) * rowsz + h * DK + 2 * lane);
-                    xq[r] = BufAct<Act>::load2(rq, e);
-                    xk[r] = BufAct<Act>::load2(rk, e);
-                    xv[r] = BufAct<Act>::load2(rv, e);
-                }
-            }
-#pragma unroll
-            for (int sl = 0; sl < CQ; ++sl)
-                bta[sl] = (lane == 0 && j0 + sl < L) ? p.beta[(rng.lo + j0 + sl) * p.H + h] : 0.f;
-#pragma unroll
-            for (int sl = 0; sl < CQ; ++sl) {
-                const int t = wave * CQ + sl;
-                const bool valid = j0 + sl < L;       // wavefront-uniform
-                float2 qh = make_float2(0.f, 0.f), kh = qh, vh = qh;
-                if (valid) {
-                    const float aq0 = silu(cconv4(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
-                    const float aq1 = silu(cconv4(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
-                    const float ak0 = silu(cconv4(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
-                    const float ak1 = silu(cconv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
-                    vh.x = silu(cconv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
-                    vh.y = silu(cconv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
-                    const float rq = rsqrtf(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
-                    const float rk = rsqrtf(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
-                    qh = make_float2(aq0 * rq, aq1 * rq);
-                    kh = make_float2(ak0 * rk, ak1 * rk);
-                }
-                *reinterpret_cast<float2 *>(&s_qa[t][chq]) = qh;
-                *reinterpret_cast<float2 *>(&s_ka[t][chq]) = kh;
-                *reinterpret_cast<float2 *>(&s_v[t][chq]) = vh;
-                if (lane == 0) s_beta[t] = bta[sl];
-            }
-            // log-decay accumulated over the chunk, one key channel per thread;
-            // held constant past the last valid token
-            if (tid < DK) {
-                const Rsrc rf = tok_rsrc(p.f, 4, c0, c0 + nv);
-                float fv[CC];
-#pragma unroll
-                for (int t = 0; t < CC; ++t)      // rows past the end read as 0
-                    fv[t] = bld_f32(rf, (uint32_t)((h * DK + dch) * 4), (uint32_t)(t * rowsz * 4));
-                float G = 0.f;
-#pragma unroll
-                for (int t = 0; t < CC; ++t) {
-                    if (t < nv) G += p.lb * sigmoid(eA * (fv[t] + dtb));
-                    s_G[t][dch] = G;
-                }
-            }
+            for (int q = 1; q < NPART; ++q) a += ld4(&s_Lp[q][t][s0]);
+            const float bt = s_beta[buf][t];
+            a.x = (s0 + 0 < t) ? bt * a.x : 0.f;
+            a.y = (s0 + 1 < t) ? bt * a.y : 0.f;
+            a.z = (s0 + 2 < t) ? bt * a.z : 0.f;
+            a.w = (s0 + 3 < t) ? bt * a.w : 0.f;
+            st4(&s_A[t][s0], a);
         }
-        __syncthreads();
-
-        // ================= phase Q: decay-weighted operands (channel dch, 8 tokens)
-        {
-            const int t0 = (tid >> 7) * (CC / 2);
-            const float gr = s_G[CC / 2 - 1][dch];     // reference: middle of the chunk
-            const float gc = s_G[CC - 1][dch];
-#pragma unroll
-            for (int u = 0; u < CC / 2; ++u) {
-                const int t = t0 + u;
-                const float G = s_G[t][dch];
-                const float kh = s_ka[t][dch], qh = s_qa[t][dch];
-                const float eg = __expf(G), ef = __expf(G - gr), eb = __expf(gr - G);
-                s_ka[t][dch] = eg * kh;
-                s_qa[t][dch] = eg * qh;
-                s_kt[t][dch] = ef * kh;
-                s_qt[t][dch] = ef * qh;
-                s_kb[t][dch] = eb * kh;
-                s_E[dch][t] = __expf(gc - G) * kh;
-            }
-            if (tid < DK) s_gC[dch] = __expf(gc);
-        }
-        __syncthreads();
-
-        // ================= phase M1: P, R (this wavefront's columns); L, M partials
-        f32x4 Pt[2], Rt[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) { Pt[j] = f32x4{0.f, 0.f, 0.f, 0.f}; Rt[j] = Pt[j]; }
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            const float4 ak = *reinterpret_cast<const float4 *>(&s_ka[n16][16 * rt + 4 * g4]);
-            const float4 aq = *reinterpret_cast<const float4 *>(&s_qa[n16][16 * rt + 4 * g4]);
-            const float akv[4] = {ak.x, ak.y, ak.z, ak.w};
-            const float aqv[4] = {aq.x, aq.y, aq.z, aq.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    Pt[j] = mfma4(akv[r], st[rt][j][r], Pt[j]);
-                    Rt[j] = mfma4(aqv[r], st[rt][j][r], Rt[j]);
-                }
-        }
-        {
-            // channels 32 w + 8 (l / 16) + s, s = 0..7, in MFMA step s
-            const float *kt = &s_kt[n16][col0 + 8 * g4];
-            const float *qt = &s_qt[n16][col0 + 8 * g4];
-            const float *kb = &s_kb[n16][col0 + 8 * g4];
-            f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
-#pragma unroll
-            for (int s4 = 0; s4 < 2; ++s4) {
-                const float4 a = *reinterpret_cast<const float4 *>(kt + 4 * s4);
-                const float4 c = *reinterpret_cast<const float4 *>(qt + 4 * s4);
-                const float4 b = *reinterpret_cast<const float4 *>(kb + 4 * s4);
-                Lt = mfma4(a.x, b.x, Lt); Mt = mfma4(c.x, b.x, Mt);
-                Lt = mfma4(a.y, b.y, Lt); Mt = mfma4(c.y, b.y, Mt);
-                Lt = mfma4(a.z, b.z, Lt); Mt = mfma4(c.z, b.z, Mt);
-                Lt = mfma4(a.w, b.w, Lt); Mt = mfma4(c.w, b.w, Mt);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s_Lp[wave][4 * g4 + r][n16] = Lt[r];
-                s_Mp[wave][4 * g4 + r][n16] = Mt[r];
-            }
-        }
-        __syncthreads();
-
-        // ================= phase T: (I + Diag(b) L)^{-1} by forward substitution
-        // (wavefront 0, lane j < 16 builds column j); the other lanes idle here
-        if (wave == 0 && lane < CC) {
-            const int jc = lane;
-            float Tcol[CC];
+        wave_lds_sync();
+        if (lane < CC) {                           // lane j builds column j
+            float Tc[CC];
 #pragma unroll
             for (int t = 0; t < CC; ++t) {
-                float acc = (t == jc) ? 1.0f : 0.0f;
-                const float bt = s_beta[t];
+                float acc = (t == lane) ? 1.0f : 0.0f;
 #pragma unroll
-                for (int s = 0; s < t; ++s) {
-                    const float lts = s_Lp[0][t][s] + s_Lp[1][t][s] + s_Lp[2][t][s] + s_Lp[3][t][s];
-                    acc -= bt * lts * Tcol[s];
+                for (int s4 = 0; s4 < t; s4 += 4) {
+                    const float4 x = ld4(&s_A[t][s4]);
+                    const float a[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (s4 + u < t) acc = fmaf(-a[u], Tc[s4 + u], acc);
                 }
-                Tcol[t] = acc;
-                s_T[t][jc] = acc;
+                Tc[t] = acc;
             }
-            // M: lower triangle with diagonal, row t
 #pragma unroll
             for (int t = 0; t < CC; ++t) {
-                const float m = s_Mp[0][t][jc] + s_Mp[1][t][jc] + s_Mp[2][t][jc] + s_Mp[3][t][jc];
-                s_M[t][jc] = (jc <= t) ? m : 0.0f;
+                const Split2 x = split2(Tc[t], 0.f);
+                reinterpret_cast<uint16_t *>(s_Th[t])[lane] = (uint16_t)x.hi;
+                reinterpret_cast<uint16_t *>(s_Tl[t])[lane] = (uint16_t)x.lo;
             }
         }
-        // W = Diag(b) (V - P), this wavefront's columns, accumulator layout (rows 4 g4 + r)
-        f32x4 Wt[2];
+    };
+    auto reduce_M = [&]() {
+        const int t = lane >> 2, s0 = 4 * (lane & 3);
+        float4 m = ld4(&s_Mp[0][t][s0]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                Wt[j][r] = s_beta[t] * (s_v[t][col0 + 16 * j + n16] - Pt[j][r]);
-            }
-        __syncthreads();
+        for (int q = 1; q < NPART; ++q) m += ld4(&s_Mp[q][t][s0]);
+        m.x = (s0 + 0 <= t) ? m.x : 0.f;
+        m.y = (s0 + 1 <= t) ? m.y : 0.f;
+        m.z = (s0 + 2 <= t) ? m.z : 0.f;
+        m.w = (s0 + 3 <= t) ? m.w : 0.f;
+        const Split2 a = split2(m.x, m.y), b = split2(m.z, m.w);
+        *reinterpret_cast<u32x2 *>(&s_Mh[t][s0 / 2]) = u32x2{a.hi, b.hi};
+        *reinterpret_cast<u32x2 *>(&s_Ml[t][s0 / 2]) = u32x2{a.lo, b.lo};
+    };
 
-        // ================= phase M2: Delta = T W; O = R + M Delta; state update
-        f32x4 Dt[2], Ot[2];
-        {
-            const float4 tr = *reinterpret_cast<const float4 *>(&s_T[n16][4 * g4]);
-            const float4 mr = *reinterpret_cast<const float4 *>(&s_M[n16][4 * g4]);
-            const float trv[4] = {tr.x, tr.y, tr.z, tr.w};
-            const float mrv[4] = {mr.x, mr.y, mr.z, mr.w};
+    // RMSNorm + gate of this wavefront's tokens of the chunk at c0 (readout in s_o, gates in rg)
+    auto epilogue = [&](int64_t c0) {
+        const int nve = (int)(L - c0 < CC ? L - c0 : CC);
+        const Rsrc ay = tok_rsrc(p.y, BA::ELEM, c0, c0 + nve);
+        const Rsrc ao = tok_rsrc(p.o_raw, 4, c0, c0 + nve);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                Dt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Dt[j] = mfma4(trv[r], Wt[j][r], Dt[j]);
-                Ot[j] = Rt[j];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Ot[j] = mfma4(mrv[r], Dt[j][r], Ot[j]);
-            }
+        for (int sl = 0; sl < TW; ++sl) {
+            const int t = t0 + sl;
+            if (t >= nve) break;                   // wavefront-uniform
+            const float2 o = ld2(&s_o[t][chq]);
+            const float r = rsqrtf(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
+            const uint32_t e = (uint32_t)(t * rowsz + h * DV + chq);
+            const float2 gg = BA::unpack2(rg[sl]);
+            float2 y;
+            y.x = sigmoid(gg.x) * gm.x * o.x * r;
+            y.y = sigmoid(gg.y) * gm.y * o.y * r;
+            BA::store2(ay, e, y);
+            if (p.o_raw) bst_f32x2(ao, o, e * 4);
         }
-        // readout of the chunk into s_kt (its L operand is no longer needed)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_kt[4 * g4 + r][col0 + 16 * j + n16] = Ot[j][r];
-        // S <- Diag(e^{G_C}) S + E^T Delta
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            const float4 dc = *reinterpret_cast<const float4 *>(&s_gC[16 * rt + 4 * g4]);
-            const float4 er = *reinterpret_cast<const float4 *>(&s_E[16 * rt + n16][4 * g4]);
-            const float dcv[4] = {dc.x, dc.y, dc.z, dc.w};
-            const float erv[4] = {er.x, er.y, er.z, er.w};
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[rt][j][r] *= dcv[r];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[rt][j] = mfma4(erv[r], Dt[j][r], st[rt][j]);
-            }
-        }
-        __syncthreads();
-    }
+    };
 
-    // epilogue of the last chunk, then the state
-    const int64_t last = ((L - 1) / CC) * CC;
-    epilogue(last, (int)(L - last));
+    // ---- state into the accumulator tiles (lane offset: row 4 g4 + r,
+    // column col0 + n16; row tile rt as the scalar offset)
+    const int col0 = 16 * wave;
+    const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
+    f32x4 st[8];
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int r = 0; r < 4; ++r)
+            st[rt][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
+
+    __syncthreads();                               // conv taps in LDS
+    // ---- chunk 0 (its past rows come from the carried window)
+    {
+        const int64_t end = chunk_end(0);
+        const Rsrc aq = tok_rsrc(p.q, BA::ELEM, 0, end);
+        const Rsrc ak = tok_rsrc(p.k, BA::ELEM, 0, end);
+        const Rsrc av = tok_rsrc(p.v, BA::ELEM, 0, end);
+        const float *W = p.win + unit * (PAST * CH);
+        float2 xq[RAWR], xk[RAWR], xv[RAWR];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                bst_f32(rs_state, st[rt][j][r], ((4 * g4 + r) * DV + col0 + 16 * j + n16) * 4,
-                        rt * 16 * DV * 4);
+        for (int r = 0; r < RAWR; ++r) {
+            const int jj = t0 - PAST + r;
+            if (jj < 0) {
+                const float *wr = W + (jj + PAST) * CH;
+                xq[r] = ld2(wr + chq);
+                xk[r] = ld2(wr + chk);
+                xv[r] = ld2(wr + chv);
+            } else {
+                const uint32_t e = (uint32_t)(jj * rowsz + h * DK + 2 * lane);
+                xq[r] = BA::load2(aq, e);
+                xk[r] = BA::load2(ak, e);
+                xv[r] = BA::load2(av, e);
+            }
+        }
+        const Rsrc af = tok_rsrc(p.f, 4, 0, end);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
+        const Rsrc ab = make_rsrc(p.beta + rng.lo * p.H, (uint32_t)(end * p.H * 4));
+        rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
+        prestep(xq, xk, xv, 0, 0);
+        if (NC > 1) issue_inputs(CC);
+    }
+    __syncthreads();
+    operands(0);
+    __syncthreads();
+
+    f32x4 Pt, Rt;
+#pragma unroll 1
+    for (int64_t i = 0; i < NC; ++i) {
+        const int cur = (int)(i & 1);
+        // ================= half 1
+        if (wave == 0) solve_T(cur);
+        else if (wave == 1) reduce_M();
+        Pt = f32x4{0.f, 0.f, 0.f, 0.f};
+        Rt = Pt;
+        // P, R: step m covers state rows 32 m .. 32 m + 31 (tiles 2 m, 2 m + 1)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int w = (n16 * OPR + m * 4 + g4) * 4;
+            const u32x4 kah = *reinterpret_cast<const u32x4 *>(&s_kah[w]);
+            const u32x4 kal = *reinterpret_cast<const u32x4 *>(&s_kal[w]);
+            const u32x4 qah = *reinterpret_cast<const u32x4 *>(&s_qah[w]);
+            const u32x4 qal = *reinterpret_cast<const u32x4 *>(&s_qal[w]);
+            const Split2 x0 = split2(st[2 * m][0], st[2 * m][1]);
+            const Split2 x1 = split2(st[2 * m][2], st[2 * m][3]);
+            const Split2 x2 = split2(st[2 * m + 1][0], st[2 * m + 1][1]);
+            const Split2 x3 = split2(st[2 * m + 1][2], st[2 * m + 1][3]);
+            const u32x4 sh = {x0.hi, x1.hi, x2.hi, x3.hi}, sl = {x0.lo, x1.lo, x2.lo, x3.lo};
+            Pt = mma32(kah, kal, sh, sl, Pt);
+            Rt = mma32(qah, qal, sh, sl, Rt);
+        }
+        if (i + 1 < NC) {
+            float2 xq[RAWR], xk[RAWR], xv[RAWR];
+#pragma unroll
+            for (int r = 0; r < RAWR; ++r) {
+                xq[r] = BA::unpack2(rq[r]);
+                xk[r] = BA::unpack2(rk[r]);
+                xv[r] = BA::unpack2(rv[r]);
+            }
+            prestep(xq, xk, xv, (i + 1) * CC, cur ^ 1);
+            if (i + 2 < NC) issue_inputs((i + 2) * CC);
+        }
+        if (i >= 1) epilogue((i - 1) * CC);
+        issue_gate(i * CC);
+        __syncthreads();
+        // ================= half 2
+        {
+            // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
+            f32x4 Wt;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                Wt[r] = s_beta[cur][t] * (s_v[cur][t][col0 + n16] - Pt[r]);
+            }
+            const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[n16][2 * g4]);
+            const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[n16][2 * g4]);
+            const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[n16][2 * g4]);
+            const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[n16][2 * g4]);
+            u32x2 wh, wl, dh, dl;
+            split4(Wt, wh, wl);
+            const f32x4 Dt = mma16(th, tl, wh, wl, f32x4{0.f, 0.f, 0.f, 0.f});
+            split4(Dt, dh, dl);
+            const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_o[4 * g4 + r][col0 + n16] = Ot[r];
+            // S <- Diag(e^{G_C}) S + E^T Delta
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) {
+                const float4 dc = ld4(&s_gC[cur][16 * rt + 4 * g4]);
+                const u32x2 eh = *reinterpret_cast<const u32x2 *>(&s_Eh[cur][16 * rt + n16][2 * g4]);
+                const u32x2 el = *reinterpret_cast<const u32x2 *>(&s_El[cur][16 * rt + n16][2 * g4]);
+                st[rt][0] *= dc.x;
+                st[rt][1] *= dc.y;
+                st[rt][2] *= dc.z;
+                st[rt][3] *= dc.w;
+                st[rt] = mma16(eh, el, dh, dl, st[rt]);
+            }
+        }
+        if (i + 1 < NC) operands(cur ^ 1);
+        __syncthreads();
+    }
+
+    epilogue((NC - 1) * CC);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            bst_f32(rs_state, st[rt][r], ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
 }
 
 // window out (same as after the column-split path): every thread reads all
@@ -409,10 +572,10 @@ hipError_t launch_chunk_as(const Params &p, hipStream_t stream) {
 
 }  // namespace
 
-bool prefill_chunk_supported(const Params &p) {
+bool prefill_chunk_supported(int32_t gate_mode, float lb, int32_t num_heads) {
     // the per-chunk buffer resources span (CC + PAST) token rows of H * 128 elements
-    return p.gate_mode == GATE_BOUNDED && p.lb <= 0.0f && -p.lb * (CC / 2) <= CHUNK_MAX_HALF_LOG_DECAY &&
-           p.H <= 4096;
+    return gate_mode == GATE_BOUNDED && lb <= 0.0f && -lb * (CC / 2) <= CHUNK_MAX_HALF_LOG_DECAY &&
+           num_heads <= 4096;
 }
 
 hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream) {

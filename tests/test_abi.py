@@ -131,10 +131,15 @@ def test_beta_needs_only_word_alignment(lib):
 
 
 def test_workspace_size_and_checks(lib):
-    # few (sequence, head) pairs: the split path wants one fp32 readout row per token.head
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 100) == 100 * 4 * 128 * 4
+    # bounded gate: AUTO takes the chunkwise kernel, which needs no workspace
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 100) == 0
+    # other gates, few (sequence, head) pairs: the split path wants one fp32
+    # readout row per token.head
+    lit = dict(gate_mode=kda.KDA_GATE_LITERAL)
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(**lit)), 2, 100) == 100 * 4 * 128 * 4
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=1)), 2, 100) == 0
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 16, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=3)), 2, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, **lit)), 16, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, prefill_path=2)), 16, 100) \
         == 100 * 64 * 128 * 4
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 0) == 0
