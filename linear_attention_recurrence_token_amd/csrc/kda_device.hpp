@@ -33,12 +33,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// two fp32 -> packed bf16 (v_cvt_pk_bf16_f32: round to nearest even, NaN
+// stays NaN); the first value in the low half
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2v x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
 }
 
 struct BF16 {
@@ -51,13 +52,12 @@ struct BF16 {
         return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
     }
     static __device__ __forceinline__ void store2(void *p, int64_t i, float2 x) {
-        uint32_t w = f32_to_bf16_bits(x.x) | (f32_to_bf16_bits(x.y) << 16);
-        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p) + i) = w;
+        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p) + i) = pack_bf16x2(x.x, x.y);
     }
     static __device__ __forceinline__ void store4(void *p, int64_t i, float4 x) {
         uint2 w;
-        w.x = f32_to_bf16_bits(x.x) | (f32_to_bf16_bits(x.y) << 16);
-        w.y = f32_to_bf16_bits(x.z) | (f32_to_bf16_bits(x.w) << 16);
+        w.x = pack_bf16x2(x.x, x.y);
+        w.y = pack_bf16x2(x.z, x.w);
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p) + i) = w;
     }
 };
@@ -108,16 +108,21 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// Across rows: v_permlane16_swap / v_permlane32_swap exchange rows 2k and
+// 2k + 1 / the two halves of the wavefront inside the VALU (no LDS round
+// trip).  With both operands equal, the two results hold the two halves of
+// every pair in every lane, so the sums below are formed in the same order
+// in all lanes.
 __device__ __forceinline__ float sum32(float x) {
     x = sum16(x);
-    x += __shfl_xor(x, 16);
-    return x;
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 __device__ __forceinline__ float sum64(float x) {
     x = sum32(x);
-    x += __shfl_xor(x, 32);
-    return x;
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 // ---------------------------------------------------------- buffer accesses
@@ -173,8 +178,7 @@ template <> struct BufAct<BF16> {
         return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
     }
     static __device__ __forceinline__ void store2(Rsrc r, uint32_t i, float2 x) {
-        const uint32_t w = f32_to_bf16_bits(x.x) | (f32_to_bf16_bits(x.y) << 16);
-        __builtin_amdgcn_raw_buffer_store_b32(w, r, i * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(x.x, x.y), r, i * 2, 0, 0);
     }
 };
 

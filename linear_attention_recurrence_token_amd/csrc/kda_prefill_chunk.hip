@@ -333,7 +333,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         }
     };
 
-    // T = (I + Diag(b) L)^{-1} by forward substitution (one wavefront)
+    // T = (I + A)^{-1}, A = Diag(b) L strictly lower, by forward substitution
+    // in blocks of 4 rows on one wavefront: lane (c = l / 4, r = l % 4) builds
+    // row 4 b + r of column c in block b, and every lane of a quad keeps the
+    // finished part of column c; the rows of a block couple through quad
+    // broadcasts.  Masked entries of A are exact zeros.
     auto solve_T = [&](int buf) {
         {
             const int t = lane >> 2, s0 = 4 * (lane & 3);
@@ -348,27 +352,38 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             st4(&s_A[t][s0], a);
         }
         wave_lds_sync();
-        if (lane < CC) {                           // lane j builds column j
-            float Tc[CC];
+        const int c = lane >> 2, r = lane & 3;
+        float Tc[CC];
 #pragma unroll
-            for (int t = 0; t < CC; ++t) {
-                float acc = (t == lane) ? 1.0f : 0.0f;
+        for (int b = 0; b < 4; ++b) {
+            const int t = 4 * b + r;
+            // y = e_c(t) - sum over the finished rows s < 4 b of A[t][s] T[s][c]
+            float acc[4] = {(t == c) ? 1.0f : 0.0f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s4 = 0; s4 < t; s4 += 4) {
-                    const float4 x = ld4(&s_A[t][s4]);
-                    const float a[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (s4 + u < t) acc = fmaf(-a[u], Tc[s4 + u], acc);
-                }
-                Tc[t] = acc;
+            for (int s4 = 0; s4 < b; ++s4) {
+                const float4 a = ld4(&s_A[t][4 * s4]);
+                acc[0] = fmaf(-a.x, Tc[4 * s4 + 0], acc[0]);
+                acc[1] = fmaf(-a.y, Tc[4 * s4 + 1], acc[1]);
+                acc[2] = fmaf(-a.z, Tc[4 * s4 + 2], acc[2]);
+                acc[3] = fmaf(-a.w, Tc[4 * s4 + 3], acc[3]);
             }
-#pragma unroll
-            for (int t = 0; t < CC; ++t) {
-                const Split2 x = split2(Tc[t], 0.f);
-                reinterpret_cast<uint16_t *>(s_Th[t])[lane] = (uint16_t)x.hi;
-                reinterpret_cast<uint16_t *>(s_Tl[t])[lane] = (uint16_t)x.lo;
-            }
+            float y = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            // inside the block: row r subtracts A[t][4 b + r'] times finished row r' < r
+            const float4 ab = ld4(&s_A[t][4 * b]);
+            const float x0 = dpp<0x00>(y);
+            y = fmaf(-ab.x, x0, y);
+            const float x1 = dpp<0x55>(y);
+            y = fmaf(-ab.y, x1, y);
+            const float x2 = dpp<0xAA>(y);
+            y = fmaf(-ab.z, x2, y);
+            const float x3 = dpp<0xFF>(y);
+            Tc[4 * b + 0] = x0;
+            Tc[4 * b + 1] = x1;
+            Tc[4 * b + 2] = x2;
+            Tc[4 * b + 3] = x3;
+            const Split2 x = split2(y, 0.f);
+            reinterpret_cast<uint16_t *>(s_Th[t])[c] = (uint16_t)x.hi;
+            reinterpret_cast<uint16_t *>(s_Tl[t])[c] = (uint16_t)x.lo;
         }
     };
     auto reduce_M = [&]() {
@@ -454,15 +469,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     __syncthreads();
 
     f32x4 Pt, Rt;
-#pragma unroll 1
-    for (int64_t i = 0; i < NC; ++i) {
-        const int cur = (int)(i & 1);
-        // ================= half 1
-        if (wave == 0) solve_T(cur);
-        else if (wave == 1) reduce_M();
+    // P, R of the current chunk: step m covers state rows 32 m .. 32 m + 31
+    // (tiles 2 m, 2 m + 1)
+    auto products_PR = [&]() {
         Pt = f32x4{0.f, 0.f, 0.f, 0.f};
         Rt = Pt;
-        // P, R: step m covers state rows 32 m .. 32 m + 31 (tiles 2 m, 2 m + 1)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int w = (n16 * OPR + m * 4 + g4) * 4;
@@ -478,6 +489,12 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             Pt = mma32(kah, kal, sh, sl, Pt);
             Rt = mma32(qah, qal, sh, sl, Rt);
         }
+    };
+    // token-wise work of half 1: pre-step of chunk i + 1, epilogue of chunk
+    // i - 1, loads for chunk i + 2 (the epilogue waits for its gate loads
+    // before the next chunk's loads are issued: the memory counter drains in
+    // order)
+    auto tokens_half1 = [&](int64_t i, int cur) {
         if (i + 1 < NC) {
             float2 xq[RAWR], xk[RAWR], xv[RAWR];
 #pragma unroll
@@ -487,45 +504,71 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 xv[r] = BA::unpack2(rv[r]);
             }
             prestep(xq, xk, xv, (i + 1) * CC, cur ^ 1);
-            if (i + 2 < NC) issue_inputs((i + 2) * CC);
         }
         if (i >= 1) epilogue((i - 1) * CC);
+        if (i + 2 < NC) issue_inputs((i + 2) * CC);
         issue_gate(i * CC);
+    };
+    // Delta, O and the state update of the current chunk
+    auto update = [&](int cur) {
+        // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
+        f32x4 Wt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g4 + r;
+            Wt[r] = s_beta[cur][t] * (s_v[cur][t][col0 + n16] - Pt[r]);
+        }
+        const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[n16][2 * g4]);
+        const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[n16][2 * g4]);
+        const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[n16][2 * g4]);
+        const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[n16][2 * g4]);
+        u32x2 wh, wl, dh, dl;
+        split4(Wt, wh, wl);
+        const f32x4 Dt = mma16(th, tl, wh, wl, f32x4{0.f, 0.f, 0.f, 0.f});
+        split4(Dt, dh, dl);
+        const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_o[4 * g4 + r][col0 + n16] = Ot[r];
+        // S <- Diag(e^{G_C}) S + E^T Delta
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const float4 dc = ld4(&s_gC[cur][16 * rt + 4 * g4]);
+            const u32x2 eh = *reinterpret_cast<const u32x2 *>(&s_Eh[cur][16 * rt + n16][2 * g4]);
+            const u32x2 el = *reinterpret_cast<const u32x2 *>(&s_El[cur][16 * rt + n16][2 * g4]);
+            st[rt][0] *= dc.x;
+            st[rt][1] *= dc.y;
+            st[rt][2] *= dc.z;
+            st[rt][3] *= dc.w;
+            st[rt] = mma16(eh, el, dh, dl, st[rt]);
+        }
+    };
+
+    // The two wavefronts that share a SIMD (w and w + 4) take the matrix work
+    // and the vector work of each half in opposite orders, so that one's
+    // MFMAs run while the other issues vector instructions.
+    const bool mfma_first = wave < 4;
+#pragma unroll 1
+    for (int64_t i = 0; i < NC; ++i) {
+        const int cur = (int)(i & 1);
+        // ================= half 1
+        if (wave == 0) solve_T(cur);
+        else if (wave == 1) reduce_M();
+        if (mfma_first) {
+            products_PR();
+            tokens_half1(i, cur);
+        } else {
+            tokens_half1(i, cur);
+            products_PR();
+        }
         __syncthreads();
         // ================= half 2
-        {
-            // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
-            f32x4 Wt;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                Wt[r] = s_beta[cur][t] * (s_v[cur][t][col0 + n16] - Pt[r]);
-            }
-            const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[n16][2 * g4]);
-            const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[n16][2 * g4]);
-            const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[n16][2 * g4]);
-            const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[n16][2 * g4]);
-            u32x2 wh, wl, dh, dl;
-            split4(Wt, wh, wl);
-            const f32x4 Dt = mma16(th, tl, wh, wl, f32x4{0.f, 0.f, 0.f, 0.f});
-            split4(Dt, dh, dl);
-            const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_o[4 * g4 + r][col0 + n16] = Ot[r];
-            // S <- Diag(e^{G_C}) S + E^T Delta
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt) {
-                const float4 dc = ld4(&s_gC[cur][16 * rt + 4 * g4]);
-                const u32x2 eh = *reinterpret_cast<const u32x2 *>(&s_Eh[cur][16 * rt + n16][2 * g4]);
-                const u32x2 el = *reinterpret_cast<const u32x2 *>(&s_El[cur][16 * rt + n16][2 * g4]);
-                st[rt][0] *= dc.x;
-                st[rt][1] *= dc.y;
-                st[rt][2] *= dc.z;
-                st[rt][3] *= dc.w;
-                st[rt] = mma16(eh, el, dh, dl, st[rt]);
-            }
+        if (mfma_first) {
+            update(cur);
+            if (i + 1 < NC) operands(cur ^ 1);
+        } else {
+            if (i + 1 < NC) operands(cur ^ 1);
+            update(cur);
         }
-        if (i + 1 < NC) operands(cur ^ 1);
         __syncthreads();
     }
 
