@@ -7,7 +7,9 @@ to back with every step's inputs already resident in HBM.  value = total
 token.heads per second.  Alongside: the decode kernel's HBM roofline, the CPU
 oracle timed on this host on a bounded sample (its only use here; parity is
 checked by the GPU tests at these same sizes), a disclosed over-cache decode
-run, and the prefill workloads (kda_sequence) with their VALU roofline.
+run, and the prefill workloads (kda_sequence): the long ones with their ALU
+roofline, the short multi-token one (64 x 32 x 13 tokens) with its HBM
+roofline.
 
   python bench.py [--gpus 1] [--steps 1000] [--warmup 10]
                   [--prefill default|all|none] [--no-cpu-baseline] [--no-overcache]
@@ -209,8 +211,10 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
     ms = float(np.median(times))
     th = int(lens.sum()) * w.H
     # the kernel the automatic choice runs (the library's rule: chunkwise for
-    # the bounded gate with |lower bound| <= 7.5, else split / fused)
-    chunk = cfg.gate_mode == kda.KDA_GATE_BOUNDED and -7.5 <= cfg.gate_lower_bound <= 0.0
+    # the bounded gate with |lower bound| <= 7.5 and >= 8 tokens per sequence
+    # on average, else split / fused)
+    chunk = (cfg.gate_mode == kda.KDA_GATE_BOUNDED and -7.5 <= cfg.gate_lower_bound <= 0.0
+             and w.total_tokens >= 8 * w.N)
     path = "chunk" if chunk else ("split" if ws_bytes > 0 else "fused")
     # HBM traffic from the committed rocprofv3 summary of this workload, if it
     # was taken on the current source of the kernel that runs it
@@ -218,13 +222,25 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
     if idx == 3 and path == "chunk":
         traffic = committed_traffic("kda_prefill_chunk.hip", "prefill_16x64x2048")
     flops = th * RECUR_FLOPS
+    # algorithmic HBM bytes: state in+out and window in+out per pair, and per
+    # token.head q, k, v, g, y (activation dtype) with f (fp32) and beta
+    act_bytes = 2 if w.act_dtype == "bf16" else 4
+    per_token = 5 * 128 * act_bytes + 512 + 4
+    hbm_bytes = w.N * w.H * (2 * DK * DV * 4 + 2 * 3 * 384 * 4) + th * per_token
     out = {"workload": w.name, "path": path, "token_heads": th, "ms": ms, "runs": runs,
            "value": th / (ms * 1e-3), "unit": UNIT,
            "ns_per_token_per_chain": ms * 1e6 / int(lens.max()),
-           "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
-                        "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-                        "traffic": traffic}}
+           "hbm_GBps_algorithmic": hbm_bytes / (ms * 1e-3) / 1e9}
+    if idx == 5:
+        # a few tokens per (sequence, head): the state round trip dominates
+        out["roofline"] = {"bound": "hbm", "achieved": hbm_bytes / (ms * 1e-3) / 1e9,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None}
+    else:
+        out["roofline"] = {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
+                           "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                           "traffic": traffic}
     del d, state0, win0
     torch.cuda.empty_cache()
     return out
@@ -334,7 +350,7 @@ def main():
         del oc
 
     if args.prefill != "none":
-        idxs = [2, 3] if args.prefill == "default" else [2, 3, 4]
+        idxs = [2, 3, 5] if args.prefill == "default" else [2, 3, 4, 5]
         result["prefill"] = []
         for idx in idxs:
             log("prefill workload %d" % idx)

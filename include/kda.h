@@ -94,8 +94,9 @@ typedef enum kda_gate_mode {
 } kda_gate_mode;
 
 /* Which prefill kernel kda_sequence runs.  All compute the same function
- * within the fp32 tolerance; AUTO takes CHUNK wherever the gate allows it,
- * otherwise SPLIT for few (sequence, head) pairs and FUSED for many.  SPLIT
+ * within the fp32 tolerance; AUTO takes CHUNK wherever the gate allows it and
+ * the sequences hold at least 8 tokens on average (total_tokens >= 8 *
+ * num_seqs), otherwise SPLIT for few (sequence, head) pairs and FUSED for many.  SPLIT
  * spreads each pair's state columns over several workgroups (for few pairs,
  * e.g. one long sequence) and needs an fp32 buffer for the pre-norm readout:
  * o_raw, or else a workspace of the size kda_sequence_workspace_size reports.

@@ -55,16 +55,26 @@ bool chunk_supported(const kda_config *cfg) {
     return kda::prefill_chunk_supported(cfg->gate_mode, cfg->gate_lower_bound, cfg->num_heads);
 }
 
+// Sequences shorter than this on average run the fused recurrent kernel under
+// AUTO: below about half a chunk the chunkwise kernel's fixed cost per
+// (sequence, head) outweighs its cheaper arithmetic (measured at 64 x 32:
+// fused faster up to 4 tokens, even at 8, chunk faster from 13 on).
+constexpr int64_t CHUNK_MIN_AVG_TOKENS = 8;
+
+bool auto_chunk(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    return chunk_supported(cfg) && total_tokens >= CHUNK_MIN_AVG_TOKENS * (int64_t)num_seqs;
+}
+
 // columns per lane of the split prefill for this shape, 0 = another kernel.
-// Automatic choice: the chunkwise kernel wherever the gate allows it (it is
-// the fastest at every batch size), else the split kernel for few
-// (sequence, head) pairs, else the fused kernel.
-int split_cols_for(const kda_config *cfg, int32_t num_seqs) {
+// Automatic choice: the chunkwise kernel wherever the gate allows it and the
+// sequences are not very short (it is the fastest at every batch size), else
+// the split kernel for few (sequence, head) pairs, else the fused kernel.
+int split_cols_for(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     const int64_t units = (int64_t)num_seqs * cfg->num_heads;
     if (cfg->prefill_path == KDA_PREFILL_FUSED || cfg->prefill_path == KDA_PREFILL_CHUNK) return 0;
     const int c = kda::prefill_split_cols(units);
     if (cfg->prefill_path == KDA_PREFILL_SPLIT) return c ? c : 4;
-    return chunk_supported(cfg) ? 0 : c;
+    return auto_chunk(cfg, num_seqs, total_tokens) ? 0 : c;
 }
 
 kda_status check_tensors(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
@@ -144,7 +154,7 @@ int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs, int
     const kda_status st = check_config(cfg, &dummy, num_seqs);
     if (st != KDA_OK) return st;
     if (total_tokens < 0) return KDA_ERR_INVALID_ARG;
-    if (num_seqs == 0 || total_tokens == 0 || split_cols_for(cfg, num_seqs) == 0) return 0;
+    if (num_seqs == 0 || total_tokens == 0 || split_cols_for(cfg, num_seqs, total_tokens) == 0) return 0;
     return total_tokens * cfg->num_heads * kda::DV * (int64_t)sizeof(float);
 }
 
@@ -172,7 +182,7 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (total_tokens > (int64_t(1) << 40) / ((int64_t)cfg->num_heads * kda::DK)) return KDA_ERR_INVALID_ARG;
     if (workspace_bytes < 0 || (workspace && !aligned16(workspace))) return KDA_ERR_INVALID_ARG;
     // the readout buffer of the split path: o_raw, else a large enough workspace
-    const int cols = split_cols_for(cfg, num_seqs);
+    const int cols = split_cols_for(cfg, num_seqs, total_tokens);
     float *obuf = nullptr;
     if (cols) {
         const int64_t need = total_tokens * cfg->num_heads * kda::DV * (int64_t)sizeof(float);
@@ -197,7 +207,8 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     hipError_t e;
     if (obuf)
         e = kda::launch_prefill_split(p, bf16, obuf, cols, s);
-    else if (cfg->prefill_path == KDA_PREFILL_CHUNK || (cfg->prefill_path == KDA_PREFILL_AUTO && chunk_ok))
+    else if (cfg->prefill_path == KDA_PREFILL_CHUNK ||
+             (cfg->prefill_path == KDA_PREFILL_AUTO && auto_chunk(cfg, num_seqs, total_tokens)))
         e = kda::launch_prefill_chunk(p, bf16, s);
     else
         e = kda::launch_prefill(p, bf16, s);

@@ -249,8 +249,10 @@ def make_workload(name: str, *, seed: int, N: int, H: int, lengths=None,
 # --- the five workloads the step is measured and checked on -----------------
 
 def workload(index: int, *, scale: Optional[dict] = None, seed: Optional[int] = None) -> Workload:
-    """Workload `index` (0..4) at full size, or shrunk by `scale` overrides
-    (keys: N, H, T, steps, max_len) for tests."""
+    """Workload `index` (0..5) at full size, or shrunk by `scale` overrides
+    (keys: N, H, T, steps, max_len) for tests.  0..4 are the configurations
+    of the method's measurement; 5 is the short multi-token prefill (13 tokens
+    per sequence over a decode-sized batch)."""
     s = dict(scale or {})
     sd = index if seed is None else seed
     if index == 0:
@@ -275,6 +277,10 @@ def workload(index: int, *, scale: Optional[dict] = None, seed: Optional[int] = 
                              lengths=lambda rng: rng.integers(1, mx + 1, size=N),
                              act_dtype="bf16", state_std=0.02, win_std=1.0,
                              gamma_range=(0.5, 1.5), fresh_prob=0.5)
+    if index == 5:
+        N, H, T = s.get("N", 64), s.get("H", 32), s.get("T", 13)
+        return make_workload("short prefill %dx%d T=%d fp32" % (N, H, T), seed=sd, N=N, H=H,
+                             lengths=[T] * N, state_std=0.02, win_std=1.0)
     raise ValueError(index)
 
 

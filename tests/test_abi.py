@@ -131,8 +131,11 @@ def test_beta_needs_only_word_alignment(lib):
 
 
 def test_workspace_size_and_checks(lib):
-    # bounded gate: AUTO takes the chunkwise kernel, which needs no workspace
+    # bounded gate: AUTO takes the chunkwise kernel, which needs no workspace,
+    # unless the sequences are very short on average (then split / fused)
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 14) == 14 * 4 * 128 * 4
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 16) == 0
     # other gates, few (sequence, head) pairs: the split path wants one fp32
     # readout row per token.head
     lit = dict(gate_mode=kda.KDA_GATE_LITERAL)

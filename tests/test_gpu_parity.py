@@ -99,6 +99,19 @@ def test_ragged_edges(gpu, act, path):
                        bf16=(act == "bf16"), label="ragged")
 
 
+@pytest.mark.parametrize("path", ["auto", "fused", "split", "chunk"])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_many_short_sequences(gpu, act, path):
+    # lengths 1..16 over many sequences: below, at and around one chunk, and
+    # on both sides of the automatic choice's length threshold
+    w = synth.make_workload("short ragged", seed=31, N=40, H=3,
+                            lengths=lambda rng: rng.integers(1, 17, size=40), act_dtype=act,
+                            state_std=0.02, win_std=1.0, fresh_prob=0.3)
+    note("many short sequences 40x3 U[1,16] %s %s" % (act, path))
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w),
+                       bf16=act == "bf16", label="short %s" % path)
+
+
 @PATHS_ANY_GATE
 @pytest.mark.parametrize("mode", [synth.GATE_LITERAL, synth.GATE_RAW])
 def test_other_gate_modes(gpu, mode, path):
@@ -266,7 +279,7 @@ def test_full_decode_64x32(gpu):
 
 def test_full_prefill_1x32x8192(gpu):
     w = synth.workload(2)
-    note("full prefill 1x32x8192 fp32, sampled heads 0, 19 (auto path: split)")
+    note("full prefill 1x32x8192 fp32, sampled heads 0, 19 (auto path: chunk)")
     full = _gpu.run_sequence(w, gpu)
     _sampled(w, full, [0], [0, 19], bf16=False)
 
@@ -276,3 +289,12 @@ def test_full_batched_prefill_16x64x2048(gpu):
     note("full batched prefill 16x64x2048 bf16, sampled 4 units")
     full = _gpu.run_sequence(w, gpu)
     _sampled(w, full, [0, 11], [3, 60], bf16=True)
+
+
+@pytest.mark.parametrize("path", ["auto", "fused", "chunk"])
+def test_full_short_prefill_64x32x13(gpu, path):
+    # the short multi-token case: 13 tokens per sequence over a decode-sized
+    # batch, state and window carried in; the oracle covers every pair
+    w = synth.workload(5)
+    note("full short prefill 64x32x13 fp32, all pairs, %s" % path)
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label=w.name)
