@@ -112,6 +112,17 @@ def test_many_short_sequences(gpu, act, path):
                        bf16=act == "bf16", label="short %s" % path)
 
 
+@pytest.mark.parametrize("path", ["auto", "chunk"])
+def test_short_average_with_long_sequences(gpu, path):
+    # a batch that is short on average (the chunk path's single-buffered
+    # variant) but holds a few sequences of several chunks
+    lens = [2] * 30 + [100, 37]
+    w = synth.make_workload("mostly short", seed=33, N=len(lens), H=2, lengths=lens,
+                            state_std=0.02, win_std=1.0, fresh_prob=0.3)
+    note("mostly-short batch with two long sequences, %s" % path)
+    _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path), _gpu.oracle_sequence(w), label="mixed")
+
+
 @PATHS_ANY_GATE
 @pytest.mark.parametrize("mode", [synth.GATE_LITERAL, synth.GATE_RAW])
 def test_other_gate_modes(gpu, mode, path):
