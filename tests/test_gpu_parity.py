@@ -112,6 +112,21 @@ def test_many_short_sequences(gpu, act, path):
                        bf16=act == "bf16", label="short %s" % path)
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_chunk_many_pairs_short_average(gpu, act):
+    # more (sequence, head) pairs than CUs and few tokens on average: the
+    # chunk path's workgroups loop over several pairs each; lengths 0..40
+    # (empty ones included) give one to three chunks per pair
+    w = synth.make_workload("many pairs", seed=35, N=150, H=2,
+                            lengths=lambda rng: rng.integers(0, 41, size=150), act_dtype=act,
+                            state_std=0.02, win_std=1.0, fresh_prob=0.3)
+    note("chunk path, 150 x 2 pairs, lengths U[0,40], %s" % act)
+    order = np.argsort(-w.lengths, kind="stable")
+    for seq_order in (None, order):
+        _gpu.assert_parity(_gpu.run_sequence(w, gpu, path="chunk", seq_order=seq_order),
+                           _gpu.oracle_sequence(w), bf16=act == "bf16", label="many pairs")
+
+
 @pytest.mark.parametrize("path", ["auto", "chunk"])
 def test_short_average_with_long_sequences(gpu, path):
     # a batch that is short on average (the chunk path's single-buffered
