@@ -94,9 +94,10 @@ typedef enum kda_gate_mode {
 } kda_gate_mode;
 
 /* Which prefill kernel kda_sequence runs.  All compute the same function
- * within the fp32 tolerance; AUTO takes CHUNK wherever the gate allows it and
- * the sequences hold at least 8 tokens on average (total_tokens >= 8 *
- * num_seqs), otherwise SPLIT for few (sequence, head) pairs and FUSED for many.  SPLIT
+ * within the fp32 tolerance.  AUTO takes SHORT when the sequences hold fewer
+ * than 8 tokens on average (total_tokens < 8 * num_seqs); otherwise CHUNK
+ * wherever the gate allows it; otherwise SPLIT for few (sequence, head) pairs
+ * and FUSED for many.  SPLIT
  * spreads each pair's state columns over several workgroups (for few pairs,
  * e.g. one long sequence) and needs an fp32 buffer for the pre-norm readout:
  * o_raw, or else a workspace of the size kda_sequence_workspace_size reports.
@@ -107,8 +108,12 @@ typedef enum kda_prefill_path {
     KDA_PREFILL_AUTO = 0,
     KDA_PREFILL_FUSED = 1,      /* one workgroup per (sequence, head)        */
     KDA_PREFILL_SPLIT = 2,      /* state columns split across workgroups    */
-    KDA_PREFILL_CHUNK = 3       /* 16-token chunks on the matrix cores; needs
+    KDA_PREFILL_CHUNK = 3,      /* 16-token chunks on the matrix cores; needs
                                    KDA_GATE_BOUNDED with |lb| <= 7.5, else
+                                   KDA_ERR_UNSUPPORTED                       */
+    KDA_PREFILL_SHORT = 4       /* the decode step's layout with a token loop,
+                                   for sequences of a few tokens; needs
+                                   total_tokens * H * 512 < 2^32, else
                                    KDA_ERR_UNSUPPORTED                       */
 } kda_prefill_path;
 

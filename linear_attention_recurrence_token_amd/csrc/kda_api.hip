@@ -44,7 +44,7 @@ kda_status check_config(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (cfg->gate_mode < KDA_GATE_BOUNDED || cfg->gate_mode > KDA_GATE_RAW) return KDA_ERR_INVALID_ARG;
     if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
     if (cfg->gate_lower_bound != cfg->gate_lower_bound) return KDA_ERR_INVALID_ARG;
-    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_CHUNK)
+    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_SHORT)
         return KDA_ERR_INVALID_ARG;
     if (cfg->head_dim_k != kda::DK || cfg->head_dim_v != kda::DV || cfg->conv_taps != kda::TAPS)
         return KDA_ERR_UNSUPPORTED;
@@ -55,26 +55,36 @@ bool chunk_supported(const kda_config *cfg) {
     return kda::prefill_chunk_supported(cfg->gate_mode, cfg->gate_lower_bound, cfg->num_heads);
 }
 
-// Sequences shorter than this on average run the fused recurrent kernel under
+// Sequences shorter than this on average run the short-sequence kernel under
 // AUTO: below about half a chunk the chunkwise kernel's fixed cost per
 // (sequence, head) outweighs its cheaper arithmetic (measured at 64 x 32:
-// fused faster up to 4 tokens, even at 8, chunk faster from 13 on).
+// the token-loop kernels are faster up to 4 tokens, even at 8, the chunk
+// kernel faster from 13 on).
 constexpr int64_t CHUNK_MIN_AVG_TOKENS = 8;
+
+bool auto_short(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
+    return total_tokens < CHUNK_MIN_AVG_TOKENS * (int64_t)num_seqs &&
+           kda::short_supported(total_tokens, num_heads);
+}
 
 bool auto_chunk(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     return chunk_supported(cfg) && total_tokens >= CHUNK_MIN_AVG_TOKENS * (int64_t)num_seqs;
 }
 
 // columns per lane of the split prefill for this shape, 0 = another kernel.
-// Automatic choice: the chunkwise kernel wherever the gate allows it and the
-// sequences are not very short (it is the fastest at every batch size), else
-// the split kernel for few (sequence, head) pairs, else the fused kernel.
+// Automatic choice: the short-sequence kernel when the sequences average
+// under 8 tokens; else the chunkwise kernel wherever the gate allows it (it
+// is the fastest at every batch size); else the split kernel for few
+// (sequence, head) pairs, else the fused kernel.
 int split_cols_for(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     const int64_t units = (int64_t)num_seqs * cfg->num_heads;
-    if (cfg->prefill_path == KDA_PREFILL_FUSED || cfg->prefill_path == KDA_PREFILL_CHUNK) return 0;
+    if (cfg->prefill_path == KDA_PREFILL_FUSED || cfg->prefill_path == KDA_PREFILL_CHUNK ||
+        cfg->prefill_path == KDA_PREFILL_SHORT)
+        return 0;
     const int c = kda::prefill_split_cols(units);
     if (cfg->prefill_path == KDA_PREFILL_SPLIT) return c ? c : 4;
-    return auto_chunk(cfg, num_seqs, total_tokens) ? 0 : c;
+    if (auto_short(num_seqs, total_tokens, cfg->num_heads) || auto_chunk(cfg, num_seqs, total_tokens)) return 0;
+    return c;
 }
 
 kda_status check_tensors(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
@@ -193,6 +203,9 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
         else if (cfg->prefill_path == KDA_PREFILL_SPLIT)
             return KDA_ERR_INVALID_ARG;
     }
+    if (cfg->prefill_path == KDA_PREFILL_CHUNK && !chunk_supported(cfg)) return KDA_ERR_UNSUPPORTED;
+    if (cfg->prefill_path == KDA_PREFILL_SHORT && !kda::short_supported(total_tokens, cfg->num_heads))
+        return KDA_ERR_UNSUPPORTED;
     st = device_ok();
     if (st != KDA_OK) return st;
     kda::Params p = make_params(cfg, t, num_seqs);
@@ -202,11 +215,12 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     p.dense_len = dense_len;
     const bool bf16 = cfg->act_dtype == KDA_BF16;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool chunk_ok = chunk_supported(cfg);
-    if (cfg->prefill_path == KDA_PREFILL_CHUNK && !chunk_ok) return KDA_ERR_UNSUPPORTED;
     hipError_t e;
     if (obuf)
         e = kda::launch_prefill_split(p, bf16, obuf, cols, s);
+    else if (cfg->prefill_path == KDA_PREFILL_SHORT ||
+             (cfg->prefill_path == KDA_PREFILL_AUTO && auto_short(num_seqs, total_tokens, cfg->num_heads)))
+        e = kda::launch_short(p, bf16, s);
     else if (cfg->prefill_path == KDA_PREFILL_CHUNK ||
              (cfg->prefill_path == KDA_PREFILL_AUTO && auto_chunk(cfg, num_seqs, total_tokens)))
         e = kda::launch_prefill_chunk(p, bf16, s);

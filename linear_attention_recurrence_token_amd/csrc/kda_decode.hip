@@ -215,6 +215,205 @@ void decode_kernel(Params p) {
     }
 }
 
+// ---------------------------------------------------------------- short sequences
+// kda_sequence for sequences of a few tokens: the decode step's layout with a
+// token loop.  The state stays in registers for all of the sequence's tokens
+// (read once, written once), the conv window shifts in registers, and each
+// token's inputs are loaded while the previous token is processed.
+//   thread i < 128:   q_i, k_i (conv, SiLU) and the decay a_i of key channel i;
+//                     it stores (a q_i, a k_i) and (a_i, k_i), unnormalised
+//   thread 128 + j:   v_j
+// The L2 norms are applied after the dot products: u = |k|^-1 S^T (a . k),
+// p = |q|^-1 S^T (a . q), and the update adds (k_i / |k|) delta_j.  Two
+// barriers per token; the per-token LDS values are double-buffered by token
+// parity.  Memory goes through buffer resources (32-bit offsets; the host
+// keeps the sequence's rows under 4 GiB per tensor).
+template <typename Act>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void short_seq_kernel(Params p) {
+    constexpr int NT = 256;
+    using Sh = DecodeShape<NT>;
+    typedef BufAct<Act> BA;
+    const int slot_n = blockIdx.x / p.H;
+    const int h = blockIdx.x - slot_n * p.H;
+    int n = slot_n;
+    if (p.seq_order) {
+        n = p.seq_order[slot_n];
+        if (n < 0 || n >= p.num_seqs) return;
+    }
+    const Range rng = seq_range(p, n);
+    if (rng.len <= 0) return;
+    const int64_t unit = (int64_t)n * p.H + h;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cg = tid & 31, rg = tid >> 5;
+
+    __shared__ float2 s_aqk[2][DK];        // (a q, a k) per key channel, by token parity
+    __shared__ float2 s_ak[2][DK];         // (a, k) per key channel
+    __shared__ float s_v[2][DV];           // activated v
+    __shared__ float s_red[Sh::NW][4];
+    __shared__ float4 s_up[Sh::NW][32][2];
+
+    float *W = p.win + unit * (PAST * CH);
+    const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+
+    const bool qk_task = tid < DK;
+    const int ch = qk_task ? tid : tid - DK;
+    const int wch = qk_task ? ch : 2 * DK + ch;       // conv / window channel of x0
+    const float4 c0 = *reinterpret_cast<const float4 *>(cw + wch * TAPS);
+    const float4 c1 = *reinterpret_cast<const float4 *>(cw + (qk_task ? DK + ch : wch) * TAPS);
+    float w0[PAST], w1[PAST];              // raw rows before the current token, oldest first
+#pragma unroll
+    for (int j = 0; j < PAST; ++j) {
+        w0[j] = W[j * CH + wch];
+        w1[j] = qk_task ? W[j * CH + DK + ch] : 0.f;
+    }
+    const float eA = qk_task ? __expf(p.A_log[h * DK + ch]) : 0.f;
+    const float dtb = qk_task ? p.dt_bias[h * DK + ch] : 0.f;
+
+    // the sequence's token rows: element offset of (token t, this head, channel c)
+    // is t * rowsz + h * DK + c
+    const int64_t rowsz = (int64_t)p.H * DK;
+    auto rows = [&](const void *base, uint32_t elem) -> Rsrc {
+        return make_rsrc(static_cast<const char *>(base) + rng.lo * rowsz * elem,
+                         (uint32_t)(rng.len * rowsz * elem));
+    };
+    const Rsrc r_q = rows(p.q, BA::ELEM);
+    const Rsrc r_k = rows(p.k, BA::ELEM);
+    const Rsrc r_v = rows(p.v, BA::ELEM);
+    const Rsrc r_f = rows(p.f, 4);
+    const Rsrc r_g = rows(p.g, BA::ELEM);
+    const Rsrc r_y = rows(p.y, BA::ELEM);
+    const Rsrc r_o = rows(p.o_raw, 4);
+    const Rsrc r_b = make_rsrc(p.beta + rng.lo * p.H, (uint32_t)(rng.len * p.H * 4));
+    const uint32_t e_ch = (uint32_t)(h * DK + ch), e_out = (uint32_t)(h * DV + 4 * cg);
+
+    float x0, x1, fa, bt;
+    float2 g01 = make_float2(0.f, 0.f), g23 = g01;
+    auto load_token = [&](int64_t t) {
+        const uint32_t tr = (uint32_t)(t * rowsz);
+        if (qk_task) {                     // wavefronts 0 and 1
+            x0 = bld_one<Act>(r_q, tr + e_ch);
+            x1 = bld_one<Act>(r_k, tr + e_ch);
+            fa = bld_f32(r_f, (tr + e_ch) * 4);
+        } else {
+            x0 = bld_one<Act>(r_v, tr + e_ch);
+            x1 = 0.f;
+            fa = 0.f;
+        }
+        bt = bld_f32(r_b, (uint32_t)((t * p.H + h) * 4));
+        if (tid < 32) {
+            g01 = BA::load2(r_g, tr + e_out);
+            g23 = BA::load2(r_g, tr + e_out + 2);
+        }
+    };
+    load_token(0);
+
+    // state rows rg + 8 m, columns 4 cg .. 4 cg + 3: lane offset plus m as the scalar offset
+    const Rsrc r_s = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
+    const uint32_t s_lane = (uint32_t)((rg * DV + 4 * cg) * 4);
+    float4 s[Sh::RPT];
+#pragma unroll
+    for (int m = 0; m < Sh::RPT; ++m) s[m] = bld_f32x4(r_s, s_lane, (uint32_t)(m * Sh::NRG * DV * 4));
+
+#pragma unroll 1
+    for (int64_t t = 0; t < rng.len; ++t) {
+        const int par = (int)(t & 1);
+        const float cx0 = x0, cx1 = x1, cfa = fa, b = bt;
+        const float2 cg01 = g01, cg23 = g23;
+        if (t + 1 < rng.len) load_token(t + 1);
+
+        // ---- pre-step of token t
+        float qq = 0.f, kk = 0.f, qk = 0.f;
+        const float a0 = silu(c0.x * w0[0] + c0.y * w0[1] + c0.z * w0[2] + c0.w * cx0);
+        if (qk_task) {
+            const float ak = silu(c1.x * w1[0] + c1.y * w1[1] + c1.z * w1[2] + c1.w * cx1);
+            const float al = decay(cfa, eA, dtb, p.gate_mode, p.lb);
+            s_aqk[par][ch] = make_float2(al * a0, al * ak);
+            s_ak[par][ch] = make_float2(al, ak);
+            qq = a0 * a0; kk = ak * ak; qk = a0 * ak;
+        } else {
+            s_v[par][ch] = a0;
+        }
+        w0[0] = w0[1]; w0[1] = w0[2]; w0[2] = cx0;
+        w1[0] = w1[1]; w1[1] = w1[2]; w1[2] = cx1;
+        qq = sum64(qq); kk = sum64(kk); qk = sum64(qk);
+        if (lane == 0) { s_red[wave][0] = qq; s_red[wave][1] = kk; s_red[wave][2] = qk; }
+        __syncthreads();
+        qq = 0.f; kk = 0.f; qk = 0.f;
+#pragma unroll
+        for (int w = 0; w < Sh::NW; ++w) { qq += s_red[w][0]; kk += s_red[w][1]; qk += s_red[w][2]; }
+        const float rq = rsqrtf(qq + p.l2_eps);
+        const float rk = rsqrtf(kk + p.l2_eps);
+        qk *= rq * rk;
+
+        // ---- unnormalised S^T (a . k), S^T (a . q) over this thread's rows
+        float4 u = make_float4(0.f, 0.f, 0.f, 0.f), pq = u;
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) {
+            const float2 c = s_aqk[par][rg + Sh::NRG * m];
+            u.x += s[m].x * c.y; u.y += s[m].y * c.y; u.z += s[m].z * c.y; u.w += s[m].w * c.y;
+            pq.x += s[m].x * c.x; pq.y += s[m].y * c.x; pq.z += s[m].z * c.x; pq.w += s[m].w * c.x;
+        }
+        u.x += __shfl_xor(u.x, 32); u.y += __shfl_xor(u.y, 32);
+        u.z += __shfl_xor(u.z, 32); u.w += __shfl_xor(u.w, 32);
+        pq.x += __shfl_xor(pq.x, 32); pq.y += __shfl_xor(pq.y, 32);
+        pq.z += __shfl_xor(pq.z, 32); pq.w += __shfl_xor(pq.w, 32);
+        if (lane < 32) { s_up[wave][cg][0] = u; s_up[wave][cg][1] = pq; }
+        __syncthreads();
+        u = s_up[0][cg][0]; pq = s_up[0][cg][1];
+#pragma unroll
+        for (int w = 1; w < Sh::NW; ++w) {
+            const float4 a = s_up[w][cg][0], c = s_up[w][cg][1];
+            u.x += a.x; u.y += a.y; u.z += a.z; u.w += a.w;
+            pq.x += c.x; pq.y += c.y; pq.z += c.z; pq.w += c.w;
+        }
+
+        // ---- delta, readout, update in registers
+        const float4 vv = *reinterpret_cast<const float4 *>(&s_v[par][4 * cg]);
+        float4 d, o, dk;
+        d.x = b * (vv.x - rk * u.x); d.y = b * (vv.y - rk * u.y);
+        d.z = b * (vv.z - rk * u.z); d.w = b * (vv.w - rk * u.w);
+        o.x = rq * pq.x + qk * d.x; o.y = rq * pq.y + qk * d.y;
+        o.z = rq * pq.z + qk * d.z; o.w = rq * pq.w + qk * d.w;
+        dk.x = rk * d.x; dk.y = rk * d.y; dk.z = rk * d.z; dk.w = rk * d.w;
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) {
+            const float2 c = s_ak[par][rg + Sh::NRG * m];      // (a_i, k_i)
+            s[m].x = c.x * s[m].x + c.y * dk.x; s[m].y = c.x * s[m].y + c.y * dk.y;
+            s[m].z = c.x * s[m].z + c.y * dk.z; s[m].w = c.x * s[m].w + c.y * dk.w;
+        }
+
+        // ---- RMSNorm over the 128 outputs, gamma, sigmoid gate
+        const float ss = sum32(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+        if (tid < 32) {
+            const float r = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
+            const float4 gm = *reinterpret_cast<const float4 *>(p.gamma + 4 * cg);
+            const uint32_t e = (uint32_t)(t * rowsz) + e_out;
+            float2 y01, y23;
+            y01.x = sigmoid(cg01.x) * gm.x * o.x * r;
+            y01.y = sigmoid(cg01.y) * gm.y * o.y * r;
+            y23.x = sigmoid(cg23.x) * gm.z * o.z * r;
+            y23.y = sigmoid(cg23.y) * gm.w * o.w * r;
+            BA::store2(r_y, e, y01);
+            BA::store2(r_y, e + 2, y23);
+            if (p.o_raw) {
+                bst_f32x2(r_o, make_float2(o.x, o.y), e * 4);
+                bst_f32x2(r_o, make_float2(o.z, o.w), (e + 2) * 4);
+            }
+        }
+    }
+
+    // ---- state and window out
+#pragma unroll
+    for (int m = 0; m < Sh::RPT; ++m) bst_f32x4(r_s, s[m], s_lane, (uint32_t)(m * Sh::NRG * DV * 4));
+#pragma unroll
+    for (int j = 0; j < PAST; ++j) {
+        W[j * CH + wch] = w0[j];
+        if (qk_task) W[j * CH + DK + ch] = w1[j];
+    }
+}
+
 template <int NT, bool NT_LOAD, bool NT_STORE, bool BLOCKED = false, int WPE = 1>
 hipError_t launch_decode_as(const Params &p, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)(p.num_seqs * p.H)), block(NT);
@@ -235,6 +434,20 @@ hipError_t launch_decode(const Params &p, bool bf16, hipStream_t stream) {
     if (state_bytes > (int64_t(256) << 20))
         return launch_decode_as<256, true, true, true>(p, bf16, stream);
     return launch_decode_as<256, true, true, false>(p, bf16, stream);
+}
+
+bool short_supported(int64_t total_tokens, int32_t num_heads) {
+    // per-tensor token rows of one sequence addressed with 32-bit byte offsets
+    return total_tokens * num_heads * DK * 4 < (int64_t(1) << 32);
+}
+
+hipError_t launch_short(const Params &p, bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.num_seqs * p.H)), block(256);
+    if (bf16)
+        hipLaunchKernelGGL((short_seq_kernel<BF16>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((short_seq_kernel<F32>), grid, block, 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace kda

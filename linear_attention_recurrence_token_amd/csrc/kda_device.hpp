@@ -152,6 +152,17 @@ __device__ __forceinline__ void bst_f32x2(Rsrc r, float2 v, uint32_t voff, uint3
     const u32x2 w = {__float_as_uint(v.x), __float_as_uint(v.y)};
     __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
 }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 bld_f32x4(Rsrc r, uint32_t voff, uint32_t soff = 0) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                       __uint_as_float(w.w));
+}
+__device__ __forceinline__ void bst_f32x4(Rsrc r, float4 v, uint32_t voff, uint32_t soff = 0) {
+    const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                     __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, 0);
+}
 // two consecutive activations (element index i, even) through a buffer
 template <typename Act> struct BufAct;
 // Raw2 / load_raw2 / unpack2 split a load from its conversion, so that a load
@@ -181,6 +192,14 @@ template <> struct BufAct<BF16> {
         __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(x.x, x.y), r, i * 2, 0, 0);
     }
 };
+
+// one activation (element index i) through a buffer
+template <typename Act> __device__ __forceinline__ float bld_one(Rsrc r, uint32_t i);
+template <> __device__ __forceinline__ float bld_one<F32>(Rsrc r, uint32_t i) { return bld_f32(r, i * 4); }
+template <> __device__ __forceinline__ float bld_one<BF16>(Rsrc r, uint32_t i) {
+    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, (i & ~1u) * 2, 0, 0);
+    return __uint_as_float((i & 1u) ? (w & 0xffff0000u) : (w << 16));
+}
 
 // ------------------------------------------------------------ sequences
 

@@ -36,6 +36,11 @@ struct Params {
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_decode(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill(const Params &p, bool bf16, hipStream_t stream);
+// Prefill of short sequences with the decode step's layout and a token loop
+// (any gate form); short_supported: the batch's token rows fit its 32-bit
+// buffer offsets.
+bool short_supported(int64_t total_tokens, int32_t num_heads);
+hipError_t launch_short(const Params &p, bool bf16, hipStream_t stream);
 
 // Column-split prefill for workloads with few (sequence, head) pairs, where
 // one workgroup per pair would leave most of the GPU idle: each pair's state

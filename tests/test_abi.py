@@ -85,7 +85,7 @@ def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8, ws=None, ws_bytes=0):
     ({"l2_eps": -1.0}, kda.KDA_ERR_INVALID_ARG),
     ({"rms_eps": float("nan")}, kda.KDA_ERR_INVALID_ARG),
     ({"gate_lower_bound": float("nan")}, kda.KDA_ERR_INVALID_ARG),
-    ({"prefill_path": 4}, kda.KDA_ERR_INVALID_ARG),
+    ({"prefill_path": 5}, kda.KDA_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected(lib, over, status):
     t = _fake_tensors()
@@ -131,10 +131,10 @@ def test_beta_needs_only_word_alignment(lib):
 
 
 def test_workspace_size_and_checks(lib):
-    # bounded gate: AUTO takes the chunkwise kernel, which needs no workspace,
-    # unless the sequences are very short on average (then split / fused)
+    # bounded gate: AUTO takes the chunkwise kernel, or the short-sequence
+    # kernel when the sequences are very short on average; neither needs one
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 100) == 0
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 14) == 14 * 4 * 128 * 4
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 14) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 16) == 0
     # other gates, few (sequence, head) pairs: the split path wants one fp32
     # readout row per token.head
@@ -142,6 +142,7 @@ def test_workspace_size_and_checks(lib):
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(**lit)), 2, 100) == 100 * 4 * 128 * 4
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=1)), 2, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=3)), 2, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=4)), 2, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, **lit)), 16, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, prefill_path=2)), 16, 100) \
         == 100 * 64 * 128 * 4
@@ -191,3 +192,13 @@ def test_python_binding_rejects_host_tensors():
                            dt_bias=torch.zeros(1, 128), gamma=torch.zeros(128),
                            state=torch.zeros(1, 1, 128, 128), conv_win=torch.zeros(1, 1, 3, 384),
                            y=torch.zeros(1, 1, 128))
+
+
+def test_path_support_checked_before_the_device(lib):
+    # both refusals depend on the arguments only, so they come back without a GPU
+    t = _fake_tensors()
+    assert _seq(lib, _cfg(prefill_path=3, gate_mode=kda.KDA_GATE_RAW), t) == kda.KDA_ERR_UNSUPPORTED
+    assert _seq(lib, _cfg(prefill_path=3, gate_lower_bound=-8.0), t) == kda.KDA_ERR_UNSUPPORTED
+    # the short path addresses a batch's token rows with 32-bit offsets
+    big = (1 << 32) // (4 * 128 * 4) + 2           # tokens with H = 4 past 4 GiB of fp32 rows
+    assert _seq(lib, _cfg(prefill_path=4), t, n=2, total=big) == kda.KDA_ERR_UNSUPPORTED

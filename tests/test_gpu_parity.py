@@ -26,8 +26,8 @@ def note(msg):
 
 # ---------------------------------------------------------------- small sizes
 
-PATHS = pytest.mark.parametrize("path", ["fused", "split", "chunk"])
-PATHS_ANY_GATE = pytest.mark.parametrize("path", ["fused", "split"])
+PATHS = pytest.mark.parametrize("path", ["fused", "split", "chunk", "short"])
+PATHS_ANY_GATE = pytest.mark.parametrize("path", ["fused", "split", "short"])
 
 
 @PATHS
@@ -99,7 +99,7 @@ def test_ragged_edges(gpu, act, path):
                        bf16=(act == "bf16"), label="ragged")
 
 
-@pytest.mark.parametrize("path", ["auto", "fused", "split", "chunk"])
+@pytest.mark.parametrize("path", ["auto", "fused", "split", "chunk", "short"])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_many_short_sequences(gpu, act, path):
     # lengths 1..16 over many sequences: below, at and around one chunk, and
@@ -127,7 +127,7 @@ def test_chunk_many_pairs_short_average(gpu, act):
                            _gpu.oracle_sequence(w), bf16=act == "bf16", label="many pairs")
 
 
-@pytest.mark.parametrize("path", ["auto", "chunk"])
+@pytest.mark.parametrize("path", ["auto", "chunk", "short"])
 def test_short_average_with_long_sequences(gpu, path):
     # a batch that is short on average (the chunk path's single-buffered
     # variant) but holds a few sequences of several chunks
@@ -195,7 +195,7 @@ def test_decode_large_state(gpu):
 
 # ---------------------------------------------------------------- invariances
 
-@pytest.mark.parametrize("other", ["split", "chunk"])
+@pytest.mark.parametrize("other", ["split", "chunk", "short"])
 def test_prefill_paths_agree(gpu, other):
     w = synth.workload(3, scale={"N": 3, "H": 5, "T": 131})
     note("%s vs fused prefill" % other)
@@ -317,7 +317,7 @@ def test_full_batched_prefill_16x64x2048(gpu):
     _sampled(w, full, [0, 11], [3, 60], bf16=True)
 
 
-@pytest.mark.parametrize("path", ["auto", "fused", "chunk"])
+@pytest.mark.parametrize("path", ["auto", "fused", "chunk", "short"])
 def test_full_short_prefill_64x32x13(gpu, path):
     # the short multi-token case: 13 tokens per sequence over a decode-sized
     # batch, state and window carried in; the oracle covers every pair
