@@ -494,8 +494,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // i - 1, loads for chunk i + 2 (the epilogue waits for its gate loads
     // before the next chunk's loads are issued: the memory counter drains in
     // order)
+    // (past the last chunk the pre-step and the operands run on masked tokens
+    // into buffers nothing reads: running them unconditionally keeps each half
+    // one straight-line block for the scheduler)
     auto tokens_half1 = [&](int64_t i, int cur) {
-        if (i + 1 < NC) {
+        {
             float2 xq[RAWR], xk[RAWR], xv[RAWR];
 #pragma unroll
             for (int r = 0; r < RAWR; ++r) {
@@ -564,9 +567,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         // ================= half 2
         if (mfma_first) {
             update(cur);
-            if (i + 1 < NC) operands(cur ^ 1);
+            operands(cur ^ 1);
         } else {
-            if (i + 1 < NC) operands(cur ^ 1);
+            operands(cur ^ 1);
             update(cur);
         }
         __syncthreads();
