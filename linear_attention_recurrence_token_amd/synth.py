@@ -354,3 +354,63 @@ def to_device(w: Workload, device="cuda:0", *, with_o_raw: bool = True, decode_s
              o_raw=torch.empty((T, w.H, w.dv), dtype=torch.float32, device=device) if with_o_raw else None)
     d["cu_seqlens"] = torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(device)
     return d
+
+
+# --- inputs of the projections around the step -------------------------------
+
+@dataclasses.dataclass
+class ProjectionInputs:
+    """Host copy of the projection problem for T token rows (fp32 arrays;
+    bf16 problems hold bf16-exact values in x, y, w_g and w_o).
+
+    Hidden width D and rank r are not fixed by the method's description: the
+    measured shapes take D = H * dk (the heads' total width) and r = dk."""
+    name: str
+    T: int
+    H: int
+    D: int
+    r: int
+    act_dtype: str                 # x, y, w_g, w_o, g, out
+    x: np.ndarray                  # [T, D] hidden rows
+    w_fa: np.ndarray               # [r, D]       fp32
+    w_fb: np.ndarray               # [H * 128, r] fp32
+    w_bp: np.ndarray               # [H, D]       fp32
+    w_g: np.ndarray                # [H * 128, D] act dtype
+    y: np.ndarray                  # [T, H * 128] act dtype (stand-in for the step's output)
+    w_o: np.ndarray                # [D, H * 128] act dtype
+
+
+def projection_inputs(name: str, *, seed: int, T: int, H: int, D: int, r: int = 128,
+                      act_dtype: str = "f32", dk: int = 128, dv: int = 128) -> ProjectionInputs:
+    """x, y ~ N(0, 1); every weight ~ N(0, 1 / fan_in), so that each product
+    is ~N(0, 1) per output (beta logits ~N(0, 1) as in the step's own inputs).
+    bf16 problems round x, y, w_g, w_o to bf16 (ties to even)."""
+    root = np.random.SeedSequence([seed, 0x5052_4F4A])
+    ss_x, ss_fa, ss_fb, ss_bp, ss_g, ss_y, ss_o = root.spawn(7)
+    x = _normal(ss_x, (T, D))
+    w_fa = _normal(ss_fa, (r, D), D ** -0.5)
+    w_fb = _normal(ss_fb, (H * dk, r), r ** -0.5)
+    w_bp = _normal(ss_bp, (H, D), D ** -0.5)
+    w_g = _normal(ss_g, (H * dv, D), D ** -0.5)
+    y = _normal(ss_y, (T, H * dv))
+    w_o = _normal(ss_o, (D, H * dv), (H * dv) ** -0.5)
+    if act_dtype == "bf16":
+        for a in (x, w_g, y, w_o):
+            _round_inplace_bf16(a)
+    elif act_dtype != "f32":
+        raise ValueError(act_dtype)
+    return ProjectionInputs(name=name, T=T, H=H, D=D, r=r, act_dtype=act_dtype, x=x, w_fa=w_fa,
+                            w_fb=w_fb, w_bp=w_bp, w_g=w_g, y=y, w_o=w_o)
+
+
+def projection_workload(index: int, *, scale: Optional[dict] = None) -> ProjectionInputs:
+    """The projections for the token rows of step workload `index` (1: the
+    64 x 32 decode step's 64 rows; 2: 1 x 32 x 8192 fp32; 3: 16 x 64 x 2048
+    bf16), D = H * 128, r = 128; `scale` overrides T, H, D, r for tests."""
+    s = dict(scale or {})
+    shapes = {1: (64, 32, "f32"), 2: (8192, 32, "f32"), 3: (32768, 64, "bf16")}
+    T, H, dt = shapes[index]
+    T, H = s.get("T", T), s.get("H", H)
+    D, r = s.get("D", H * 128), s.get("r", 128)
+    return projection_inputs("projections T=%d H=%d D=%d r=%d %s" % (T, H, D, r, dt), seed=100 + index,
+                             T=T, H=H, D=D, r=r, act_dtype=dt)
