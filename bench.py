@@ -7,9 +7,10 @@ to back with every step's inputs already resident in HBM.  value = total
 token.heads per second.  Alongside: the decode kernel's HBM roofline, the CPU
 oracle timed on this host on a bounded sample (its only use here; parity is
 checked by the GPU tests at these same sizes), a disclosed over-cache decode
-run, and the prefill workloads (kda_sequence): the long ones with their ALU
+run, the prefill workloads (kda_sequence): the long ones with their ALU
 roofline, the short multi-token one (64 x 32 x 13 tokens) with its HBM
-roofline.
+roofline; and the projections on either side of the step (low-rank decay and
+beta, output gate, output) for the decode and the batched-prefill token rows.
 
   python bench.py [--gpus 1] [--steps 1000] [--warmup 10]
                   [--prefill default|all|none] [--no-cpu-baseline] [--no-overcache]
@@ -247,6 +248,87 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix cores, published
+MFMA_FP32_PEAK_TFLOPS = 157.3         # MI355X dense fp32 matrix cores, published
+
+
+def bench_projections(torch, kda, synth, dev, idx, runs):
+    """The matrix products on either side of the step for the token rows of
+    step workload idx: kda_lowrank_gates (f and beta), kda_gate_projection
+    (g) and kda_output_projection (W_o y), each timed alone."""
+    import numpy as np
+    p = synth.projection_workload(idx)
+    bf = p.act_dtype == "bf16"
+    act = torch.bfloat16 if bf else torch.float32
+    eb = 2 if bf else 4
+    cfg = kda.KdaConfig(num_heads=p.H, act_dtype=kda.KDA_BF16 if bf else kda.KDA_F32)
+    x = torch.from_numpy(p.x).to(dev).to(act)
+    wab = torch.from_numpy(np.concatenate([p.w_fa, p.w_bp])).to(dev)
+    wfb = torch.from_numpy(p.w_fb).to(dev)
+    f = torch.empty(p.T, p.H, 128, device=dev)
+    beta = torch.empty(p.T, p.H, device=dev)
+    wg = torch.from_numpy(p.w_g).to(dev).to(act)
+    g = torch.empty(p.T, p.H, 128, device=dev, dtype=act)
+    y = torch.from_numpy(p.y).to(dev).to(act).view(p.T, p.H, 128)
+    wo = torch.from_numpy(p.w_o).to(dev).to(act)
+    out = torch.empty(p.T, p.D, device=dev, dtype=act)
+    T, H, D, r, HD = p.T, p.H, p.D, p.r, p.H * 128
+    stream = torch.cuda.current_stream()
+    ws = {}
+    for which, rank in ((kda.KDA_PROJ_LOWRANK_GATES, r), (kda.KDA_PROJ_GATE, 0), (kda.KDA_PROJ_OUTPUT, 0)):
+        n = kda.projection_workspace_size(cfg, which, D, T, rank)
+        ws[which] = torch.empty(max(n, 1), dtype=torch.uint8, device=dev) if n > 0 else None
+
+    def timed(fn):
+        times = []
+        for rep in range(runs + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    res = {"workload": p.name, "tokens": T, "heads": H, "hidden": D, "rank": r, "act_dtype": p.act_dtype}
+    ms = timed(lambda: kda.kda_lowrank_gates(cfg, x=x, w_fa_bp=wab, w_fb=wfb, f=f, beta=beta,
+                                             workspace=ws[kda.KDA_PROJ_LOWRANK_GATES]))
+    # algorithmic bytes: x, both weights, f and beta out, the rank-r factor out and back in
+    by = T * D * eb + (r + H) * D * 4 + HD * r * 4 + T * HD * 4 + T * H * 4 + 2 * T * r * 4
+    fl = 2 * T * D * (r + H) + 2 * T * r * HD
+    res["lowrank_gates"] = {
+        "ms": ms, "tflops_fp32_equiv": fl / (ms * 1e-3) / 1e12,
+        "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None}}
+    for name, fn, K, N in (
+            ("gate_projection", lambda: kda.kda_gate_projection(cfg, x=x, w_g=wg, g=g,
+                                                                workspace=ws[kda.KDA_PROJ_GATE]), D, HD),
+            ("output_projection", lambda: kda.kda_output_projection(cfg, y=y, w_o=wo, out=out,
+                                                                    workspace=ws[kda.KDA_PROJ_OUTPUT]), HD, D)):
+        ms = timed(fn)
+        fl = 2 * T * K * N
+        by = (T * K + N * K + T * N) * eb
+        tf = fl / (ms * 1e-3) / 1e12
+        gbs = by / (ms * 1e-3) / 1e9
+        # the bound from the arithmetic intensity against the machine balance
+        # of the data type's matrix-core peak (fp32 problems run as three
+        # bf16 products per product, reported against the fp32 peak)
+        peak = MFMA_BF16_PEAK_TFLOPS if bf else MFMA_FP32_PEAK_TFLOPS
+        if fl / by < peak * 1e3 / HBM_PEAK_GBS:
+            rl = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+        else:
+            rl = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
+                  "traffic": None}
+            if not bf:
+                rl["bf16_mfma_issued_frac"] = 3 * tf / MFMA_BF16_PEAK_TFLOPS
+        res[name] = {"ms": ms, "tflops": tf, "hbm_GBps_algorithmic": gbs, "roofline": rl}
+    del x, wab, wfb, f, beta, wg, g, y, wo, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +336,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prefill", choices=["none", "default", "all"], default="default")
     ap.add_argument("--prefill-runs", type=int, default=5)
+    ap.add_argument("--projections", choices=["none", "default", "all"], default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-overcache", action="store_true")
@@ -293,6 +376,8 @@ def main():
         if args.only == "decode":
             dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup)
             out["us_per_step"] = dec["ms_total"] / steps * 1e3
+        elif args.only.startswith("proj:"):
+            out.update(bench_projections(torch, kda, synth, dev, int(args.only.split(":")[1]), args.prefill_runs))
         elif args.only.startswith("prefill:"):
             r = bench_prefill(torch, kda, synth, dev, int(args.only.split(":")[1]), args.prefill_runs)
             out.update(r)
@@ -358,6 +443,14 @@ def main():
             r = bench_prefill(torch, kda, synth, dev, idx, args.prefill_runs)
             log("prefill: %s" % r)
             result["prefill"].append(r)
+
+    if args.projections != "none":
+        result["projections"] = []
+        for idx in ([1, 3] if args.projections == "default" else [1, 2, 3]):
+            log("projections for workload %d" % idx)
+            r = bench_projections(torch, kda, synth, dev, idx, args.prefill_runs)
+            log("projections: %s" % r)
+            result["projections"].append(r)
 
     result["device"] = {"name": torch.cuda.get_device_name(dev), "rocm_smi_before": smi_before,
                         "rocm_smi_after": rocm_smi_snapshot()}

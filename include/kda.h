@@ -197,6 +197,75 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t,
 int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                     int64_t total_tokens);
 
+/*
+ * Projections on either side of the step: matrix products on the matrix
+ * cores, one token row at a time (rows are independent).  Not part of the
+ * step; they produce its f, beta and g inputs and consume its output y.
+ * Layouts: row-major, device memory, 16-byte aligned (beta: 4-byte); no
+ * output may overlap an input or another output.  An fp32 operand enters the
+ * matrix cores split into two bf16 parts, the product formed from three bf16
+ * products (about 2^-16 relative error each, fp32 sums); bf16 x bf16
+ * products are exact, with fp32 sums.  Errors as for the step: nothing is
+ * enqueued unless KDA_OK or KDA_ERR_LAUNCH comes back; tokens == 0 is a no-op
+ * after cfg is checked.  workspace (caller-owned, 16-byte aligned, scratch)
+ * lets calls with few token rows split each sum across more workgroups; its
+ * size for the fastest run is kda_projection_workspace_size.
+ */
+typedef enum kda_projection {
+    KDA_PROJ_LOWRANK_GATES = 0,  /* kda_lowrank_gates     */
+    KDA_PROJ_GATE = 1,           /* kda_gate_projection   */
+    KDA_PROJ_OUTPUT = 2          /* kda_output_projection */
+} kda_projection;
+
+/*
+ * Bytes of workspace for the fastest run of projection `which` (rank is read
+ * for KDA_PROJ_LOWRANK_GATES only), or a negative kda_status.
+ */
+int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int32_t hidden,
+                                      int32_t rank, int64_t tokens);
+
+/*
+ * The decay pre-activation and beta from the layer's hidden rows
+ * ("Kimi K3 Metal Gap Analysis", §2 KDA Attention, row "Decay compute": the
+ * decay is formed from W_fb W_fa x; "Metal (Apple GPU) backend for Kimi K3",
+ * table "What runs where": fa, fb and bp are fp32 low-rank products; beta as
+ * the sigmoid of the bp product is a reading).  For each token row t:
+ *   a[t]       = W_fa x[t]                               (rank values)
+ *   f[t, h, i] = sum_j W_fb[h * 128 + i, j] a[t, j]
+ *   beta[t, h] = sigmoid(W_bp[h] . x[t])
+ * x [tokens, hidden] act dtype; w_fa_bp [rank + H, hidden] fp32 (the rank
+ * rows of W_fa, then the H rows of W_bp, so that one pass over x serves
+ * both); w_fb [H * 128, rank] fp32; f [tokens, H, 128] fp32 out and beta
+ * [tokens, H] fp32 out: the f and beta inputs of kda_token_step and
+ * kda_sequence.  workspace: required, at least tokens * rank * 4 bytes
+ * rounded up to 256 (it holds a).  hidden: a positive multiple of 32;
+ * rank: a multiple of 32 in [32, 1024].
+ */
+kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *w_fa_bp,
+                             const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
+                             float *f, float *beta, void *workspace, int64_t workspace_bytes,
+                             void *stream);
+
+/*
+ * g = W_g x, the input of the step's output gate (Gap Analysis §2, row "O
+ * projection").  x [tokens, hidden] act dtype; w_g [H * 128, hidden] act
+ * dtype; g [tokens, H, 128] act dtype out.  hidden: a positive multiple of
+ * 32.  workspace optional.
+ */
+kda_status kda_gate_projection(const kda_config *cfg, const void *x, const void *w_g,
+                               int32_t hidden, int64_t tokens, void *g,
+                               void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * out = W_o y, the output projection of the step's output (Gap Analysis §2,
+ * row "O projection").  y [tokens, H, 128] act dtype; w_o [hidden, H * 128]
+ * act dtype; out [tokens, hidden] act dtype.  hidden: a positive multiple of
+ * 4.  workspace optional.
+ */
+kda_status kda_output_projection(const kda_config *cfg, const void *y, const void *w_o,
+                                 int32_t hidden, int64_t tokens, void *out,
+                                 void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kda_status_string(int32_t status);
 

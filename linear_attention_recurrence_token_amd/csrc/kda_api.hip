@@ -3,6 +3,7 @@
 // was enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -109,6 +110,68 @@ kda_status check_tensors(const kda_config *cfg, const kda_tensors *t, int32_t nu
     }
     if ((int64_t)num_seqs * cfg->num_heads > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
     return KDA_OK;
+}
+
+// the configuration fields the projections use (heads, activation type, and
+// the same validity rules as the step)
+kda_status check_proj_config(const kda_config *cfg) {
+    kda_tensors dummy;
+    std::memset(&dummy, 0, sizeof(dummy));
+    return check_config(cfg, &dummy, 0);
+}
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+};
+bool overlap(Span a, Span b) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+// every pointer non-null and 16-byte aligned; no output overlaps an input or
+// another output
+kda_status check_spans(const Span *ins, int n_in, const Span *outs, int n_out) {
+    for (int i = 0; i < n_in; ++i)
+        if (!ins[i].p || !aligned16(ins[i].p)) return KDA_ERR_INVALID_ARG;
+    for (int o = 0; o < n_out; ++o) {
+        if (!outs[o].p || !aligned16(outs[o].p)) return KDA_ERR_INVALID_ARG;
+        for (int i = 0; i < n_in; ++i)
+            if (overlap(outs[o], ins[i])) return KDA_ERR_INVALID_ARG;
+        for (int b = o + 1; b < n_out; ++b)
+            if (overlap(outs[o], outs[b])) return KDA_ERR_INVALID_ARG;
+    }
+    return KDA_OK;
+}
+
+constexpr int32_t PROJ_MAX_HIDDEN = 1 << 20;
+constexpr int32_t PROJ_MAX_RANK = 1024;
+constexpr int64_t PROJ_MAX_TOKENS = int64_t(1) << 31;
+constexpr int64_t WS_ALIGN = 256;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// the two products of the low-rank gates: x -> (a | beta), a -> f
+void lowrank_products(const kda_config *cfg, const void *x, const float *w_fa_bp, const float *w_fb,
+                      int32_t hidden, int32_t rank, int64_t tokens, float *f, float *beta, float *a,
+                      kda::ProjGemm &g1, kda::ProjGemm &g2) {
+    const int32_t H = cfg->num_heads;
+    g1.A = x; g1.B = w_fa_bp; g1.M = tokens; g1.N = rank + H; g1.K = hidden;
+    g1.a_bf16 = cfg->act_dtype == KDA_BF16; g1.b_bf16 = false; g1.c_bf16 = false;
+    g1.C0 = a; g1.ldc0 = rank; g1.C1 = beta; g1.ldc1 = H; g1.n_split = rank;
+    g2.A = a; g2.B = w_fb; g2.M = tokens; g2.N = H * kda::DK; g2.K = rank;
+    g2.a_bf16 = false; g2.b_bf16 = false; g2.c_bf16 = false;
+    g2.C0 = f; g2.ldc0 = (int64_t)H * kda::DK; g2.C1 = nullptr; g2.ldc1 = 0; g2.n_split = g2.N;
+}
+
+// one product with the activation type on every side
+kda::ProjGemm act_product(const kda_config *cfg, const void *A, const void *B, int64_t M, int32_t N,
+                          int32_t K, void *C) {
+    kda::ProjGemm g;
+    const bool bf = cfg->act_dtype == KDA_BF16;
+    g.A = A; g.B = B; g.M = M; g.N = N; g.K = K;
+    g.a_bf16 = g.b_bf16 = g.c_bf16 = bf;
+    g.C0 = C; g.ldc0 = N; g.C1 = nullptr; g.ldc1 = 0; g.n_split = N;
+    return g;
 }
 
 kda::Params make_params(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs) {
@@ -227,6 +290,117 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     else
         e = kda::launch_prefill(p, bf16, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int32_t hidden,
+                                      int32_t rank, int64_t tokens) {
+    const kda_status st = check_proj_config(cfg);
+    if (st != KDA_OK) return st;
+    if (hidden <= 0 || hidden > PROJ_MAX_HIDDEN || tokens < 0 || tokens > PROJ_MAX_TOKENS)
+        return KDA_ERR_INVALID_ARG;
+    const int32_t HD = cfg->num_heads * kda::DV;
+    if (tokens == 0) return 0;
+    if (which == KDA_PROJ_LOWRANK_GATES) {
+        if (rank < 32 || rank > PROJ_MAX_RANK || rank % 32 != 0 || hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
+        kda::ProjGemm g1, g2;
+        lowrank_products(cfg, nullptr, nullptr, nullptr, hidden, rank, tokens, nullptr, nullptr, nullptr, g1, g2);
+        const int64_t scratch = std::max(kda::proj_gemm_scratch_bytes(g1), kda::proj_gemm_scratch_bytes(g2));
+        return round_up(tokens * rank * 4, WS_ALIGN) + scratch;
+    }
+    if (which == KDA_PROJ_GATE) {
+        if (hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
+        return kda::proj_gemm_scratch_bytes(act_product(cfg, nullptr, nullptr, tokens, HD, hidden, nullptr));
+    }
+    if (which == KDA_PROJ_OUTPUT) {
+        if (hidden % 4 != 0) return KDA_ERR_INVALID_ARG;
+        return kda::proj_gemm_scratch_bytes(act_product(cfg, nullptr, nullptr, tokens, hidden, HD, nullptr));
+    }
+    return KDA_ERR_INVALID_ARG;
+}
+
+kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *w_fa_bp,
+                             const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
+                             float *f, float *beta, void *workspace, int64_t workspace_bytes,
+                             void *stream) {
+    kda_status st = check_proj_config(cfg);
+    if (st != KDA_OK) return st;
+    if (hidden <= 0 || hidden > PROJ_MAX_HIDDEN || hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
+    if (rank < 32 || rank > PROJ_MAX_RANK || rank % 32 != 0) return KDA_ERR_INVALID_ARG;
+    if (tokens < 0 || tokens > PROJ_MAX_TOKENS || workspace_bytes < 0) return KDA_ERR_INVALID_ARG;
+    if (tokens == 0) return KDA_OK;       // pointers are not inspected
+    const int32_t H = cfg->num_heads;
+    const int64_t eb = cfg->act_dtype == KDA_BF16 ? 2 : 4;
+    const int64_t a_bytes = round_up(tokens * rank * 4, WS_ALIGN);
+    if (workspace_bytes < a_bytes) return KDA_ERR_INVALID_ARG;
+    const Span ins[] = {{x, tokens * hidden * eb}, {w_fa_bp, (int64_t)(rank + H) * hidden * 4},
+                        {w_fb, (int64_t)H * kda::DK * rank * 4}};
+    const Span outs[] = {{f, tokens * H * kda::DK * 4}, {workspace, workspace_bytes}};
+    st = check_spans(ins, 3, outs, 2);
+    if (st != KDA_OK) return st;
+    // beta needs word alignment only (it is written one value at a time)
+    const Span bs = {beta, tokens * H * 4};
+    if (!beta || (reinterpret_cast<uintptr_t>(beta) & 3u)) return KDA_ERR_INVALID_ARG;
+    for (const Span &o : ins)
+        if (overlap(bs, o)) return KDA_ERR_INVALID_ARG;
+    for (const Span &o : outs)
+        if (overlap(bs, o)) return KDA_ERR_INVALID_ARG;
+    kda::ProjGemm g1, g2;
+    float *a = static_cast<float *>(workspace);
+    lowrank_products(cfg, x, w_fa_bp, w_fb, hidden, rank, tokens, f, beta, a, g1, g2);
+    if (!kda::proj_gemm_shape_ok(g1) || !kda::proj_gemm_shape_ok(g2)) return KDA_ERR_INVALID_ARG;
+    st = device_ok();
+    if (st != KDA_OK) return st;
+    float *scratch = reinterpret_cast<float *>(static_cast<char *>(workspace) + a_bytes);
+    const int64_t scratch_bytes = workspace_bytes - a_bytes;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_proj_gemm(g1, scratch_bytes > 0 ? scratch : nullptr, scratch_bytes, s);
+    if (e == hipSuccess) e = kda::launch_proj_gemm(g2, scratch_bytes > 0 ? scratch : nullptr, scratch_bytes, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+namespace {
+kda_status run_act_product(const kda_config *cfg, const kda::ProjGemm &g, int64_t a_bytes, int64_t b_bytes,
+                           int64_t c_bytes, void *workspace, int64_t workspace_bytes, void *stream) {
+    if (workspace_bytes < 0 || (workspace && !aligned16(workspace))) return KDA_ERR_INVALID_ARG;
+    const Span ins[] = {{g.A, a_bytes}, {g.B, b_bytes}};
+    const Span outs[] = {{g.C0, c_bytes}, {workspace, workspace ? workspace_bytes : 0}};
+    kda_status st = check_spans(ins, 2, outs, workspace ? 2 : 1);
+    if (st != KDA_OK) return st;
+    if (!kda::proj_gemm_shape_ok(g)) return KDA_ERR_INVALID_ARG;
+    st = device_ok();
+    if (st != KDA_OK) return st;
+    const hipError_t e = kda::launch_proj_gemm(g, static_cast<float *>(workspace), workspace ? workspace_bytes : 0,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+}  // namespace
+
+kda_status kda_gate_projection(const kda_config *cfg, const void *x, const void *w_g, int32_t hidden,
+                               int64_t tokens, void *g, void *workspace, int64_t workspace_bytes,
+                               void *stream) {
+    const kda_status st = check_proj_config(cfg);
+    if (st != KDA_OK) return st;
+    if (hidden <= 0 || hidden > PROJ_MAX_HIDDEN || hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
+    if (tokens < 0 || tokens > PROJ_MAX_TOKENS) return KDA_ERR_INVALID_ARG;
+    if (tokens == 0) return KDA_OK;
+    const int32_t HD = cfg->num_heads * kda::DV;
+    const int64_t eb = cfg->act_dtype == KDA_BF16 ? 2 : 4;
+    return run_act_product(cfg, act_product(cfg, x, w_g, tokens, HD, hidden, g), tokens * hidden * eb,
+                           (int64_t)HD * hidden * eb, tokens * HD * eb, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_output_projection(const kda_config *cfg, const void *y, const void *w_o, int32_t hidden,
+                                 int64_t tokens, void *out, void *workspace, int64_t workspace_bytes,
+                                 void *stream) {
+    const kda_status st = check_proj_config(cfg);
+    if (st != KDA_OK) return st;
+    if (hidden <= 0 || hidden > PROJ_MAX_HIDDEN || hidden % 4 != 0) return KDA_ERR_INVALID_ARG;
+    if (tokens < 0 || tokens > PROJ_MAX_TOKENS) return KDA_ERR_INVALID_ARG;
+    if (tokens == 0) return KDA_OK;
+    const int32_t HD = cfg->num_heads * kda::DV;
+    const int64_t eb = cfg->act_dtype == KDA_BF16 ? 2 : 4;
+    return run_act_product(cfg, act_product(cfg, y, w_o, tokens, hidden, HD, out), tokens * HD * eb,
+                           (int64_t)hidden * HD * eb, tokens * hidden * eb, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

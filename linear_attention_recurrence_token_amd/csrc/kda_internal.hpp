@@ -58,4 +58,30 @@ hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_split(const Params &p, bool bf16, float *obuf, int cols_per_lane,
                                 hipStream_t stream);
 
+// Matrix products on either side of the step (the low-rank decay and beta
+// projections, the output-gate and output projections):
+//   C[m, n] = sum_k A[m, k] B[n, k],  A [M, K] token rows, B [N, K] weights;
+// columns [0, n_split) go to C0 (row stride ldc0, bf16 or fp32), columns
+// [n_split, N) through a sigmoid to C1 (fp32, row stride ldc1).
+struct ProjGemm {
+    const void *A;
+    const void *B;
+    int64_t M;
+    int32_t N, K;
+    bool a_bf16, b_bf16, c_bf16;   // supported: all bf16; bf16 A with fp32 B, C; all fp32
+    void *C0;
+    int64_t ldc0;
+    float *C1;
+    int64_t ldc1;
+    int32_t n_split;
+};
+// K a multiple of 32, n_split a multiple of 4, sizes within the kernel's
+// 32-bit buffer offsets
+bool proj_gemm_shape_ok(const ProjGemm &g);
+// fp32 scratch with which the product splits K across workgroups (few token
+// rows); 0 if it would not split
+int64_t proj_gemm_scratch_bytes(const ProjGemm &g);
+// scratch may be null or smaller than proj_gemm_scratch_bytes: then K is not split
+hipError_t launch_proj_gemm(const ProjGemm &g, float *scratch, int64_t scratch_bytes, hipStream_t stream);
+
 }  // namespace kda

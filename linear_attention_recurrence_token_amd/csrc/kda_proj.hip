@@ -1,0 +1,358 @@
+// kda_proj.hip -- the matrix products on either side of the KDA step, on the
+// matrix cores ("Kimi K3 Metal Gap Analysis", §2 KDA Attention, rows "Decay
+// compute" and "O projection"; "Metal (Apple GPU) backend for Kimi K3", table
+// "What runs where (per layer)": the KDA projections and the fp32 low-rank
+// products fa, fb, bp run as GPU matrix products):
+//
+//   C[m, n] = sum_k A[m, k] B[n, k]     A: token rows [M, K], B: weight rows [N, K]
+//
+// with an epilogue that stores columns [0, n_split) in the output type and
+// passes columns [n_split, N) through a sigmoid (the beta logits).
+//
+// Precision.  Operands enter the 16x16x32 bf16 MFMA as bf16: bf16 data as it
+// is, fp32 data split into hi = bf16(x) and lo = bf16(x - hi).  A product
+// with an fp32 side is formed as hi*hi + hi*lo + lo*hi (the lo*lo term lies
+// below fp32 rounding): about 2^-16 relative error per product, fp32
+// accumulation -- the fp32 products of the pages at a third of the bf16
+// matrix-core rate, still well above what fp32 MFMA gives.  bf16 x bf16 is
+// exact in the products.
+//
+// Tiling.  256 threads = 4 wavefronts in a 2 x 2 grid; a workgroup tile of BM
+// tokens x BN outputs, K consumed 32 columns per stage through a double-
+// buffered LDS tile (rows padded to 80 bytes: the 16 rows a 16-lane group
+// reads fall on distinct banks).  The next stage's global loads are issued
+// before the current stage's MFMAs.  The weight tile is the MFMA's A operand
+// and the token tile its B operand, so each lane's accumulator holds 4
+// consecutive outputs of one token: one 16- (fp32) or 8-byte (bf16) store.
+// Few tiles (decode-sized M) split K across workgroups into an fp32 scratch
+// that a second kernel sums before the epilogue.
+#include "kda_device.hpp"
+
+namespace kda {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int GT = 256;          // threads per workgroup
+constexpr int BK = 32;           // K columns per stage
+constexpr int BKP = BK + 8;      // LDS row length in bf16 elements (80 bytes)
+
+template <typename T> struct Opnd;
+template <> struct Opnd<F32> { static constexpr int PARTS = 2, ELEM = 4; };
+template <> struct Opnd<BF16> { static constexpr int PARTS = 1, ELEM = 2; };
+
+struct GemmArgs {
+    const void *A;               // [M, K] token rows
+    const void *B;               // [N, K] weight rows
+    int64_t M;
+    int32_t N, K;
+    int32_t k_len;               // K columns per split (multiple of BK)
+    int32_t splits;
+    int32_t tiles_m, tiles_n;
+    void *C0;                    // columns [0, n_split), output type
+    int64_t ldc0;
+    float *C1;                   // columns [n_split, N) through a sigmoid, or null
+    int64_t ldc1;
+    int32_t n_split;
+    int32_t np;                  // N rounded up to 4 (row length of the scratch)
+    float *partial;              // [splits, M, np] fp32, or null (epilogue in place)
+};
+
+// one operand tile of R rows x BK columns: global (buffer) loads into
+// registers, then into LDS as bf16 parts
+template <typename T, int R>
+struct Tile {
+    static constexpr int ELEM = Opnd<T>::ELEM;
+    static constexpr int CPR = BK * ELEM / 16;         // 16-byte chunks per row
+    static constexpr int CHUNKS = R * CPR;
+    static constexpr int PER = (CHUNKS + GT - 1) / GT;
+    u32x4 v[PER];
+
+    __device__ __forceinline__ void issue(Rsrc r, int tid, uint32_t row_bytes, uint32_t kbyte) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = tid + GT * j;
+            if (CHUNKS % GT == 0 || c < CHUNKS) {
+                const uint32_t row = c / CPR, col = c % CPR;
+                v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, row * row_bytes + kbyte + col * 16, 0, 0);
+            }
+        }
+    }
+    // s: [PARTS][R][BKP] bf16 bits
+    __device__ __forceinline__ void store(uint16_t *s, int tid) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = tid + GT * j;
+            if (CHUNKS % GT == 0 || c < CHUNKS) {
+                const int row = c / CPR, col = c % CPR;
+                if constexpr (Opnd<T>::PARTS == 2) {
+                    const f32x4v x = {__uint_as_float(v[j].x), __uint_as_float(v[j].y),
+                                      __uint_as_float(v[j].z), __uint_as_float(v[j].w)};
+                    const bf16x4v h = __builtin_convertvector(x, bf16x4v);
+                    const f32x4v hf = __builtin_convertvector(h, f32x4v);
+                    const bf16x4v l = __builtin_convertvector(x - hf, bf16x4v);
+                    uint16_t *p = s + row * BKP + col * 4;
+                    *reinterpret_cast<u32x2 *>(p) = __builtin_bit_cast(u32x2, h);
+                    *reinterpret_cast<u32x2 *>(p + R * BKP) = __builtin_bit_cast(u32x2, l);
+                } else {
+                    *reinterpret_cast<u32x4 *>(s + row * BKP + col * 8) = v[j];
+                }
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <typename TC>
+__device__ __forceinline__ void store_out(const GemmArgs &g, int64_t m, int n, f32x4 v) {
+    if (n < g.n_split) {
+        // n_split is a multiple of 4: the four columns are all on this side
+        if constexpr (Opnd<TC>::PARTS == 2) {
+            *reinterpret_cast<float4 *>(static_cast<float *>(g.C0) + m * g.ldc0 + n) =
+                make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+            uint2 w;
+            w.x = pack_bf16x2(v[0], v[1]);
+            w.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(g.C0) + m * g.ldc0 + n) = w;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (n + r < g.N) g.C1[m * g.ldc1 + (n + r - g.n_split)] = sigmoid(v[r]);
+    }
+}
+
+template <typename TA, typename TB, typename TC, int BM, int BN>
+__global__ __launch_bounds__(GT) void proj_gemm_kernel(GemmArgs g) {
+    constexpr int PA = Opnd<TA>::PARTS, PB = Opnd<TB>::PARTS;
+    constexpr int EA = Opnd<TA>::ELEM, EB = Opnd<TB>::ELEM;
+    constexpr int WM = BM / 2, WN = BN / 2;            // wavefront tile (tokens x outputs)
+    constexpr int TM = WM / 16, TN = WN / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][PA][BM][BKP];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][PB][BN][BKP];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+
+    // workgroup -> (split, tile): consecutive workgroups land on different
+    // XCDs, so first give each XCD a contiguous range of the tile order;
+    // within it, groups of 8 token tiles sweep the weight tiles (the token
+    // rows and the weight rows of a group stay in that XCD's L2)
+    const int total = g.tiles_m * g.tiles_n * g.splits;
+    int bid = blockIdx.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int per_split = g.tiles_m * g.tiles_n;
+    const int z = bid / per_split;
+    const int t = bid - z * per_split;
+    constexpr int GROUP = 8;
+    const int group = t / (GROUP * g.tiles_n);
+    const int first_m = group * GROUP;
+    const int gsize = min(GROUP, g.tiles_m - first_m);
+    const int in_group = t - group * GROUP * g.tiles_n;
+    const int tm = first_m + in_group % gsize, tn = in_group / gsize;
+
+    const int64_t m0 = (int64_t)tm * BM;
+    const int n0 = tn * BN;
+    const int rows_a = (int)min((int64_t)BM, g.M - m0);
+    const int rows_b = min(BN, g.N - n0);
+    // one buffer resource per tile: rows past the end read as zero
+    const Rsrc ra = make_rsrc(static_cast<const char *>(g.A) + m0 * g.K * EA, (uint32_t)(rows_a * g.K * EA));
+    const Rsrc rb = make_rsrc(static_cast<const char *>(g.B) + (int64_t)n0 * g.K * EB,
+                              (uint32_t)(rows_b * g.K * EB));
+    const int k0 = z * g.k_len;
+    const int nst = min(g.k_len, g.K - k0) / BK;
+
+    f32x4 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Tile<TA, BM> la;
+    Tile<TB, BN> lb;
+    la.issue(ra, tid, g.K * EA, k0 * EA);
+    lb.issue(rb, tid, g.K * EB, k0 * EB);
+    la.store(&sA[0][0][0][0], tid);
+    lb.store(&sB[0][0][0][0], tid);
+    __syncthreads();
+
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+#pragma unroll 1
+    for (int s = 0; s < nst; ++s) {
+        const int cur = s & 1;
+        const bool more = s + 1 < nst;
+        if (more) {
+            la.issue(ra, tid, g.K * EA, (k0 + (s + 1) * BK) * EA);
+            lb.issue(rb, tid, g.K * EB, (k0 + (s + 1) * BK) * EB);
+        }
+        u32x4 fw[TN][PB], fx[TM][PA];
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int p = 0; p < PB; ++p)
+                fw[i][p] = *reinterpret_cast<const u32x4 *>(&sB[cur][p][wn0 + 16 * i + fr][fk]);
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int p = 0; p < PA; ++p)
+                fx[j][p] = *reinterpret_cast<const u32x4 *>(&sA[cur][p][wm0 + 16 * j + fr][fk]);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                if constexpr (PB == 2) acc[i][j] = mfma(fw[i][1], fx[j][0], acc[i][j]);
+                if constexpr (PA == 2) acc[i][j] = mfma(fw[i][0], fx[j][1], acc[i][j]);
+                acc[i][j] = mfma(fw[i][0], fx[j][0], acc[i][j]);
+            }
+        if (more) {
+            la.store(&sA[cur ^ 1][0][0][0], tid);
+            lb.store(&sB[cur ^ 1][0][0][0], tid);
+        }
+        __syncthreads();
+    }
+
+    // accumulator (i, j): token wm0 + 16 j + (lane & 15), outputs
+    // wn0 + 16 i + 4 (lane >> 4) .. + 3
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int64_t m = m0 + wm0 + 16 * j + fr;
+            const int n = n0 + wn0 + 16 * i + 4 * (lane >> 4);
+            if (m >= g.M || n >= g.N) continue;
+            if (g.partial) {
+                const f32x4 v = acc[i][j];
+                *reinterpret_cast<float4 *>(g.partial + ((int64_t)z * g.M + m) * g.np + n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                store_out<TC>(g, m, n, acc[i][j]);
+            }
+        }
+}
+
+// sum of the split-K partial products, then the epilogue; one thread per
+// token and group of four outputs
+template <typename TC>
+__global__ __launch_bounds__(256) void proj_finalize_kernel(GemmArgs g) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int groups = g.np >> 2;
+    const int64_t m = idx / groups;
+    if (m >= g.M) return;
+    const int n = (int)(idx - m * groups) * 4;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < g.splits; ++z) {
+        const float4 p = *reinterpret_cast<const float4 *>(g.partial + ((int64_t)z * g.M + m) * g.np + n);
+        v[0] += p.x;
+        v[1] += p.y;
+        v[2] += p.z;
+        v[3] += p.w;
+    }
+    store_out<TC>(g, m, n, v);
+}
+
+// tile shapes: large for many token rows, small for decode-sized batches
+constexpr int L_BM = 128, L_BN = 128, S_BM = 64, S_BN = 64;
+constexpr int64_t LARGE_MIN_M = 512;
+constexpr int SPLIT_MIN_K = 256;          // K columns per split at least
+constexpr int TARGET_WORKGROUPS = 512;    // two per compute unit
+
+struct Plan {
+    bool large;
+    int tiles_m, tiles_n, splits, k_len;
+};
+
+Plan plan_for(const ProjGemm &pg, int64_t scratch_bytes) {
+    Plan p;
+    p.large = pg.M >= LARGE_MIN_M;
+    const int bm = p.large ? L_BM : S_BM, bn = p.large ? L_BN : S_BN;
+    p.tiles_m = (int)((pg.M + bm - 1) / bm);
+    p.tiles_n = (pg.N + bn - 1) / bn;
+    p.splits = 1;
+    p.k_len = pg.K;
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles < TARGET_WORKGROUPS && pg.K >= 2 * SPLIT_MIN_K) {
+        int want = (int)((TARGET_WORKGROUPS + tiles - 1) / tiles);
+        want = min(want, pg.K / SPLIT_MIN_K);
+        int k_len = (pg.K + want - 1) / want;
+        k_len = (k_len + BK - 1) / BK * BK;
+        const int splits = (pg.K + k_len - 1) / k_len;
+        const int64_t np = (pg.N + 3) / 4 * 4;
+        if (splits > 1 && (int64_t)splits * pg.M * np * 4 <= scratch_bytes) {
+            p.splits = splits;
+            p.k_len = k_len;
+        }
+    }
+    return p;
+}
+
+template <typename TA, typename TB, typename TC>
+hipError_t launch_typed(const GemmArgs &a, bool large, hipStream_t stream) {
+    const int total = a.tiles_m * a.tiles_n * a.splits;
+    if (large)
+        hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, L_BM, L_BN>), dim3(total), dim3(GT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, S_BM, S_BN>), dim3(total), dim3(GT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.partial) return e;
+    const int64_t threads = a.M * (a.np / 4);
+    hipLaunchKernelGGL((proj_finalize_kernel<TC>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t proj_gemm_scratch_bytes(const ProjGemm &pg) {
+    const Plan p = plan_for(pg, INT64_MAX);
+    if (p.splits == 1) return 0;
+    return (int64_t)p.splits * pg.M * ((pg.N + 3) / 4 * 4) * 4;
+}
+
+bool proj_gemm_shape_ok(const ProjGemm &pg) {
+    if (pg.M < 0 || pg.N <= 0 || pg.K <= 0 || pg.K % BK != 0) return false;
+    if (pg.n_split < 0 || pg.n_split > pg.N || pg.n_split % 4 != 0) return false;
+    if (pg.n_split < pg.N && !pg.C1) return false;
+    // tile buffer resources: at most 128 rows x K x 4 bytes each
+    if ((int64_t)L_BM * pg.K * 4 > 0xffffffffLL) return false;
+    // one-dimensional grid
+    const int64_t tm = (pg.M + S_BM - 1) / S_BM, tn = (pg.N + S_BN - 1) / S_BN;
+    if (tm * tn > 0x7fffffffLL) return false;
+    return true;
+}
+
+hipError_t launch_proj_gemm(const ProjGemm &pg, float *scratch, int64_t scratch_bytes, hipStream_t stream) {
+    if (pg.M == 0) return hipSuccess;
+    const Plan p = plan_for(pg, scratch ? scratch_bytes : 0);
+    GemmArgs a;
+    a.A = pg.A;
+    a.B = pg.B;
+    a.M = pg.M;
+    a.N = pg.N;
+    a.K = pg.K;
+    a.k_len = p.k_len;
+    a.splits = p.splits;
+    a.tiles_m = p.tiles_m;
+    a.tiles_n = p.tiles_n;
+    a.C0 = pg.C0;
+    a.ldc0 = pg.ldc0;
+    a.C1 = pg.C1;
+    a.ldc1 = pg.ldc1;
+    a.n_split = pg.n_split;
+    a.np = (pg.N + 3) / 4 * 4;
+    a.partial = p.splits > 1 ? scratch : nullptr;
+    if (pg.a_bf16 && pg.b_bf16 && pg.c_bf16) return launch_typed<BF16, BF16, BF16>(a, p.large, stream);
+    if (pg.a_bf16 && !pg.b_bf16 && !pg.c_bf16) return launch_typed<BF16, F32, F32>(a, p.large, stream);
+    if (!pg.a_bf16 && !pg.b_bf16 && !pg.c_bf16) return launch_typed<F32, F32, F32>(a, p.large, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

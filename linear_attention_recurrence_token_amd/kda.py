@@ -44,7 +44,11 @@ class kda_tensors(ctypes.Structure):
 
 
 EXPORTS = ("kda_token_step", "kda_sequence", "kda_sequence_workspace_size",
-           "kda_status_string", "kda_version", "kda_device_check")
+           "kda_status_string", "kda_version", "kda_device_check",
+           "kda_projection_workspace_size", "kda_lowrank_gates", "kda_gate_projection",
+           "kda_output_projection")
+
+KDA_PROJ_LOWRANK_GATES, KDA_PROJ_GATE, KDA_PROJ_OUTPUT = 0, 1, 2
 
 
 class KdaError(RuntimeError):
@@ -81,6 +85,15 @@ def lib() -> ctypes.CDLL:
             L.kda_version.argtypes = []
             L.kda_device_check.restype = ctypes.c_int32
             L.kda_device_check.argtypes = []
+            vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+            L.kda_projection_workspace_size.restype = i64
+            L.kda_projection_workspace_size.argtypes = [cfgp, i32, i32, i32, i64]
+            L.kda_lowrank_gates.restype = i32
+            L.kda_lowrank_gates.argtypes = [cfgp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i64, vp]
+            L.kda_gate_projection.restype = i32
+            L.kda_gate_projection.argtypes = [cfgp, vp, vp, i32, i64, vp, vp, i64, vp]
+            L.kda_output_projection.restype = i32
+            L.kda_output_projection.argtypes = [cfgp, vp, vp, i32, i64, vp, vp, i64, vp]
             _lib = L
     return _lib
 
@@ -229,3 +242,104 @@ def device_check() -> int:
 
 def version() -> int:
     return int(lib().kda_version())
+
+
+# --- projections on either side of the step -----------------------------------
+
+def _gpu_tensor(name, t, shape, dtype, dev=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if dev is not None and t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def projection_workspace_size(config: KdaConfig, which: int, hidden: int, tokens: int, rank: int = 0) -> int:
+    c = config.to_c()
+    return int(lib().kda_projection_workspace_size(ctypes.byref(c), int(which), int(hidden), int(rank),
+                                                   int(tokens)))
+
+
+def _workspace(config, which, hidden, tokens, rank, workspace, device):
+    import torch
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a GPU tensor")
+        need = projection_workspace_size(config, which, hidden, tokens, rank)
+        if need < 0:
+            raise KdaError(need, "kda_projection_workspace_size")
+        workspace = torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def kda_lowrank_gates(config: KdaConfig, *, x, w_fa_bp, w_fb, f, beta, workspace="auto", stream=None,
+                      check: bool = True) -> None:
+    """f = W_fb (W_fa x) and beta = sigmoid(W_bp x) for hidden rows x [T, D]
+    (C: kda_lowrank_gates).  w_fa_bp [r + H, D] fp32 stacks W_fa over W_bp;
+    w_fb [H * 128, r] fp32; f [T, H, 128] and beta [T, H] fp32 out.
+    workspace: "auto" allocates (through torch) what
+    kda_projection_workspace_size reports, or a GPU tensor."""
+    import torch
+    T, D = int(x.shape[0]), int(x.shape[1])
+    H = config.num_heads
+    r = int(w_fb.shape[1])
+    if check:
+        act = torch.bfloat16 if config.act_dtype == KDA_BF16 else torch.float32
+        _gpu_tensor("x", x, (T, D), act)
+        for name, t, shape in (("w_fa_bp", w_fa_bp, (r + H, D)), ("w_fb", w_fb, (H * DK, r)),
+                               ("f", f, (T, H, DK)), ("beta", beta, (T, H))):
+            _gpu_tensor(name, t, shape, torch.float32, x.device)
+    c = config.to_c()
+    ws_ptr, ws_bytes = _workspace(config, KDA_PROJ_LOWRANK_GATES, D, T, r, workspace, x.device)
+    st = lib().kda_lowrank_gates(ctypes.byref(c), _ptr(x), _ptr(w_fa_bp), _ptr(w_fb), D, r, T, _ptr(f),
+                                 _ptr(beta), ws_ptr, ws_bytes, _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_lowrank_gates")
+
+
+def kda_gate_projection(config: KdaConfig, *, x, w_g, g, workspace="auto", stream=None,
+                        check: bool = True) -> None:
+    """g = W_g x (C: kda_gate_projection): x [T, D], w_g [H * 128, D],
+    g [T, H, 128], all in the activation dtype."""
+    import torch
+    T, D = int(x.shape[0]), int(x.shape[1])
+    H = config.num_heads
+    if check:
+        act = torch.bfloat16 if config.act_dtype == KDA_BF16 else torch.float32
+        _gpu_tensor("x", x, (T, D), act)
+        _gpu_tensor("w_g", w_g, (H * DV, D), act, x.device)
+        _gpu_tensor("g", g, (T, H, DV), act, x.device)
+    c = config.to_c()
+    ws_ptr, ws_bytes = _workspace(config, KDA_PROJ_GATE, D, T, 0, workspace, x.device)
+    st = lib().kda_gate_projection(ctypes.byref(c), _ptr(x), _ptr(w_g), D, T, _ptr(g), ws_ptr, ws_bytes,
+                                   _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_gate_projection")
+
+
+def kda_output_projection(config: KdaConfig, *, y, w_o, out, workspace="auto", stream=None,
+                          check: bool = True) -> None:
+    """out = W_o y (C: kda_output_projection): y [T, H, 128], w_o [D, H * 128],
+    out [T, D], all in the activation dtype."""
+    import torch
+    T = int(y.shape[0])
+    H = config.num_heads
+    D = int(w_o.shape[0])
+    if check:
+        act = torch.bfloat16 if config.act_dtype == KDA_BF16 else torch.float32
+        _gpu_tensor("y", y, (T, H, DV), act)
+        _gpu_tensor("w_o", w_o, (D, H * DV), act, y.device)
+        _gpu_tensor("out", out, (T, D), act, y.device)
+    c = config.to_c()
+    ws_ptr, ws_bytes = _workspace(config, KDA_PROJ_OUTPUT, D, T, 0, workspace, y.device)
+    st = lib().kda_output_projection(ctypes.byref(c), _ptr(y), _ptr(w_o), D, T, _ptr(out), ws_ptr, ws_bytes,
+                                     _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_output_projection")

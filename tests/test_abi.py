@@ -202,3 +202,109 @@ def test_path_support_checked_before_the_device(lib):
     # the short path addresses a batch's token rows with 32-bit offsets
     big = (1 << 32) // (4 * 128 * 4) + 2           # tokens with H = 4 past 4 GiB of fp32 rows
     assert _seq(lib, _cfg(prefill_path=4), t, n=2, total=big) == kda.KDA_ERR_UNSUPPORTED
+
+
+# --- the projections ------------------------------------------------------------
+
+def _lowrank(lib, cfg=None, x=1 << 40, w=(1 << 40) + (1 << 30), wfb=(1 << 40) + (2 << 30),
+             hidden=64, rank=32, tokens=10, f=(1 << 40) + (3 << 30), beta=(1 << 40) + (4 << 30),
+             ws=(1 << 40) + (5 << 30), ws_bytes=1 << 20):
+    cfg = cfg or _cfg()
+    return lib.kda_lowrank_gates(ctypes.byref(cfg), x, w, wfb, hidden, rank, tokens, f, beta, ws, ws_bytes, None)
+
+
+def _proj(lib, fn, cfg=None, a=1 << 40, w=(1 << 40) + (1 << 30), hidden=64, tokens=10,
+          out=(1 << 40) + (2 << 30), ws=None, ws_bytes=0):
+    cfg = cfg or _cfg()
+    return getattr(lib, fn)(ctypes.byref(cfg), a, w, hidden, tokens, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"hidden": 0}, kda.KDA_ERR_INVALID_ARG),
+    ({"hidden": 48}, kda.KDA_ERR_INVALID_ARG),        # not a multiple of 32
+    ({"rank": 16}, kda.KDA_ERR_INVALID_ARG),
+    ({"rank": 48}, kda.KDA_ERR_INVALID_ARG),
+    ({"rank": 2048}, kda.KDA_ERR_INVALID_ARG),
+    ({"tokens": -1}, kda.KDA_ERR_INVALID_ARG),
+    ({"x": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"w": (1 << 40) + (1 << 30) + 8}, kda.KDA_ERR_INVALID_ARG),
+    ({"f": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"beta": (1 << 40) + (4 << 30) + 2}, kda.KDA_ERR_INVALID_ARG),
+    ({"ws": None, "ws_bytes": 0}, kda.KDA_ERR_INVALID_ARG),   # the rank-r factor needs a home
+    ({"ws_bytes": 10 * 32 * 4 - 4}, kda.KDA_ERR_INVALID_ARG),
+    ({"f": (1 << 40) + 64}, kda.KDA_ERR_INVALID_ARG),          # f overlaps x
+    ({"beta": (1 << 40) + (3 << 30) + 64}, kda.KDA_ERR_INVALID_ARG),   # beta inside f
+    ({"ws": (1 << 40) + (3 << 30) + 4096}, kda.KDA_ERR_INVALID_ARG),   # workspace inside f
+    ({"cfg": _cfg(head_dim_k=64)}, kda.KDA_ERR_UNSUPPORTED),
+    ({"cfg": _cfg(act_dtype=5)}, kda.KDA_ERR_INVALID_ARG),
+])
+def test_lowrank_gates_rejects(lib, over, status):
+    assert _lowrank(lib, **over) == status
+
+
+@pytest.mark.parametrize("fn", ["kda_gate_projection", "kda_output_projection"])
+@pytest.mark.parametrize("over,status", [
+    ({"hidden": 0}, kda.KDA_ERR_INVALID_ARG),
+    ({"hidden": 66}, kda.KDA_ERR_INVALID_ARG),
+    ({"tokens": -3}, kda.KDA_ERR_INVALID_ARG),
+    ({"a": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"w": (1 << 40) + (1 << 30) + 4}, kda.KDA_ERR_INVALID_ARG),
+    ({"out": (1 << 40) + (1 << 30)}, kda.KDA_ERR_INVALID_ARG),        # out is the weight
+    ({"ws": (1 << 40) + (2 << 30) + 256, "ws_bytes": 1 << 20}, kda.KDA_ERR_INVALID_ARG),  # inside out
+    ({"ws": (1 << 41) + 8, "ws_bytes": 1 << 20}, kda.KDA_ERR_INVALID_ARG),
+    ({"ws_bytes": -1}, kda.KDA_ERR_INVALID_ARG),
+    ({"cfg": _cfg(head_dim_v=64)}, kda.KDA_ERR_UNSUPPORTED),
+])
+def test_projections_reject(lib, fn, over, status):
+    assert _proj(lib, fn, **over) == status
+
+
+def test_gate_projection_hidden_multiple_of_32_output_of_4(lib):
+    # K = hidden must be a multiple of 32 for the gate projection; the output
+    # projection only writes hidden columns (groups of 4)
+    assert _proj(lib, "kda_gate_projection", hidden=68) == kda.KDA_ERR_INVALID_ARG
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return
+    except ImportError:
+        pass
+    assert _proj(lib, "kda_output_projection", hidden=68) == kda.KDA_ERR_DEVICE
+
+
+def test_projections_zero_tokens_and_no_device(lib):
+    assert _lowrank(lib, tokens=0, x=None, f=None, beta=None, ws=None, ws_bytes=0) == kda.KDA_OK
+    for fn in ("kda_gate_projection", "kda_output_projection"):
+        assert _proj(lib, fn, tokens=0, a=None, w=None, out=None) == kda.KDA_OK
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return
+    except ImportError:
+        pass
+    assert _lowrank(lib) == kda.KDA_ERR_DEVICE
+    assert _proj(lib, "kda_gate_projection") == kda.KDA_ERR_DEVICE
+    assert _proj(lib, "kda_output_projection", ws=1 << 42, ws_bytes=1 << 20) == kda.KDA_ERR_DEVICE
+
+
+def test_projection_workspace_size(lib):
+    size = lambda which, hidden, rank, tokens, cfg=None: lib.kda_projection_workspace_size(
+        ctypes.byref(cfg or _cfg()), which, hidden, rank, tokens)
+    c32 = _cfg(num_heads=32)
+    # low-rank gates: the rank-r factor (rounded to 256 bytes), plus split-K
+    # scratch for few token rows
+    assert size(kda.KDA_PROJ_LOWRANK_GATES, 4096, 128, 32768, c32) == 32768 * 128 * 4
+    assert size(kda.KDA_PROJ_LOWRANK_GATES, 4096, 128, 3, c32) > 2048
+    assert size(kda.KDA_PROJ_LOWRANK_GATES, 64, 32, 3) == 512
+    # gate / output: scratch only when the sum is split (few token rows, long sums)
+    assert size(kda.KDA_PROJ_GATE, 4096, 0, 64, c32) > 0
+    assert size(kda.KDA_PROJ_OUTPUT, 4096, 0, 64, c32) > 0
+    assert size(kda.KDA_PROJ_GATE, 4096, 0, 32768, c32) == 0
+    assert size(kda.KDA_PROJ_GATE, 64, 0, 64) == 0          # too short a sum to split
+    assert size(kda.KDA_PROJ_GATE, 4096, 0, 0, c32) == 0
+    assert size(3, 64, 0, 10) == kda.KDA_ERR_INVALID_ARG
+    assert size(kda.KDA_PROJ_LOWRANK_GATES, 64, 40, 10) == kda.KDA_ERR_INVALID_ARG
+    assert size(kda.KDA_PROJ_GATE, 48, 0, 10) == kda.KDA_ERR_INVALID_ARG
+    assert size(kda.KDA_PROJ_OUTPUT, 68, 0, 10) == 2 * 10 * 68 * 4   # K = 4 heads x 128: two splits
+    assert size(kda.KDA_PROJ_GATE, 64, 0, -1) == kda.KDA_ERR_INVALID_ARG
+    assert size(kda.KDA_PROJ_GATE, 64, 0, 10, _cfg(head_dim_k=64)) == kda.KDA_ERR_UNSUPPORTED
