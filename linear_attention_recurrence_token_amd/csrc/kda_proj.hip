@@ -259,8 +259,16 @@ __global__ __launch_bounds__(256) void proj_finalize_kernel(GemmArgs g) {
     store_out<TC>(g, m, n, v);
 }
 
-// tile shapes: large for many token rows, small for decode-sized batches
-constexpr int L_BM = 128, L_BN = 128, S_BM = 64, S_BN = 64;
+// tile shapes (tokens x outputs): large for many token rows, small for
+// decode-sized batches.  A wavefront's LDS reads per 32 columns of K are
+// (WM + WN) rows of 64 bytes for 2 WM WN 32 flops, so the large tiles give
+// each wavefront 128 x 128 (bf16) or 64 x 128 (fp32 split into two parts,
+// whose LDS tile is twice as large)
+template <typename TA, typename TB> struct Shapes;
+template <> struct Shapes<BF16, BF16> { static constexpr int L_BM = 256, L_BN = 256; };
+template <> struct Shapes<BF16, F32> { static constexpr int L_BM = 128, L_BN = 128; };
+template <> struct Shapes<F32, F32> { static constexpr int L_BM = 128, L_BN = 256; };
+constexpr int S_BM = 64, S_BN = 64;
 constexpr int64_t LARGE_MIN_M = 512;
 constexpr int SPLIT_MIN_K = 256;          // K columns per split at least
 constexpr int TARGET_WORKGROUPS = 512;    // two per compute unit
@@ -270,10 +278,11 @@ struct Plan {
     int tiles_m, tiles_n, splits, k_len;
 };
 
-Plan plan_for(const ProjGemm &pg, int64_t scratch_bytes) {
+template <typename TA, typename TB>
+Plan plan_typed(const ProjGemm &pg, int64_t scratch_bytes) {
     Plan p;
     p.large = pg.M >= LARGE_MIN_M;
-    const int bm = p.large ? L_BM : S_BM, bn = p.large ? L_BN : S_BN;
+    const int bm = p.large ? Shapes<TA, TB>::L_BM : S_BM, bn = p.large ? Shapes<TA, TB>::L_BN : S_BN;
     p.tiles_m = (int)((pg.M + bm - 1) / bm);
     p.tiles_n = (pg.N + bn - 1) / bn;
     p.splits = 1;
@@ -294,11 +303,18 @@ Plan plan_for(const ProjGemm &pg, int64_t scratch_bytes) {
     return p;
 }
 
+Plan plan_for(const ProjGemm &pg, int64_t scratch_bytes) {
+    if (pg.a_bf16 && pg.b_bf16) return plan_typed<BF16, BF16>(pg, scratch_bytes);
+    if (pg.a_bf16) return plan_typed<BF16, F32>(pg, scratch_bytes);
+    return plan_typed<F32, F32>(pg, scratch_bytes);
+}
+
 template <typename TA, typename TB, typename TC>
 hipError_t launch_typed(const GemmArgs &a, bool large, hipStream_t stream) {
     const int total = a.tiles_m * a.tiles_n * a.splits;
+    constexpr int BM = Shapes<TA, TB>::L_BM, BN = Shapes<TA, TB>::L_BN;
     if (large)
-        hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, L_BM, L_BN>), dim3(total), dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, BM, BN>), dim3(total), dim3(GT), 0, stream, a);
     else
         hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, S_BM, S_BN>), dim3(total), dim3(GT), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -321,8 +337,8 @@ bool proj_gemm_shape_ok(const ProjGemm &pg) {
     if (pg.M < 0 || pg.N <= 0 || pg.K <= 0 || pg.K % BK != 0) return false;
     if (pg.n_split < 0 || pg.n_split > pg.N || pg.n_split % 4 != 0) return false;
     if (pg.n_split < pg.N && !pg.C1) return false;
-    // tile buffer resources: at most 128 rows x K x 4 bytes each
-    if ((int64_t)L_BM * pg.K * 4 > 0xffffffffLL) return false;
+    // tile buffer resources: at most 256 rows x K x 4 bytes each
+    if ((int64_t)256 * pg.K * 4 > 0xffffffffLL) return false;
     // one-dimensional grid
     const int64_t tm = (pg.M + S_BM - 1) / S_BM, tn = (pg.N + S_BN - 1) / S_BN;
     if (tm * tn > 0x7fffffffLL) return false;
