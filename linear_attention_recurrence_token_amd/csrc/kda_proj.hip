@@ -37,6 +37,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// Tiles of the direct-to-LDS bf16 kernel: 128 tokens x 256 outputs (64 x 128
+// per wavefront), 3 stages in LDS (72 KiB), two workgroups per compute unit --
+// measured the fastest of 256 x 256 with 4 stages and one workgroup, 256 x 128
+// and 128 x 128.  Its limit is the rate at which tiles arrive from L2 (about
+// 17 bytes per clock per compute unit on 32768 x 8192 x 8192), not the MFMA.
+#ifndef PROJ_DMA_BM
+#define PROJ_DMA_BM 128
+#define PROJ_DMA_BN 256
+#define PROJ_DMA_NS 3
+#define PROJ_DMA_WPE 2
+#endif
+
 constexpr int GT = 256;          // threads per workgroup
 constexpr int BK = 32;           // K columns per stage
 constexpr int BKP = BK + 8;      // LDS row length in bf16 elements (80 bytes)
@@ -239,6 +251,157 @@ __global__ __launch_bounds__(GT) void proj_gemm_kernel(GemmArgs g) {
         }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 x bf16 with the K tiles loaded straight into LDS (buffer_load ... lds):
+// no registers hold the next stage, so 4 stages are in flight per workgroup
+// and the wavefront's registers go to the 128 x 128 accumulator tile.
+//
+// LDS: per stage and operand, R rows x 32 bf16 (64 bytes), unpadded; the
+// 16-byte chunk c of row r is stored at chunk c ^ f(r & 15) with
+// f(r) = ((r >> 1) ^ (r >> 3)) & 3: the 16 rows a 16-lane group reads at one
+// chunk then fall on distinct 16-byte bank groups both within each 256-byte
+// window (16 lanes per clock) and within each 128-byte window (8 lanes per
+// clock).  A wavefront's load fills one 1 KiB block (16 rows): lane i lands at
+// byte 16 i of the block, so it fetches row i / 4, chunk (i & 3) ^ f(i / 4).
+// Each stage and operand has its own LDS array: the compiler then waits, before
+// a stage's reads, only for the loads into that array.
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+template <int R>
+__device__ __forceinline__ void dma_issue(Rsrc r, uint8_t *stage, int wave, int lane, uint32_t row_bytes,
+                                          uint32_t kbyte) {
+    const uint32_t rr = lane >> 2;
+    const uint32_t c = (lane & 3) ^ (((rr >> 1) ^ (rr >> 3)) & 3);
+#pragma unroll
+    for (int j = 0; j < R / 64; ++j) {
+        const int b = wave + 4 * j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + b * 1024), 16,
+                                                 (16 * b + rr) * row_bytes + 16 * c, kbyte, 0, 0);
+    }
+}
+
+// wait until at most N of this wavefront's global loads are outstanding and
+// its LDS reads are complete, then the workgroup barrier (no memory fence:
+// that would wait for every load in flight)
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+
+template <int BM, int BN, int NS, typename TC>
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(PROJ_DMA_WPE)))
+void proj_gemm_dma_kernel(GemmArgs g) {
+    static_assert(NS == 3 || NS == 4, "stages in flight");
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int TM = WM / 16, TN = WN / 16;
+    constexpr int LOADS = (BM + BN) / 64;          // loads per wavefront per stage
+    __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 64], sA1[BM * 64], sA2[BM * 64];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 64], sB1[BN * 64], sB2[BN * 64];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA3[NS == 4 ? BM * 64 : 16], sB3[NS == 4 ? BN * 64 : 16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+
+    const int total = g.tiles_m * g.tiles_n * g.splits;
+    int bid = blockIdx.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int per_split = g.tiles_m * g.tiles_n;
+    const int z = bid / per_split;
+    const int t = bid - z * per_split;
+    constexpr int GROUP = 8;
+    const int group = t / (GROUP * g.tiles_n);
+    const int first_m = group * GROUP;
+    const int gsize = min(GROUP, g.tiles_m - first_m);
+    const int in_group = t - group * GROUP * g.tiles_n;
+    const int tm = first_m + in_group % gsize, tn = in_group / gsize;
+
+    const int64_t m0 = (int64_t)tm * BM;
+    const int n0 = tn * BN;
+    const int rows_a = (int)min((int64_t)BM, g.M - m0);
+    const int rows_b = min(BN, g.N - n0);
+    const Rsrc ra = make_rsrc(static_cast<const char *>(g.A) + m0 * g.K * 2, (uint32_t)(rows_a * g.K * 2));
+    const Rsrc rb = make_rsrc(static_cast<const char *>(g.B) + (int64_t)n0 * g.K * 2, (uint32_t)(rows_b * g.K * 2));
+    const uint32_t rowb = (uint32_t)g.K * 2;
+    const int k0 = z * g.k_len;
+    const int nst = min(g.k_len, g.K - k0) / BK;
+
+    f32x4 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int s, uint8_t *a, uint8_t *b) {
+        const uint32_t kb = (uint32_t)(k0 + s * BK) * 2;
+        dma_issue<BM>(ra, a, wave, lane, rowb, kb);
+        dma_issue<BN>(rb, b, wave, lane, rowb, kb);
+    };
+    // fragment of row (base + lane & 15), logical chunk lane >> 4
+    const int fr = lane & 15;
+    const uint32_t foff = fr * 64 + 16 * ((lane >> 4) ^ (((fr >> 1) ^ (fr >> 3)) & 3));
+    auto compute = [&](const uint8_t *a, const uint8_t *b) {
+        u32x4 fw[TN];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) fw[i] = *reinterpret_cast<const u32x4 *>(b + (wn0 + 16 * i) * 64 + foff);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const u32x4 fx = *reinterpret_cast<const u32x4 *>(a + (wm0 + 16 * j) * 64 + foff);
+#pragma unroll
+            for (int i = 0; i < TN; ++i) acc[i][j] = mfma(fw[i], fx, acc[i][j]);
+        }
+    };
+    // one K stage: its loads done everywhere (and every wavefront's reads of
+    // the previous stage complete), the loads NS - 1 stages ahead into the
+    // buffer the previous stage used, then the products
+    auto stage = [&](int s, const uint8_t *a, const uint8_t *b, uint8_t *na, uint8_t *nb) {
+        if (s >= nst) return;
+        // outstanding after stage s: stages s + 1 .. min(s + NS - 2, nst - 1)
+        const int after = min(NS - 2, nst - 1 - s);
+        if (NS == 4 && after == 2)
+            wait_then_barrier<2 * LOADS>();
+        else if (after >= 1)
+            wait_then_barrier<LOADS>();
+        else
+            wait_then_barrier<0>();
+        if (s + NS - 1 < nst) issue(s + NS - 1, na, nb);
+        compute(a, b);
+    };
+
+    issue(0, sA0, sB0);
+    if (1 < nst) issue(1, sA1, sB1);
+    if (NS == 4 && 2 < nst) issue(2, sA2, sB2);
+#pragma unroll 1
+    for (int s = 0; s < nst; s += NS) {
+        if constexpr (NS == 4) {
+            stage(s, sA0, sB0, sA3, sB3);
+            stage(s + 1, sA1, sB1, sA0, sB0);
+            stage(s + 2, sA2, sB2, sA1, sB1);
+            stage(s + 3, sA3, sB3, sA2, sB2);
+        } else {
+            stage(s, sA0, sB0, sA2, sB2);
+            stage(s + 1, sA1, sB1, sA0, sB0);
+            stage(s + 2, sA2, sB2, sA1, sB1);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int64_t m = m0 + wm0 + 16 * j + fr;
+            const int n = n0 + wn0 + 16 * i + 4 * (lane >> 4);
+            if (m >= g.M || n >= g.N) continue;
+            if (g.partial) {
+                const f32x4 v = acc[i][j];
+                *reinterpret_cast<float4 *>(g.partial + ((int64_t)z * g.M + m) * g.np + n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                store_out<TC>(g, m, n, acc[i][j]);
+            }
+        }
+}
+
 // sum of the split-K partial products, then the epilogue; one thread per
 // token and group of four outputs
 template <typename TC>
@@ -261,13 +424,14 @@ __global__ __launch_bounds__(256) void proj_finalize_kernel(GemmArgs g) {
 
 // tile shapes (tokens x outputs): large for many token rows, small for
 // decode-sized batches.  A wavefront's LDS reads per 32 columns of K are
-// (WM + WN) rows of 64 bytes for 2 WM WN 32 flops, so the large tiles give
-// each wavefront 128 x 128 (bf16) or 64 x 128 (fp32 split into two parts,
-// whose LDS tile is twice as large)
+// (WM + WN) rows of 64 bytes for 2 WM WN 32 flops, so bf16 takes 128 x 128
+// per wavefront; split fp32 (three products per pair of fragments, two-part
+// LDS tiles) stays at 64 x 64, where two workgroups fit a compute unit
+// (measured faster than 64 x 128 with one)
 template <typename TA, typename TB> struct Shapes;
-template <> struct Shapes<BF16, BF16> { static constexpr int L_BM = 256, L_BN = 256; };
+template <> struct Shapes<BF16, BF16> { static constexpr int L_BM = PROJ_DMA_BM, L_BN = PROJ_DMA_BN; };
 template <> struct Shapes<BF16, F32> { static constexpr int L_BM = 128, L_BN = 128; };
-template <> struct Shapes<F32, F32> { static constexpr int L_BM = 128, L_BN = 256; };
+template <> struct Shapes<F32, F32> { static constexpr int L_BM = 128, L_BN = 128; };
 constexpr int S_BM = 64, S_BN = 64;
 constexpr int64_t LARGE_MIN_M = 512;
 constexpr int SPLIT_MIN_K = 256;          // K columns per split at least
@@ -313,8 +477,12 @@ template <typename TA, typename TB, typename TC>
 hipError_t launch_typed(const GemmArgs &a, bool large, hipStream_t stream) {
     const int total = a.tiles_m * a.tiles_n * a.splits;
     constexpr int BM = Shapes<TA, TB>::L_BM, BN = Shapes<TA, TB>::L_BN;
-    if (large)
-        hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, BM, BN>), dim3(total), dim3(GT), 0, stream, a);
+    if (large) {
+        if constexpr (Opnd<TA>::PARTS == 1 && Opnd<TB>::PARTS == 1)
+            hipLaunchKernelGGL((proj_gemm_dma_kernel<BM, BN, PROJ_DMA_NS, TC>), dim3(total), dim3(GT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, BM, BN>), dim3(total), dim3(GT), 0, stream, a);
+    }
     else
         hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, S_BM, S_BN>), dim3(total), dim3(GT), 0, stream, a);
     hipError_t e = hipGetLastError();
