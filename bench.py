@@ -252,10 +252,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix cores, publishe
 MFMA_FP32_PEAK_TFLOPS = 157.3         # MI355X dense fp32 matrix cores, published
 
 
-def bench_projections(torch, kda, synth, dev, idx, runs):
+def bench_projections(torch, kda, synth, dev, idx, runs, only=None):
     """The matrix products on either side of the step for the token rows of
     step workload idx: kda_lowrank_gates (f and beta), kda_gate_projection
-    (g) and kda_output_projection (W_o y), each timed alone."""
+    (g) and kda_output_projection (W_o y), each timed alone (only: one of
+    'lowrank', 'gate', 'output' for profiling runs)."""
     import numpy as np
     p = synth.projection_workload(idx)
     bf = p.act_dtype == "bf16"
@@ -292,20 +293,25 @@ def bench_projections(torch, kda, synth, dev, idx, runs):
         return float(np.median(times))
 
     res = {"workload": p.name, "tokens": T, "heads": H, "hidden": D, "rank": r, "act_dtype": p.act_dtype}
-    ms = timed(lambda: kda.kda_lowrank_gates(cfg, x=x, w_fa_bp=wab, w_fb=wfb, f=f, beta=beta,
-                                             workspace=ws[kda.KDA_PROJ_LOWRANK_GATES]))
-    # algorithmic bytes: x, both weights, f and beta out, the rank-r factor out and back in
-    by = T * D * eb + (r + H) * D * 4 + HD * r * 4 + T * HD * 4 + T * H * 4 + 2 * T * r * 4
-    fl = 2 * T * D * (r + H) + 2 * T * r * HD
-    res["lowrank_gates"] = {
-        "ms": ms, "tflops_fp32_equiv": fl / (ms * 1e-3) / 1e12,
-        "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None}}
+    key = "%dx%dx%d_%s" % (T, H, D, p.act_dtype)
+    if only in (None, "lowrank"):
+        ms = timed(lambda: kda.kda_lowrank_gates(cfg, x=x, w_fa_bp=wab, w_fb=wfb, f=f, beta=beta,
+                                                 workspace=ws[kda.KDA_PROJ_LOWRANK_GATES]))
+        # algorithmic bytes: x, both weights, f and beta out, the rank-r factor out and back in
+        by = T * D * eb + (r + H) * D * 4 + HD * r * 4 + T * HD * 4 + T * H * 4 + 2 * T * r * 4
+        fl = 2 * T * D * (r + H) + 2 * T * r * HD
+        res["lowrank_gates"] = {
+            "ms": ms, "tflops_fp32_equiv": fl / (ms * 1e-3) / 1e12, "bytes_per_call": by,
+            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": committed_traffic("kda_proj.hip", "proj_lowrank_" + key)}}
     for name, fn, K, N in (
             ("gate_projection", lambda: kda.kda_gate_projection(cfg, x=x, w_g=wg, g=g,
                                                                 workspace=ws[kda.KDA_PROJ_GATE]), D, HD),
             ("output_projection", lambda: kda.kda_output_projection(cfg, y=y, w_o=wo, out=out,
                                                                     workspace=ws[kda.KDA_PROJ_OUTPUT]), HD, D)):
+        if only is not None and not name.startswith(only):
+            continue
         ms = timed(fn)
         fl = 2 * T * K * N
         by = (T * K + N * K + T * N) * eb
@@ -315,12 +321,13 @@ def bench_projections(torch, kda, synth, dev, idx, runs):
         # of the data type's matrix-core peak (fp32 problems run as three
         # bf16 products per product, reported against the fp32 peak)
         peak = MFMA_BF16_PEAK_TFLOPS if bf else MFMA_FP32_PEAK_TFLOPS
+        traffic = committed_traffic("kda_proj.hip", "proj_%s_%s" % (name.split("_")[0], key))
         if fl / by < peak * 1e3 / HBM_PEAK_GBS:
             rl = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+                  "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}
         else:
             rl = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
-                  "traffic": None}
+                  "traffic": traffic}
             if not bf:
                 rl["bf16_mfma_issued_frac"] = 3 * tf / MFMA_BF16_PEAK_TFLOPS
         res[name] = {"ms": ms, "tflops": tf, "hbm_GBps_algorithmic": gbs, "roofline": rl}
@@ -341,7 +348,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-overcache", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="profiling runs: 'decode' or 'prefill:<workload index>' alone, no baselines")
+                    help="profiling runs: 'decode', 'prefill:<workload index>' or "
+                         "'proj:<workload index>[:lowrank|gate|output]' alone, no baselines")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (torch copy "
                          "kernel of known size, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -377,7 +385,9 @@ def main():
             dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup)
             out["us_per_step"] = dec["ms_total"] / steps * 1e3
         elif args.only.startswith("proj:"):
-            out.update(bench_projections(torch, kda, synth, dev, int(args.only.split(":")[1]), args.prefill_runs))
+            parts = args.only.split(":")
+            out.update(bench_projections(torch, kda, synth, dev, int(parts[1]), args.prefill_runs,
+                                         parts[2] if len(parts) > 2 else None))
         elif args.only.startswith("prefill:"):
             r = bench_prefill(torch, kda, synth, dev, int(args.only.split(":")[1]), args.prefill_runs)
             out.update(r)

@@ -434,8 +434,12 @@ template <> struct Shapes<BF16, F32> { static constexpr int L_BM = 128, L_BN = 1
 template <> struct Shapes<F32, F32> { static constexpr int L_BM = 128, L_BN = 128; };
 constexpr int S_BM = 64, S_BN = 64;
 constexpr int64_t LARGE_MIN_M = 512;
-constexpr int SPLIT_MIN_K = 256;          // K columns per split at least
-constexpr int TARGET_WORKGROUPS = 512;    // two per compute unit
+#ifndef PROJ_SPLIT_MIN_K
+#define PROJ_SPLIT_MIN_K 256
+#define PROJ_TARGET_WG 512
+#endif
+constexpr int SPLIT_MIN_K = PROJ_SPLIT_MIN_K;          // K columns per split at least
+constexpr int TARGET_WORKGROUPS = PROJ_TARGET_WG;     // two per compute unit
 
 struct Plan {
     bool large;
