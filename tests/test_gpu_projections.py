@@ -75,6 +75,8 @@ SMALL = [  # T, H, D, r
     (300, 2, 256, 128),
     (700, 3, 160, 96),     # the large-tile path with ragged token and output tails
     (1100, 1, 544, 128),
+    (530, 2, 64, 256),     # larger ranks: K of the second product spans 8 and 9 stages
+    (520, 2, 64, 288),
 ]
 
 
