@@ -207,7 +207,8 @@ int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs,
  * products (about 2^-16 relative error each, fp32 sums); bf16 x bf16
  * products are exact, with fp32 sums.  Errors as for the step: nothing is
  * enqueued unless KDA_OK or KDA_ERR_LAUNCH comes back; tokens == 0 is a no-op
- * after cfg is checked.  workspace (caller-owned, 16-byte aligned, scratch)
+ * after cfg is checked; cfg->num_heads may be at most 65536 here.  workspace
+ * (caller-owned, 16-byte aligned, scratch)
  * lets calls with few token rows split each sum across more workgroups; its
  * size for the fastest run is kda_projection_workspace_size.
  */

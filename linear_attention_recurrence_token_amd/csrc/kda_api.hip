@@ -112,12 +112,16 @@ kda_status check_tensors(const kda_config *cfg, const kda_tensors *t, int32_t nu
     return KDA_OK;
 }
 
+constexpr int32_t PROJ_MAX_HEADS = 1 << 16;     // H * 128 outputs stay well inside 32-bit sizes
+
 // the configuration fields the projections use (heads, activation type, and
 // the same validity rules as the step)
 kda_status check_proj_config(const kda_config *cfg) {
     kda_tensors dummy;
     std::memset(&dummy, 0, sizeof(dummy));
-    return check_config(cfg, &dummy, 0);
+    const kda_status st = check_config(cfg, &dummy, 0);
+    if (st != KDA_OK) return st;
+    return cfg->num_heads > PROJ_MAX_HEADS ? KDA_ERR_INVALID_ARG : KDA_OK;
 }
 
 struct Span {

@@ -237,6 +237,8 @@ def _proj(lib, fn, cfg=None, a=1 << 40, w=(1 << 40) + (1 << 30), hidden=64, toke
     ({"ws": (1 << 40) + (3 << 30) + 4096}, kda.KDA_ERR_INVALID_ARG),   # workspace inside f
     ({"cfg": _cfg(head_dim_k=64)}, kda.KDA_ERR_UNSUPPORTED),
     ({"cfg": _cfg(act_dtype=5)}, kda.KDA_ERR_INVALID_ARG),
+    ({"cfg": _cfg(num_heads=(1 << 16) + 1)}, kda.KDA_ERR_INVALID_ARG),
+    ({"cfg": _cfg(num_heads=(1 << 31) - 1)}, kda.KDA_ERR_INVALID_ARG),
 ])
 def test_lowrank_gates_rejects(lib, over, status):
     assert _lowrank(lib, **over) == status
@@ -254,6 +256,7 @@ def test_lowrank_gates_rejects(lib, over, status):
     ({"ws": (1 << 41) + 8, "ws_bytes": 1 << 20}, kda.KDA_ERR_INVALID_ARG),
     ({"ws_bytes": -1}, kda.KDA_ERR_INVALID_ARG),
     ({"cfg": _cfg(head_dim_v=64)}, kda.KDA_ERR_UNSUPPORTED),
+    ({"cfg": _cfg(num_heads=1 << 20)}, kda.KDA_ERR_INVALID_ARG),
 ])
 def test_projections_reject(lib, fn, over, status):
     assert _proj(lib, fn, **over) == status
