@@ -23,7 +23,8 @@
 // reads fall on distinct banks).  The next stage's global loads are issued
 // before the current stage's MFMAs.  The weight tile is the MFMA's A operand
 // and the token tile its B operand, so each lane's accumulator holds 4
-// consecutive outputs of one token: one 16- (fp32) or 8-byte (bf16) store.
+// consecutive outputs of one token; the output tile then goes through LDS so
+// that consecutive lanes write consecutive 16-byte pieces of one output row.
 // Few tiles (decode-sized M) split K across workgroups into an fp32 scratch
 // that a second kernel sums before the epilogue.
 #include "kda_device.hpp"
@@ -149,8 +150,14 @@ __global__ __launch_bounds__(GT) void proj_gemm_kernel(GemmArgs g) {
     constexpr int EA = Opnd<TA>::ELEM, EB = Opnd<TB>::ELEM;
     constexpr int WM = BM / 2, WN = BN / 2;            // wavefront tile (tokens x outputs)
     constexpr int TM = WM / 16, TN = WN / 16;
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][PA][BM][BKP];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][PB][BN][BKP];
+    // the K tiles, and after the K loop the output tile (rows of BN + 4 floats)
+    constexpr int SA_BYTES = 2 * PA * BM * BKP * 2, SB_BYTES = 2 * PB * BN * BKP * 2;
+    constexpr int SC_BYTES = BM * (BN + 4) * 4;
+    constexpr int S_BYTES = SA_BYTES + SB_BYTES > SC_BYTES ? SA_BYTES + SB_BYTES : SC_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S_BYTES];
+    auto sA = reinterpret_cast<uint16_t(*)[PA][BM][BKP]>(smem);
+    auto sB = reinterpret_cast<uint16_t(*)[PB][BN][BKP]>(smem + SA_BYTES);
+    auto sC = reinterpret_cast<float(*)[BN + 4]>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
@@ -234,21 +241,40 @@ __global__ __launch_bounds__(GT) void proj_gemm_kernel(GemmArgs g) {
 
     // accumulator (i, j): token wm0 + 16 j + (lane & 15), outputs
     // wn0 + 16 i + 4 (lane >> 4) .. + 3
+    if (g.partial) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                const int64_t m = m0 + wm0 + 16 * j + fr;
+                const int n = n0 + wn0 + 16 * i + 4 * (lane >> 4);
+                if (m >= g.M || n >= g.N) continue;
+                const f32x4 v = acc[i][j];
+                *reinterpret_cast<float4 *>(g.partial + ((int64_t)z * g.M + m) * g.np + n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+        return;
+    }
+    // through LDS, so that consecutive lanes write consecutive 16-byte pieces
+    // of one output row (the K loop ended with a barrier: the tiles are free)
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
-            const int64_t m = m0 + wm0 + 16 * j + fr;
-            const int n = n0 + wn0 + 16 * i + 4 * (lane >> 4);
-            if (m >= g.M || n >= g.N) continue;
-            if (g.partial) {
-                const f32x4 v = acc[i][j];
-                *reinterpret_cast<float4 *>(g.partial + ((int64_t)z * g.M + m) * g.np + n) =
-                    make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-                store_out<TC>(g, m, n, acc[i][j]);
-            }
+            const f32x4 v = acc[i][j];
+            *reinterpret_cast<float4 *>(&sC[wm0 + 16 * j + fr][wn0 + 16 * i + 4 * (lane >> 4)]) =
+                make_float4(v[0], v[1], v[2], v[3]);
         }
+    __syncthreads();
+    constexpr int G4 = BN / 4;
+    for (int c = tid; c < BM * G4; c += GT) {
+        const int row = c / G4, col = (c - row * G4) * 4;
+        const int64_t m = m0 + row;
+        const int n = n0 + col;
+        if (m >= g.M || n >= g.N) continue;
+        const float4 v = *reinterpret_cast<const float4 *>(&sC[row][col]);
+        store_out<TC>(g, m, n, f32x4{v.x, v.y, v.z, v.w});
+    }
 }
 
 // ---------------------------------------------------------------------------
