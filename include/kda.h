@@ -95,9 +95,10 @@ typedef enum kda_gate_mode {
 
 /* Which prefill kernel kda_sequence runs.  All compute the same function
  * within the fp32 tolerance.  AUTO takes SHORT when the sequences hold fewer
- * than 8 tokens on average (total_tokens < 8 * num_seqs); otherwise CHUNK
- * wherever the gate allows it; otherwise SPLIT for few (sequence, head) pairs
- * and FUSED for many.  SPLIT
+ * than 8 tokens on average (total_tokens < 8 * num_seqs); otherwise, where
+ * the gate allows the chunk form, SCAN for at most 128 (sequence, head) pairs
+ * averaging 256 tokens or more when the workspace is large enough, else
+ * CHUNK; otherwise SPLIT for few pairs and FUSED for many.  SPLIT
  * spreads each pair's state columns over several workgroups (for few pairs,
  * e.g. one long sequence) and needs an fp32 buffer for the pre-norm readout:
  * o_raw, or else a workspace of the size kda_sequence_workspace_size reports.
@@ -111,10 +112,18 @@ typedef enum kda_prefill_path {
     KDA_PREFILL_CHUNK = 3,      /* 16-token chunks on the matrix cores; needs
                                    KDA_GATE_BOUNDED with |lb| <= 7.5, else
                                    KDA_ERR_UNSUPPORTED                       */
-    KDA_PREFILL_SHORT = 4       /* the decode step's layout with a token loop,
+    KDA_PREFILL_SHORT = 4,      /* the decode step's layout with a token loop,
                                    for sequences of a few tokens; needs
                                    total_tokens * H * 512 < 2^32, else
                                    KDA_ERR_UNSUPPORTED                       */
+    KDA_PREFILL_SCAN = 5        /* CHUNK in two passes: every chunk's
+                                   input-only operands at once, then the
+                                   chunks in order with each pair's state
+                                   columns over 8 wavefronts; for few pairs of
+                                   long sequences.  Same gate rule as CHUNK;
+                                   needs the workspace kda_sequence_workspace_size
+                                   reports (less the readout part when o_raw
+                                   is given), else KDA_ERR_INVALID_ARG       */
 } kda_prefill_path;
 
 typedef struct kda_config {
@@ -188,11 +197,14 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t,
  * Bytes of device workspace with which kda_sequence runs its faster path for
  * this shape (num_seqs sequences, total_tokens token rows, cfg->num_heads
  * heads, cfg->prefill_path); 0 if that path needs none.  A negative value is
- * a kda_status for bad arguments.  The workspace is needed only when o_raw is
- * NULL; with a smaller or NULL workspace kda_sequence falls back to the fused
- * kernel under KDA_PREFILL_AUTO and fails with KDA_ERR_INVALID_ARG under
- * KDA_PREFILL_SPLIT.  Caller-owned, 16-byte aligned, no initialisation
- * needed, not kept after the call; its contents are scratch.
+ * a kda_status for bad arguments.  SPLIT uses it for its fp32 readout, which
+ * o_raw replaces when given; SCAN for every chunk's operands (about 2.2 KiB
+ * per token and head) followed by the readout (not needed with o_raw).  With
+ * a smaller or NULL workspace kda_sequence falls back under
+ * KDA_PREFILL_AUTO (to CHUNK or FUSED) and fails with KDA_ERR_INVALID_ARG
+ * under KDA_PREFILL_SPLIT and KDA_PREFILL_SCAN.  Caller-owned, 16-byte
+ * aligned, no initialisation needed, not kept after the call; its contents
+ * are scratch.
  */
 int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                     int64_t total_tokens);

@@ -45,7 +45,7 @@ kda_status check_config(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (cfg->gate_mode < KDA_GATE_BOUNDED || cfg->gate_mode > KDA_GATE_RAW) return KDA_ERR_INVALID_ARG;
     if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
     if (cfg->gate_lower_bound != cfg->gate_lower_bound) return KDA_ERR_INVALID_ARG;
-    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_SHORT)
+    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_SCAN)
         return KDA_ERR_INVALID_ARG;
     if (cfg->head_dim_k != kda::DK || cfg->head_dim_v != kda::DV || cfg->conv_taps != kda::TAPS)
         return KDA_ERR_UNSUPPORTED;
@@ -72,6 +72,29 @@ bool auto_chunk(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     return chunk_supported(cfg) && total_tokens >= CHUNK_MIN_AVG_TOKENS * (int64_t)num_seqs;
 }
 
+// The two-pass chunk path pays for writing and reading every chunk's operands
+// once; it wins when the one-pass kernel, one workgroup per (sequence, head),
+// would leave most compute units idle (at most half of them busy) and the
+// sequences are long enough for the operand pass to amortise.
+constexpr int64_t SCAN_MAX_UNITS = 128;
+constexpr int64_t SCAN_MIN_AVG_TOKENS = 256;
+
+bool scan_shape(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    const int64_t units = (int64_t)num_seqs * cfg->num_heads;
+    return chunk_supported(cfg) && num_seqs > 0 && units <= SCAN_MAX_UNITS &&
+           total_tokens >= SCAN_MIN_AVG_TOKENS * (int64_t)num_seqs;
+}
+
+// workspace of the two-pass path: the chunk records, then (without o_raw)
+// the fp32 readout
+int64_t scan_record_bytes(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    const int64_t r = kda::prefill_scan_record_bytes(total_tokens, num_seqs, cfg->num_heads);
+    return (r + 255) / 256 * 256;
+}
+int64_t readout_bytes(const kda_config *cfg, int64_t total_tokens) {
+    return total_tokens * cfg->num_heads * kda::DV * (int64_t)sizeof(float);
+}
+
 // columns per lane of the split prefill for this shape, 0 = another kernel.
 // Automatic choice: the short-sequence kernel when the sequences average
 // under 8 tokens; else the chunkwise kernel wherever the gate allows it (it
@@ -80,7 +103,7 @@ bool auto_chunk(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
 int split_cols_for(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     const int64_t units = (int64_t)num_seqs * cfg->num_heads;
     if (cfg->prefill_path == KDA_PREFILL_FUSED || cfg->prefill_path == KDA_PREFILL_CHUNK ||
-        cfg->prefill_path == KDA_PREFILL_SHORT)
+        cfg->prefill_path == KDA_PREFILL_SHORT || cfg->prefill_path == KDA_PREFILL_SCAN)
         return 0;
     const int c = kda::prefill_split_cols(units);
     if (cfg->prefill_path == KDA_PREFILL_SPLIT) return c ? c : 4;
@@ -231,8 +254,12 @@ int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs, int
     const kda_status st = check_config(cfg, &dummy, num_seqs);
     if (st != KDA_OK) return st;
     if (total_tokens < 0) return KDA_ERR_INVALID_ARG;
-    if (num_seqs == 0 || total_tokens == 0 || split_cols_for(cfg, num_seqs, total_tokens) == 0) return 0;
-    return total_tokens * cfg->num_heads * kda::DV * (int64_t)sizeof(float);
+    if (num_seqs == 0 || total_tokens == 0) return 0;
+    if (cfg->prefill_path == KDA_PREFILL_SCAN ||
+        (cfg->prefill_path == KDA_PREFILL_AUTO && scan_shape(cfg, num_seqs, total_tokens)))
+        return scan_record_bytes(cfg, num_seqs, total_tokens) + readout_bytes(cfg, total_tokens);
+    if (split_cols_for(cfg, num_seqs, total_tokens) == 0) return 0;
+    return readout_bytes(cfg, total_tokens);
 }
 
 kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
@@ -270,6 +297,21 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
         else if (cfg->prefill_path == KDA_PREFILL_SPLIT)
             return KDA_ERR_INVALID_ARG;
     }
+    // the two-pass path: records in the workspace, the readout in o_raw or after them
+    uint8_t *scan_records = nullptr;
+    float *scan_obuf = nullptr;
+    if (cfg->prefill_path == KDA_PREFILL_SCAN ||
+        (cfg->prefill_path == KDA_PREFILL_AUTO && scan_shape(cfg, num_seqs, total_tokens))) {
+        if (cfg->prefill_path == KDA_PREFILL_SCAN && !chunk_supported(cfg)) return KDA_ERR_UNSUPPORTED;
+        const int64_t rb = scan_record_bytes(cfg, num_seqs, total_tokens);
+        const int64_t need = rb + (t->o_raw ? 0 : readout_bytes(cfg, total_tokens));
+        if (workspace && workspace_bytes >= need) {
+            scan_records = static_cast<uint8_t *>(workspace);
+            scan_obuf = t->o_raw ? t->o_raw : reinterpret_cast<float *>(scan_records + rb);
+        } else if (cfg->prefill_path == KDA_PREFILL_SCAN) {
+            return KDA_ERR_INVALID_ARG;
+        }
+    }
     if (cfg->prefill_path == KDA_PREFILL_CHUNK && !chunk_supported(cfg)) return KDA_ERR_UNSUPPORTED;
     if (cfg->prefill_path == KDA_PREFILL_SHORT && !kda::short_supported(total_tokens, cfg->num_heads))
         return KDA_ERR_UNSUPPORTED;
@@ -283,7 +325,9 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     const bool bf16 = cfg->act_dtype == KDA_BF16;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (obuf)
+    if (scan_records)
+        e = kda::launch_prefill_scan(p, bf16, scan_records, scan_obuf, s);
+    else if (obuf)
         e = kda::launch_prefill_split(p, bf16, obuf, cols, s);
     else if (cfg->prefill_path == KDA_PREFILL_SHORT ||
              (cfg->prefill_path == KDA_PREFILL_AUTO && auto_short(num_seqs, total_tokens, cfg->num_heads)))

@@ -57,6 +57,17 @@ bool prefill_chunk_supported(int32_t gate_mode, float lb, int32_t num_heads);
 hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_split(const Params &p, bool bf16, float *obuf, int cols_per_lane,
                                 hipStream_t stream);
+// RMSNorm + gate from a pre-norm readout buffer ([T, H, 128] fp32) into y, and
+// the window out (the column-split path's last two kernels)
+hipError_t launch_split_finish(const Params &p, bool bf16, const float *obuf, hipStream_t stream);
+
+// Chunkwise prefill in two passes for few (sequence, head) pairs: every
+// chunk's input-only operands in parallel into records (prefill_scan_record_bytes
+// of them), then the chunks of each pair in order with its state columns over
+// eight wavefronts, the readout into obuf, then launch_split_finish.  Same gate
+// support as the one-pass chunk kernel.
+int64_t prefill_scan_record_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads);
+hipError_t launch_prefill_scan(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream);
 
 // Matrix products on either side of the step (the low-rank decay and beta
 // projections, the output-gate and output projections):

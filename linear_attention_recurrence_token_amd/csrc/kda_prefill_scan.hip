@@ -1,0 +1,465 @@
+// kda_prefill_scan.hip -- chunkwise KDA prefill in two passes, for batches of
+// few (sequence, head) pairs.
+//
+// The chunk form (kda_prefill_chunk.hip; "Kimi K3 Metal Gap Analysis", §2,
+// row "Recurrence") splits each 16-token chunk's work in two:
+//   * quantities that depend only on the chunk's own inputs -- the activated
+//     and normalised q, k, v, the decays, (e^G . K), (e^G . Q), E,
+//     T = (I + Diag(b) L)^{-1} and M -- and
+//   * the products with the state entering the chunk, which chain the chunks.
+// The one-pass kernel gives a (sequence, head) pair one workgroup that does
+// both, chunk after chunk; with few pairs most of the GPU then idles.  Here
+// pass 1 computes the first kind for every chunk of every pair at once (one
+// workgroup per chunk and head, all independent) into a record per chunk in
+// the caller's workspace, and pass 2 walks the chunks of a pair with only the
+// state products left, its 128 state columns spread over 8 wavefronts in two
+// workgroups.  The pre-norm readout goes to an fp32 buffer; the RMSNorm +
+// gate and the window are written by the column-split path's finishing
+// kernels.
+//
+// Arithmetic is that of the one-pass kernel: state products on bf16 MFMA with
+// split operands (hi + lo, about 2^-16 relative error per product, fp32
+// sums and state); L and M in fp32 with the chunk-middle reference r = G at
+// token 7 keeping every exponential inside e^{+-|lb| C / 2}.
+#include "kda_device.hpp"
+
+namespace kda {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+constexpr int CC = 16;                 // tokens per chunk
+
+// ---- the per-chunk record (bytes); bf16 parts as [hi block][lo block]
+//   KA, QA  split e^G . k_hat, e^G . q_hat in the order of the state product:
+//           16-byte slot (m, g, t) holds channels 32 m + 4 g + {0..3} and
+//           32 m + 16 + 4 g + {0..3} of token t, at slot index (m * 4 + g) * 16 + t
+//   E       split e^{G_C - G_t} . k_hat_t, [channel][token]
+//   T, M    split (I + Diag(b) L)^{-1} and M (lower, with the diagonal), [row][column]
+//   GC      e^{G_C} per channel, fp32
+//   V       activated v, [token][channel] fp32 (zero past the sequence end)
+//   B       beta per token (zero past the end)
+constexpr int R_KA = 0, R_QA = 8192, R_E = 16384, R_T = 24576, R_M = 25600, R_GC = 26624,
+              R_V = 27136, R_B = 35328, REC = 35840;   // REC: 35 KiB
+static_assert(REC % 1024 == 0, "a record is a whole number of 1 KiB load blocks");
+
+__device__ __forceinline__ uint16_t bf16_hi(float x) { return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
+__device__ __forceinline__ void split_store(uint8_t *rec, int off_hi, int part_bytes, int idx, float x) {
+    const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
+    const float lo = x - __uint_as_float(h << 16);
+    reinterpret_cast<uint16_t *>(rec + off_hi)[idx] = (uint16_t)h;
+    reinterpret_cast<uint16_t *>(rec + off_hi + part_bytes)[idx] = bf16_hi(lo);
+}
+
+// record slot of chunk c of sequence n: slots floor(cu[n] / 16) + n + c never
+// collide (a sequence of len tokens has at most floor(len / 16) + 1 chunks)
+__device__ __forceinline__ int64_t slot_base(const Params &p, int n) {
+    const int64_t lo = p.cu_seqlens ? (int64_t)p.cu_seqlens[n] : (int64_t)n * p.dense_len;
+    const int64_t c = lo < 0 ? 0 : (lo > p.total_tokens ? p.total_tokens : lo);
+    return c / CC + n;
+}
+
+// ---------------------------------------------------------------- pass 1
+constexpr int PREP_THREADS = 256;
+constexpr int XP = CH + 4;              // raw / activated row length in LDS
+constexpr int FP = DK + 4;              // L, M factor rows: 16-byte aligned, and the 16
+                                        // rows a 16-lane group reads at one column on distinct banks
+constexpr int RAW_PER = ((CC + PAST) * CH + PREP_THREADS - 1) / PREP_THREADS;   // raw loads per thread
+
+template <typename Act>
+__global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8_t *records) {
+    const int64_t slot = blockIdx.x;
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x;
+    // the sequence owning this slot: the last n with slot_base(n) <= slot
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (slot_base(p, mid) <= slot) lo = mid; else hi = mid - 1;
+    }
+    const int n = lo;
+    const Range rng = seq_range(p, n);
+    const int64_t c = slot - slot_base(p, n);
+    const int64_t c0 = c * CC;
+    if (c < 0 || c0 >= rng.len) return;
+    const int nv = (int)(rng.len - c0 < CC ? rng.len - c0 : CC);
+    uint8_t *rec = records + (slot * p.H + h) * REC;
+
+    __shared__ float s_x[CC + PAST][XP];    // raw rows c0 - 3 .. c0 + 15, then activated rows 3 .. 18
+    __shared__ float s_nrm[CC][2];          // L2 scales of q, k
+    __shared__ float s_G[CC][DK];           // log-decay summed from the chunk start
+    __shared__ __attribute__((aligned(16))) float s_kl[CC][FP], s_ql[CC][FP], s_kr[CC][FP];
+    __shared__ float s_A[CC][CC], s_b[CC];
+    __shared__ __attribute__((aligned(16))) float s_cw[CH][TAPS];
+
+    const int64_t rowsz = (int64_t)p.H * DK;
+    const float *W = p.win + ((int64_t)n * p.H + h) * (PAST * CH);
+    // every global load of the chunk first (they are independent), then LDS
+    float xr[RAW_PER], fv[CC];
+#pragma unroll
+    for (int u = 0; u < RAW_PER; ++u) {
+        const int idx = tid + u * PREP_THREADS;
+        const int r = idx / CH, ch = idx - r * CH;
+        const int64_t j = c0 - PAST + r;
+        float x = 0.f;
+        if (idx < (CC + PAST) * CH) {
+            if (j < 0) {
+                x = W[(j + PAST) * CH + ch];
+            } else if (j < rng.len) {
+                const void *src = ch < DK ? p.q : (ch < 2 * DK ? p.k : p.v);
+                x = Act::load1(src, (rng.lo + j) * rowsz + (int64_t)h * DK + (ch & (DK - 1)));
+            }
+        }
+        xr[u] = x;
+    }
+    float eA = 0.f, dtb = 0.f, bt = 0.f;
+    if (tid < DK) {
+#pragma unroll
+        for (int t = 0; t < CC; ++t)
+            fv[t] = t < nv ? p.f[(rng.lo + c0 + t) * rowsz + h * DK + tid] : 0.f;
+        eA = p.A_log[h * DK + tid];
+        dtb = p.dt_bias[h * DK + tid];
+    } else if (tid < DK + CC) {
+        const int t = tid - DK;
+        bt = t < nv ? p.beta[(rng.lo + c0 + t) * p.H + h] : 0.f;
+    }
+    float4 cw0 = *reinterpret_cast<const float4 *>(p.conv_w + ((int64_t)h * CH + tid) * TAPS);
+    float4 cw1 = tid < CH - PREP_THREADS
+                     ? *reinterpret_cast<const float4 *>(p.conv_w + ((int64_t)h * CH + PREP_THREADS + tid) * TAPS)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4 *>(s_cw[tid]) = cw0;
+    if (tid < CH - PREP_THREADS) *reinterpret_cast<float4 *>(s_cw[PREP_THREADS + tid]) = cw1;
+#pragma unroll
+    for (int u = 0; u < RAW_PER; ++u) {
+        const int idx = tid + u * PREP_THREADS;
+        const int r = idx / CH, ch = idx - r * CH;
+        if (idx < (CC + PAST) * CH) s_x[r][ch] = xr[u];
+    }
+    __syncthreads();
+    // conv + SiLU (tokens past the end give zeros); each thread keeps its
+    // results in registers until every tap has been read
+    float act[(CC * CH) / PREP_THREADS];
+#pragma unroll
+    for (int u = 0; u < (CC * CH) / PREP_THREADS; ++u) {
+        const int idx = tid + u * PREP_THREADS;
+        const int t = idx / CH, ch = idx - t * CH;
+        const float4 w = *reinterpret_cast<const float4 *>(s_cw[ch]);
+        const float a = w.x * s_x[t][ch] + w.y * s_x[t + 1][ch] + w.z * s_x[t + 2][ch] + w.w * s_x[t + 3][ch];
+        act[u] = t < nv ? silu(a) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < (CC * CH) / PREP_THREADS; ++u) {
+        const int idx = tid + u * PREP_THREADS;
+        const int t = idx / CH, ch = idx - t * CH;
+        s_x[PAST + t][ch] = act[u];
+    }
+    // decays: channel i's log-decay summed over the chunk's tokens
+    if (tid < DK) {
+        const int i = tid;
+        eA = __expf(eA);
+        float G = 0.f;                         // held constant past the last token
+#pragma unroll
+        for (int t = 0; t < CC; ++t) {
+            if (t < nv) G += p.lb * sigmoid(eA * (fv[t] + dtb));
+            s_G[t][i] = G;
+        }
+    } else if (tid < DK + CC) {
+        const int t = tid - DK;
+        s_b[t] = bt;
+        reinterpret_cast<float *>(rec + R_B)[t] = bt;
+    }
+    __syncthreads();
+    // L2 scales: 8 lanes per (token, q or k)
+    {
+        const int grp = tid >> 3, sub = tid & 7;
+        const int t = grp >> 1, which = grp & 1;
+        float ss = 0.f;
+#pragma unroll
+        for (int u = 0; u < DK / 8; ++u) {
+            const float a = s_x[PAST + t][which * DK + sub * (DK / 8) + u];
+            ss += a * a;
+        }
+        ss = sum8(ss);
+        if (sub == 0) s_nrm[t][which] = rsqrtf(ss + p.l2_eps);
+    }
+    __syncthreads();
+    // operands of the state products, and the L, M factors
+    for (int idx = tid; idx < CC * DK; idx += PREP_THREADS) {
+        const int t = idx / DK, i = idx - t * DK;
+        const float qh = s_x[PAST + t][i] * s_nrm[t][0];
+        const float kh = s_x[PAST + t][DK + i] * s_nrm[t][1];
+        const float G = s_G[t][i], GC = s_G[CC - 1][i], r = s_G[CC / 2 - 1][i];
+        const float eg = __expf(G);
+        const int m = i >> 5, g = (i & 15) >> 2, e = ((i & 31) >> 4) * 4 + (i & 3);
+        const int sidx = ((m * 4 + g) * CC + t) * 8 + e;
+        split_store(rec, R_KA, 4096, sidx, eg * kh);
+        split_store(rec, R_QA, 4096, sidx, eg * qh);
+        split_store(rec, R_E, 4096, i * CC + t, __expf(GC - G) * kh);
+        reinterpret_cast<float *>(rec + R_V)[t * DK + i] = s_x[PAST + t][2 * DK + i];
+        if (t == 0) reinterpret_cast<float *>(rec + R_GC)[i] = __expf(GC);
+        const float ef = __expf(G - r), eb = __expf(r - G);
+        s_kl[t][i] = ef * kh;
+        s_ql[t][i] = ef * qh;
+        s_kr[t][i] = eb * kh;
+    }
+    __syncthreads();
+    // L (strictly lower, times beta: the matrix A of the solve) and M (lower
+    // with the diagonal): one (t, s) pair per thread
+    {
+        const int t = tid >> 4, s = tid & 15;
+        float l = 0.f, mm = 0.f;
+        if (s <= t) {
+#pragma unroll 8
+            for (int i = 0; i < DK; i += 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(&s_kl[t][i]);
+                const float4 q = *reinterpret_cast<const float4 *>(&s_ql[t][i]);
+                const float4 b = *reinterpret_cast<const float4 *>(&s_kr[s][i]);
+                l = fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, fmaf(a.w, b.w, l))));
+                mm = fmaf(q.x, b.x, fmaf(q.y, b.y, fmaf(q.z, b.z, fmaf(q.w, b.w, mm))));
+            }
+        }
+        s_A[t][s] = s < t ? s_b[t] * l : 0.f;
+        split_store(rec, R_M, 512, t * CC + s, s <= t ? mm : 0.f);
+    }
+    __syncthreads();
+    // T = (I + A)^{-1} by forward substitution, one column per thread
+    if (tid < CC) {
+        const int col = tid;
+        float x[CC];
+#pragma unroll
+        for (int t = 0; t < CC; ++t) {
+            float y = (t == col) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int s = 0; s < t; ++s) y = fmaf(-s_A[t][s], x[s], y);
+            x[t] = t < col ? 0.f : y;
+            split_store(rec, R_T, 512, t * CC + col, x[t]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- pass 2
+constexpr int SCAN_WAVES = 4;           // wavefronts per workgroup: 64 of the 128 columns
+constexpr int SCAN_GROUPS = DV / (16 * SCAN_WAVES);
+constexpr int RING = 4;                 // record buffers per workgroup (3 loading while 1 is used)
+
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
+                                                     c, 0, 0, 0);
+}
+struct Split2 {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float x0, float x1) {
+    const uint32_t hb = pack_bf16x2(x0, x1);
+    return {hb, pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u))};
+}
+__device__ __forceinline__ void split4(f32x4 d, u32x2 &h, u32x2 &l) {
+    const Split2 a = split2(d[0], d[1]), b = split2(d[2], d[3]);
+    h = u32x2{a.hi, b.hi};
+    l = u32x2{a.lo, b.lo};
+}
+// c + a b with both operands split
+__device__ __forceinline__ f32x4 mma32(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+    c = mfma32(al, bh, c);
+    c = mfma32(ah, bl, c);
+    return mfma32(ah, bh, c);
+}
+__device__ __forceinline__ f32x4 mma16(u32x2 ah, u32x2 al, u32x2 bh, u32x2 bl, f32x4 c) {
+    c = mfma16(al, bh, c);
+    c = mfma16(ah, bl, c);
+    return mfma16(ah, bh, c);
+}
+
+// wait until at most N of this wavefront's loads are outstanding and its LDS
+// reads are complete, then the workgroup barrier (no fence: that would wait
+// for the loads still in flight)
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// a record into LDS: 35 blocks of 1 KiB, block b by wavefront b % 4
+constexpr int REC_BLOCKS = REC / 1024;
+constexpr int LOADS_PER_WAVE = (REC_BLOCKS + SCAN_WAVES - 1) / SCAN_WAVES;   // 9 (the last is partial)
+__device__ __forceinline__ void rec_issue(Rsrc r, uint8_t *dst, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+        const int b = wave + SCAN_WAVES * j;
+        // every wavefront issues the same number of loads (the wait counts
+        // assume it): past the record's last block the load repeats block 0
+        // into a spare block of the buffer
+        const int bb = b < REC_BLOCKS ? b : 0;
+        const int db = b < REC_BLOCKS ? b : REC_BLOCKS;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(dst + db * 1024), 16, bb * 1024 + lane * 16, 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const uint8_t *records, float *obuf) {
+    // one LDS buffer per record in flight (+1 spare block each), separate
+    // arrays so that the compiler's waits track each one alone
+    __shared__ __attribute__((aligned(1024))) uint8_t sR0[REC + 1024], sR1[REC + 1024], sR2[REC + 1024],
+        sR3[REC + 1024];
+    const int grp = blockIdx.x % SCAN_GROUPS;
+    const int slot_n = blockIdx.x / SCAN_GROUPS / p.H;
+    const int h = blockIdx.x / SCAN_GROUPS - slot_n * p.H;
+    int n = slot_n;
+    if (p.seq_order) {
+        n = p.seq_order[slot_n];
+        if (n < 0 || n >= p.num_seqs) return;
+    }
+    const Range rng = seq_range(p, n);
+    if (rng.len <= 0) return;
+    const int64_t NC = (rng.len + CC - 1) / CC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int col0 = 16 * (grp * SCAN_WAVES + wave);
+    const int64_t unit = (int64_t)n * p.H + h;
+    const int64_t sb = slot_base(p, n);
+    const uint8_t *recs = records + (sb * p.H + h) * REC;   // chunk c at + c * H * REC
+
+    // the state: tile rt, element r = S[16 rt + 4 g4 + r][col0 + n16]
+    const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
+    f32x4 st[8];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            st[rt][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
+
+    auto rec_rsrc = [&](int64_t c) { return make_rsrc(recs + c * p.H * REC, REC); };
+    const int64_t rowsz = (int64_t)p.H * DV;
+
+    auto chunk = [&](int64_t c, const uint8_t *R) {
+        // P, R: step m over state rows 32 m .. 32 m + 31 (tiles 2 m, 2 m + 1)
+        // the three parts of each split product in separate accumulators:
+        // four dependent steps per chain instead of twelve
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 P0 = z4, P1 = z4, P2 = z4, R0 = z4, R1 = z4, R2 = z4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int so = ((m * 4 + g4) * CC + n16) * 16;
+            const u32x4 kah = *reinterpret_cast<const u32x4 *>(R + R_KA + so);
+            const u32x4 kal = *reinterpret_cast<const u32x4 *>(R + R_KA + 4096 + so);
+            const u32x4 qah = *reinterpret_cast<const u32x4 *>(R + R_QA + so);
+            const u32x4 qal = *reinterpret_cast<const u32x4 *>(R + R_QA + 4096 + so);
+            const Split2 x0 = split2(st[2 * m][0], st[2 * m][1]);
+            const Split2 x1 = split2(st[2 * m][2], st[2 * m][3]);
+            const Split2 x2 = split2(st[2 * m + 1][0], st[2 * m + 1][1]);
+            const Split2 x3 = split2(st[2 * m + 1][2], st[2 * m + 1][3]);
+            const u32x4 sh = {x0.hi, x1.hi, x2.hi, x3.hi}, sl = {x0.lo, x1.lo, x2.lo, x3.lo};
+            P0 = mfma32(kal, sh, P0);
+            R0 = mfma32(qal, sh, R0);
+            P1 = mfma32(kah, sl, P1);
+            R1 = mfma32(qah, sl, R1);
+            P2 = mfma32(kah, sh, P2);
+            R2 = mfma32(qah, sh, R2);
+        }
+        const f32x4 Pt = (P0 + P1) + P2, Rt = (R0 + R1) + R2;
+        // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
+        f32x4 Wt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g4 + r;
+            Wt[r] = reinterpret_cast<const float *>(R + R_B)[t] *
+                    (reinterpret_cast<const float *>(R + R_V)[t * DK + col0 + n16] - Pt[r]);
+        }
+        const int to = (n16 * CC + 4 * g4) * 2;
+        const u32x2 th = *reinterpret_cast<const u32x2 *>(R + R_T + to);
+        const u32x2 tl = *reinterpret_cast<const u32x2 *>(R + R_T + 512 + to);
+        const u32x2 mh = *reinterpret_cast<const u32x2 *>(R + R_M + to);
+        const u32x2 ml = *reinterpret_cast<const u32x2 *>(R + R_M + 512 + to);
+        u32x2 wh, wl, dh, dl;
+        split4(Wt, wh, wl);
+        const f32x4 Dt = mma16(th, tl, wh, wl, f32x4{0.f, 0.f, 0.f, 0.f});
+        split4(Dt, dh, dl);
+        const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
+        const int nv = (int)(rng.len - c * CC < CC ? rng.len - c * CC : CC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g4 + r;
+            if (t < nv) obuf[(rng.lo + c * CC + t) * rowsz + (int64_t)h * DV + col0 + n16] = Ot[r];
+        }
+        // S <- Diag(e^{G_C}) S + E^T Delta
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const float4 dc = *reinterpret_cast<const float4 *>(R + R_GC + (16 * rt + 4 * g4) * 4);
+            const int eo = ((16 * rt + n16) * CC + 4 * g4) * 2;
+            const u32x2 eh = *reinterpret_cast<const u32x2 *>(R + R_E + eo);
+            const u32x2 el = *reinterpret_cast<const u32x2 *>(R + R_E + 4096 + eo);
+            st[rt][0] *= dc.x;
+            st[rt][1] *= dc.y;
+            st[rt][2] *= dc.z;
+            st[rt][3] *= dc.w;
+            st[rt] = mma16(eh, el, dh, dl, st[rt]);
+        }
+    };
+    // chunk c: its record landed everywhere (and every wavefront is done with
+    // chunk c - 1's buffer), the record RING - 1 chunks ahead into that
+    // buffer, then the chunk
+    auto step = [&](int64_t c, const uint8_t *cur, uint8_t *prev) {
+        if (c >= NC) return;
+        const int64_t after = NC - 1 - c < RING - 2 ? NC - 1 - c : RING - 2;
+        if (after >= 2)
+            wait_then_barrier<2 * LOADS_PER_WAVE>();
+        else if (after == 1)
+            wait_then_barrier<LOADS_PER_WAVE>();
+        else
+            wait_then_barrier<0>();
+        if (c + RING - 1 < NC) rec_issue(rec_rsrc(c + RING - 1), prev, wave, lane);
+        chunk(c, cur);
+    };
+    rec_issue(rec_rsrc(0), sR0, wave, lane);
+    if (NC > 1) rec_issue(rec_rsrc(1), sR1, wave, lane);
+    if (NC > 2) rec_issue(rec_rsrc(2), sR2, wave, lane);
+#pragma unroll 1
+    for (int64_t c = 0; c < NC; c += RING) {
+        step(c, sR0, sR3);
+        step(c + 1, sR1, sR0);
+        step(c + 2, sR2, sR1);
+        step(c + 3, sR3, sR2);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            bst_f32(rs_state, st[rt][r], ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
+}
+
+template <typename Act>
+hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream) {
+    const int64_t slots = p.total_tokens / CC + p.num_seqs;
+    hipLaunchKernelGGL((scan_prep_kernel<Act>), dim3((unsigned)slots, (unsigned)p.H), dim3(PREP_THREADS), 0,
+                       stream, p, records);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (int64_t)p.num_seqs * p.H * SCAN_GROUPS;
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(64 * SCAN_WAVES), 0, stream, p,
+                       (const uint8_t *)records, obuf);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_split_finish(p, bf16, obuf, stream);
+}
+
+}  // namespace
+
+int64_t prefill_scan_record_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads) {
+    return (total_tokens / CC + num_seqs) * num_heads * (int64_t)REC;
+}
+
+hipError_t launch_prefill_scan(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream) {
+    return bf16 ? launch_scan_as<BF16>(p, true, records, obuf, stream)
+                : launch_scan_as<F32>(p, false, records, obuf, stream);
+}
+
+}  // namespace kda

@@ -355,7 +355,24 @@ hipError_t launch_split_cols(const Params &p, float *obuf, int C, hipStream_t st
     }
 }
 
+template <typename Act>
+hipError_t launch_finish_as(const Params &p, const float *obuf, hipStream_t stream) {
+    const int64_t rows = p.total_tokens * p.H;
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL((split_epilogue_kernel<Act>), dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
+                       dim3(256), 0, stream, p, obuf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t units = (int64_t)p.num_seqs * p.H;
+    hipLaunchKernelGGL((split_window_kernel<Act>), dim3((unsigned)units), dim3(128), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_split_finish(const Params &p, bool bf16, const float *obuf, hipStream_t stream) {
+    return bf16 ? launch_finish_as<BF16>(p, obuf, stream) : launch_finish_as<F32>(p, obuf, stream);
+}
 
 int prefill_split_cols(int64_t units) {
     if (units <= 48) return 1;      // 8 workgroups per pair

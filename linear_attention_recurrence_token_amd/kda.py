@@ -22,6 +22,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE, KDA_ERR_LAUNCH
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_BOUNDED, KDA_GATE_LITERAL, KDA_GATE_RAW = 0, 1, 2
 KDA_PREFILL_AUTO, KDA_PREFILL_FUSED, KDA_PREFILL_SPLIT, KDA_PREFILL_CHUNK, KDA_PREFILL_SHORT = 0, 1, 2, 3, 4
+KDA_PREFILL_SCAN = 5
 DK = DV = 128
 TAPS = 4
 CH = 2 * DK + DV
@@ -216,7 +217,7 @@ def kda_sequence(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bi
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a GPU tensor")
-        need = int(lib().kda_sequence_workspace_size(ctypes.byref(c), N, T)) if o_raw is None else 0
+        need = int(lib().kda_sequence_workspace_size(ctypes.byref(c), N, T))
         if need < 0:
             raise KdaError(need, "kda_sequence_workspace_size")
         if need > 0:

@@ -85,7 +85,7 @@ def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8, ws=None, ws_bytes=0):
     ({"l2_eps": -1.0}, kda.KDA_ERR_INVALID_ARG),
     ({"rms_eps": float("nan")}, kda.KDA_ERR_INVALID_ARG),
     ({"gate_lower_bound": float("nan")}, kda.KDA_ERR_INVALID_ARG),
-    ({"prefill_path": 5}, kda.KDA_ERR_INVALID_ARG),
+    ({"prefill_path": 6}, kda.KDA_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected(lib, over, status):
     t = _fake_tensors()
@@ -143,6 +143,17 @@ def test_workspace_size_and_checks(lib):
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=1)), 2, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=3)), 2, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=4)), 2, 100) == 0
+    # the two-pass chunk path: records (35 KiB per chunk slot and head; a
+    # sequence of len tokens takes at most len // 16 + 1 slots), then the readout
+    rec = lambda T, N, H: ((T // 16 + N) * H * 35840 + 255) // 256 * 256
+    out = lambda T, H: T * H * 128 * 4
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=5)), 2, 100) == rec(100, 2, 4) + out(100, 4)
+    # AUTO takes it for few pairs (here 8) averaging at least 256 tokens
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 512) == rec(512, 2, 4) + out(512, 4)
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 510) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 3, 8192) == 0   # 192 pairs
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 2, 8192) == \
+        rec(8192, 2, 64) + out(8192, 64)
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, **lit)), 16, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, prefill_path=2)), 16, 100) \
         == 100 * 64 * 128 * 4
@@ -199,6 +210,10 @@ def test_path_support_checked_before_the_device(lib):
     t = _fake_tensors()
     assert _seq(lib, _cfg(prefill_path=3, gate_mode=kda.KDA_GATE_RAW), t) == kda.KDA_ERR_UNSUPPORTED
     assert _seq(lib, _cfg(prefill_path=3, gate_lower_bound=-8.0), t) == kda.KDA_ERR_UNSUPPORTED
+    assert _seq(lib, _cfg(prefill_path=5, gate_mode=kda.KDA_GATE_LITERAL), t) == kda.KDA_ERR_UNSUPPORTED
+    # the two-pass path without the workspace it needs
+    assert _seq(lib, _cfg(prefill_path=5), t, ws=1 << 41, ws_bytes=1 << 10) == kda.KDA_ERR_INVALID_ARG
+    assert _seq(lib, _cfg(prefill_path=5), t) == kda.KDA_ERR_INVALID_ARG
     # the short path addresses a batch's token rows with 32-bit offsets
     big = (1 << 32) // (4 * 128 * 4) + 2           # tokens with H = 4 past 4 GiB of fp32 rows
     assert _seq(lib, _cfg(prefill_path=4), t, n=2, total=big) == kda.KDA_ERR_UNSUPPORTED

@@ -26,7 +26,7 @@ def note(msg):
 
 # ---------------------------------------------------------------- small sizes
 
-PATHS = pytest.mark.parametrize("path", ["fused", "split", "chunk", "short"])
+PATHS = pytest.mark.parametrize("path", ["fused", "split", "chunk", "short", "scan"])
 PATHS_ANY_GATE = pytest.mark.parametrize("path", ["fused", "split", "short"])
 
 
@@ -99,7 +99,7 @@ def test_ragged_edges(gpu, act, path):
                        bf16=(act == "bf16"), label="ragged")
 
 
-@pytest.mark.parametrize("path", ["auto", "fused", "split", "chunk", "short"])
+@pytest.mark.parametrize("path", ["auto", "fused", "split", "chunk", "short", "scan"])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_many_short_sequences(gpu, act, path):
     # lengths 1..16 over many sequences: below, at and around one chunk, and
@@ -159,8 +159,8 @@ def test_bounded_gate_other_bounds(gpu, lb, path):
     w = synth.make_workload("lb", seed=70, N=2, H=2, lengths=[29, 12], lower_bound=lb,
                             decay=(lo, 0.999), state_std=0.02, win_std=1.0)
     assert np.all(np.isfinite(w.f))
-    if path == "chunk" and lb < -7.5:
-        # the chunkwise form needs |lb| <= 7.5 and says so
+    if path in ("chunk", "scan") and lb < -7.5:
+        # the chunkwise forms need |lb| <= 7.5 and say so
         with pytest.raises(kda.KdaError) as ei:
             _gpu.run_sequence(w, gpu, path=path)
         assert ei.value.status == kda.KDA_ERR_UNSUPPORTED
@@ -195,7 +195,7 @@ def test_decode_large_state(gpu):
 
 # ---------------------------------------------------------------- invariances
 
-@pytest.mark.parametrize("other", ["split", "chunk", "short"])
+@pytest.mark.parametrize("other", ["split", "chunk", "short", "scan"])
 def test_prefill_paths_agree(gpu, other):
     w = synth.workload(3, scale={"N": 3, "H": 5, "T": 131})
     note("%s vs fused prefill" % other)
@@ -207,10 +207,11 @@ def test_prefill_paths_agree(gpu, other):
     np.testing.assert_array_equal(a["win"], b["win"])
 
 
-def test_chunk_path_rejects_unbounded_gates(gpu):
+@pytest.mark.parametrize("path", ["chunk", "scan"])
+def test_chunk_path_rejects_unbounded_gates(gpu, path):
     w = synth.make_workload("raw", seed=5, N=1, H=2, lengths=[20], gate_mode=synth.GATE_RAW)
     with pytest.raises(kda.KdaError) as ei:
-        _gpu.run_sequence(w, gpu, path="chunk")
+        _gpu.run_sequence(w, gpu, path=path)
     assert ei.value.status == kda.KDA_ERR_UNSUPPORTED
 
 
@@ -303,10 +304,12 @@ def test_full_decode_64x32(gpu):
     _gpu.assert_parity(got, ref, label="decode full")
 
 
-def test_full_prefill_1x32x8192(gpu):
+@pytest.mark.parametrize("path", ["auto", "chunk"])
+def test_full_prefill_1x32x8192(gpu, path):
+    # auto: the two-pass chunk path (32 pairs of 8192 tokens)
     w = synth.workload(2)
-    note("full prefill 1x32x8192 fp32, sampled heads 0, 19 (auto path: chunk)")
-    full = _gpu.run_sequence(w, gpu)
+    note("full prefill 1x32x8192 fp32, sampled heads 0, 19, %s" % path)
+    full = _gpu.run_sequence(w, gpu, path=path)
     _sampled(w, full, [0], [0, 19], bf16=False)
 
 
