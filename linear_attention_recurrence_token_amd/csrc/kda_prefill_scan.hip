@@ -57,6 +57,16 @@ __device__ __forceinline__ void split_store(uint8_t *rec, int off_hi, int part_b
     reinterpret_cast<uint16_t *>(rec + off_hi + part_bytes)[idx] = bf16_hi(lo);
 }
 
+// two fp32 values as packed bf16 high parts and packed bf16 remainders (the
+// first value in the low half)
+struct Split2 {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float x0, float x1) {
+    const uint32_t hb = pack_bf16x2(x0, x1);
+    return {hb, pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u))};
+}
+
 // record slot of chunk c of sequence n: slots floor(cu[n] / 16) + n + c never
 // collide (a sequence of len tokens has at most floor(len / 16) + 1 chunks)
 __device__ __forceinline__ int64_t slot_base(const Params &p, int n) {
@@ -91,7 +101,7 @@ __global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8
     const int nv = (int)(rng.len - c0 < CC ? rng.len - c0 : CC);
     uint8_t *rec = records + (slot * p.H + h) * REC;
 
-    __shared__ float s_x[CC + PAST][XP];    // raw rows c0 - 3 .. c0 + 15, then activated rows 3 .. 18
+    __shared__ __attribute__((aligned(16))) float s_x[CC + PAST][XP];   // raw rows c0 - 3 .. c0 + 15, then activated rows 3 .. 18
     __shared__ float s_nrm[CC][2];          // L2 scales of q, k
     __shared__ float s_G[CC][DK];           // log-decay summed from the chunk start
     __shared__ __attribute__((aligned(16))) float s_kl[CC][FP], s_ql[CC][FP], s_kr[CC][FP];
@@ -190,24 +200,67 @@ __global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8
         if (sub == 0) s_nrm[t][which] = rsqrtf(ss + p.l2_eps);
     }
     __syncthreads();
-    // operands of the state products, and the L, M factors
-    for (int idx = tid; idx < CC * DK; idx += PREP_THREADS) {
-        const int t = idx / DK, i = idx - t * DK;
-        const float qh = s_x[PAST + t][i] * s_nrm[t][0];
-        const float kh = s_x[PAST + t][DK + i] * s_nrm[t][1];
-        const float G = s_G[t][i], GC = s_G[CC - 1][i], r = s_G[CC / 2 - 1][i];
-        const float eg = __expf(G);
-        const int m = i >> 5, g = (i & 15) >> 2, e = ((i & 31) >> 4) * 4 + (i & 3);
-        const int sidx = ((m * 4 + g) * CC + t) * 8 + e;
-        split_store(rec, R_KA, 4096, sidx, eg * kh);
-        split_store(rec, R_QA, 4096, sidx, eg * qh);
-        split_store(rec, R_E, 4096, i * CC + t, __expf(GC - G) * kh);
-        reinterpret_cast<float *>(rec + R_V)[t * DK + i] = s_x[PAST + t][2 * DK + i];
-        if (t == 0) reinterpret_cast<float *>(rec + R_GC)[i] = __expf(GC);
-        const float ef = __expf(G - r), eb = __expf(r - G);
-        s_kl[t][i] = ef * kh;
-        s_ql[t][i] = ef * qh;
-        s_kr[t][i] = eb * kh;
+    // operands of the state products, one 16-byte record slot per thread:
+    // token t, channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3}; and
+    // the L, M factors of those channels
+    {
+        const int t = tid & 15, g = (tid >> 4) & 3, m = tid >> 6;
+        float ka[8], qa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 32 * m + 16 * (e >> 2) + 4 * g + (e & 3);
+            const float qh = s_x[PAST + t][i] * s_nrm[t][0];
+            const float kh = s_x[PAST + t][DK + i] * s_nrm[t][1];
+            const float G = s_G[t][i], r = s_G[CC / 2 - 1][i];
+            const float eg = __expf(G);
+            ka[e] = eg * kh;
+            qa[e] = eg * qh;
+            const float ef = __expf(G - r), eb = __expf(r - G);
+            s_kl[t][i] = ef * kh;
+            s_ql[t][i] = ef * qh;
+            s_kr[t][i] = eb * kh;
+        }
+        const int so = (((m * 4 + g) * CC) + t) * 16;
+        u32x4 kh4, kl4, qh4, ql4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const Split2 a = split2(ka[2 * e], ka[2 * e + 1]), b = split2(qa[2 * e], qa[2 * e + 1]);
+            kh4[e] = a.hi;
+            kl4[e] = a.lo;
+            qh4[e] = b.hi;
+            ql4[e] = b.lo;
+        }
+        *reinterpret_cast<u32x4 *>(rec + R_KA + so) = kh4;
+        *reinterpret_cast<u32x4 *>(rec + R_KA + 4096 + so) = kl4;
+        *reinterpret_cast<u32x4 *>(rec + R_QA + so) = qh4;
+        *reinterpret_cast<u32x4 *>(rec + R_QA + 4096 + so) = ql4;
+    }
+    // E: one channel's 16 tokens per thread; and e^{G_C}
+    if (tid < DK) {
+        const int i = tid;
+        const float GC = s_G[CC - 1][i];
+        u32x4 eh[2], el[2];
+#pragma unroll
+        for (int t2 = 0; t2 < CC / 2; ++t2) {
+            const float e0 = __expf(GC - s_G[2 * t2][i]) * (s_x[PAST + 2 * t2][DK + i] * s_nrm[2 * t2][1]);
+            const float e1 = __expf(GC - s_G[2 * t2 + 1][i]) * (s_x[PAST + 2 * t2 + 1][DK + i] * s_nrm[2 * t2 + 1][1]);
+            const Split2 a = split2(e0, e1);
+            eh[t2 >> 2][t2 & 3] = a.hi;
+            el[t2 >> 2][t2 & 3] = a.lo;
+        }
+        *reinterpret_cast<u32x4 *>(rec + R_E + i * 32) = eh[0];
+        *reinterpret_cast<u32x4 *>(rec + R_E + i * 32 + 16) = eh[1];
+        *reinterpret_cast<u32x4 *>(rec + R_E + 4096 + i * 32) = el[0];
+        *reinterpret_cast<u32x4 *>(rec + R_E + 4096 + i * 32 + 16) = el[1];
+        reinterpret_cast<float *>(rec + R_GC)[i] = __expf(GC);
+    }
+    // v: four channels per store
+#pragma unroll
+    for (int u = 0; u < (CC * DV / 4) / PREP_THREADS; ++u) {
+        const int idx = tid + u * PREP_THREADS;
+        const int t = idx / (DV / 4), i4 = (idx - t * (DV / 4)) * 4;
+        *reinterpret_cast<float4 *>(rec + R_V + (t * DV + i4) * 4) =
+            *reinterpret_cast<const float4 *>(&s_x[PAST + t][2 * DK + i4]);
     }
     __syncthreads();
     // L (strictly lower, times beta: the matrix A of the solve) and M (lower
@@ -256,13 +309,6 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
                                                      c, 0, 0, 0);
-}
-struct Split2 {
-    uint32_t hi, lo;
-};
-__device__ __forceinline__ Split2 split2(float x0, float x1) {
-    const uint32_t hb = pack_bf16x2(x0, x1);
-    return {hb, pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u))};
 }
 __device__ __forceinline__ void split4(f32x4 d, u32x2 &h, u32x2 &l) {
     const Split2 a = split2(d[0], d[1]), b = split2(d[2], d[3]);
