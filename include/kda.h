@@ -119,7 +119,7 @@ typedef enum kda_prefill_path {
     KDA_PREFILL_SCAN = 5        /* CHUNK in two passes: every chunk's
                                    input-only operands at once, then the
                                    chunks in order with each pair's state
-                                   columns over 8 wavefronts; for few pairs of
+                                   columns over 16 wavefronts; for few pairs of
                                    long sequences.  Same gate rule as CHUNK;
                                    needs the workspace kda_sequence_workspace_size
                                    reports (less the readout part when o_raw

@@ -12,8 +12,8 @@
 // pass 1 computes the first kind for every chunk of every pair at once (one
 // workgroup per chunk and head, all independent) into a record per chunk in
 // the caller's workspace, and pass 2 walks the chunks of a pair with only the
-// state products left, its 128 state columns spread over 8 wavefronts in two
-// workgroups.  The pre-norm readout goes to an fp32 buffer; the RMSNorm +
+// state products left, its 128 state columns spread over 16 wavefronts in
+// four workgroups (each 16-column block split in two 64-row halves).  The pre-norm readout goes to an fp32 buffer; the RMSNorm +
 // gate and the window are written by the column-split path's finishing
 // kernels.
 //
@@ -298,8 +298,12 @@ __global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8
 }
 
 // ---------------------------------------------------------------- pass 2
-constexpr int SCAN_WAVES = 4;           // wavefronts per workgroup: 64 of the 128 columns
-constexpr int SCAN_GROUPS = DV / (16 * SCAN_WAVES);
+// Wavefront w of a workgroup: state columns 16 (2 grp + w / 2) .. + 15, key
+// rows 64 (w % 2) .. + 63; the two row halves of a column block add their
+// partial P, R through LDS.
+constexpr int SCAN_WAVES = 4;
+constexpr int SCAN_COLS = 2;            // 16-column blocks per workgroup
+constexpr int SCAN_GROUPS = DV / (16 * SCAN_COLS);
 constexpr int RING = 4;                 // record buffers per workgroup (3 loading while 1 is used)
 
 __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
@@ -334,6 +338,8 @@ template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// LDS writes complete, then the workgroup barrier (loads may stay in flight)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // a record into LDS: 35 blocks of 1 KiB, block b by wavefront b % 4
 constexpr int REC_BLOCKS = REC / 1024;
@@ -369,40 +375,44 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
     const int64_t NC = (rng.len + CC - 1) / CC;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n16 = lane & 15, g4 = lane >> 4;
-    const int col0 = 16 * (grp * SCAN_WAVES + wave);
+    const int rh = wave & 1;                               // key rows 64 rh .. 64 rh + 63
+    const int col0 = 16 * (grp * SCAN_COLS + (wave >> 1));
     const int64_t unit = (int64_t)n * p.H + h;
     const int64_t sb = slot_base(p, n);
     const uint8_t *recs = records + (sb * p.H + h) * REC;   // chunk c at + c * H * REC
+    // partial P, R of each wavefront: [wave][P, R][element r][lane]
+    __shared__ __attribute__((aligned(16))) float sX[SCAN_WAVES][2][4][64];
 
-    // the state: tile rt, element r = S[16 rt + 4 g4 + r][col0 + n16]
+    // the state: tile j, element r = S[16 (4 rh + j) + 4 g4 + r][col0 + n16]
     const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
-    f32x4 st[8];
+    f32x4 st[4];
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            st[rt][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
+            st[j][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, (4 * rh + j) * 16 * DV * 4);
 
     auto rec_rsrc = [&](int64_t c) { return make_rsrc(recs + c * p.H * REC, REC); };
     const int64_t rowsz = (int64_t)p.H * DV;
 
     auto chunk = [&](int64_t c, const uint8_t *R) {
-        // P, R: step m over state rows 32 m .. 32 m + 31 (tiles 2 m, 2 m + 1)
-        // the three parts of each split product in separate accumulators:
-        // four dependent steps per chain instead of twelve
+        // partial P, R over this wavefront's key rows: steps m = 2 rh, 2 rh + 1
+        // (rows 32 m .. 32 m + 31, tiles 2 (m - 2 rh), + 1); the three parts of
+        // each split product in separate accumulators
         const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
         f32x4 P0 = z4, P1 = z4, P2 = z4, R0 = z4, R1 = z4, R2 = z4;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int mm = 0; mm < 2; ++mm) {
+            const int m = 2 * rh + mm;
             const int so = ((m * 4 + g4) * CC + n16) * 16;
             const u32x4 kah = *reinterpret_cast<const u32x4 *>(R + R_KA + so);
             const u32x4 kal = *reinterpret_cast<const u32x4 *>(R + R_KA + 4096 + so);
             const u32x4 qah = *reinterpret_cast<const u32x4 *>(R + R_QA + so);
             const u32x4 qal = *reinterpret_cast<const u32x4 *>(R + R_QA + 4096 + so);
-            const Split2 x0 = split2(st[2 * m][0], st[2 * m][1]);
-            const Split2 x1 = split2(st[2 * m][2], st[2 * m][3]);
-            const Split2 x2 = split2(st[2 * m + 1][0], st[2 * m + 1][1]);
-            const Split2 x3 = split2(st[2 * m + 1][2], st[2 * m + 1][3]);
+            const Split2 x0 = split2(st[2 * mm][0], st[2 * mm][1]);
+            const Split2 x1 = split2(st[2 * mm][2], st[2 * mm][3]);
+            const Split2 x2 = split2(st[2 * mm + 1][0], st[2 * mm + 1][1]);
+            const Split2 x3 = split2(st[2 * mm + 1][2], st[2 * mm + 1][3]);
             const u32x4 sh = {x0.hi, x1.hi, x2.hi, x3.hi}, sl = {x0.lo, x1.lo, x2.lo, x3.lo};
             P0 = mfma32(kal, sh, P0);
             R0 = mfma32(qal, sh, R0);
@@ -411,7 +421,22 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
             P2 = mfma32(kah, sh, P2);
             R2 = mfma32(qah, sh, R2);
         }
-        const f32x4 Pt = (P0 + P1) + P2, Rt = (R0 + R1) + R2;
+        const f32x4 Pp = (P0 + P1) + P2, Rp = (R0 + R1) + R2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sX[wave][0][r][lane] = Pp[r];
+            sX[wave][1][r][lane] = Rp[r];
+        }
+        lds_barrier();
+        // whole P, R: the lower row half's part plus the upper's, in that order
+        // in both wavefronts, so that both form the same Delta
+        f32x4 Pt, Rt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float po = sX[wave ^ 1][0][r][lane], ro = sX[wave ^ 1][1][r][lane];
+            Pt[r] = rh == 0 ? Pp[r] + po : po + Pp[r];
+            Rt[r] = rh == 0 ? Rp[r] + ro : ro + Rp[r];
+        }
         // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
         f32x4 Wt;
 #pragma unroll
@@ -423,31 +448,34 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
         const int to = (n16 * CC + 4 * g4) * 2;
         const u32x2 th = *reinterpret_cast<const u32x2 *>(R + R_T + to);
         const u32x2 tl = *reinterpret_cast<const u32x2 *>(R + R_T + 512 + to);
-        const u32x2 mh = *reinterpret_cast<const u32x2 *>(R + R_M + to);
-        const u32x2 ml = *reinterpret_cast<const u32x2 *>(R + R_M + 512 + to);
         u32x2 wh, wl, dh, dl;
         split4(Wt, wh, wl);
         const f32x4 Dt = mma16(th, tl, wh, wl, f32x4{0.f, 0.f, 0.f, 0.f});
         split4(Dt, dh, dl);
-        const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
-        const int nv = (int)(rng.len - c * CC < CC ? rng.len - c * CC : CC);
+        if (rh == 0) {
+            const u32x2 mh = *reinterpret_cast<const u32x2 *>(R + R_M + to);
+            const u32x2 ml = *reinterpret_cast<const u32x2 *>(R + R_M + 512 + to);
+            const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
+            const int nv = (int)(rng.len - c * CC < CC ? rng.len - c * CC : CC);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g4 + r;
-            if (t < nv) obuf[(rng.lo + c * CC + t) * rowsz + (int64_t)h * DV + col0 + n16] = Ot[r];
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                if (t < nv) obuf[(rng.lo + c * CC + t) * rowsz + (int64_t)h * DV + col0 + n16] = Ot[r];
+            }
         }
-        // S <- Diag(e^{G_C}) S + E^T Delta
+        // S <- Diag(e^{G_C}) S + E^T Delta on this wavefront's rows
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
+        for (int j = 0; j < 4; ++j) {
+            const int rt = 4 * rh + j;
             const float4 dc = *reinterpret_cast<const float4 *>(R + R_GC + (16 * rt + 4 * g4) * 4);
             const int eo = ((16 * rt + n16) * CC + 4 * g4) * 2;
             const u32x2 eh = *reinterpret_cast<const u32x2 *>(R + R_E + eo);
             const u32x2 el = *reinterpret_cast<const u32x2 *>(R + R_E + 4096 + eo);
-            st[rt][0] *= dc.x;
-            st[rt][1] *= dc.y;
-            st[rt][2] *= dc.z;
-            st[rt][3] *= dc.w;
-            st[rt] = mma16(eh, el, dh, dl, st[rt]);
+            st[j][0] *= dc.x;
+            st[j][1] *= dc.y;
+            st[j][2] *= dc.z;
+            st[j][3] *= dc.w;
+            st[j] = mma16(eh, el, dh, dl, st[j]);
         }
     };
     // chunk c: its record landed everywhere (and every wavefront is done with
@@ -476,10 +504,10 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
         step(c + 3, sR3, sR2);
     }
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            bst_f32(rs_state, st[rt][r], ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
+            bst_f32(rs_state, st[j][r], ((4 * g4 + r) * DV + col0 + n16) * 4, (4 * rh + j) * 16 * DV * 4);
 }
 
 template <typename Act>
