@@ -220,12 +220,12 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
     # the kernel the automatic choice runs (the library's rule: the short-
     # sequence kernel under 8 tokens per sequence on average; else, for the
     # bounded gate with |lower bound| <= 7.5, the two-pass chunk path for at
-    # most 128 pairs averaging 256 tokens or more (given its workspace) and the
+    # most 64 pairs averaging 128 tokens or more (given its workspace) and the
     # one-pass chunk kernel otherwise; else split / fused)
     short = w.total_tokens < 8 * w.N
     chunk = (cfg.gate_mode == kda.KDA_GATE_BOUNDED and -7.5 <= cfg.gate_lower_bound <= 0.0
              and not short)
-    scan = chunk and w.N * w.H <= 128 and w.total_tokens >= 256 * w.N and ws_bytes > 0
+    scan = chunk and w.N * w.H <= 64 and w.total_tokens >= 128 * w.N and ws_bytes > 0
     path = ("short" if short else ("scan" if scan else ("chunk" if chunk else
                                                         ("split" if ws_bytes > 0 else "fused"))))
     # HBM traffic from the committed rocprofv3 summary of this workload, if it

