@@ -171,9 +171,10 @@ def cpu_baseline_decode(synth, w, target_s):
     steps = int(max(1, min(w.decode_steps, target_s / max(t1, 1e-6))))
     wall = run(steps)
     passes = 1
-    # when every step fits in well under the target, run the same steps again
-    # (from the same initial state) until about target_s of oracle work is timed
-    while wall < 0.8 * target_s and steps == w.decode_steps:
+    # when the workload's steps fit in well under the target, run the same
+    # steps again (from the same initial state) until about target_s of oracle
+    # work is timed
+    while wall < 0.8 * target_s:
         wall += run(steps)
         passes += 1
     th = w.N * w.H * steps * passes
