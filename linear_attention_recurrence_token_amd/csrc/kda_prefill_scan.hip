@@ -82,8 +82,16 @@ constexpr int FP = DK + 4;              // L, M factor rows: 16-byte aligned, an
                                         // rows a 16-lane group reads at one column on distinct banks
 constexpr int RAW_PER = ((CC + PAST) * CH + PREP_THREADS - 1) / PREP_THREADS;   // raw loads per thread
 
+// LDS of the operand pass: the raw / activated rows, later the L, M factor
+// rows in the same bytes; the conv taps, later the decay sums in the same bytes
+constexpr int X_BYTES = (CC + PAST) * XP * 4, F_BYTES = 3 * CC * FP * 4;
+constexpr int R1_BYTES = X_BYTES > F_BYTES ? X_BYTES : F_BYTES;
+constexpr int G_BYTES = CC * DK * 4, CW_BYTES = CH * TAPS * 4;
+constexpr int R2_BYTES = G_BYTES > CW_BYTES ? G_BYTES : CW_BYTES;
+
 template <typename Act>
-__global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8_t *records) {
+__global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
+void scan_prep_kernel(Params p, uint8_t *records) {
     const int64_t slot = blockIdx.x;
     const int h = blockIdx.y;
     const int tid = threadIdx.x;
@@ -101,12 +109,18 @@ __global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8
     const int nv = (int)(rng.len - c0 < CC ? rng.len - c0 : CC);
     uint8_t *rec = records + (slot * p.H + h) * REC;
 
-    __shared__ __attribute__((aligned(16))) float s_x[CC + PAST][XP];   // raw rows c0 - 3 .. c0 + 15, then activated rows 3 .. 18
+    __shared__ __attribute__((aligned(16))) uint8_t smem[R1_BYTES + R2_BYTES];
+    // raw rows c0 - 3 .. c0 + 15, then activated rows 3 .. 18
+    float(*s_x)[XP] = reinterpret_cast<float(*)[XP]>(smem);
+    // L, M factors (after the last read of s_x)
+    float(*s_kl)[FP] = reinterpret_cast<float(*)[FP]>(smem);
+    float(*s_ql)[FP] = reinterpret_cast<float(*)[FP]>(smem + CC * FP * 4);
+    float(*s_kr)[FP] = reinterpret_cast<float(*)[FP]>(smem + 2 * CC * FP * 4);
+    float(*s_cw)[TAPS] = reinterpret_cast<float(*)[TAPS]>(smem + R1_BYTES);
+    // log-decay summed from the chunk start (after the conv's last read of s_cw)
+    float(*s_G)[DK] = reinterpret_cast<float(*)[DK]>(smem + R1_BYTES);
     __shared__ float s_nrm[CC][2];          // L2 scales of q, k
-    __shared__ float s_G[CC][DK];           // log-decay summed from the chunk start
-    __shared__ __attribute__((aligned(16))) float s_kl[CC][FP], s_ql[CC][FP], s_kr[CC][FP];
     __shared__ float s_A[CC][CC], s_b[CC];
-    __shared__ __attribute__((aligned(16))) float s_cw[CH][TAPS];
 
     const int64_t rowsz = (int64_t)p.H * DK;
     const float *W = p.win + ((int64_t)n * p.H + h) * (PAST * CH);
@@ -202,38 +216,15 @@ __global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8
     __syncthreads();
     // operands of the state products, one 16-byte record slot per thread:
     // token t, channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3}; and
-    // the L, M factors of those channels
-    {
-        const int t = tid & 15, g = (tid >> 4) & 3, m = tid >> 6;
-        float ka[8], qa[8];
+    // the L, M factors of those channels.  The slot's q_hat, k_hat are read
+    // now: the factors go into the bytes of s_x after the next barrier.
+    const int st_t = tid & 15, st_g = (tid >> 4) & 3, st_m = tid >> 6;
+    float sq[8], sk[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = 32 * m + 16 * (e >> 2) + 4 * g + (e & 3);
-            const float qh = s_x[PAST + t][i] * s_nrm[t][0];
-            const float kh = s_x[PAST + t][DK + i] * s_nrm[t][1];
-            const float G = s_G[t][i], r = s_G[CC / 2 - 1][i];
-            const float eg = __expf(G);
-            ka[e] = eg * kh;
-            qa[e] = eg * qh;
-            const float ef = __expf(G - r), eb = __expf(r - G);
-            s_kl[t][i] = ef * kh;
-            s_ql[t][i] = ef * qh;
-            s_kr[t][i] = eb * kh;
-        }
-        const int so = (((m * 4 + g) * CC) + t) * 16;
-        u32x4 kh4, kl4, qh4, ql4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const Split2 a = split2(ka[2 * e], ka[2 * e + 1]), b = split2(qa[2 * e], qa[2 * e + 1]);
-            kh4[e] = a.hi;
-            kl4[e] = a.lo;
-            qh4[e] = b.hi;
-            ql4[e] = b.lo;
-        }
-        *reinterpret_cast<u32x4 *>(rec + R_KA + so) = kh4;
-        *reinterpret_cast<u32x4 *>(rec + R_KA + 4096 + so) = kl4;
-        *reinterpret_cast<u32x4 *>(rec + R_QA + so) = qh4;
-        *reinterpret_cast<u32x4 *>(rec + R_QA + 4096 + so) = ql4;
+    for (int e = 0; e < 8; ++e) {
+        const int i = 32 * st_m + 16 * (e >> 2) + 4 * st_g + (e & 3);
+        sq[e] = s_x[PAST + st_t][i] * s_nrm[st_t][0];
+        sk[e] = s_x[PAST + st_t][DK + i] * s_nrm[st_t][1];
     }
     // E: one channel's 16 tokens per thread; and e^{G_C}
     if (tid < DK) {
@@ -261,6 +252,36 @@ __global__ __launch_bounds__(PREP_THREADS) void scan_prep_kernel(Params p, uint8
         const int t = idx / (DV / 4), i4 = (idx - t * (DV / 4)) * 4;
         *reinterpret_cast<float4 *>(rec + R_V + (t * DV + i4) * 4) =
             *reinterpret_cast<const float4 *>(&s_x[PAST + t][2 * DK + i4]);
+    }
+    __syncthreads();                           // s_x is dead from here on
+    {
+        float ka[8], qa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 32 * st_m + 16 * (e >> 2) + 4 * st_g + (e & 3);
+            const float G = s_G[st_t][i], r = s_G[CC / 2 - 1][i];
+            const float eg = __expf(G);
+            ka[e] = eg * sk[e];
+            qa[e] = eg * sq[e];
+            const float ef = __expf(G - r), eb = __expf(r - G);
+            s_kl[st_t][i] = ef * sk[e];
+            s_ql[st_t][i] = ef * sq[e];
+            s_kr[st_t][i] = eb * sk[e];
+        }
+        const int so = (((st_m * 4 + st_g) * CC) + st_t) * 16;
+        u32x4 kh4, kl4, qh4, ql4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const Split2 a = split2(ka[2 * e], ka[2 * e + 1]), b = split2(qa[2 * e], qa[2 * e + 1]);
+            kh4[e] = a.hi;
+            kl4[e] = a.lo;
+            qh4[e] = b.hi;
+            ql4[e] = b.lo;
+        }
+        *reinterpret_cast<u32x4 *>(rec + R_KA + so) = kh4;
+        *reinterpret_cast<u32x4 *>(rec + R_KA + 4096 + so) = kl4;
+        *reinterpret_cast<u32x4 *>(rec + R_QA + so) = qh4;
+        *reinterpret_cast<u32x4 *>(rec + R_QA + 4096 + so) = ql4;
     }
     __syncthreads();
     // L (strictly lower, times beta: the matrix A of the solve) and M (lower
