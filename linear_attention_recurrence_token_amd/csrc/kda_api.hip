@@ -75,8 +75,8 @@ bool auto_chunk(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
 // The two-pass chunk path pays for writing and reading every chunk's operands
 // once; it wins when the one-pass kernel, one workgroup per (sequence, head),
 // would leave most compute units idle.  Measured against the one-pass kernel:
-// 2.1x faster at 32 pairs x 8192 tokens, 1.4x at 64 x 4096, 1.1x at 32 x 128;
-// 0.74x at 128 pairs x 2048, 0.4x from 256 pairs on.
+// 2.4x faster at 32 pairs x 8192 tokens, 1.6x at 64 x 4096, 1.15x at 32 x 128;
+// 0.88x at 128 pairs x 2048, about 0.5x from 256 pairs on.
 constexpr int64_t SCAN_MAX_UNITS = 64;
 constexpr int64_t SCAN_MIN_AVG_TOKENS = 128;
 
