@@ -325,6 +325,7 @@ void scan_prep_kernel(Params p, uint8_t *records) {
 constexpr int SCAN_WAVES = 4;
 constexpr int SCAN_COLS = 2;            // 16-column blocks per workgroup
 constexpr int SCAN_GROUPS = DV / (16 * SCAN_COLS);
+constexpr int XCDS = 8;
 constexpr int RING = 4;                 // record buffers per workgroup (3 loading while 1 is used)
 
 __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
@@ -383,9 +384,15 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
     // arrays so that the compiler's waits track each one alone
     __shared__ __attribute__((aligned(1024))) uint8_t sR0[REC + 1024], sR1[REC + 1024], sR2[REC + 1024],
         sR3[REC + 1024];
-    const int grp = blockIdx.x % SCAN_GROUPS;
-    const int slot_n = blockIdx.x / SCAN_GROUPS / p.H;
-    const int h = blockIdx.x / SCAN_GROUPS - slot_n * p.H;
+    // workgroups are dealt to the XCDs in turn: the SCAN_GROUPS workgroups
+    // of one (sequence, head) pair are XCDS apart in the grid, so that they
+    // share one XCD and its L2 fetches each record once for all of them
+    const int xcd = blockIdx.x % XCDS;
+    const int grp = blockIdx.x / XCDS % SCAN_GROUPS;
+    const int pair = blockIdx.x / (XCDS * SCAN_GROUPS) * XCDS + xcd;
+    if (pair >= p.num_seqs * p.H) return;
+    const int slot_n = pair / p.H;
+    const int h = pair - slot_n * p.H;
     int n = slot_n;
     if (p.seq_order) {
         n = p.seq_order[slot_n];
@@ -538,7 +545,8 @@ hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *o
                        stream, p, records);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t blocks = (int64_t)p.num_seqs * p.H * SCAN_GROUPS;
+    const int64_t pairs = (int64_t)p.num_seqs * p.H;
+    const int64_t blocks = (pairs + XCDS - 1) / XCDS * XCDS * SCAN_GROUPS;
     hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(64 * SCAN_WAVES), 0, stream, p,
                        (const uint8_t *)records, obuf);
     e = hipGetLastError();
