@@ -14,7 +14,9 @@
 //     u = S^T (alpha * k) and p = S^T (alpha * q), because the readout of the
 //     updated state equals p + beta (q.k) (v - u)  (expand S_new^T q with
 //     S_new = Diag(alpha) S + beta k (v - u)^T, "Kimi K3 Metal Gap Analysis",
-//     §2, rows "Recurrence" and "O projection");
+//     §2, rows "Recurrence" and "O projection"); the thread of key channel i
+//     stores (alpha_i q_i, alpha_i k_i, alpha_i, k_i) once, so a row costs one
+//     LDS read, and the L2 norms scale the two sums instead of every row;
 //   * the update is written back in place with 16-byte stores; the RMSNorm +
 //     sigmoid gate epilogue needs only a 32-lane reduction.
 //
@@ -36,26 +38,20 @@ struct DecodeShape {
     static_assert(NT == 128 || NT == 256 || NT == 512, "decode workgroup size");
 };
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes of state through the pair's buffer resource; nontemporal (the
+// cache policy's NT bit) or not
+constexpr int CPOL_NT = 2;
 template <bool NTMP>
-__device__ __forceinline__ float4 ld_state(const float *p) {
-    if constexpr (NTMP) {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-        return make_float4(v.x, v.y, v.z, v.w);
-    } else {
-        return *reinterpret_cast<const float4 *>(p);
-    }
+__device__ __forceinline__ float4 ld_state(Rsrc r, uint32_t voff, uint32_t soff) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NTMP ? CPOL_NT : 0);
+    return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
 }
 
 template <bool NTMP>
-__device__ __forceinline__ void st_state(float *p, float4 v) {
-    if constexpr (NTMP) {
-        const f32x4 w = {v.x, v.y, v.z, v.w};
-        __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p));
-    } else {
-        *reinterpret_cast<float4 *>(p) = v;
-    }
+__device__ __forceinline__ void st_state(Rsrc r, float4 v, uint32_t voff, uint32_t soff) {
+    const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, NTMP ? CPOL_NT : 0);
 }
 
 // Row owned by row group rg at step m: interleaved (rg + NRG m: one load
@@ -77,8 +73,10 @@ void decode_kernel(Params p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int cg = tid & 31, rg = tid >> 5;
 
-    __shared__ float s_act[CH];            // activated q | k | v of this token
-    __shared__ float s_alpha[DK];
+    // key row i: (a_i q_i, a_i k_i, a_i, k_i) with q, k after conv + SiLU and
+    // before the L2 norms, which are applied to the sums over rows instead
+    __shared__ float4 s_row[DK];
+    __shared__ float s_v[DV];              // activated v of this token
     __shared__ float s_red[Sh::NW][4];     // per-wave partial sums (qq, kk, qk)
     __shared__ float4 s_up[Sh::NW][32][2]; // per-wave partial u, p per column group
 
@@ -90,7 +88,7 @@ void decode_kernel(Params p) {
     // ---- 1. the pre-step's inputs first: loads return in issue order, so
     // issuing these few before the state lets the pre-step run while the
     // 64 KiB of state is still arriving.  Task i < 128 is the (q_i, k_i)
-    // channel pair, task 128 + j the v channel j and the decay of key channel j.
+    // channel pair and the decay of key channel i, task 128 + j the v channel j.
     constexpr int TPT = (2 * DK + NT - 1) / NT;   // pre-step tasks per thread
     float x0[TPT], x1[TPT], w0[TPT][PAST], w1[TPT][PAST], fa[TPT], fb[TPT], fc[TPT];
     float4 c0[TPT], c1[TPT];
@@ -105,24 +103,27 @@ void decode_kernel(Params p) {
             c1[r] = *reinterpret_cast<const float4 *>(cw + (DK + i) * TAPS);
 #pragma unroll
             for (int j = 0; j < PAST; ++j) { w0[r][j] = W[j * CH + i]; w1[r][j] = W[j * CH + DK + i]; }
+            fa[r] = p.f[row + i];
+            fb[r] = p.A_log[h * DK + i];
+            fc[r] = p.dt_bias[h * DK + i];
         } else if (task < 2 * DK) {
             const int j = task - DK;
             x0[r] = Act::load1(p.v, row + j);
             c0[r] = *reinterpret_cast<const float4 *>(cw + (2 * DK + j) * TAPS);
 #pragma unroll
             for (int jj = 0; jj < PAST; ++jj) w0[r][jj] = W[jj * CH + 2 * DK + j];
-            fa[r] = p.f[row + j];
-            fb[r] = p.A_log[h * DK + j];
-            fc[r] = p.dt_bias[h * DK + j];
         }
     }
     const float b = p.beta[unit];
 
-    // ---- 2. put the whole state in flight
+    // ---- 2. put the whole state in flight: one buffer resource for the
+    // pair's 64 KiB, a per-lane offset, and each row step's offset a constant
+    const Rsrc rs = make_rsrc(S, DK * DV * 4);
+    const uint32_t s_lane = (uint32_t)(dec_row<NT, BLOCKED>(rg, 0) * DV + 4 * cg) * 4;
+    constexpr uint32_t ROW_STEP = (BLOCKED ? 1 : Sh::NRG) * DV * 4;
     float4 s[Sh::RPT];
 #pragma unroll
-    for (int m = 0; m < Sh::RPT; ++m)
-        s[m] = ld_state<NT_LOAD>(S + dec_row<NT, BLOCKED>(rg, m) * DV + 4 * cg);
+    for (int m = 0; m < Sh::RPT; ++m) s[m] = ld_state<NT_LOAD>(rs, s_lane, m * ROW_STEP);
 
     // ---- 3. pre-step: conv4 + SiLU, window shift, L2 partial sums, decay
     float qq = 0.f, kk = 0.f, qk = 0.f;
@@ -135,14 +136,13 @@ void decode_kernel(Params p) {
             const float ak = silu(c1[r].x * w1[r][0] + c1[r].y * w1[r][1] + c1[r].z * w1[r][2] + c1[r].w * x1[r]);
             W[i] = w0[r][1]; W[CH + i] = w0[r][2]; W[2 * CH + i] = x0[r];
             W[DK + i] = w1[r][1]; W[CH + DK + i] = w1[r][2]; W[2 * CH + DK + i] = x1[r];
-            s_act[i] = aq;
-            s_act[DK + i] = ak;
+            const float al = decay(fa[r], __expf(fb[r]), fc[r], p.gate_mode, p.lb);
+            s_row[i] = make_float4(al * aq, al * ak, al, ak);
             qq += aq * aq; kk += ak * ak; qk += aq * ak;
         } else if (task < 2 * DK) {
             const int j = task - DK;
-            s_act[2 * DK + j] = silu(c0[r].x * w0[r][0] + c0[r].y * w0[r][1] + c0[r].z * w0[r][2] + c0[r].w * x0[r]);
+            s_v[j] = silu(c0[r].x * w0[r][0] + c0[r].y * w0[r][1] + c0[r].z * w0[r][2] + c0[r].w * x0[r]);
             W[2 * DK + j] = w0[r][1]; W[CH + 2 * DK + j] = w0[r][2]; W[2 * CH + 2 * DK + j] = x0[r];
-            s_alpha[j] = decay(fa[r], __expf(fb[r]), fc[r], p.gate_mode, p.lb);
         }
     }
     qq = sum64(qq); kk = sum64(kk); qk = sum64(qk);
@@ -156,16 +156,14 @@ void decode_kernel(Params p) {
     const float rk = rsqrtf(kk + p.l2_eps);
     qk *= rq * rk;
 
-    // ---- 3. one pass: u = S^T (alpha k_hat), p = S^T (alpha q_hat)
+    // ---- 3. one pass: u = S^T (alpha k_hat), p = S^T (alpha q_hat), summed
+    // over rows with the unnormalised q, k and scaled by 1/|k|, 1/|q| after
     float4 u = make_float4(0.f, 0.f, 0.f, 0.f), pq = u;
 #pragma unroll
     for (int m = 0; m < Sh::RPT; ++m) {
-        const int i = dec_row<NT, BLOCKED>(rg, m);
-        const float al = s_alpha[i];
-        const float ak = al * s_act[DK + i] * rk;
-        const float aq = al * s_act[i] * rq;
-        u.x += s[m].x * ak; u.y += s[m].y * ak; u.z += s[m].z * ak; u.w += s[m].w * ak;
-        pq.x += s[m].x * aq; pq.y += s[m].y * aq; pq.z += s[m].z * aq; pq.w += s[m].w * aq;
+        const float4 rw = s_row[dec_row<NT, BLOCKED>(rg, m)];
+        u.x += s[m].x * rw.y; u.y += s[m].y * rw.y; u.z += s[m].z * rw.y; u.w += s[m].w * rw.y;
+        pq.x += s[m].x * rw.x; pq.y += s[m].y * rw.x; pq.z += s[m].z * rw.x; pq.w += s[m].w * rw.x;
     }
     // the two row groups of this wavefront, then the wavefronts
     u.x += __shfl_xor(u.x, 32); u.y += __shfl_xor(u.y, 32);
@@ -181,21 +179,23 @@ void decode_kernel(Params p) {
         u.x += a.x; u.y += a.y; u.z += a.z; u.w += a.w;
         pq.x += c.x; pq.y += c.y; pq.z += c.z; pq.w += c.w;
     }
+    u.x *= rk; u.y *= rk; u.z *= rk; u.w *= rk;
+    pq.x *= rq; pq.y *= rq; pq.z *= rq; pq.w *= rq;
 
-    // ---- 4. delta, readout, in-place update
-    const float4 vv = *reinterpret_cast<const float4 *>(&s_act[2 * DK + 4 * cg]);
-    float4 d, o;
+    // ---- 4. delta, readout, in-place update S <- Diag(alpha) S + k_hat delta^T
+    // (k_hat_i delta = k_i (delta / |k|))
+    const float4 vv = *reinterpret_cast<const float4 *>(&s_v[4 * cg]);
+    float4 d, o, dk;
     d.x = b * (vv.x - u.x); d.y = b * (vv.y - u.y); d.z = b * (vv.z - u.z); d.w = b * (vv.w - u.w);
     o.x = pq.x + qk * d.x; o.y = pq.y + qk * d.y; o.z = pq.z + qk * d.z; o.w = pq.w + qk * d.w;
+    dk.x = d.x * rk; dk.y = d.y * rk; dk.z = d.z * rk; dk.w = d.w * rk;
 #pragma unroll
     for (int m = 0; m < Sh::RPT; ++m) {
-        const int i = dec_row<NT, BLOCKED>(rg, m);
-        const float al = s_alpha[i];
-        const float kh = s_act[DK + i] * rk;
+        const float2 ak = *reinterpret_cast<const float2 *>(&s_row[dec_row<NT, BLOCKED>(rg, m)].z);
         float4 t;
-        t.x = al * s[m].x + kh * d.x; t.y = al * s[m].y + kh * d.y;
-        t.z = al * s[m].z + kh * d.z; t.w = al * s[m].w + kh * d.w;
-        st_state<NT_STORE>(S + i * DV + 4 * cg, t);
+        t.x = ak.x * s[m].x + ak.y * dk.x; t.y = ak.x * s[m].y + ak.y * dk.y;
+        t.z = ak.x * s[m].z + ak.y * dk.z; t.w = ak.x * s[m].w + ak.y * dk.w;
+        st_state<NT_STORE>(rs, t, s_lane, m * ROW_STEP);
     }
 
     // ---- 5. RMSNorm over the 128 outputs (32 lanes x 4), gamma, sigmoid gate
