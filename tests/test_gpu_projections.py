@@ -186,3 +186,17 @@ def test_lowrank_gates_feed_the_step(gpu):
     got = {"y": _np(d["y"]), "o_raw": _np(d["o_raw"]), "state": _np(d["state"]),
            "win": d["conv_win"].cpu().numpy()}
     _gpu.assert_parity(got, ref, label="low-rank gates -> step")
+
+
+@pytest.mark.parametrize("T,H,D", [(4200, 32, 64), (4200, 2, 4352)])
+def test_bf16_many_tiles_every_element(gpu, T, H, D):
+    """More than two grid rounds of 128-token x 256-output tiles, with ragged
+    tiles on the token side and (4352 outputs) on the output side; every
+    element is checked."""
+    p = synth.projection_inputs("many tiles", seed=T + D, T=T, H=H, D=D, r=32, act_dtype="bf16")
+    if H * 128 > 1024:
+        g = _np(_run_gate(p, gpu)).reshape(T, H * 128)
+        _check_bf16(g, gate_projection(p.x, p.w_g), "g")
+    else:
+        out = _np(_run_out(p, gpu))
+        _check_bf16(out, output_projection(p.y, p.w_o), "out")
