@@ -401,7 +401,9 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
     const Range rng = seq_range(p, n);
     if (rng.len <= 0) return;
     const int64_t NC = (rng.len + CC - 1) / CC;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wavefront index is uniform: read it into a scalar register, so that
+    // the record loads' LDS destinations are scalar too
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     const int rh = wave & 1;                               // key rows 64 rh .. 64 rh + 63
     const int col0 = 16 * (grp * SCAN_COLS + (wave >> 1));
@@ -423,12 +425,18 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
     auto rec_rsrc = [&](int64_t c) { return make_rsrc(recs + c * p.H * REC, REC); };
     const int64_t rowsz = (int64_t)p.H * DV;
 
+    // O rows of a chunk through a buffer resource per chunk: the lane offsets
+    // are constant, and rows past the sequence end fall outside the buffer's
+    // range, where stores are dropped
+    uint32_t o_off[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o_off[r] = (uint32_t)(((4 * g4 + r) * rowsz + n16) * 4);
     auto chunk = [&](int64_t c, const uint8_t *R) {
         // partial P, R over this wavefront's key rows: steps m = 2 rh, 2 rh + 1
         // (rows 32 m .. 32 m + 31, tiles 2 (m - 2 rh), + 1); the three parts of
-        // each split product in separate accumulators
+        // each split product accumulate in one chain
         const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 P0 = z4, P1 = z4, P2 = z4, R0 = z4, R1 = z4, R2 = z4;
+        f32x4 Pp = z4, Rp = z4;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
             const int m = 2 * rh + mm;
@@ -442,14 +450,13 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
             const Split2 x2 = split2(st[2 * mm + 1][0], st[2 * mm + 1][1]);
             const Split2 x3 = split2(st[2 * mm + 1][2], st[2 * mm + 1][3]);
             const u32x4 sh = {x0.hi, x1.hi, x2.hi, x3.hi}, sl = {x0.lo, x1.lo, x2.lo, x3.lo};
-            P0 = mfma32(kal, sh, P0);
-            R0 = mfma32(qal, sh, R0);
-            P1 = mfma32(kah, sl, P1);
-            R1 = mfma32(qah, sl, R1);
-            P2 = mfma32(kah, sh, P2);
-            R2 = mfma32(qah, sh, R2);
+            Pp = mfma32(kal, sh, Pp);
+            Rp = mfma32(qal, sh, Rp);
+            Pp = mfma32(kah, sl, Pp);
+            Rp = mfma32(qah, sl, Rp);
+            Pp = mfma32(kah, sh, Pp);
+            Rp = mfma32(qah, sh, Rp);
         }
-        const f32x4 Pp = (P0 + P1) + P2, Rp = (R0 + R1) + R2;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             sX[wave][0][r][lane] = Pp[r];
@@ -484,12 +491,11 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
             const u32x2 mh = *reinterpret_cast<const u32x2 *>(R + R_M + to);
             const u32x2 ml = *reinterpret_cast<const u32x2 *>(R + R_M + 512 + to);
             const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
-            const int nv = (int)(rng.len - c * CC < CC ? rng.len - c * CC : CC);
+            const int64_t nv = rng.len - c * CC < CC ? rng.len - c * CC : CC;
+            const Rsrc ro = make_rsrc(obuf + (rng.lo + c * CC) * rowsz + (int64_t)h * DV + col0,
+                                      (uint32_t)(((nv - 1) * rowsz + DV) * 4));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                if (t < nv) obuf[(rng.lo + c * CC + t) * rowsz + (int64_t)h * DV + col0 + n16] = Ot[r];
-            }
+            for (int r = 0; r < 4; ++r) bst_f32(ro, Ot[r], o_off[r]);
         }
         // S <- Diag(e^{G_C}) S + E^T Delta on this wavefront's rows
 #pragma unroll
