@@ -129,8 +129,9 @@ __device__ __forceinline__ void store_out(const GemmArgs &g, int64_t m, int n, f
     if (n < g.n_split) {
         // n_split is a multiple of 4: the four columns are all on this side
         if constexpr (Opnd<TC>::PARTS == 2) {
-            *reinterpret_cast<float4 *>(static_cast<float *>(g.C0) + m * g.ldc0 + n) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            // nontemporal: the product's output is not read again here, and
+            // streaming it past L2 keeps the operand panels there
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(static_cast<float *>(g.C0) + m * g.ldc0 + n));
         } else {
             uint2 w;
             w.x = pack_bf16x2(v[0], v[1]);
