@@ -46,7 +46,12 @@
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
  * stream) and the call returns at once.  A kernel fault surfaces at the
- * caller's next synchronisation, as for any HIP launch.
+ * caller's next synchronisation, as for any HIP launch.  One path (the
+ * two-pass prefill of long sequences over at most 32 (sequence, head)
+ * pairs) also runs part of its work on a second stream of the library's own,
+ * joined to `stream` by events: that work starts after everything enqueued
+ * on `stream` before the call, and everything enqueued on `stream` after the
+ * call starts after it, exactly as if it ran on `stream`.
  *
  * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED and KDA_ERR_DEVICE mean
  * nothing was enqueued and no buffer was touched, so the caller may run
@@ -56,7 +61,9 @@
  * for a call that enqueues several kernels, the ones before it stay enqueued.
  * The library itself never computes on the CPU.
  *
- * Thread safety: stateless apart from a per-device capability cache; calls
+ * Thread safety: stateless apart from a per-device capability cache and, for
+ * the path above, the per-device second stream and its events (created on
+ * first use, kept until the process ends, enqueued to under a lock); calls
  * on different streams with disjoint buffers may run concurrently.
  */
 #ifndef KDA_H

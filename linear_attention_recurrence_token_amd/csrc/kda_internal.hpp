@@ -60,6 +60,12 @@ hipError_t launch_prefill_split(const Params &p, bool bf16, float *obuf, int col
 // RMSNorm + gate from a pre-norm readout buffer ([T, H, 128] fp32) into y, and
 // the window out (the column-split path's last two kernels)
 hipError_t launch_split_finish(const Params &p, bool bf16, const float *obuf, hipStream_t stream);
+// the two parts of launch_split_finish on their own: RMSNorm + gate of token
+// rows [row_lo, row_lo + rows) of each of nseq sequences seq_rows rows apart
+// (a row is one token of one head), and the window out
+hipError_t launch_split_epilogue(const Params &p, bool bf16, const float *obuf, int64_t row_lo, int64_t rows,
+                                 int64_t seq_rows, int32_t nseq, hipStream_t stream);
+hipError_t launch_split_window(const Params &p, bool bf16, hipStream_t stream);
 
 // Chunkwise prefill in two passes for few (sequence, head) pairs: every
 // chunk's input-only operands in parallel into records (prefill_scan_record_bytes

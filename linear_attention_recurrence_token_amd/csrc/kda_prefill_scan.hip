@@ -23,6 +23,8 @@
 // token 7 keeping every exponential inside e^{+-|lb| C / 2}.
 #include "kda_device.hpp"
 
+#include <mutex>
+
 namespace kda {
 
 namespace {
@@ -91,19 +93,29 @@ constexpr int R2_BYTES = G_BYTES > CW_BYTES ? G_BYTES : CW_BYTES;
 
 template <typename Act>
 __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
-void scan_prep_kernel(Params p, uint8_t *records) {
-    const int64_t slot = blockIdx.x;
+void scan_prep_kernel(Params p, uint8_t *records, int32_t seg_lo) {
     const int h = blockIdx.y;
     const int tid = threadIdx.x;
-    // the sequence owning this slot: the last n with slot_base(n) <= slot
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (slot_base(p, mid) <= slot) lo = mid; else hi = mid - 1;
+    int n;
+    int64_t slot, c;
+    if (seg_lo < 0) {
+        // the whole batch: one workgroup per record slot; the sequence owning
+        // this slot is the last n with slot_base(n) <= slot
+        slot = blockIdx.x;
+        int lo = 0, hi = p.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (slot_base(p, mid) <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+        c = slot - slot_base(p, n);
+    } else {
+        // one segment of chunks: chunk seg_lo + x of sequence z
+        n = blockIdx.z;
+        c = seg_lo + (int64_t)blockIdx.x;
+        slot = slot_base(p, n) + c;
     }
-    const int n = lo;
     const Range rng = seq_range(p, n);
-    const int64_t c = slot - slot_base(p, n);
     const int64_t c0 = c * CC;
     if (c < 0 || c0 >= rng.len) return;
     const int nv = (int)(rng.len - c0 < CC ? rng.len - c0 : CC);
@@ -379,7 +391,10 @@ __device__ __forceinline__ void rec_issue(Rsrc r, uint8_t *dst, int wave, int la
     }
 }
 
-__global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const uint8_t *records, float *obuf) {
+// chunks [c_lo, c_hi) of each pair: the state is read at the start and
+// written at the end, so consecutive ranges chain through it
+__global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const uint8_t *records, float *obuf,
+                                                               int32_t c_lo, int32_t c_hi) {
     // one LDS buffer per record in flight (+1 spare block each), separate
     // arrays so that the compiler's waits track each one alone
     __shared__ __attribute__((aligned(1024))) uint8_t sR0[REC + 1024], sR1[REC + 1024], sR2[REC + 1024],
@@ -400,7 +415,9 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
     }
     const Range rng = seq_range(p, n);
     if (rng.len <= 0) return;
-    const int64_t NC = (rng.len + CC - 1) / CC;
+    const int64_t NCS = (rng.len + CC - 1) / CC;
+    const int64_t NC = NCS < c_hi ? NCS : c_hi;    // one past this launch's last chunk
+    if (c_lo >= NC) return;
     // the wavefront index is uniform: read it into a scalar register, so that
     // the record loads' LDS destinations are scalar too
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -527,11 +544,11 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
         if (c + RING - 1 < NC) rec_issue(rec_rsrc(c + RING - 1), prev, wave, lane);
         chunk(c, cur);
     };
-    rec_issue(rec_rsrc(0), sR0, wave, lane);
-    if (NC > 1) rec_issue(rec_rsrc(1), sR1, wave, lane);
-    if (NC > 2) rec_issue(rec_rsrc(2), sR2, wave, lane);
+    rec_issue(rec_rsrc(c_lo), sR0, wave, lane);
+    if (NC > c_lo + 1) rec_issue(rec_rsrc(c_lo + 1), sR1, wave, lane);
+    if (NC > c_lo + 2) rec_issue(rec_rsrc(c_lo + 2), sR2, wave, lane);
 #pragma unroll 1
-    for (int64_t c = 0; c < NC; c += RING) {
+    for (int64_t c = c_lo; c < NC; c += RING) {
         step(c, sR0, sR3);
         step(c + 1, sR1, sR0);
         step(c + 2, sR2, sR1);
@@ -544,20 +561,143 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
             bst_f32(rs_state, st[j][r], ((4 * g4 + r) * DV + col0 + n16) * 4, (4 * rh + j) * 16 * DV * 4);
 }
 
+// ---- the schedule
+//
+// A pair's state pass keeps one workgroup per CU busy (its LDS), so with at
+// most 32 pairs it fills at most half of the 256 CUs, and the operand pass,
+// which has the whole GPU to itself, would otherwise run first and alone.
+// With enough chunks the chunks are cut into segments: segment s + 1's
+// operand pass runs on a second stream, on the idle CUs, while segment s's
+// state pass runs, and each state-pass launch continues from the state the
+// previous one wrote.  The two streams are ordered by events only.
+constexpr int SEG_MAX = 4;              // segments at most
+constexpr int SEG_CHUNKS = 128;         // chunks per segment aimed at (at least 2 segments from here)
+constexpr int64_t SEG_MAX_PAIRS = 32;   // state-pass workgroups on at most half the CUs
+
+// chunks of the longest sequence when the host knows it (dense batches, or a
+// single sequence), else 0
+int64_t scan_max_chunks(const Params &p) {
+    if (!p.cu_seqlens) return ((int64_t)p.dense_len + CC - 1) / CC;
+    if (p.num_seqs == 1) return (p.total_tokens + CC - 1) / CC;
+    return 0;
+}
+
+int scan_segments(const Params &p) {
+    const int64_t pairs = (int64_t)p.num_seqs * p.H;
+    const int64_t nc = scan_max_chunks(p);
+    if (pairs > SEG_MAX_PAIRS || nc < SEG_CHUNKS) return 1;
+    const int64_t s = nc / SEG_CHUNKS;
+    return (int)(s < 2 ? 2 : (s < SEG_MAX ? s : SEG_MAX));
+}
+
+// the second stream and its events, one set per device, created on first use
+// and kept for the life of the process; a call holds the lock while it
+// enqueues, so that the events it records are the ones its waits refer to
+struct SideStream {
+    bool tried = false, ok = false;
+    hipStream_t s = nullptr;
+    hipEvent_t ev[2 * SEG_MAX] = {};
+};
+constexpr int SIDE_DEVICES = 64;
+std::mutex g_side_mu;
+SideStream g_side[SIDE_DEVICES];
+
+SideStream *side_stream(int dev) {   // with g_side_mu held
+    if (dev < 0 || dev >= SIDE_DEVICES) return nullptr;
+    SideStream &ss = g_side[dev];
+    if (!ss.tried) {
+        ss.tried = true;
+        ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+        for (int i = 0; ss.ok && i < 2 * SEG_MAX; ++i)
+            ss.ok = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming) == hipSuccess;
+        if (!ss.ok) (void)hipGetLastError();
+    }
+    return ss.ok ? &ss : nullptr;
+}
+
 template <typename Act>
-hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream) {
-    const int64_t slots = p.total_tokens / CC + p.num_seqs;
-    hipLaunchKernelGGL((scan_prep_kernel<Act>), dim3((unsigned)slots, (unsigned)p.H), dim3(PREP_THREADS), 0,
-                       stream, p, records);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_prep(const Params &p, uint8_t *records, int64_t c_lo, int64_t c_hi, bool whole,
+                       hipStream_t stream) {
+    if (whole) {
+        const int64_t slots = p.total_tokens / CC + p.num_seqs;
+        hipLaunchKernelGGL((scan_prep_kernel<Act>), dim3((unsigned)slots, (unsigned)p.H), dim3(PREP_THREADS), 0,
+                           stream, p, records, -1);
+    } else {
+        hipLaunchKernelGGL((scan_prep_kernel<Act>), dim3((unsigned)(c_hi - c_lo), (unsigned)p.H, (unsigned)p.num_seqs),
+                           dim3(PREP_THREADS), 0, stream, p, records, (int32_t)c_lo);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_state_pass(const Params &p, const uint8_t *records, float *obuf, int64_t c_lo, int64_t c_hi,
+                             hipStream_t stream) {
     const int64_t pairs = (int64_t)p.num_seqs * p.H;
     const int64_t blocks = (pairs + XCDS - 1) / XCDS * XCDS * SCAN_GROUPS;
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(64 * SCAN_WAVES), 0, stream, p,
-                       (const uint8_t *)records, obuf);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_split_finish(p, bf16, obuf, stream);
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(64 * SCAN_WAVES), 0, stream, p, records, obuf,
+                       (int32_t)c_lo, (int32_t)(c_hi < INT32_MAX ? c_hi : INT32_MAX));
+    return hipGetLastError();
+}
+
+template <typename Act>
+hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream) {
+    int nseg = scan_segments(p);
+    std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+    SideStream *side = nullptr;
+    if (nseg > 1) {
+        int dev = -1;
+        lock.lock();
+        if (hipGetDevice(&dev) == hipSuccess) side = side_stream(dev);
+        if (!side) {
+            nseg = 1;
+            lock.unlock();
+        }
+    }
+    hipError_t e;
+    if (nseg == 1) {
+        e = launch_prep<Act>(p, records, 0, 0, true, stream);
+        if (e == hipSuccess) e = launch_state_pass(p, records, obuf, 0, INT64_MAX, stream);
+        if (e == hipSuccess) e = launch_split_finish(p, bf16, obuf, stream);
+        return e;
+    }
+    const int64_t nc = scan_max_chunks(p);
+    auto bound = [&](int s) { return nc * s / nseg; };
+    // token rows of segment s: tokens [16 bound(s), 16 bound(s + 1)) of every
+    // sequence (all of them dense_len long, or the one sequence)
+    const int64_t len = p.cu_seqlens ? p.total_tokens : p.dense_len;
+    const int32_t nseq = p.cu_seqlens ? 1 : p.num_seqs;
+    auto epilogue = [&](int s, hipStream_t st) {
+        const int64_t t0 = CC * bound(s), t1 = s + 1 < nseg ? CC * bound(s + 1) : len;
+        return launch_split_epilogue(p, bf16, obuf, t0 * p.H, (t1 - t0) * p.H, len * p.H, nseq, st);
+    };
+    hipEvent_t *ev = side->ev;   // [0] start, [s] operands of s, [nseg + s] state pass of s, [2 nseg - 1] epilogues
+    // segment 0's operands on the caller's stream; the others on the side
+    // stream, after it (and so after the caller's earlier work)
+    e = launch_prep<Act>(p, records, 0, bound(1), false, stream);
+    if (e == hipSuccess) e = hipEventRecord(ev[0], stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, ev[0], 0);
+    for (int s = 1; e == hipSuccess && s < nseg; ++s) {
+        e = launch_prep<Act>(p, records, bound(s), bound(s + 1), false, side->s);
+        if (e == hipSuccess) e = hipEventRecord(ev[s], side->s);
+    }
+    // the state passes in order on the caller's stream, each after its operands
+    for (int s = 0; e == hipSuccess && s < nseg; ++s) {
+        if (s > 0) e = hipStreamWaitEvent(stream, ev[s], 0);
+        if (e == hipSuccess)
+            e = launch_state_pass(p, records, obuf, bound(s), s + 1 < nseg ? bound(s + 1) : INT64_MAX, stream);
+        if (e == hipSuccess && s + 1 < nseg) e = hipEventRecord(ev[nseg + s], stream);
+    }
+    // RMSNorm + gate of each finished segment on the side stream while the
+    // later state passes run; the last segment's and the window (which the
+    // first operand pass has read) on the caller's stream, after them
+    for (int s = 0; e == hipSuccess && s + 1 < nseg; ++s) {
+        e = hipStreamWaitEvent(side->s, ev[nseg + s], 0);
+        if (e == hipSuccess) e = epilogue(s, side->s);
+    }
+    if (e == hipSuccess) e = hipEventRecord(ev[2 * nseg - 1], side->s);
+    if (e == hipSuccess) e = epilogue(nseg - 1, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ev[2 * nseg - 1], 0);
+    if (e == hipSuccess) e = launch_split_window(p, bf16, stream);
+    return e;
 }
 
 }  // namespace

@@ -283,16 +283,17 @@ __global__ __launch_bounds__(SP_THREADS) void prefill_split_kernel(Params p, flo
         for (int c = 0; c < C; ++c) S[(8 * rg + m) * DV + col0 + c] = s[m][c];
 }
 
-// RMSNorm over the 128 readouts of one (token, head) row, gamma, sigmoid gate:
-// one wavefront per row
+// RMSNorm over the 128 readouts of one (token, head) row, gamma, sigmoid gate,
+// one wavefront per row, for rows [row_lo, row_lo + rows) after
+// seq_rows * blockIdx.y
 template <typename Act>
-__global__ __launch_bounds__(256) void split_epilogue_kernel(Params p, const float *obuf) {
-    const int64_t rows = p.total_tokens * p.H;
+__global__ __launch_bounds__(256) void split_epilogue_kernel(Params p, const float *obuf, int64_t row_lo,
+                                                             int64_t rows, int64_t seq_rows) {
+    const int64_t base = (int64_t)blockIdx.y * seq_rows + row_lo;
     const int lane = threadIdx.x & 63;
     const float2 gm = *reinterpret_cast<const float2 *>(p.gamma + 2 * lane);
-    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
-         row += (int64_t)gridDim.x * 4) {
-        const int64_t off = row * DV + 2 * lane;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4) {
+        const int64_t off = (base + row) * DV + 2 * lane;
         const float2 o = *reinterpret_cast<const float2 *>(obuf + off);
         const float ss = sum64(o.x * o.x + o.y * o.y);
         const float r = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
@@ -328,6 +329,17 @@ __global__ __launch_bounds__(128) void split_window_kernel(Params p) {
     }
 }
 
+template <typename Act>
+hipError_t launch_epilogue_as(const Params &p, const float *obuf, int64_t row_lo, int64_t rows, int64_t seq_rows,
+                              int32_t nseq, hipStream_t stream) {
+    if (rows <= 0 || nseq <= 0) return hipSuccess;
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL((split_epilogue_kernel<Act>),
+                       dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20)), (unsigned)nseq), dim3(256), 0,
+                       stream, p, obuf, row_lo, rows, seq_rows);
+    return hipGetLastError();
+}
+
 template <typename Act, bool FOLD, int C>
 hipError_t launch_split_as(const Params &p, float *obuf, hipStream_t stream) {
     constexpr int G = DV / (16 * C);
@@ -336,11 +348,7 @@ hipError_t launch_split_as(const Params &p, float *obuf, hipStream_t stream) {
                        dim3(SP_THREADS), 0, stream, p, obuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t rows = p.total_tokens * p.H;
-    const int64_t blocks = (rows + 3) / 4;
-    hipLaunchKernelGGL((split_epilogue_kernel<Act>), dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
-                       dim3(256), 0, stream, p, (const float *)obuf);
-    e = hipGetLastError();
+    e = launch_epilogue_as<Act>(p, obuf, 0, p.total_tokens * p.H, 0, 1, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((split_window_kernel<Act>), dim3((unsigned)units), dim3(128), 0, stream, p);
     return hipGetLastError();
@@ -356,13 +364,7 @@ hipError_t launch_split_cols(const Params &p, float *obuf, int C, hipStream_t st
 }
 
 template <typename Act>
-hipError_t launch_finish_as(const Params &p, const float *obuf, hipStream_t stream) {
-    const int64_t rows = p.total_tokens * p.H;
-    const int64_t blocks = (rows + 3) / 4;
-    hipLaunchKernelGGL((split_epilogue_kernel<Act>), dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
-                       dim3(256), 0, stream, p, obuf);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_window_as(const Params &p, hipStream_t stream) {
     const int64_t units = (int64_t)p.num_seqs * p.H;
     hipLaunchKernelGGL((split_window_kernel<Act>), dim3((unsigned)units), dim3(128), 0, stream, p);
     return hipGetLastError();
@@ -371,7 +373,19 @@ hipError_t launch_finish_as(const Params &p, const float *obuf, hipStream_t stre
 }  // namespace
 
 hipError_t launch_split_finish(const Params &p, bool bf16, const float *obuf, hipStream_t stream) {
-    return bf16 ? launch_finish_as<BF16>(p, obuf, stream) : launch_finish_as<F32>(p, obuf, stream);
+    hipError_t e = launch_split_epilogue(p, bf16, obuf, 0, p.total_tokens * p.H, 0, 1, stream);
+    if (e != hipSuccess) return e;
+    return bf16 ? launch_window_as<BF16>(p, stream) : launch_window_as<F32>(p, stream);
+}
+
+hipError_t launch_split_epilogue(const Params &p, bool bf16, const float *obuf, int64_t row_lo, int64_t rows,
+                                 int64_t seq_rows, int32_t nseq, hipStream_t stream) {
+    return bf16 ? launch_epilogue_as<BF16>(p, obuf, row_lo, rows, seq_rows, nseq, stream)
+                : launch_epilogue_as<F32>(p, obuf, row_lo, rows, seq_rows, nseq, stream);
+}
+
+hipError_t launch_split_window(const Params &p, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_window_as<BF16>(p, stream) : launch_window_as<F32>(p, stream);
 }
 
 int prefill_split_cols(int64_t units) {

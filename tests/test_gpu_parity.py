@@ -268,6 +268,25 @@ def test_repeat_runs_bitwise_and_o_raw_optional(gpu, path):
         np.testing.assert_array_equal(c[k], e[k])
 
 
+@pytest.mark.parametrize("path", ["auto", "scan"])
+@pytest.mark.parametrize("N,H,T,act,dense", [(2, 3, 2100, "bf16", True),    # 132 chunks: 2 segments
+                                             (1, 2, 6200, "f32", False),    # 388 chunks: 3, ragged tail
+                                             (1, 1, 9000, "f32", False)])   # 563 chunks: 4
+def test_scan_segments_long_sequences(gpu, N, H, T, act, dense, path):
+    # few pairs and at least 128 chunks each: the two-pass path cuts the
+    # chunks into segments whose operand passes run on a second stream while
+    # the previous segment's state pass runs; every element against the oracle,
+    # and a second call bit-identical to the first
+    w = synth.make_workload("segments", seed=300 + T, N=N, H=H, lengths=[T] * N, act_dtype=act,
+                            state_std=0.02, win_std=1.0)
+    note("two-pass segments %dx%dx%d %s dense=%s %s" % (N, H, T, act, dense, path))
+    a = _gpu.run_sequence(w, gpu, dense=dense, path=path)
+    _gpu.assert_parity(a, _gpu.oracle_sequence(w), bf16=act == "bf16", label="segments T=%d" % T)
+    b = _gpu.run_sequence(w, gpu, dense=dense, path=path)
+    for k in ("y", "o_raw", "state", "win"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
 def test_empty_calls_are_noops(gpu):
     import torch
     w = synth.make_workload("e", seed=3, N=2, H=2, lengths=[0, 0], state_std=0.02, win_std=1.0)
