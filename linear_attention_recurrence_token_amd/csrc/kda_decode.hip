@@ -48,10 +48,19 @@ __device__ __forceinline__ float4 ld_state(Rsrc r, uint32_t voff, uint32_t soff)
     return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
 }
 
+// The store's whole offset is a per-lane VGPR and its scalar offset the
+// constant 0.  A 16-byte store reads its data registers after it issues, and
+// an instruction that writes one of them right behind it can change what is
+// stored.  With an SGPR scalar offset the compiler does not separate the two
+// (on this chip that lost a few state rows per launch, at random); with a
+// constant scalar offset it inserts the wait state.  The opaque copy keeps the
+// row offset from being folded back into an SGPR.
 template <bool NTMP>
-__device__ __forceinline__ void st_state(Rsrc r, float4 v, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void st_state(Rsrc r, float4 v, uint32_t voff, uint32_t off) {
     const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-    __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, NTMP ? CPOL_NT : 0);
+    uint32_t vo = voff + off;
+    asm volatile("" : "+v"(vo));
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo, 0, NTMP ? CPOL_NT : 0);
 }
 
 // Row owned by row group rg at step m: interleaved (rg + NRG m: one load

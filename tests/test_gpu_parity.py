@@ -323,6 +323,22 @@ def test_full_decode_64x32(gpu):
     _gpu.assert_parity(got, ref, label="decode full")
 
 
+def test_decode_64x32_every_pair_repeated(gpu):
+    # every (sequence, head) pair of the 64x32 decode step against the oracle
+    # over 8 chained steps, then four more runs bit-identical to the first:
+    # 40 launches of 2048 workgroups, enough to catch a state store that loses
+    # data to a register write right behind it (such a store corrupted two
+    # rows of one pair or two in about one launch of three)
+    w = synth.workload(1, scale={"steps": 8})
+    note("decode 64x32, 8 steps, every pair, 5 runs")
+    first = _gpu.run_decode(w, gpu)
+    _gpu.assert_parity(first, _gpu.oracle_decode(w), label="decode 64x32 every pair")
+    for rep in range(4):
+        again = _gpu.run_decode(w, gpu)
+        for k in ("y", "o_raw", "state", "win"):
+            np.testing.assert_array_equal(again[k], first[k])
+
+
 @pytest.mark.parametrize("path", ["auto", "chunk"])
 def test_full_prefill_1x32x8192(gpu, path):
     # auto: the two-pass chunk path (32 pairs of 8192 tokens)

@@ -1,0 +1,92 @@
+"""The compiled kernels against one hazard of the vector-memory pipeline.
+
+A store of more than 64 bits (dwordx3/x4) reads its data registers after it
+issues; an instruction that writes one of those registers immediately behind
+it can change the stored data.  The compiler inserts the wait state for most
+forms but not for a buffer store with an SGPR scalar offset, and on gfx950
+that form lost data (two state rows of a pair in about one decode launch of
+three).  This test compiles every kernel source for gfx950 with the
+library's own flags and checks that no such store is followed directly by a
+vector-ALU (or matrix) instruction writing one of its data registers.
+Host-side only: it needs hipcc, not a GPU.
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+from linear_attention_recurrence_token_amd import _build
+
+STORE = re.compile(r'^(buffer_store_dwordx[34]|global_store_dwordx[34]|flat_store_dwordx[34])\s+(.*)$')
+WRITE = re.compile(r'^(v_\S+)\s+(v\[\d+:\d+\]|v\d+)')
+
+
+def _regs(spec):
+    m = re.match(r'v\[(\d+):(\d+)\]$', spec)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r'v(\d+)$', spec)
+    return {int(m.group(1))} if m else set()
+
+
+def hazards(asm_text):
+    """(function, store, next instruction) for each exposed wide store."""
+    out = []
+    func = None
+    lines = [l.strip() for l in asm_text.splitlines()]
+    code = [(i, l) for i, l in enumerate(lines) if l and not l.startswith((';', '.', '//'))]
+    for k, (i, l) in enumerate(code):
+        if re.match(r'^_Z\S*:', l) or re.match(r'^\w+:$', l) and not l.startswith('.'):
+            if l.startswith('_Z'):
+                func = l.split(':')[0]
+            continue
+        m = STORE.match(l)
+        if not m:
+            continue
+        ops = [o.strip() for o in m.group(2).split(',')]
+        # buffer stores: vdata first; global / flat stores: vaddr, vdata
+        data = ops[0] if m.group(1).startswith('buffer') else ops[1]
+        dregs = _regs(data)
+        if k + 1 >= len(code):
+            continue
+        nxt = code[k + 1][1]
+        w = WRITE.match(nxt)
+        if w and not w.group(1).startswith(('v_cmp', 'v_readfirstlane', 'v_readlane')) and _regs(w.group(2)) & dregs:
+            out.append((func, l, nxt))
+    return out
+
+
+def test_scanner_finds_the_pattern():
+    bad = "_Zk:\n\tbuffer_store_dwordx4 v[2:5], v6, s[4:7], s0 offen nt\n\tv_add_f32_e32 v2, v70, v74\n"
+    good = "_Zk:\n\tbuffer_store_dwordx4 v[2:5], v6, s[4:7], 0 offen nt\n\ts_nop 1\n\tv_add_f32_e32 v2, v70, v74\n"
+    other = "_Zk:\n\tglobal_store_dwordx4 v[2:3], v[6:9], off\n\tv_add_co_u32_e32 v2, vcc, 16, v2\n"
+    assert len(hazards(bad)) == 1
+    assert hazards(good) == [] and hazards(other) == []
+
+
+@pytest.mark.skipif(not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")), reason="needs hipcc")
+def test_no_wide_store_followed_by_a_write_to_its_data():
+    hipcc = _build.hipcc()
+    tmp = tempfile.mkdtemp(prefix="kda_isa_")
+
+    def asm(src):
+        out = os.path.join(tmp, src + ".s")
+        cmd = [hipcc, "--offload-arch=" + _build.ARCH, "-O3", "-std=c++17", "-w",
+               "-I", os.path.join(_build.ROOT, "include")] + _build.DEVICE_FLAGS + \
+              ["--offload-device-only", "-S", "-o", out, os.path.join(_build.CSRC, src)]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+        with open(out) as fh:
+            return src, fh.read()
+
+    try:
+        with ThreadPoolExecutor(max_workers=min(8, len(_build.SOURCES))) as ex:
+            texts = list(ex.map(asm, [s for s in _build.SOURCES if s != "kda_api.hip"]))
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    found = [(src,) + h for src, text in texts for h in hazards(text)]
+    assert not found, "\n".join("%s %s: %s -> %s" % f for f in found[:10])
