@@ -23,6 +23,7 @@ from linear_attention_recurrence_token_amd import _build
 
 STORE = re.compile(r'^(buffer_store_dwordx[34]|global_store_dwordx[34]|flat_store_dwordx[34])\s+(.*)$')
 WRITE = re.compile(r'^(v_\S+)\s+(v\[\d+:\d+\]|v\d+)')
+WAIT_STATES = 2    # what the compiler inserts for this hazard on gfx940-class chips
 
 
 def _regs(spec):
@@ -51,18 +52,26 @@ def hazards(asm_text):
         # buffer stores: vdata first; global / flat stores: vaddr, vdata
         data = ops[0] if m.group(1).startswith('buffer') else ops[1]
         dregs = _regs(data)
-        if k + 1 >= len(code):
-            continue
-        nxt = code[k + 1][1]
-        w = WRITE.match(nxt)
-        if w and not w.group(1).startswith(('v_cmp', 'v_readfirstlane', 'v_readlane')) and _regs(w.group(2)) & dregs:
-            out.append((func, l, nxt))
+        # the instructions within WAIT_STATES wait states of the store (one
+        # per instruction, N + 1 for s_nop N) must not write its data
+        waited = 0
+        for _, nxt in code[k + 1:]:
+            if waited >= WAIT_STATES or nxt.endswith(':') or nxt.startswith(('s_endpgm', 's_branch', 's_cbranch')):
+                break
+            w = WRITE.match(nxt)
+            if w and not w.group(1).startswith(('v_cmp', 'v_readfirstlane', 'v_readlane')) and _regs(w.group(2)) & dregs:
+                out.append((func, l, nxt))
+                break
+            m_nop = re.match(r'^s_nop\s+(\d+)', nxt)
+            waited += int(m_nop.group(1)) + 1 if m_nop else 1
     return out
 
 
 def test_scanner_finds_the_pattern():
     bad = "_Zk:\n\tbuffer_store_dwordx4 v[2:5], v6, s[4:7], s0 offen nt\n\tv_add_f32_e32 v2, v70, v74\n"
     good = "_Zk:\n\tbuffer_store_dwordx4 v[2:5], v6, s[4:7], 0 offen nt\n\ts_nop 1\n\tv_add_f32_e32 v2, v70, v74\n"
+    near = "_Zk:\n\tbuffer_store_dwordx4 v[2:5], v6, s[4:7], s0 offen\n\tv_mov_b32 v9, 0\n\tv_add_f32_e32 v3, v70, v74\n"
+    assert len(hazards(near)) == 1
     other = "_Zk:\n\tglobal_store_dwordx4 v[2:3], v[6:9], off\n\tv_add_co_u32_e32 v2, vcc, 16, v2\n"
     assert len(hazards(bad)) == 1
     assert hazards(good) == [] and hazards(other) == []
