@@ -355,6 +355,38 @@ def test_full_batched_prefill_16x64x2048(gpu):
     _sampled(w, full, [0, 11], [3, 60], bf16=True)
 
 
+def test_full_ragged_prefill_256x32(gpu):
+    # the ragged batch at full size (256 sequences of U[1, 4096] tokens, 32
+    # heads, bf16, fresh and carried states mixed), launched as the bench
+    # launches it (automatic path, longest sequence first); the longest, the
+    # shortest, a fresh and a carried sequence at three heads against the
+    # oracle, sliced on the device
+    import torch
+    w = synth.workload(4)
+    lens = w.lengths
+    fresh = [n for n in range(w.N) if not w.state0[n].any()]
+    carried = [n for n in range(w.N) if w.state0[n].any()]
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), fresh[len(fresh) // 2], carried[len(carried) // 2]})
+    heads = [0, 13, 31]
+    note("full ragged prefill 256x32 bf16 (%d tokens), sequences %s (lengths %s), heads %s"
+         % (w.total_tokens, seqs, [int(lens[n]) for n in seqs], heads))
+    d = synth.to_device(w, gpu)
+    order = torch.as_tensor(np.argsort(-lens, kind="stable").astype(np.int32), device=gpu)
+    kda.kda_sequence(_gpu.cfg_of(w), **_gpu.tensors(d), cu_seqlens=d["cu_seqlens"], seq_order=order,
+                     num_seqs=w.N)
+    torch.cuda.synchronize()
+    rows = torch.as_tensor(np.concatenate([np.arange(w.cu_seqlens[n], w.cu_seqlens[n + 1]) for n in seqs]),
+                           device=gpu)
+    hs, ns = torch.as_tensor(heads, device=gpu), torch.as_tensor(seqs, device=gpu)
+    got = {"y": _gpu._np(d["y"].index_select(0, rows).index_select(1, hs)),
+           "o_raw": _gpu._np(d["o_raw"].index_select(0, rows).index_select(1, hs)),
+           "state": _gpu._np(d["state"].index_select(0, ns).index_select(1, hs)),
+           "win": d["conv_win"].index_select(0, ns).index_select(1, hs).cpu().numpy()}
+    del d
+    torch.cuda.empty_cache()
+    _gpu.assert_parity(got, _gpu.oracle_sequence(synth.subset(w, seqs, heads)), bf16=True, label=w.name)
+
+
 @pytest.mark.parametrize("path", ["auto", "fused", "chunk", "short"])
 def test_full_short_prefill_64x32x13(gpu, path):
     # the short multi-token case: 13 tokens per sequence over a decode-sized
