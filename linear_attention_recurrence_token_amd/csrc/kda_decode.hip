@@ -48,19 +48,12 @@ __device__ __forceinline__ float4 ld_state(Rsrc r, uint32_t voff, uint32_t soff)
     return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
 }
 
-// The store's whole offset is a per-lane VGPR and its scalar offset the
-// constant 0.  A 16-byte store reads its data registers after it issues, and
-// an instruction that writes one of them right behind it can change what is
-// stored.  With an SGPR scalar offset the compiler does not separate the two
-// (on this chip that lost a few state rows per launch, at random); with a
-// constant scalar offset it inserts the wait state.  The opaque copy keeps the
-// row offset from being folded back into an SGPR.
+// (bst_f32x4_at: the whole offset per lane, so that the compiler separates
+// the store from later writes to its data registers; with an SGPR scalar
+// offset it did not, and a few state rows per launch were lost at random)
 template <bool NTMP>
 __device__ __forceinline__ void st_state(Rsrc r, float4 v, uint32_t voff, uint32_t off) {
-    const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-    uint32_t vo = voff + off;
-    asm volatile("" : "+v"(vo));
-    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo, 0, NTMP ? CPOL_NT : 0);
+    bst_f32x4_at<NTMP ? CPOL_NT : 0>(r, v, voff + off);
 }
 
 // Row owned by row group rg at step m: interleaved (rg + NRG m: one load
@@ -415,7 +408,7 @@ void short_seq_kernel(Params p) {
 
     // ---- state and window out
 #pragma unroll
-    for (int m = 0; m < Sh::RPT; ++m) bst_f32x4(r_s, s[m], s_lane, (uint32_t)(m * Sh::NRG * DV * 4));
+    for (int m = 0; m < Sh::RPT; ++m) bst_f32x4_at(r_s, s[m], s_lane + (uint32_t)(m * Sh::NRG * DV * 4));
 #pragma unroll
     for (int j = 0; j < PAST; ++j) {
         W[j * CH + wch] = w0[j];

@@ -163,6 +163,20 @@ __device__ __forceinline__ void bst_f32x4(Rsrc r, float4 v, uint32_t voff, uint3
                      __float_as_uint(v.w)};
     __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, 0);
 }
+// A 16-byte store reads its data registers after it issues; an instruction
+// that writes one of them right behind it can change what is stored.  The
+// compiler puts the needed wait states behind a buffer store whose scalar
+// offset is a constant, but not behind one with an SGPR scalar offset (on
+// gfx950 that form lost stored data).  This store therefore takes its whole
+// offset per lane, through an opaque copy that keeps a constant part from
+// being moved back into an SGPR, and the scalar offset 0.
+template <int CPOL = 0>
+__device__ __forceinline__ void bst_f32x4_at(Rsrc r, float4 v, uint32_t off) {
+    const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                     __float_as_uint(v.w)};
+    asm volatile("" : "+v"(off));
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, CPOL);
+}
 // two consecutive activations (element index i, even) through a buffer
 template <typename Act> struct BufAct;
 // Raw2 / load_raw2 / unpack2 split a load from its conversion, so that a load

@@ -24,6 +24,7 @@ from linear_attention_recurrence_token_amd import _build
 STORE = re.compile(r'^(buffer_store_dwordx[34]|global_store_dwordx[34]|flat_store_dwordx[34])\s+(.*)$')
 WRITE = re.compile(r'^(v_\S+)\s+(v\[\d+:\d+\]|v\d+)')
 WAIT_STATES = 2    # what the compiler inserts for this hazard on gfx940-class chips
+WIDE_SGPR_SOFFSET = re.compile(r'^buffer_store_dwordx[34]\s+\S+,\s*\S+,\s*s\[\d+:\d+\],\s*s\d+\b')
 
 
 def _regs(spec):
@@ -72,6 +73,8 @@ def test_scanner_finds_the_pattern():
     good = "_Zk:\n\tbuffer_store_dwordx4 v[2:5], v6, s[4:7], 0 offen nt\n\ts_nop 1\n\tv_add_f32_e32 v2, v70, v74\n"
     near = "_Zk:\n\tbuffer_store_dwordx4 v[2:5], v6, s[4:7], s0 offen\n\tv_mov_b32 v9, 0\n\tv_add_f32_e32 v3, v70, v74\n"
     assert len(hazards(near)) == 1
+    assert WIDE_SGPR_SOFFSET.match("buffer_store_dwordx4 v[2:5], v86, s[4:7], s0 offen nt")
+    assert not WIDE_SGPR_SOFFSET.match("buffer_store_dwordx4 v[2:5], v86, s[4:7], 0 offen nt")
     other = "_Zk:\n\tglobal_store_dwordx4 v[2:3], v[6:9], off\n\tv_add_co_u32_e32 v2, vcc, 16, v2\n"
     assert len(hazards(bad)) == 1
     assert hazards(good) == [] and hazards(other) == []
@@ -99,3 +102,8 @@ def test_no_wide_store_followed_by_a_write_to_its_data():
         shutil.rmtree(tmp, ignore_errors=True)
     found = [(src,) + h for src, text in texts for h in hazards(text)]
     assert not found, "\n".join("%s %s: %s -> %s" % f for f in found[:10])
+    # and no wide buffer store takes an SGPR scalar offset, the form the
+    # compiler does not guard at all
+    sgpr = [(src, l.strip()) for src, text in texts for l in text.splitlines()
+            if WIDE_SGPR_SOFFSET.match(l.strip())]
+    assert not sgpr, "\n".join("%s: %s" % f for f in sgpr[:10])
