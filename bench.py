@@ -232,8 +232,9 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
     # HBM traffic from the committed rocprofv3 summary of this workload, if it
     # was taken on the current source of the kernel that runs it
     traffic = None
-    if idx == 3 and path == "chunk":
-        traffic = committed_traffic("kda_prefill_chunk.hip", "prefill_16x64x2048")
+    keys = {2: "prefill_1x32x8192", 3: "prefill_16x64x2048", 4: "prefill_ragged_256x32", 5: "prefill_short_64x32x13"}
+    if path in ("chunk", "scan") and idx in keys:
+        traffic = committed_traffic("kda_prefill_%s.hip" % path, keys[idx])
     flops = th * RECUR_FLOPS
     # algorithmic HBM bytes: state in+out and window in+out per pair, and per
     # token.head q, k, v, g, y (activation dtype) with f (fp32) and beta
