@@ -249,7 +249,7 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
         # a few tokens per (sequence, head): the state round trip dominates
         out["roofline"] = {"bound": "hbm", "achieved": hbm_bytes / (ms * 1e-3) / 1e9,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None}
+                           "frac": hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic}
     else:
         out["roofline"] = {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
                            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
