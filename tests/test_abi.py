@@ -119,8 +119,8 @@ def test_aliasing_rejected(lib):
 
 
 def test_beta_needs_only_word_alignment(lib):
-    # passes validation, then stops at the device check (no GPU here) -- or launches nothing
-    # on a GPU machine because the fake pointers never reach a kernel: skip there
+    # passes validation, then stops at the device check when no GPU is present;
+    # with a GPU it would go on to launch on the fake pointers, so it is skipped there
     try:
         import torch
         if torch.cuda.is_available():
