@@ -285,6 +285,11 @@ def test_scan_segments_long_sequences(gpu, N, H, T, act, dense, path):
     b = _gpu.run_sequence(w, gpu, dense=dense, path=path)
     for k in ("y", "o_raw", "state", "win"):
         np.testing.assert_array_equal(a[k], b[k])
+    # without o_raw the readout lives in the workspace after the chunk records,
+    # where the segments' RMSNorm + gate read it
+    c = _gpu.run_sequence(w, gpu, dense=dense, path=path, with_o_raw=False)
+    for k in ("y", "state", "win"):
+        np.testing.assert_array_equal(c[k], a[k])
 
 
 def test_empty_calls_are_noops(gpu):
