@@ -290,6 +290,12 @@ def test_scan_segments_long_sequences(gpu, N, H, T, act, dense, path):
     c = _gpu.run_sequence(w, gpu, dense=dense, path=path, with_o_raw=False)
     for k in ("y", "state", "win"):
         np.testing.assert_array_equal(c[k], a[k])
+    if N > 1:
+        # the state passes take pairs in the scheduling order, the operand
+        # passes in natural order: the result does not depend on the order
+        r = _gpu.run_sequence(w, gpu, dense=dense, path=path, seq_order=list(range(N))[::-1])
+        for k in ("y", "o_raw", "state", "win"):
+            np.testing.assert_array_equal(r[k], a[k])
 
 
 def test_empty_calls_are_noops(gpu):
