@@ -51,7 +51,8 @@
  * pairs) also runs part of its work on a second stream of the library's own,
  * joined to `stream` by events: that work starts after everything enqueued
  * on `stream` before the call, and everything enqueued on `stream` after the
- * call starts after it, exactly as if it ran on `stream`.
+ * call starts after it, exactly as if it ran on `stream`.  `stream` must
+ * belong to the current device (the second stream is that device's).
  *
  * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED and KDA_ERR_DEVICE mean
  * nothing was enqueued and no buffer was touched, so the caller may run
