@@ -191,6 +191,14 @@ void lowrank_products(const kda_config *cfg, const void *x, const float *w_fa_bp
     g2.C0 = f; g2.ldc0 = (int64_t)H * kda::DK; g2.C1 = nullptr; g2.ldc1 = 0; g2.n_split = g2.N;
 }
 
+// From this many token rows the first low-rank product reads its fp32 weights
+// [W_fa; W_bp] as bf16 parts split once per call into the workspace, instead
+// of splitting them again in every K stage of every token tile.
+constexpr int64_t LOWRANK_PRESPLIT_MIN_TOKENS = 512;
+int64_t lowrank_planes_bytes(int32_t H, int32_t rank, int32_t hidden) {
+    return round_up((int64_t)(rank + H) * hidden * 2 * 2, WS_ALIGN);
+}
+
 // one product with the activation type on every side
 kda::ProjGemm act_product(const kda_config *cfg, const void *A, const void *B, int64_t M, int32_t N,
                           int32_t K, void *C) {
@@ -353,8 +361,13 @@ int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int3
         if (rank < 32 || rank > PROJ_MAX_RANK || rank % 32 != 0 || hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
         kda::ProjGemm g1, g2;
         lowrank_products(cfg, nullptr, nullptr, nullptr, hidden, rank, tokens, nullptr, nullptr, nullptr, g1, g2);
+        int64_t planes = 0;
+        if (tokens >= LOWRANK_PRESPLIT_MIN_TOKENS) {
+            g1.b_presplit = true;
+            planes = lowrank_planes_bytes(cfg->num_heads, rank, hidden);
+        }
         const int64_t scratch = std::max(kda::proj_gemm_scratch_bytes(g1), kda::proj_gemm_scratch_bytes(g2));
-        return round_up(tokens * rank * 4, WS_ALIGN) + scratch;
+        return round_up(tokens * rank * 4, WS_ALIGN) + planes + scratch;
     }
     if (which == KDA_PROJ_GATE) {
         if (hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
@@ -399,10 +412,22 @@ kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *
     if (!kda::proj_gemm_shape_ok(g1) || !kda::proj_gemm_shape_ok(g2)) return KDA_ERR_INVALID_ARG;
     st = device_ok();
     if (st != KDA_OK) return st;
-    float *scratch = reinterpret_cast<float *>(static_cast<char *>(workspace) + a_bytes);
-    const int64_t scratch_bytes = workspace_bytes - a_bytes;
+    // the weights' bf16 parts after a, when the workspace holds them
+    const int64_t planes = lowrank_planes_bytes(H, rank, hidden);
+    uint16_t *wparts = nullptr;
+    int64_t used = a_bytes;
+    if (tokens >= LOWRANK_PRESPLIT_MIN_TOKENS && workspace_bytes >= a_bytes + planes) {
+        wparts = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + a_bytes);
+        g1.B = wparts;
+        g1.b_presplit = true;
+        used += planes;
+    }
+    float *scratch = reinterpret_cast<float *>(static_cast<char *>(workspace) + used);
+    const int64_t scratch_bytes = workspace_bytes - used;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = kda::launch_proj_gemm(g1, scratch_bytes > 0 ? scratch : nullptr, scratch_bytes, s);
+    hipError_t e = hipSuccess;
+    if (wparts) e = kda::launch_split_planes(w_fa_bp, wparts, (int64_t)(rank + H) * hidden, s);
+    if (e == hipSuccess) e = kda::launch_proj_gemm(g1, scratch_bytes > 0 ? scratch : nullptr, scratch_bytes, s);
     if (e == hipSuccess) e = kda::launch_proj_gemm(g2, scratch_bytes > 0 ? scratch : nullptr, scratch_bytes, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -86,6 +86,8 @@ struct ProjGemm {
     int64_t M;
     int32_t N, K;
     bool a_bf16, b_bf16, c_bf16;   // supported: all bf16; bf16 A with fp32 B, C; all fp32
+    bool b_presplit = false;       // fp32 B given as bf16 parts: the high parts of the N rows
+                                   // [N, K], then the low parts [N, K] (launch_split_planes)
     void *C0;
     int64_t ldc0;
     float *C1;
@@ -100,5 +102,8 @@ bool proj_gemm_shape_ok(const ProjGemm &g);
 int64_t proj_gemm_scratch_bytes(const ProjGemm &g);
 // scratch may be null or smaller than proj_gemm_scratch_bytes: then K is not split
 hipError_t launch_proj_gemm(const ProjGemm &g, float *scratch, int64_t scratch_bytes, hipStream_t stream);
+// n fp32 values (a multiple of 4) as bf16 parts: out[0, n) the high parts,
+// out[n, 2 n) the remainders (the layout of ProjGemm::b_presplit)
+hipError_t launch_split_planes(const float *w, uint16_t *out, int64_t n, hipStream_t stream);
 
 }  // namespace kda

@@ -29,6 +29,8 @@
 // that a second kernel sums before the epilogue.
 #include "kda_device.hpp"
 
+#include <type_traits>
+
 namespace kda {
 
 namespace {
@@ -57,6 +59,10 @@ constexpr int BKP = BK + 8;      // LDS row length in bf16 elements (80 bytes)
 template <typename T> struct Opnd;
 template <> struct Opnd<F32> { static constexpr int PARTS = 2, ELEM = 4; };
 template <> struct Opnd<BF16> { static constexpr int PARTS = 1, ELEM = 2; };
+// fp32 operand already split into bf16 parts: the high parts of all N rows,
+// then the low parts (ProjGemm::b_presplit); ELEM is the bytes per part
+struct F32P {};
+template <> struct Opnd<F32P> { static constexpr int PARTS = 2, ELEM = 2; };
 
 struct GemmArgs {
     const void *A;               // [M, K] token rows
@@ -84,7 +90,20 @@ struct Tile {
     static constexpr int CHUNKS = R * CPR;
     static constexpr int PER = (CHUNKS + GT - 1) / GT;
     u32x4 v[PER];
+    u32x4 v2[std::is_same<T, F32P>::value ? PER : 1];   // the low parts (F32P)
 
+    // F32P: both parts, from the high and the low plane
+    __device__ __forceinline__ void issue2(Rsrc r, Rsrc r2, int tid, uint32_t row_bytes, uint32_t kbyte) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = tid + GT * j;
+            if (CHUNKS % GT == 0 || c < CHUNKS) {
+                const uint32_t row = c / CPR, col = c % CPR;
+                v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, row * row_bytes + kbyte + col * 16, 0, 0);
+                v2[j] = __builtin_amdgcn_raw_buffer_load_b128(r2, row * row_bytes + kbyte + col * 16, 0, 0);
+            }
+        }
+    }
     __device__ __forceinline__ void issue(Rsrc r, int tid, uint32_t row_bytes, uint32_t kbyte) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -102,7 +121,10 @@ struct Tile {
             const int c = tid + GT * j;
             if (CHUNKS % GT == 0 || c < CHUNKS) {
                 const int row = c / CPR, col = c % CPR;
-                if constexpr (Opnd<T>::PARTS == 2) {
+                if constexpr (std::is_same<T, F32P>::value) {
+                    *reinterpret_cast<u32x4 *>(s + row * BKP + col * 8) = v[j];
+                    *reinterpret_cast<u32x4 *>(s + R * BKP + row * BKP + col * 8) = v2[j];
+                } else if constexpr (Opnd<T>::PARTS == 2) {
                     const f32x4v x = {__uint_as_float(v[j].x), __uint_as_float(v[j].y),
                                       __uint_as_float(v[j].z), __uint_as_float(v[j].w)};
                     const bf16x4v h = __builtin_convertvector(x, bf16x4v);
@@ -188,6 +210,9 @@ __global__ __launch_bounds__(GT) void proj_gemm_kernel(GemmArgs g) {
     const Rsrc ra = make_rsrc(static_cast<const char *>(g.A) + m0 * g.K * EA, (uint32_t)(rows_a * g.K * EA));
     const Rsrc rb = make_rsrc(static_cast<const char *>(g.B) + (int64_t)n0 * g.K * EB,
                               (uint32_t)(rows_b * g.K * EB));
+    // F32P: the low plane follows the high plane's N rows
+    const Rsrc rb2 = make_rsrc(static_cast<const char *>(g.B) + ((int64_t)g.N + n0) * g.K * EB,
+                               (uint32_t)(rows_b * g.K * EB));
     const int k0 = z * g.k_len;
     const int nst = min(g.k_len, g.K - k0) / BK;
 
@@ -200,7 +225,10 @@ __global__ __launch_bounds__(GT) void proj_gemm_kernel(GemmArgs g) {
     Tile<TA, BM> la;
     Tile<TB, BN> lb;
     la.issue(ra, tid, g.K * EA, k0 * EA);
-    lb.issue(rb, tid, g.K * EB, k0 * EB);
+    if constexpr (std::is_same<TB, F32P>::value)
+        lb.issue2(rb, rb2, tid, g.K * EB, k0 * EB);
+    else
+        lb.issue(rb, tid, g.K * EB, k0 * EB);
     la.store(&sA[0][0][0][0], tid);
     lb.store(&sB[0][0][0][0], tid);
     __syncthreads();
@@ -212,7 +240,10 @@ __global__ __launch_bounds__(GT) void proj_gemm_kernel(GemmArgs g) {
         const bool more = s + 1 < nst;
         if (more) {
             la.issue(ra, tid, g.K * EA, (k0 + (s + 1) * BK) * EA);
-            lb.issue(rb, tid, g.K * EB, (k0 + (s + 1) * BK) * EB);
+            if constexpr (std::is_same<TB, F32P>::value)
+                lb.issue2(rb, rb2, tid, g.K * EB, (k0 + (s + 1) * BK) * EB);
+            else
+                lb.issue(rb, tid, g.K * EB, (k0 + (s + 1) * BK) * EB);
         }
         u32x4 fw[TN][PB], fx[TM][PA];
 #pragma unroll
@@ -462,6 +493,8 @@ template <typename TA, typename TB> struct Shapes;
 template <> struct Shapes<BF16, BF16> { static constexpr int L_BM = PROJ_DMA_BM, L_BN = PROJ_DMA_BN; };
 template <> struct Shapes<BF16, F32> { static constexpr int L_BM = 128, L_BN = 64; };
 template <> struct Shapes<F32, F32> { static constexpr int L_BM = 128, L_BN = 128; };
+template <> struct Shapes<BF16, F32P> : Shapes<BF16, F32> {};
+template <> struct Shapes<F32, F32P> : Shapes<F32, F32> {};
 constexpr int S_BM = 64, S_BN = 64;
 constexpr int64_t LARGE_MIN_M = 512;
 #ifndef PROJ_SPLIT_MIN_K
@@ -502,6 +535,8 @@ Plan plan_typed(const ProjGemm &pg, int64_t scratch_bytes) {
 }
 
 Plan plan_for(const ProjGemm &pg, int64_t scratch_bytes) {
+    if (pg.b_presplit) return pg.a_bf16 ? plan_typed<BF16, F32P>(pg, scratch_bytes)
+                                        : plan_typed<F32, F32P>(pg, scratch_bytes);
     if (pg.a_bf16 && pg.b_bf16) return plan_typed<BF16, BF16>(pg, scratch_bytes);
     if (pg.a_bf16) return plan_typed<BF16, F32>(pg, scratch_bytes);
     return plan_typed<F32, F32>(pg, scratch_bytes);
@@ -527,7 +562,31 @@ hipError_t launch_typed(const GemmArgs &a, bool large, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// fp32 values into two bf16 planes: hi = bf16(x) (RNE) and lo = bf16(x - hi),
+// four values per thread
+__global__ __launch_bounds__(256) void split_planes_kernel(const float *w, uint16_t *hi, uint16_t *lo, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 x = reinterpret_cast<const float4 *>(w)[i];
+    const uint32_t h01 = pack_bf16x2(x.x, x.y), h23 = pack_bf16x2(x.z, x.w);
+    uint2 h, l;
+    h.x = h01;
+    h.y = h23;
+    l.x = pack_bf16x2(x.x - __uint_as_float(h01 << 16), x.y - __uint_as_float(h01 & 0xffff0000u));
+    l.y = pack_bf16x2(x.z - __uint_as_float(h23 << 16), x.w - __uint_as_float(h23 & 0xffff0000u));
+    reinterpret_cast<uint2 *>(hi)[i] = h;
+    reinterpret_cast<uint2 *>(lo)[i] = l;
+}
+
 }  // namespace
+
+hipError_t launch_split_planes(const float *w, uint16_t *out, int64_t n, hipStream_t stream) {
+    const int64_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, w, out,
+                       out + n, n4);
+    return hipGetLastError();
+}
 
 int64_t proj_gemm_scratch_bytes(const ProjGemm &pg) {
     const Plan p = plan_for(pg, INT64_MAX);
@@ -567,6 +626,11 @@ hipError_t launch_proj_gemm(const ProjGemm &pg, float *scratch, int64_t scratch_
     a.n_split = pg.n_split;
     a.np = (pg.N + 3) / 4 * 4;
     a.partial = p.splits > 1 ? scratch : nullptr;
+    if (pg.b_presplit) {
+        if (pg.b_bf16 || pg.c_bf16) return hipErrorInvalidValue;
+        return pg.a_bf16 ? launch_typed<BF16, F32P, F32>(a, p.large, stream)
+                         : launch_typed<F32, F32P, F32>(a, p.large, stream);
+    }
     if (pg.a_bf16 && pg.b_bf16 && pg.c_bf16) return launch_typed<BF16, BF16, BF16>(a, p.large, stream);
     if (pg.a_bf16 && !pg.b_bf16 && !pg.c_bf16) return launch_typed<BF16, F32, F32>(a, p.large, stream);
     if (!pg.a_bf16 && !pg.b_bf16 && !pg.c_bf16) return launch_typed<F32, F32, F32>(a, p.large, stream);

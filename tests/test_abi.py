@@ -310,8 +310,9 @@ def test_projection_workspace_size(lib):
         ctypes.byref(cfg or _cfg()), which, hidden, rank, tokens)
     c32 = _cfg(num_heads=32)
     # low-rank gates: the rank-r factor (rounded to 256 bytes), plus split-K
-    # scratch for few token rows
-    assert size(kda.KDA_PROJ_LOWRANK_GATES, 4096, 128, 32768, c32) == 32768 * 128 * 4
+    # scratch for few token rows; from 512 token rows also the bf16 parts of
+    # the (r + H) x hidden weights of the first product
+    assert size(kda.KDA_PROJ_LOWRANK_GATES, 4096, 128, 32768, c32) == 32768 * 128 * 4 + (128 + 32) * 4096 * 4
     assert size(kda.KDA_PROJ_LOWRANK_GATES, 4096, 128, 3, c32) > 2048
     assert size(kda.KDA_PROJ_LOWRANK_GATES, 64, 32, 3) == 512
     # gate / output: scratch only when the sum is split (few token rows, long sums)
