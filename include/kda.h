@@ -259,8 +259,11 @@ int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int3
  * both); w_fb [H * 128, rank] fp32; f [tokens, H, 128] fp32 out and beta
  * [tokens, H] fp32 out: the f and beta inputs of kda_token_step and
  * kda_sequence.  workspace: required, at least tokens * rank * 4 bytes
- * rounded up to 256 (it holds a).  hidden: a positive multiple of 32;
- * rank: a multiple of 32 in [32, 1024].
+ * rounded up to 256 (it holds a).  From 512 token rows, with the bytes
+ * kda_projection_workspace_size reports, it also holds w_fa_bp split into
+ * bf16 parts once per call (the product then reads those instead of
+ * splitting the fp32 weights itself; the results are the same).  hidden: a
+ * positive multiple of 32; rank: a multiple of 32 in [32, 1024].
  */
 kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *w_fa_bp,
                              const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
