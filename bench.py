@@ -4,13 +4,20 @@
 Headline (one JSON line on stdout): decode over 64 sequences x 32 heads,
 dk = dv = 128, fp32 state, one kda_token_step launch per token, K steps back
 to back with every step's inputs already resident in HBM.  value = total
-token.heads per second.  Alongside: the decode kernel's HBM roofline, the CPU
-oracle timed on this host on a bounded sample (its only use here; parity is
-checked by the GPU tests at these same sizes), a disclosed over-cache decode
-run, the prefill workloads (kda_sequence): the long ones with their ALU
-roofline, the short multi-token one (64 x 32 x 13 tokens) with its HBM
-roofline; and the projections on either side of the step (low-rank decay and
-beta, output gate, output) for the decode and the batched-prefill token rows.
+token.heads per second; roofline.frac = state bytes (64 KiB read + 64 KiB
+written per pair and step) per second over the 8 TB/s HBM peak, frac_total
+counting every byte of the launch.
+
+Alongside: the CPU leg (the only part of this file that touches the oracle):
+the single-precision oracle timed on this host over the same decode workload
+(cpu_baseline), and the fp64 oracle checking a sample of every timed GPU run
+(parity: two sequences x all heads of the decode run, every step's y and the
+final state and window; sampled pairs of every prefill run).  A run whose
+sample misses the tolerance prints value null.  Then a disclosed over-cache
+decode run, the prefill workloads (kda_sequence; the chunk paths against the
+bf16 matrix-core peak with the flops they issue, the short multi-token one
+against HBM), the non-default gate forms, and the projections on either side
+of the step (low-rank decay and beta, output gate, output).
 
   python bench.py [--gpus 1] [--steps 1000] [--warmup 10]
                   [--prefill default|all|none] [--no-cpu-baseline] [--no-overcache]
@@ -30,43 +37,96 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA tokens·heads/sec (decode + prefill); achieved HBM GB/s vs peak"
 UNIT = "token·heads/s"
 HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E, published
-FP32_VECTOR_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published (packed FP32)
+MFMA_BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix cores, published
+MFMA_FP32_PEAK_TFLOPS = 157.3         # MI355X dense fp32 matrix cores, published
+# fp32 vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz = 78.6
+# TFLOP/s without packed FP32, which every kernel here is built without (the
+# published 157.3 counts the packed two-wide FMA)
+FP32_VALU_UNPACKED_TFLOPS = 78.6
 DK = DV = 128
 STATE_BYTES = DK * DV * 4 * 2         # state read + write per (sequence, head) per decode token
 # per decode token.head: q, k, v (3 x 512) + window in/out (2 x 3 x 384 x 4) + f 512 + beta 4 + g 512 + y 512
 DECODE_OTHER_BYTES = 3 * 512 + 2 * 3 * 384 * 4 + 512 + 4 + 512 + 512
 RECUR_FLOPS = 7 * DK * DV             # u, p dot products (2 FMAs), decay multiply, rank-1 FMA
+FP32_TOL, BF16_TOL = 1e-4, 2e-2
+
+# Matrix-core flops the chunkwise kernels issue per 16-token chunk of one
+# (sequence, head) pair, every split product counted as its three bf16
+# products (16x16x32 step: 16384 flops, 16x16x16 step: 8192):
+#   one-pass kernel, 8 wavefronts: P and R 24 x 16x16x32, Delta, O 2 x 3 and the
+#   state update 8 x 3 16x16x16 steps each -> 8 x (24 x 16384 + 30 x 8192);
+#   two-pass state pass, 16 wavefronts (two row halves of 8 column blocks): P, R
+#   12 x 16x16x32, Delta 3 and the update 4 x 3 16x16x16 each, O 3 x 16x16x16
+#   on the 8 lower halves.
+# (The one-pass kernel also issues L and M on fp32 MFMA: 8 x 8 16x16x4 steps
+# = 131072 flops per chunk, not counted.)
+CHUNK_MFMA_FLOPS = {"chunk": 8 * (24 * 16384 + 30 * 8192),
+                    "scan": 16 * (12 * 16384 + 15 * 8192) + 8 * 3 * 8192}
+CHUNK = 16
+
+# source files each measured path compiles from, besides the ones every path
+# shares; a committed traffic summary counts only if it was taken on exactly
+# these sources and build flags
+CSRC = os.path.join(ROOT, "linear_attention_recurrence_token_amd", "csrc")
+COMMON_SOURCES = ["kda_api.hip", "kda_device.hpp", "kda_internal.hpp", "../../include/kda.h"]
+PATH_SOURCES = {"decode": ["kda_decode.hip"], "short": ["kda_decode.hip"],
+                "chunk": ["kda_prefill_chunk.hip"], "scan": ["kda_prefill_scan.hip", "kda_prefill_split.hip"],
+                "split": ["kda_prefill_split.hip"], "fused": ["kda_prefill.hip", "kda_prefill_split.hip"],
+                "proj": ["kda_proj.hip"]}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def file_sha(path):
+def source_key(path):
+    """sha256 (16 hex digits) over the sources `path`'s kernels compile from
+    and the device build flags."""
+    from linear_attention_recurrence_token_amd import _build
     h = hashlib.sha256()
-    with open(path, "rb") as fh:
-        h.update(fh.read())
+    for name in sorted(PATH_SOURCES[path]) + COMMON_SOURCES:
+        h.update(os.path.basename(name).encode() + b"\0")
+        with open(os.path.normpath(os.path.join(CSRC, name)), "rb") as fh:
+            h.update(fh.read())
+    h.update((" ".join(["--offload-arch=" + _build.ARCH] + _build.DEVICE_FLAGS)).encode())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel_file, workload_key):
-    """HBM bytes per dispatch from the committed rocprofv3 PMC summary, if it was
-    taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload_key)
-    if not os.path.exists(path):
+def committed_traffic(path, workload_key):
+    """HBM bytes per dispatch (or per call) from the committed rocprofv3 PMC
+    summary profiles/traffic_<workload_key>.txt, if it was taken on the current
+    sources and flags of `path` (else None)."""
+    fn = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload_key)
+    if not os.path.exists(fn):
         return None
     vals = {}
-    for line in open(path):
-        if ":" in line:
+    for line in open(fn):
+        if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "linear_attention_recurrence_token_amd", "csrc", kernel_file)
-    if vals.get("kernel_source_sha256_16") != file_sha(src):
+    if vals.get("source_key_sha256_16") != source_key(path):
         return None
     try:
         return float(vals["hbm_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
+
+
+def committed_sq_busy(workload_key, kernel):
+    """VALU and MFMA busy fractions of `kernel` from the committed SQ counter
+    summary profiles/sq_counters_<workload_key>.txt (its 'busy:' lines)."""
+    fn = os.path.join(ROOT, "profiles", "sq_counters_%s.txt" % workload_key)
+    if not os.path.exists(fn):
+        return None
+    for line in open(fn):
+        if line.startswith("busy:") and kernel in line:
+            parts = dict(kv.split("=") for kv in line.split()[2:] if "=" in kv)
+            try:
+                return {"valu_busy": float(parts["valu"]), "mfma_busy": float(parts["mfma"]),
+                        "source": "profiles/sq_counters_%s.txt" % workload_key}
+            except (KeyError, ValueError):
+                return None
+    return None
 
 
 def rocm_smi_snapshot():
@@ -83,6 +143,20 @@ def rocm_smi_snapshot():
         return keep
     except Exception as e:  # the snapshot is informational only
         return {"error": str(e)[:80]}
+
+
+def host_cpu():
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info[k.strip()] = v.strip()
+    except Exception:
+        pass
+    return {"model": info.get("Model name"), "threads_per_core": info.get("Thread(s) per core"),
+            "cpus_online": info.get("CPU(s)")}
 
 
 class TokenStepRunner:
@@ -116,7 +190,11 @@ class TokenStepRunner:
             raise RuntimeError("kda_token_step returned %d" % st)
 
 
-def bench_decode(torch, kda, synth, dev, N, H, steps, warmup):
+def bench_decode(torch, kda, synth, dev, N, H, steps, warmup, check_seqs=()):
+    """K = steps timed kda_token_step launches from the initial state, after
+    `warmup` untimed ones (the state and window are restored in between).
+    Returns the timing and, for check_seqs, every step's y rows and the final
+    state and window of those sequences (host arrays) for the parity check."""
     w = synth.workload(1, scale={"N": N, "H": H, "steps": steps})
     d = synth.to_device(w, dev, with_o_raw=False)
     state0, win0 = d["state"].clone(), d["conv_win"].clone()
@@ -138,57 +216,123 @@ def bench_decode(torch, kda, synth, dev, N, H, steps, warmup):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1)
     res = {"w": w, "ms_total": ms, "wall_s": wall}
+    if check_seqs:
+        ns = torch.as_tensor(list(check_seqs), device=dev)
+        y = d["y"].view(steps, N, H, DV).index_select(1, ns).transpose(0, 1).contiguous()
+        res["got"] = {"y": y.view(-1, H, DV).double().cpu().numpy(),
+                      "state": d["state"].index_select(0, ns).double().cpu().numpy(),
+                      "win": d["conv_win"].index_select(0, ns).cpu().numpy()}
+        res["check_seqs"] = list(check_seqs)
     del d, state0, win0
     torch.cuda.empty_cache()
     return res
 
 
-def decode_as_prefill(synth, w, steps=None):
-    import dataclasses
+# ---------------------------------------------------------------- the CPU leg
+# (the only code here that touches oracle/: the baseline timing and the parity
+# checks of the timed GPU runs)
+
+def cpu_baseline_decode(w, target_s):
+    """The single-precision oracle, as it stands, on this host: the decode
+    workload's steps in order from its initial state, one call per step (every
+    sequence's token, state and window updated in place), as many steps as fit
+    in about target_s (all of them when they fit)."""
     import numpy as np
-    steps = w.decode_steps if steps is None else steps
-    T = steps * w.N
-    ww = dataclasses.replace(w, decode_steps=steps, q=w.q[:T], k=w.k[:T], v=w.v[:T], f=w.f[:T],
-                             beta=w.beta[:T], g=w.g[:T])
-    re = {k: synth.decode_rows_as_sequences(ww, getattr(ww, k)) for k in ("q", "k", "v", "f", "beta", "g")}
-    cu = np.arange(w.N + 1, dtype=np.int64) * steps
-    return dataclasses.replace(ww, decode_steps=0, cu_seqlens=cu, **re)
-
-
-def cpu_baseline_decode(synth, w, target_s):
-    """The oracle as it stands, on this host, over all (sequence, head) pairs of
-    the decode workload for as many of its steps as fit in about target_s."""
     import oracle
+    N, H = w.N, w.H
+    S = w.state0.copy()
+    W = w.win0.copy()
+    y = np.empty((N, H, DV), np.float32)
+    cu = np.arange(N + 1, dtype=np.int64)
 
-    def run(steps):
-        sw = decode_as_prefill(synth, w, steps)
-        t = time.perf_counter()
-        oracle.kda_reference(sw.q, sw.k, sw.v, sw.f, sw.beta, sw.g, sw.conv_w, sw.A_log,
-                             sw.dt_bias, sw.gamma, sw.state0, sw.win0, sw.cu_seqlens,
-                             want_o_raw=False)
-        return time.perf_counter() - t
-    t1 = run(2) / 2.0
-    steps = int(max(1, min(w.decode_steps, target_s / max(t1, 1e-6))))
-    wall = run(steps)
-    passes = 1
-    # when the workload's steps fit in well under the target, run the same
-    # steps again (from the same initial state) until about target_s of oracle
-    # work is timed
-    while wall < 0.8 * target_s:
-        wall += run(steps)
-        passes += 1
-    th = w.N * w.H * steps * passes
-    return {"value": th / wall, "unit": UNIT, "cores": oracle.omp_threads(), "kind": "oracle",
-            "sample": "all %d x %d (sequence, head) pairs, first %d decode steps x %d pass(es), fp64 oracle, %.1f s"
-                      % (w.N, w.H, steps, passes, wall)}
+    def step(s):
+        sl = slice(s * N, (s + 1) * N)
+        oracle.kda_reference_f32_inplace(w.q[sl], w.k[sl], w.v[sl], w.f[sl], w.beta[sl], w.g[sl], w.conv_w,
+                                         w.A_log, w.dt_bias, w.gamma, S, W, y, cu)
+    # (no OMP_PROC_BIND: binding would pin this process's main thread to one
+    # CPU for the rest of the run, the input generation of later workloads
+    # included)
+    threads = oracle.omp_threads()
+    step(0)                                   # loads the library and starts its threads
+    S[...] = w.state0
+    W[...] = w.win0
+    t = time.perf_counter()
+    done = 0
+    while done < w.decode_steps:
+        step(done)
+        done += 1
+        if time.perf_counter() - t > target_s:
+            break
+    wall = time.perf_counter() - t
+    cpu = host_cpu()
+    return {"value": N * H * done / wall, "unit": UNIT, "cores": min(threads, N * H), "kind": "oracle",
+            "sample": "decode %d x %d, the first %d of %d steps from the initial state (%s), single-precision "
+                      "oracle (kda_oracle_run_f32, one call per step, OpenMP over the %d (sequence, head) "
+                      "pairs), %.1f s" % (N, H, done, w.decode_steps,
+                                          "all of them" if done == w.decode_steps else "bounded by time",
+                                          N * H, wall),
+            "host_cpu": cpu["model"], "threads_per_core": cpu["threads_per_core"], "omp_threads": threads}
 
 
-def bench_prefill(torch, kda, synth, dev, idx, runs):
+def parity_errors(got, ref, bf16):
+    """max|delta| / max|ref| per output (y at the bf16 bound for bf16 runs,
+    the state always at the fp32 bound) and the window bit-exact."""
     import numpy as np
-    w = synth.workload(idx)
+    out = {"pass": True}
+    for k in ("y", "state"):
+        if k not in got:
+            continue
+        scale = float(np.max(np.abs(ref[k]))) if ref[k].size else 0.0
+        e = float(np.max(np.abs(got[k] - ref[k]))) / max(scale, 1e-30) if ref[k].size else 0.0
+        tol = BF16_TOL if (bf16 and k == "y") else FP32_TOL
+        out[k + "_rel_err"] = e
+        out[k + "_tol"] = tol
+        out["pass"] = out["pass"] and e <= tol
+    same = bool(np.array_equal(got["win"], ref["win"].astype(np.float32)))
+    out["window_bit_exact"] = same
+    out["pass"] = out["pass"] and same
+    return out
+
+
+def decode_parity(synth, w, got, seqs):
+    import oracle
+    sub = synth.decode_subset(w, seqs)
+    ref = oracle.kda_reference(sub.q, sub.k, sub.v, sub.f, sub.beta, sub.g, sub.conv_w, sub.A_log,
+                               sub.dt_bias, sub.gamma, sub.state0, sub.win0, sub.cu_seqlens, want_o_raw=False)
+    r = parity_errors(got, ref, bf16=False)
+    r["sample"] = "sequences %s x all %d heads, every one of the %d timed steps' y, final state and window, " \
+                  "fp64 oracle" % (seqs, w.H, w.decode_steps)
+    return r
+
+
+def prefill_parity(synth, w, got, seqs, heads):
+    import oracle
+    sub = synth.subset(w, seqs, heads)
+    ref = oracle.kda_reference(sub.q, sub.k, sub.v, sub.f, sub.beta, sub.g, sub.conv_w, sub.A_log,
+                               sub.dt_bias, sub.gamma, sub.state0, sub.win0, sub.cu_seqlens,
+                               gate_mode=sub.gate_mode, lower_bound=sub.lower_bound, want_o_raw=False)
+    r = parity_errors(got, ref, bf16=w.act_dtype == "bf16")
+    r["sample"] = "sequences %s x heads %s of the last timed call, fp64 oracle" % (seqs, heads)
+    return r
+
+
+# ---------------------------------------------------------------- prefill
+
+def prefill_samples(w):
+    """(sequences, heads) each prefill run is checked on."""
+    import numpy as np
+    lens = w.lengths
+    seqs = sorted({0, w.N - 1, int(np.argmax(lens)), int(np.argmin(lens))})
+    heads = sorted({0, w.H - 1})
+    return seqs[:4], heads
+
+
+def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=True):
+    import numpy as np
     d = synth.to_device(w, dev, with_o_raw=False)
     state0, win0 = d["state"].clone(), d["conv_win"].clone()
-    cfg = kda.KdaConfig(num_heads=w.H, act_dtype=kda.KDA_BF16 if w.act_dtype == "bf16" else kda.KDA_F32)
+    cfg = kda.KdaConfig(num_heads=w.H, act_dtype=kda.KDA_BF16 if w.act_dtype == "bf16" else kda.KDA_F32,
+                        gate_mode=w.gate_mode, gate_lower_bound=w.lower_bound)
     stream = torch.cuda.current_stream()
     L = kda.lib()
     ccfg = cfg.to_c()
@@ -229,40 +373,56 @@ def bench_prefill(torch, kda, synth, dev, idx, runs):
     scan = chunk and w.N * w.H <= 64 and w.total_tokens >= 128 * w.N and ws_bytes > 0
     path = ("short" if short else ("scan" if scan else ("chunk" if chunk else
                                                         ("split" if ws_bytes > 0 else "fused"))))
-    # HBM traffic from the committed rocprofv3 summary of this workload, if it
-    # was taken on the current source of the kernel that runs it
-    traffic = None
-    keys = {2: "prefill_1x32x8192", 3: "prefill_16x64x2048", 4: "prefill_ragged_256x32", 5: "prefill_short_64x32x13"}
-    if path in ("chunk", "scan") and idx in keys:
-        traffic = committed_traffic("kda_prefill_%s.hip" % path, keys[idx])
-    flops = th * RECUR_FLOPS
+    traffic = committed_traffic(path, traffic_key) if traffic_key else None
     # algorithmic HBM bytes: state in+out and window in+out per pair, and per
     # token.head q, k, v, g, y (activation dtype) with f (fp32) and beta
     act_bytes = 2 if w.act_dtype == "bf16" else 4
     per_token = 5 * 128 * act_bytes + 512 + 4
     hbm_bytes = w.N * w.H * (2 * DK * DV * 4 + 2 * 3 * 384 * 4) + th * per_token
+    recur_tf = th * RECUR_FLOPS / (ms * 1e-3) / 1e12
     out = {"workload": w.name, "path": path, "token_heads": th, "ms": ms, "runs": runs,
            "value": th / (ms * 1e-3), "unit": UNIT,
            "ns_per_token_per_chain": ms * 1e6 / int(lens.max()),
-           "hbm_GBps_algorithmic": hbm_bytes / (ms * 1e-3) / 1e9}
-    if idx == 5:
+           "hbm_GBps_algorithmic": hbm_bytes / (ms * 1e-3) / 1e9,
+           "recurrent_form": {"flops_per_token_head": RECUR_FLOPS, "achieved_TFLOPs": recur_tf,
+                              "frac_of_fp32_valu_unpacked": recur_tf / FP32_VALU_UNPACKED_TFLOPS}}
+    if path in ("chunk", "scan") and not short and int(lens.max()) >= 2 * CHUNK:
+        chunks = int(sum((int(n) + CHUNK - 1) // CHUNK for n in lens)) * w.H
+        fl = chunks * CHUNK_MFMA_FLOPS[path]
+        tf = fl / (ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                           "flops": "bf16 matrix-core flops issued: %d chunks of 16 tokens x %d per chunk "
+                                    "(every split product as three bf16 products)" % (chunks, CHUNK_MFMA_FLOPS[path])}
+    elif path in ("fused", "split") and int(lens.max()) >= 2 * CHUNK:
+        # the recurrent kernels: 7 dk dv flops per token.head on the vector ALU
+        out["roofline"] = {"bound": "alu", "achieved": recur_tf, "peak": FP32_VALU_UNPACKED_TFLOPS,
+                           "unit": "TFLOP/s", "frac": recur_tf / FP32_VALU_UNPACKED_TFLOPS, "traffic": traffic,
+                           "flops": "7 dk dv per token.head (recurrent form) against the unpacked fp32 vector peak"}
+    else:
         # a few tokens per (sequence, head): the state round trip dominates
         out["roofline"] = {"bound": "hbm", "achieved": hbm_bytes / (ms * 1e-3) / 1e9,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic}
-    else:
-        out["roofline"] = {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
-                           "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-                           "traffic": traffic}
+    if traffic_key:
+        busy = committed_sq_busy(traffic_key, {"chunk": "prefill_chunk_kernel", "scan": "scan_kernel"}.get(path, path))
+        if busy:
+            out["roofline"]["sq_busy"] = busy
+    if want_check:
+        seqs, heads = prefill_samples(w)
+        ns, hs = torch.as_tensor(seqs, device=dev), torch.as_tensor(heads, device=dev)
+        rows = torch.as_tensor(np.concatenate([np.arange(w.cu_seqlens[n], w.cu_seqlens[n + 1]) for n in seqs]),
+                               device=dev, dtype=torch.int64)
+        out["_check"] = (seqs, heads, {
+            "y": d["y"].index_select(0, rows).index_select(1, hs).double().cpu().numpy(),
+            "state": d["state"].index_select(0, ns).index_select(1, hs).double().cpu().numpy(),
+            "win": d["conv_win"].index_select(0, ns).index_select(1, hs).cpu().numpy()})
     del d, state0, win0
     torch.cuda.empty_cache()
     return out
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix cores, published
-MFMA_FP32_PEAK_TFLOPS = 157.3         # MI355X dense fp32 matrix cores, published
-
+# ---------------------------------------------------------------- projections
 
 def bench_projections(torch, kda, synth, dev, idx, runs, only=None):
     """The matrix products on either side of the step for the token rows of
@@ -343,7 +503,7 @@ def bench_projections(torch, kda, synth, dev, idx, runs, only=None):
             "ms": ms, "tflops_fp32_equiv": fl / (ms * 1e-3) / 1e12, "bytes_per_call": by,
             "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": committed_traffic("kda_proj.hip", "proj_lowrank_" + key)}}
+                         "traffic": committed_traffic("proj", "proj_lowrank_" + key)}}
     for name, fn, K, N in (
             ("gate_projection", c_call(L.kda_gate_projection, x.data_ptr(), wg.data_ptr(), D, T, g.data_ptr(),
                                        *wsa(kda.KDA_PROJ_GATE)), D, HD),
@@ -356,19 +516,23 @@ def bench_projections(torch, kda, synth, dev, idx, runs, only=None):
         by = (T * K + N * K + T * N) * eb
         tf = fl / (ms * 1e-3) / 1e12
         gbs = by / (ms * 1e-3) / 1e9
+        traffic = committed_traffic("proj", "proj_%s_%s" % (name.split("_")[0], key))
         # the bound from the arithmetic intensity against the machine balance
-        # of the data type's matrix-core peak (fp32 problems run as three
-        # bf16 products per product, reported against the fp32 peak)
-        peak = MFMA_BF16_PEAK_TFLOPS if bf else MFMA_FP32_PEAK_TFLOPS
-        traffic = committed_traffic("kda_proj.hip", "proj_%s_%s" % (name.split("_")[0], key))
-        if fl / by < peak * 1e3 / HBM_PEAK_GBS:
+        # of the unit the product runs on: bf16 matrix cores for bf16; for
+        # fp32, three bf16 products per product, i.e. a third of the bf16 peak
+        # in fp32-equivalent flops
+        eff_peak = MFMA_BF16_PEAK_TFLOPS if bf else MFMA_BF16_PEAK_TFLOPS / 3
+        if fl / by < eff_peak * 1e3 / HBM_PEAK_GBS:
             rl = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}
+        elif bf:
+            rl = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
         else:
-            rl = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
-                  "traffic": traffic}
-            if not bf:
-                rl["bf16_mfma_issued_frac"] = 3 * tf / MFMA_BF16_PEAK_TFLOPS
+            rl = {"bound": "mfma", "achieved": 3 * tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": 3 * tf / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                  "flops": "bf16 matrix-core flops issued (three bf16 products per fp32 product)",
+                  "fp32_equiv_vs_fp32_mfma_peak": tf / MFMA_FP32_PEAK_TFLOPS}
         res[name] = {"ms": ms, "tflops": tf, "hbm_GBps_algorithmic": gbs, "roofline": rl}
     del x, wab, wfb, f, beta, wg, g, y, wo, out, ws
     torch.cuda.empty_cache()
@@ -383,8 +547,9 @@ def main():
     ap.add_argument("--prefill", choices=["none", "default", "all"], default="default")
     ap.add_argument("--prefill-runs", type=int, default=5)
     ap.add_argument("--projections", choices=["none", "default", "all"], default="default")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg: no oracle baseline and no parity check of the timed runs")
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-overcache", action="store_true")
     ap.add_argument("--only", default=None,
                     help="profiling runs: 'decode', 'prefill:<workload index>' or "
@@ -392,8 +557,14 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (torch copy "
                          "kernel of known size, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--source-key", default=None, metavar="PATH",
+                    help="print the source key of a path's kernels (decode, chunk, scan, short, split, "
+                         "fused, proj), as the traffic summaries record it, and exit")
     args = ap.parse_args()
 
+    if args.source_key:
+        print(source_key(args.source_key))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
@@ -417,6 +588,8 @@ def main():
 
     N, H = 64, 32
     steps, warmup = max(1, args.steps), max(0, args.warmup)
+    prefill_keys = {2: "prefill_1x32x8192", 3: "prefill_16x64x2048", 4: "prefill_ragged_256x32",
+                    5: "prefill_short_64x32x13"}
 
     if args.only:
         out = {"only": args.only}
@@ -428,7 +601,9 @@ def main():
             out.update(bench_projections(torch, kda, synth, dev, int(parts[1]), args.prefill_runs,
                                          parts[2] if len(parts) > 2 else None))
         elif args.only.startswith("prefill:"):
-            r = bench_prefill(torch, kda, synth, dev, int(args.only.split(":")[1]), args.prefill_runs)
+            idx = int(args.only.split(":")[1])
+            r = bench_prefill(torch, kda, synth, dev, synth.workload(idx), args.prefill_runs,
+                              prefill_keys.get(idx), want_check=False)
             out.update(r)
         else:
             raise SystemExit("unknown --only %r" % args.only)
@@ -444,14 +619,17 @@ def main():
         print(json.dumps(out), flush=True)
         return
     log("decode %dx%d: generating %d steps of inputs" % (N, H, steps))
-    dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup)
+    check = not args.no_cpu_baseline
+    dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup, check_seqs=(0, N - 1) if check else ())
     ms_step = dec["ms_total"] / steps
     units = N * H
     value = units * steps / (dec["ms_total"] * 1e-3)
     bytes_launch = units * (STATE_BYTES + DECODE_OTHER_BYTES)
-    achieved = bytes_launch / (ms_step * 1e-3) / 1e9
-    traffic = committed_traffic("kda_decode.hip", "decode_64x32")
-    log("decode: %.2f us/step, %.3g token.heads/s, %.0f GB/s algorithmic" % (ms_step * 1e3, value, achieved))
+    state_gbs = units * STATE_BYTES / (ms_step * 1e-3) / 1e9
+    total_gbs = bytes_launch / (ms_step * 1e-3) / 1e9
+    traffic = committed_traffic("decode", "decode_64x32")
+    log("decode: %.2f us/step, %.3g token.heads/s, state %.0f GB/s, all bytes %.0f GB/s"
+        % (ms_step * 1e3, value, state_gbs, total_gbs))
 
     result = {
         "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": steps,
@@ -461,16 +639,23 @@ def main():
                                "conv window carried in, one kda_token_step launch per token",
                    "num_seqs": N, "num_heads": H, "head_dim": DK, "act_dtype": "fp32",
                    "gate": "bounded", "tokens_per_step": 1},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "state_only_GBps": units * STATE_BYTES / (ms_step * 1e-3) / 1e9,
-                     "bytes_per_launch": bytes_launch},
+        "roofline": {"bound": "hbm", "achieved": state_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": state_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "bytes": "state only: %d pairs x %d B (64 KiB read + 64 KiB written) per launch"
+                              % (units, STATE_BYTES),
+                     "achieved_total_GBps": total_gbs, "frac_total": total_gbs / HBM_PEAK_GBS,
+                     "bytes_per_launch_total": bytes_launch},
     }
 
-    if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on this host (~%.0f s)" % args.cpu_seconds)
-        result["cpu_baseline"] = cpu_baseline_decode(synth, dec["w"], args.cpu_seconds)
+    if check:
+        log("cpu leg: single-precision oracle on this host (up to ~%.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_decode(dec["w"], args.cpu_seconds)
         log("cpu baseline: %s" % result["cpu_baseline"])
+        log("cpu leg: parity of the timed decode run (fp64 oracle)")
+        result["parity"] = decode_parity(synth, dec["w"], dec["got"], dec["check_seqs"])
+        log("parity: %s" % result["parity"])
+    else:
+        result["parity"] = {"pass": None, "sample": "not checked (--no-cpu-baseline)"}
     del dec
 
     if not args.no_overcache:
@@ -480,21 +665,46 @@ def main():
         result["overcache_decode"] = {
             "workload": "decode 512 x 32 heads (1 GiB state, exceeds the 256 MB Infinity Cache); disclosed, not the baseline",
             "us_per_step": oms * 1e3, "value": 512 * H * 100 / (oc["ms_total"] * 1e-3),
+            "state_GBps": 512 * H * STATE_BYTES / (oms * 1e-3) / 1e9,
             "achieved_GBps": 512 * H * (STATE_BYTES + DECODE_OTHER_BYTES) / (oms * 1e-3) / 1e9}
         log("over-cache: %s" % result["overcache_decode"])
         del oc
 
+    prefill_fail = False
     if args.prefill != "none":
         # every prefill workload: 1x32x8192 fp32, 16x64x2048 bf16, the ragged
-        # 256x32 bf16 batch and the short 64x32x13 (all = default since the
-        # ragged batch generates in seconds on the GPU host's threads)
-        idxs = [2, 3, 4, 5]
+        # 256x32 bf16 batch and the short 64x32x13; then the 16x64x2048 shape
+        # with the two other gate forms (they run the recurrent kernels)
+        runs = [(idx, synth.workload(idx), prefill_keys[idx]) for idx in (2, 3, 4, 5)]
         result["prefill"] = []
-        for idx in idxs:
+        for idx, w, key in runs:
             log("prefill workload %d" % idx)
-            r = bench_prefill(torch, kda, synth, dev, idx, args.prefill_runs)
+            r = bench_prefill(torch, kda, synth, dev, w, args.prefill_runs, key, want_check=check)
+            if "_check" in r:
+                seqs, heads, got = r.pop("_check")
+                r["parity"] = prefill_parity(synth, w, got, seqs, heads)
+                if not r["parity"]["pass"]:
+                    prefill_fail = True
+                    r["value"] = None
             log("prefill: %s" % r)
             result["prefill"].append(r)
+            del w
+        result["prefill_gate_forms"] = []
+        for mode, name in ((kda.KDA_GATE_LITERAL, "literal"), (kda.KDA_GATE_RAW, "raw")):
+            w = synth.make_workload("batched prefill 16x64 T=2048 bf16, %s gate" % name, seed=3, N=16, H=64,
+                                    lengths=[2048] * 16, act_dtype="bf16", state_std=0.02, win_std=1.0,
+                                    decay=(0.8, 0.999), gate_mode=mode)
+            log("prefill 16x64x2048, %s gate" % name)
+            r = bench_prefill(torch, kda, synth, dev, w, max(1, args.prefill_runs // 2), None, want_check=check)
+            if "_check" in r:
+                seqs, heads, got = r.pop("_check")
+                r["parity"] = prefill_parity(synth, w, got, seqs, heads)
+                if not r["parity"]["pass"]:
+                    prefill_fail = True
+                    r["value"] = None
+            log("prefill: %s" % r)
+            result["prefill_gate_forms"].append(r)
+            del w
 
     if args.projections != "none":
         result["projections"] = []
@@ -506,7 +716,13 @@ def main():
 
     result["device"] = {"name": torch.cuda.get_device_name(dev), "rocm_smi_before": smi_before,
                         "rocm_smi_after": rocm_smi_snapshot()}
+    failed = result["parity"]["pass"] is False or prefill_fail
+    if failed:
+        # a timed run that misses the oracle's tolerance reports no throughput
+        result["value"] = None
     print(json.dumps(result), flush=True)
+    if failed:
+        sys.exit(1)
 
 
 if __name__ == "__main__":

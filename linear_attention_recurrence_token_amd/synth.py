@@ -298,6 +298,26 @@ def sequence_rows_as_decode(w: Workload, arr: np.ndarray) -> np.ndarray:
                                 .reshape((steps * N,) + arr.shape[1:]))
 
 
+def decode_subset(w: Workload, seqs) -> Workload:
+    """The sequences `seqs` (every head) of a decode run, as a prefill-layout
+    workload of len(seqs) sequences of decode_steps tokens each, without
+    reordering the other sequences' rows."""
+    if not w.decode_steps:
+        raise ValueError("not a decode workload")
+    seqs = np.asarray(seqs, dtype=np.int64)
+    steps, N = w.decode_steps, w.N
+
+    def tok(a):
+        sel = a.reshape((steps, N) + a.shape[1:])[:, seqs]          # [steps, n, ...]
+        return np.ascontiguousarray(sel.swapaxes(0, 1)).reshape((steps * len(seqs),) + a.shape[1:])
+    cu = np.arange(len(seqs) + 1, dtype=np.int64) * steps
+    return dataclasses.replace(
+        w, name=w.name + " (sequences %s)" % list(map(int, seqs)), N=len(seqs), cu_seqlens=cu,
+        q=tok(w.q), k=tok(w.k), v=tok(w.v), f=tok(w.f), beta=tok(w.beta), g=tok(w.g),
+        state0=np.ascontiguousarray(w.state0[seqs]), win0=np.ascontiguousarray(w.win0[seqs]),
+        decode_steps=0)
+
+
 def subset(w: Workload, seqs, heads) -> Workload:
     """The sub-problem made of the given sequences and heads (prefill layout)."""
     if w.decode_steps:

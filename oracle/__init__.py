@@ -6,8 +6,11 @@ shares no code with it.
 
 ``kda_reference`` runs the plain fp64 C implementation in ``kda_oracle.c``
 (steps in the order of "Kimi K3 Metal Gap Analysis", §2 KDA Attention table:
-Conv4 + SiLU, L2 normalize q/k, Decay compute, Recurrence, O projection).
-The shared object is compiled with gcc on first use if it is missing.
+Conv4 + SiLU, L2 normalize q/k, Decay compute, Recurrence, O projection);
+it is the parity reference.  ``kda_reference_f32_inplace`` runs the same
+loops in single precision with the state updated in place: the CPU
+baseline's timed mode, pinned to the fp64 one.  The shared object is
+compiled with gcc on first use if it is missing.
 """
 from __future__ import annotations
 
@@ -55,6 +58,15 @@ def _load():
                 fp, fp, fp, fp,
                 ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                 dp, dp, dp, dp,
+            ]
+            lib.kda_oracle_run_f32.restype = ctypes.c_int32
+            lib.kda_oracle_run_f32.argtypes = [
+                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                ctypes.POINTER(ctypes.c_int64),
+                fp, fp, fp, fp, fp, fp,
+                fp, fp, fp, fp,
+                ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                fp, fp, fp, fp,
             ]
             lib.kda_oracle_version.restype = ctypes.c_int32
             _lib = lib
@@ -118,6 +130,42 @@ def kda_reference(q, k, v, f, beta, g, conv_w, A_log, dt_bias, gamma,
     if rc != 0:
         raise ValueError("kda_oracle_run rejected its arguments (rc=%d)" % rc)
     return {"y": y, "o_raw": o, "state": S, "win": W}
+
+
+def kda_reference_f32_inplace(q, k, v, f, beta, g, conv_w, A_log, dt_bias, gamma,
+                              state, win, y, cu_seqlens, o_raw=None, *, gate_mode=GATE_BOUNDED,
+                              lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-6):
+    """The single-precision oracle (the CPU baseline's timed mode).
+
+    Same shapes as kda_reference.  state [N, H, dk, dv] and win [N, H,
+    taps-1, C] must be C-contiguous float32 arrays and are updated in place;
+    y (and o_raw when given) [T, H, dv] float32 are written.  Every array is
+    used as it is (no conversion or copy), so callers pass float32,
+    C-contiguous inputs.  Nothing is returned."""
+    lib = _load()
+    arrs = (q, k, v, f, beta, g, conv_w, A_log, dt_bias, gamma, state, win, y)
+    for a in arrs + ((o_raw,) if o_raw is not None else ()):
+        if a.dtype != np.float32 or not a.flags.c_contiguous:
+            raise ValueError("kda_reference_f32_inplace takes C-contiguous float32 arrays")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    taps = conv_w.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    assert k.shape == (T, H, dk) and f.shape == (T, H, dk) and beta.shape == (T, H)
+    assert g.shape == (T, H, dv) and y.shape == (T, H, dv)
+    assert state.shape == (N, H, dk, dv) and win.shape == (N, H, taps - 1, 2 * dk + dv)
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    fp = ctypes.c_float
+    rc = lib.kda_oracle_run_f32(
+        N, H, dk, dv, taps, _ptr(cu, ctypes.c_int64),
+        _ptr(q, fp), _ptr(k, fp), _ptr(v, fp), _ptr(f, fp), _ptr(beta, fp), _ptr(g, fp),
+        _ptr(conv_w, fp), _ptr(A_log, fp), _ptr(dt_bias, fp), _ptr(gamma, fp),
+        int(gate_mode), float(lower_bound), float(l2_eps), float(rms_eps),
+        _ptr(state, fp), _ptr(win, fp), _ptr(y, fp),
+        _ptr(o_raw, fp) if o_raw is not None else ctypes.POINTER(fp)())
+    if rc != 0:
+        raise ValueError("kda_oracle_run_f32 rejected its arguments (rc=%d)" % rc)
 
 
 def omp_threads() -> int:

@@ -350,13 +350,48 @@ def test_decode_64x32_every_pair_repeated(gpu):
             np.testing.assert_array_equal(again[k], first[k])
 
 
+def test_decode_64x32_1000_steps(gpu):
+    # the decode workload as stated: 1000 consecutive kda_token_step launches
+    # over 64 sequences x 32 heads, every step's inputs resident in HBM,
+    # step-major (the layout the bench times); three sequences, every head,
+    # against the oracle: every step's y and o_raw, the final state and window.
+    # Slow-decay channels (alpha up to 0.999) carry state over the whole run.
+    import torch
+    w = synth.workload(1)
+    seqs = [0, 31, 63]
+    note("decode 64x32, 1000 chained steps, sequences %s x all 32 heads" % seqs)
+    d = synth.to_device(w, gpu)
+    N, steps = w.N, w.decode_steps
+    cfg = _gpu.cfg_of(w)
+    for s in range(steps):
+        sl = slice(s * N, (s + 1) * N)
+        kda.kda_token_step(cfg, q=d["q"][sl], k=d["k"][sl], v=d["v"][sl], f=d["f"][sl],
+                           beta=d["beta"][sl], g=d["g"][sl], conv_w=d["conv_w"], A_log=d["A_log"],
+                           dt_bias=d["dt_bias"], gamma=d["gamma"], state=d["state"],
+                           conv_win=d["conv_win"], y=d["y"][sl], o_raw=d["o_raw"][sl])
+    torch.cuda.synchronize()
+    ns = torch.as_tensor(seqs, device=gpu)
+
+    def seq_major(t):      # [steps * N, H, dv] -> the sampled sequences' rows, sequence-major
+        sel = t.view(steps, N, w.H, w.dv).index_select(1, ns)
+        return _gpu._np(sel.transpose(0, 1).contiguous().view(-1, w.H, w.dv))
+    got = {"y": seq_major(d["y"]), "o_raw": seq_major(d["o_raw"]),
+           "state": _gpu._np(d["state"].index_select(0, ns)),
+           "win": d["conv_win"].index_select(0, ns).cpu().numpy()}
+    del d
+    torch.cuda.empty_cache()
+    errs = _gpu.assert_parity(got, _gpu.oracle_sequence(synth.decode_subset(w, seqs)), label="decode 1000 steps")
+    note("decode 1000 steps: relative errors %s" % errs)
+
+
 @pytest.mark.parametrize("path", ["auto", "chunk"])
 def test_full_prefill_1x32x8192(gpu, path):
-    # auto: the two-pass chunk path (32 pairs of 8192 tokens)
+    # auto: the two-pass chunk path (32 pairs of 8192 tokens); every head
+    # against the oracle
     w = synth.workload(2)
-    note("full prefill 1x32x8192 fp32, sampled heads 0, 19, %s" % path)
+    note("full prefill 1x32x8192 fp32, all 32 heads, %s" % path)
     full = _gpu.run_sequence(w, gpu, path=path)
-    _sampled(w, full, [0], [0, 19], bf16=False)
+    _sampled(w, full, [0], list(range(w.H)), bf16=False)
 
 
 def test_full_batched_prefill_16x64x2048(gpu):

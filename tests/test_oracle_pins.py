@@ -10,6 +10,7 @@ SiLU, L2 normalize q/k, Decay compute, Recurrence, O projection);
 check: output over v times beta equals the dot product of the normalised q
 and k) and Design notes (state and conv windows persist across tokens).
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -386,3 +387,97 @@ def test_oracle_rejects_bad_arguments():
     p = _tiny.blank(T=2)
     with pytest.raises(ValueError):
         run(p, gate_mode=7)
+
+
+# --- P10: the single-precision oracle (the CPU baseline's mode) against the fp64 one ---
+
+def _run_f32(p, **kw):
+    T, H, dv = p["g"].shape
+    f32 = {kk: np.ascontiguousarray(vv, dtype=np.float32) for kk, vv in p.items() if kk != "cu_seqlens"}
+    y = np.empty((T, H, dv), np.float32)
+    o = np.empty((T, H, dv), np.float32)
+    oracle.kda_reference_f32_inplace(f32["q"], f32["k"], f32["v"], f32["f"], f32["beta"], f32["g"],
+                                     f32["conv_w"], f32["A_log"], f32["dt_bias"], f32["gamma"],
+                                     f32["state"], f32["win"], y, p["cu_seqlens"], o, **kw)
+    return {"y": y, "o_raw": o, "state": f32["state"], "win": f32["win"]}
+
+
+def _workload_dict(w):
+    return {"q": w.q, "k": w.k, "v": w.v, "f": w.f, "beta": w.beta, "g": w.g, "conv_w": w.conv_w,
+            "A_log": w.A_log, "dt_bias": w.dt_bias, "gamma": w.gamma, "state": w.state0,
+            "win": w.win0, "cu_seqlens": w.cu_seqlens}
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a.astype(np.float64) - b))) / float(np.max(np.abs(b)))
+
+
+def test_f32_mode_matches_fp64_on_the_64_token_workload():
+    from linear_attention_recurrence_token_amd import synth
+    p = _workload_dict(synth.workload(0))
+    ref = run(p)
+    got = _run_f32(p)
+    for key in ("y", "o_raw", "state"):
+        assert _rel(got[key], ref[key]) <= 1e-5, key
+    # the window holds raw fp32 rows: exact in both modes
+    np.testing.assert_array_equal(got["win"], ref["win"].astype(np.float32))
+
+
+@pytest.mark.parametrize("mode,lb", [(GATE_BOUNDED, -5.0), (GATE_LITERAL, -5.0), (GATE_RAW, 0.0)])
+def test_f32_mode_matches_fp64_carried_state_every_gate(mode, lb):
+    from linear_attention_recurrence_token_amd import synth
+    w = synth.make_workload("p10", seed=31 + mode, N=3, H=2, lengths=[5, 0, 23], state_std=0.02,
+                            win_std=1.0, gate_mode=mode, lower_bound=lb if mode != GATE_RAW else -5.0)
+    p = _workload_dict(w)
+    kw = {"gate_mode": mode, "lower_bound": w.lower_bound}
+    ref = run(p, **kw)
+    got = _run_f32(p, **kw)
+    for key in ("y", "o_raw", "state"):
+        assert _rel(got[key], ref[key]) <= 1e-5, key
+    np.testing.assert_array_equal(got["win"], ref["win"].astype(np.float32))
+
+
+def test_f32_mode_per_step_calls_equal_one_call():
+    # the CPU baseline runs a decode workload one step (one token of every
+    # sequence) per call, with the state updated in place
+    rng = np.random.default_rng(41)
+    p = _tiny.random_dense(rng, N=3, H=2, T=5 * 3, dk=8, dv=8, lengths=[5, 5, 5])
+    whole = _run_f32(p)
+    f32 = {kk: np.ascontiguousarray(vv, dtype=np.float32) for kk, vv in p.items() if kk != "cu_seqlens"}
+    S, W = f32["state"].copy(), f32["win"].copy()
+    ys = np.empty_like(whole["y"])
+    for t in range(5):
+        rows = [n * 5 + t for n in range(3)]     # token t of every sequence
+        step = {kk: np.ascontiguousarray(f32[kk][rows]) for kk in ("q", "k", "v", "f", "beta", "g")}
+        y = np.empty((3,) + whole["y"].shape[1:], np.float32)
+        oracle.kda_reference_f32_inplace(step["q"], step["k"], step["v"], step["f"], step["beta"], step["g"],
+                                         f32["conv_w"], f32["A_log"], f32["dt_bias"], f32["gamma"], S, W, y,
+                                         np.arange(4))
+        ys[rows] = y
+    np.testing.assert_array_equal(ys, whole["y"])
+    np.testing.assert_array_equal(S, whole["state"])
+    np.testing.assert_array_equal(W, whole["win"])
+
+
+def test_f32_mode_refuses_arrays_it_would_have_to_copy():
+    rng = np.random.default_rng(42)
+    p = _tiny.random_dense(rng, T=3, dk=4, dv=4)
+    f64 = {kk: np.asarray(vv, dtype=np.float64) for kk, vv in p.items()}
+    with pytest.raises(ValueError):
+        oracle.kda_reference_f32_inplace(f64["q"], f64["k"], f64["v"], f64["f"], f64["beta"], f64["g"],
+                                         f64["conv_w"], f64["A_log"], f64["dt_bias"], f64["gamma"],
+                                         f64["state"], f64["win"], np.empty((3, 1, 4)), p["cu_seqlens"])
+
+
+def test_synth_decode_subset_matches_reordering():
+    # the sampled-sequence layout the 1000-step decode parity test uses
+    from linear_attention_recurrence_token_amd import synth
+    w = synth.workload(1, scale={"N": 5, "H": 3, "steps": 4})
+    seqs = [0, 3, 4]
+    a = synth.decode_subset(w, seqs)
+    sw = dataclasses.replace(w, decode_steps=0, cu_seqlens=np.arange(6, dtype=np.int64) * 4,
+                             **{kk: synth.decode_rows_as_sequences(w, getattr(w, kk))
+                                for kk in ("q", "k", "v", "f", "beta", "g")})
+    b = synth.subset(sw, seqs, list(range(3)))
+    for kk in ("q", "k", "v", "f", "beta", "g", "state0", "win0", "cu_seqlens"):
+        np.testing.assert_array_equal(getattr(a, kk), getattr(b, kk), err_msg=kk)
