@@ -83,7 +83,9 @@ typedef enum kda_status {
     KDA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or enum */
     KDA_ERR_UNSUPPORTED = -2,   /* dims other than dk = dv = 128, 4 taps     */
     KDA_ERR_DEVICE = -3,        /* no current HIP device, or not gfx950      */
-    KDA_ERR_LAUNCH = -4         /* the HIP runtime refused the launch        */
+    KDA_ERR_LAUNCH = -4,        /* the HIP runtime refused the launch        */
+    KDA_ERR_SCRATCH_LIMIT = -5  /* a no-allocation call needs more than the
+                                   library's static scratch                  */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -269,6 +271,27 @@ kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *
                              const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
                              float *f, float *beta, void *workspace, int64_t workspace_bytes,
                              void *stream);
+
+/*
+ * kda_lowrank_gates without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as
+ * kda_lowrank_gates, except that the workspace is the library's own static
+ * scratch: a device array of KDA_NOALLOC_SCRATCH_BYTES (16 MiB) that each
+ * device the library runs on holds until the process ends.  The call
+ * allocates nothing.  Limit: tokens * rank * 4 bytes, rounded up to 256, must
+ * fit in the scratch, else KDA_ERR_SCRATCH_LIMIT and nothing is enqueued;
+ * the bf16 weight parts and the split-K partial sums use what is left of it
+ * when they fit (the results equal those of kda_lowrank_gates with a
+ * workspace of the same size).  Every call on a device shares that device's
+ * scratch: calls that overlap in time on one device (different streams,
+ * threads or processes) race and must not be issued.  A failure to reach the
+ * scratch on the current device returns KDA_ERR_DEVICE.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES 16777216
+kda_status kda_lowrank_gates_noalloc(const kda_config *cfg, const void *x, const float *w_fa_bp,
+                                     const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
+                                     float *f, float *beta, void *stream);
 
 /*
  * g = W_g x, the input of the step's output gate (Gap Analysis §2, row "O

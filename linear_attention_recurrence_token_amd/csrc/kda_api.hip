@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
@@ -34,6 +35,37 @@ kda_status device_ok() {
         g_dev_kind[dev].store(kind, std::memory_order_relaxed);
     }
     return kind == 1 ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+// The no-allocation entry point's scratch: one array per device, held until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol); it uses the device address
+// that hipGetSymbolAddress returns, taken once per device with that device
+// current.  Calls that overlap on one device share it and so race; nothing in
+// it needs to start at zero (every byte a call reads, the call wrote first).
+__device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];
+bool g_scratch_tried[kMaxDevices];
+
+// the current device's address of `scratch`, or null if it cannot be had
+void *noalloc_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_tried[dev]) {
+        g_scratch_tried[dev] = true;
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr)
+            g_scratch_addr[dev] = ptr;
+        else
+            (void)hipGetLastError();
+    }
+    return g_scratch_addr[dev];
 }
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -238,6 +270,9 @@ const char *kda_status_string(int32_t status) {
         case KDA_ERR_UNSUPPORTED: return "unsupported shape (libkda needs dk = dv = 128 and 4 conv taps)";
         case KDA_ERR_DEVICE: return "no usable device (no current HIP device, or it is not gfx950)";
         case KDA_ERR_LAUNCH: return "kernel launch failed";
+        case KDA_ERR_SCRATCH_LIMIT:
+            return "the call needs more than the library's static scratch (KDA_NOALLOC_SCRATCH_BYTES); "
+                   "use the variant that takes a workspace";
         default: return "unknown status";
     }
 }
@@ -380,10 +415,15 @@ int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int3
     return KDA_ERR_INVALID_ARG;
 }
 
-kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *w_fa_bp,
-                             const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
-                             float *f, float *beta, void *workspace, int64_t workspace_bytes,
-                             void *stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_lowrank_gates with its workspace given (the caller's, or the static
+// scratch of the no-allocation variant)
+kda_status lowrank_gates_impl(const kda_config *cfg, const void *x, const float *w_fa_bp, const float *w_fb,
+                              int32_t hidden, int32_t rank, int64_t tokens, float *f, float *beta,
+                              void *workspace, int64_t workspace_bytes, void *stream, bool static_scratch) {
     kda_status st = check_proj_config(cfg);
     if (st != KDA_OK) return st;
     if (hidden <= 0 || hidden > PROJ_MAX_HIDDEN || hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
@@ -393,25 +433,37 @@ kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *
     const int32_t H = cfg->num_heads;
     const int64_t eb = cfg->act_dtype == KDA_BF16 ? 2 : 4;
     const int64_t a_bytes = round_up(tokens * rank * 4, WS_ALIGN);
-    if (workspace_bytes < a_bytes) return KDA_ERR_INVALID_ARG;
+    if (static_scratch) {
+        if (a_bytes > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH_LIMIT;
+    } else if (workspace_bytes < a_bytes) {
+        return KDA_ERR_INVALID_ARG;
+    }
     const Span ins[] = {{x, tokens * hidden * eb}, {w_fa_bp, (int64_t)(rank + H) * hidden * 4},
                         {w_fb, (int64_t)H * kda::DK * rank * 4}};
+    // (the static scratch is the library's own array: no caller buffer can overlap it)
     const Span outs[] = {{f, tokens * H * kda::DK * 4}, {workspace, workspace_bytes}};
-    st = check_spans(ins, 3, outs, 2);
+    st = check_spans(ins, 3, outs, static_scratch ? 1 : 2);
     if (st != KDA_OK) return st;
     // beta needs word alignment only (it is written one value at a time)
     const Span bs = {beta, tokens * H * 4};
     if (!beta || (reinterpret_cast<uintptr_t>(beta) & 3u)) return KDA_ERR_INVALID_ARG;
     for (const Span &o : ins)
         if (overlap(bs, o)) return KDA_ERR_INVALID_ARG;
-    for (const Span &o : outs)
-        if (overlap(bs, o)) return KDA_ERR_INVALID_ARG;
+    for (int o = 0; o < (static_scratch ? 1 : 2); ++o)
+        if (overlap(bs, outs[o])) return KDA_ERR_INVALID_ARG;
     kda::ProjGemm g1, g2;
-    float *a = static_cast<float *>(workspace);
-    lowrank_products(cfg, x, w_fa_bp, w_fb, hidden, rank, tokens, f, beta, a, g1, g2);
+    lowrank_products(cfg, x, w_fa_bp, w_fb, hidden, rank, tokens, f, beta, nullptr, g1, g2);
     if (!kda::proj_gemm_shape_ok(g1) || !kda::proj_gemm_shape_ok(g2)) return KDA_ERR_INVALID_ARG;
     st = device_ok();
     if (st != KDA_OK) return st;
+    if (static_scratch) {
+        workspace = noalloc_scratch();
+        if (!workspace) return KDA_ERR_DEVICE;
+        workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
+    float *a = static_cast<float *>(workspace);
+    g1.C0 = a;
+    g2.A = a;
     // the weights' bf16 parts after a, when the workspace holds them
     const int64_t planes = lowrank_planes_bytes(H, rank, hidden);
     uint16_t *wparts = nullptr;
@@ -422,14 +474,32 @@ kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *
         g1.b_presplit = true;
         used += planes;
     }
-    float *scratch = reinterpret_cast<float *>(static_cast<char *>(workspace) + used);
+    float *scratch_f = reinterpret_cast<float *>(static_cast<char *>(workspace) + used);
     const int64_t scratch_bytes = workspace_bytes - used;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (wparts) e = kda::launch_split_planes(w_fa_bp, wparts, (int64_t)(rank + H) * hidden, s);
-    if (e == hipSuccess) e = kda::launch_proj_gemm(g1, scratch_bytes > 0 ? scratch : nullptr, scratch_bytes, s);
-    if (e == hipSuccess) e = kda::launch_proj_gemm(g2, scratch_bytes > 0 ? scratch : nullptr, scratch_bytes, s);
+    if (e == hipSuccess) e = kda::launch_proj_gemm(g1, scratch_bytes > 0 ? scratch_f : nullptr, scratch_bytes, s);
+    if (e == hipSuccess) e = kda::launch_proj_gemm(g2, scratch_bytes > 0 ? scratch_f : nullptr, scratch_bytes, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *w_fa_bp,
+                             const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
+                             float *f, float *beta, void *workspace, int64_t workspace_bytes,
+                             void *stream) {
+    return lowrank_gates_impl(cfg, x, w_fa_bp, w_fb, hidden, rank, tokens, f, beta, workspace, workspace_bytes,
+                              stream, false);
+}
+
+kda_status kda_lowrank_gates_noalloc(const kda_config *cfg, const void *x, const float *w_fa_bp,
+                                     const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
+                                     float *f, float *beta, void *stream) {
+    return lowrank_gates_impl(cfg, x, w_fa_bp, w_fb, hidden, rank, tokens, f, beta, nullptr, 0, stream, true);
 }
 
 namespace {

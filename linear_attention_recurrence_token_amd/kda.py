@@ -19,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE, KDA_ERR_LAUNCH = 0, -1, -2, -3, -4
+KDA_ERR_SCRATCH_LIMIT = -5
+KDA_NOALLOC_SCRATCH_BYTES = 16 << 20
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_BOUNDED, KDA_GATE_LITERAL, KDA_GATE_RAW = 0, 1, 2
 KDA_PREFILL_AUTO, KDA_PREFILL_FUSED, KDA_PREFILL_SPLIT, KDA_PREFILL_CHUNK, KDA_PREFILL_SHORT = 0, 1, 2, 3, 4
@@ -47,7 +49,7 @@ class kda_tensors(ctypes.Structure):
 EXPORTS = ("kda_token_step", "kda_sequence", "kda_sequence_workspace_size",
            "kda_status_string", "kda_version", "kda_device_check",
            "kda_projection_workspace_size", "kda_lowrank_gates", "kda_gate_projection",
-           "kda_output_projection")
+           "kda_output_projection", "kda_lowrank_gates_noalloc")
 
 KDA_PROJ_LOWRANK_GATES, KDA_PROJ_GATE, KDA_PROJ_OUTPUT = 0, 1, 2
 
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
             L.kda_gate_projection.argtypes = [cfgp, vp, vp, i32, i64, vp, vp, i64, vp]
             L.kda_output_projection.restype = i32
             L.kda_output_projection.argtypes = [cfgp, vp, vp, i32, i64, vp, vp, i64, vp]
+            L.kda_lowrank_gates_noalloc.restype = i32
+            L.kda_lowrank_gates_noalloc.argtypes = [cfgp, vp, vp, vp, i32, i32, i64, vp, vp, vp]
             _lib = L
     return _lib
 
@@ -303,6 +307,29 @@ def kda_lowrank_gates(config: KdaConfig, *, x, w_fa_bp, w_fb, f, beta, workspace
                                  _ptr(beta), ws_ptr, ws_bytes, _stream_handle(stream))
     if st != KDA_OK:
         raise KdaError(st, "kda_lowrank_gates")
+
+
+def kda_lowrank_gates_noalloc(config: KdaConfig, *, x, w_fa_bp, w_fb, f, beta, stream=None,
+                              check: bool = True) -> None:
+    """kda_lowrank_gates with the library's static scratch as its workspace
+    (C: kda_lowrank_gates_noalloc): nothing is allocated; T * r * 4 bytes
+    must fit in KDA_NOALLOC_SCRATCH_BYTES, else KdaError(KDA_ERR_SCRATCH_LIMIT).
+    Calls that overlap in time on one device race on that scratch."""
+    import torch
+    T, D = int(x.shape[0]), int(x.shape[1])
+    H = config.num_heads
+    r = int(w_fb.shape[1])
+    if check:
+        act = torch.bfloat16 if config.act_dtype == KDA_BF16 else torch.float32
+        _gpu_tensor("x", x, (T, D), act)
+        for name, t, shape in (("w_fa_bp", w_fa_bp, (r + H, D)), ("w_fb", w_fb, (H * DK, r)),
+                               ("f", f, (T, H, DK)), ("beta", beta, (T, H))):
+            _gpu_tensor(name, t, shape, torch.float32, x.device)
+    c = config.to_c()
+    st = lib().kda_lowrank_gates_noalloc(ctypes.byref(c), _ptr(x), _ptr(w_fa_bp), _ptr(w_fb), D, r, T,
+                                         _ptr(f), _ptr(beta), _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_lowrank_gates_noalloc")
 
 
 def kda_gate_projection(config: KdaConfig, *, x, w_g, g, workspace="auto", stream=None,

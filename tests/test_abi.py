@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.kda_version() == 1
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         s = kda.status_string(st)
         assert s and s != "unknown status"
     assert kda.status_string(12345) == "unknown status"
@@ -327,3 +327,42 @@ def test_projection_workspace_size(lib):
     assert size(kda.KDA_PROJ_OUTPUT, 68, 0, 10) == 2 * 10 * 68 * 4   # K = 4 heads x 128: two splits
     assert size(kda.KDA_PROJ_GATE, 64, 0, -1) == kda.KDA_ERR_INVALID_ARG
     assert size(kda.KDA_PROJ_GATE, 64, 0, 10, _cfg(head_dim_k=64)) == kda.KDA_ERR_UNSUPPORTED
+
+
+# --- the no-allocation variant of the low-rank gates ---------------------------
+
+def _lowrank_na(lib, cfg=None, x=1 << 40, w=(1 << 40) + (1 << 30), wfb=(1 << 40) + (2 << 30),
+                hidden=64, rank=32, tokens=10, f=(1 << 40) + (3 << 30), beta=(1 << 40) + (4 << 30)):
+    cfg = cfg or _cfg()
+    return lib.kda_lowrank_gates_noalloc(ctypes.byref(cfg), x, w, wfb, hidden, rank, tokens, f, beta, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"hidden": 48}, kda.KDA_ERR_INVALID_ARG),
+    ({"rank": 16}, kda.KDA_ERR_INVALID_ARG),
+    ({"tokens": -1}, kda.KDA_ERR_INVALID_ARG),
+    ({"x": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"f": (1 << 40) + 64}, kda.KDA_ERR_INVALID_ARG),          # f overlaps x
+    ({"beta": (1 << 40) + (4 << 30) + 2}, kda.KDA_ERR_INVALID_ARG),
+    ({"cfg": _cfg(head_dim_k=64)}, kda.KDA_ERR_UNSUPPORTED),
+    # the rank-r factor alone is tokens * rank * 4 bytes: past 16 MiB it does not fit
+    ({"tokens": 32769, "rank": 128}, kda.KDA_ERR_SCRATCH_LIMIT),
+    ({"tokens": 4097, "rank": 1024}, kda.KDA_ERR_SCRATCH_LIMIT),
+])
+def test_lowrank_gates_noalloc_rejects(lib, over, status):
+    assert _lowrank_na(lib, **over) == status
+
+
+def test_lowrank_gates_noalloc_limit_and_no_device(lib):
+    assert kda.KDA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert "static scratch" in kda.status_string(kda.KDA_ERR_SCRATCH_LIMIT)
+    assert _lowrank_na(lib, tokens=0, x=None, f=None, beta=None) == kda.KDA_OK
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return
+    except ImportError:
+        pass
+    # exactly the scratch size is allowed: the call gets as far as the device check
+    assert _lowrank_na(lib, tokens=32768, rank=128) == kda.KDA_ERR_DEVICE
+    assert _lowrank_na(lib) == kda.KDA_ERR_DEVICE
