@@ -26,6 +26,8 @@
 // contiguous.
 #include "kda_device.hpp"
 
+#include <atomic>
+
 namespace kda {
 
 namespace {
@@ -214,6 +216,200 @@ void decode_kernel(Params p) {
         y.w = sigmoid(g23.y) * gm.w * o.w * r;
         Act::store4(p.y, orow, y);
         if (p.o_raw) *reinterpret_cast<float4 *>(p.o_raw + orow) = o;
+    }
+}
+
+// ---------------------------------------------------------------- persistent decode
+// The same step as decode_kernel, with G workgroups that each take the pairs
+// blockIdx.x, blockIdx.x + G, ... (G a multiple of H, so a workgroup keeps one
+// head and loads its conv taps, A_log and dt_bias once).  Each pair's
+// per-token inputs (q, k, v, f, beta, g and the conv window) are loaded while
+// the previous pair is processed, right behind that pair's state loads, so
+// they have a whole pair's time to arrive.  This matters when the state
+// itself comes back fast: a state that fits in the Infinity Cache stays there
+// between steps under the plain cache policy, while every step's inputs are
+// new rows; with one pair per workgroup their latency sits on every pair's
+// critical path.
+struct DecodeIn {
+    float x0, x1, w0[PAST], w1[PAST], fa, b;
+    float2 g01, g23;
+};
+
+template <typename Act, bool NT_LOAD, bool NT_STORE>
+__global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G) {
+    constexpr int NT = 256;
+    using Sh = DecodeShape<NT>;
+    const int P = p.num_seqs * p.H;
+    int unit = blockIdx.x;
+    if (unit >= P) return;
+    const int h = unit % p.H;                    // the same for every pair of this workgroup
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cg = tid & 31, rg = tid >> 5;
+
+    __shared__ float4 s_row[DK];
+    __shared__ float s_v[DV];
+    __shared__ float s_red[Sh::NW][4];
+    __shared__ float4 s_up[Sh::NW][32][2];
+
+    // per-head constants, in LDS for the workgroup's life: the conv taps of
+    // every channel, exp(A_log), dt_bias and gamma
+    __shared__ float4 s_cw[CH];
+    __shared__ float s_eA[DK], s_dtb[DK], s_gm[DV];
+    {
+        const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+        for (int c = tid; c < CH; c += NT) s_cw[c] = *reinterpret_cast<const float4 *>(cw + c * TAPS);
+        if (tid < DK) {
+            s_eA[tid] = __expf(p.A_log[h * DK + tid]);
+            s_dtb[tid] = p.dt_bias[h * DK + tid];
+            s_gm[tid] = p.gamma[tid];
+        }
+    }
+    // thread tid < 128: q, k channel tid and the decay of key channel tid;
+    // thread 128 + j: v channel j (wavefront-uniform split)
+    const bool qk = tid < DK;
+    const int ch = qk ? tid : tid - DK;
+
+    // Every thread issues the same twelve loads in the same order, so that
+    // the compiler's wait counts are exact on every wavefront: the v threads'
+    // second channel, second window column and decay input repeat addresses
+    // in range (their values are unused), and every thread reads a g pair
+    // (those of lanes 0-31 are used).
+    const void *x1src = qk ? p.k : p.v;
+    const int w0col = qk ? ch : 2 * DK + ch, w1col = qk ? DK + ch : 2 * DK + ch;
+    auto load_in = [&](int u, DecodeIn &in) {
+        const int64_t row = (int64_t)u * DK;
+        const float *W = p.win + (int64_t)u * (PAST * CH);
+        in.x0 = Act::load1(qk ? p.q : p.v, row + ch);
+        in.x1 = Act::load1(x1src, row + ch);
+#pragma unroll
+        for (int j = 0; j < PAST; ++j) { in.w0[j] = W[j * CH + w0col]; in.w1[j] = W[j * CH + w1col]; }
+        in.fa = p.f[row + (ch & (DK - 1))];
+        in.b = p.beta[u];
+        in.g01 = Act::load2(p.g, row + 4 * cg);
+        in.g23 = Act::load2(p.g, row + 4 * cg + 2);
+    };
+
+    const uint32_t s_lane = (uint32_t)(rg * DV + 4 * cg) * 4;
+    constexpr uint32_t ROW_STEP = Sh::NRG * DV * 4;
+
+    auto issue_state = [&](int u, float4 (&s)[Sh::RPT]) {
+        const Rsrc rs = make_rsrc(p.state + (int64_t)u * (DK * DV), DK * DV * 4);
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) s[m] = ld_state<NT_LOAD>(rs, s_lane, m * ROW_STEP);
+    };
+    // the step of pair u from its inputs and its state registers (loads in flight)
+    auto pair_body = [&](int u, const DecodeIn &in, float4 (&s)[Sh::RPT]) {
+        const Rsrc rs = make_rsrc(p.state + (int64_t)u * (DK * DV), DK * DV * 4);
+        // pre-step of this pair from its prefetched inputs; the barrier keeps
+        // the previous pair's LDS reads ahead of these writes
+        float *W = p.win + (int64_t)u * (PAST * CH);
+        float qq = 0.f, kk = 0.f, qkd = 0.f;
+        __syncthreads();
+        // window shift: six stores by every thread (a v thread writes its
+        // three values twice), so the store count is the same on every path
+#pragma unroll
+        for (int j = 0; j < PAST; ++j) {
+            W[j * CH + w0col] = j + 1 < PAST ? in.w0[j + 1] : in.x0;
+            W[j * CH + w1col] = qk ? (j + 1 < PAST ? in.w1[j + 1] : in.x1) : (j + 1 < PAST ? in.w0[j + 1] : in.x0);
+        }
+        if (qk) {
+            const float4 c0 = s_cw[ch], c1 = s_cw[DK + ch];
+            const float aq = silu(c0.x * in.w0[0] + c0.y * in.w0[1] + c0.z * in.w0[2] + c0.w * in.x0);
+            const float ak = silu(c1.x * in.w1[0] + c1.y * in.w1[1] + c1.z * in.w1[2] + c1.w * in.x1);
+            const float al = decay(in.fa, s_eA[ch], s_dtb[ch], p.gate_mode, p.lb);
+            s_row[ch] = make_float4(al * aq, al * ak, al, ak);
+            qq = aq * aq; kk = ak * ak; qkd = aq * ak;
+        } else {
+            const float4 c0 = s_cw[2 * DK + ch];
+            s_v[ch] = silu(c0.x * in.w0[0] + c0.y * in.w0[1] + c0.z * in.w0[2] + c0.w * in.x0);
+        }
+        qq = sum64(qq); kk = sum64(kk); qkd = sum64(qkd);
+        if (lane == 0) { s_red[wave][0] = qq; s_red[wave][1] = kk; s_red[wave][2] = qkd; }
+        __syncthreads();
+        qq = 0.f; kk = 0.f; qkd = 0.f;
+#pragma unroll
+        for (int w = 0; w < Sh::NW; ++w) { qq += s_red[w][0]; kk += s_red[w][1]; qkd += s_red[w][2]; }
+        const float rq = rsqrtf(qq + p.l2_eps);
+        const float rk = rsqrtf(kk + p.l2_eps);
+        qkd *= rq * rk;
+
+        // u = S^T (alpha k_hat), p = S^T (alpha q_hat) in one pass
+        float4 uu = make_float4(0.f, 0.f, 0.f, 0.f), pq = uu;
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) {
+            const float4 rw = s_row[rg + Sh::NRG * m];
+            uu.x += s[m].x * rw.y; uu.y += s[m].y * rw.y; uu.z += s[m].z * rw.y; uu.w += s[m].w * rw.y;
+            pq.x += s[m].x * rw.x; pq.y += s[m].y * rw.x; pq.z += s[m].z * rw.x; pq.w += s[m].w * rw.x;
+        }
+        uu.x += __shfl_xor(uu.x, 32); uu.y += __shfl_xor(uu.y, 32);
+        uu.z += __shfl_xor(uu.z, 32); uu.w += __shfl_xor(uu.w, 32);
+        pq.x += __shfl_xor(pq.x, 32); pq.y += __shfl_xor(pq.y, 32);
+        pq.z += __shfl_xor(pq.z, 32); pq.w += __shfl_xor(pq.w, 32);
+        if (lane < 32) { s_up[wave][cg][0] = uu; s_up[wave][cg][1] = pq; }
+        __syncthreads();
+        uu = s_up[0][cg][0]; pq = s_up[0][cg][1];
+#pragma unroll
+        for (int w = 1; w < Sh::NW; ++w) {
+            const float4 a = s_up[w][cg][0], c = s_up[w][cg][1];
+            uu.x += a.x; uu.y += a.y; uu.z += a.z; uu.w += a.w;
+            pq.x += c.x; pq.y += c.y; pq.z += c.z; pq.w += c.w;
+        }
+        uu.x *= rk; uu.y *= rk; uu.z *= rk; uu.w *= rk;
+        pq.x *= rq; pq.y *= rq; pq.z *= rq; pq.w *= rq;
+
+        // delta, readout, in-place update
+        const float4 vv = *reinterpret_cast<const float4 *>(&s_v[4 * cg]);
+        float4 d, o, dk;
+        d.x = in.b * (vv.x - uu.x); d.y = in.b * (vv.y - uu.y); d.z = in.b * (vv.z - uu.z); d.w = in.b * (vv.w - uu.w);
+        o.x = pq.x + qkd * d.x; o.y = pq.y + qkd * d.y; o.z = pq.z + qkd * d.z; o.w = pq.w + qkd * d.w;
+        dk.x = d.x * rk; dk.y = d.y * rk; dk.z = d.z * rk; dk.w = d.w * rk;
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) {
+            const float2 ak = *reinterpret_cast<const float2 *>(&s_row[rg + Sh::NRG * m].z);
+            float4 t;
+            t.x = ak.x * s[m].x + ak.y * dk.x; t.y = ak.x * s[m].y + ak.y * dk.y;
+            t.z = ak.x * s[m].z + ak.y * dk.z; t.w = ak.x * s[m].w + ak.y * dk.w;
+            st_state<NT_STORE>(rs, t, s_lane, m * ROW_STEP);
+        }
+
+        // RMSNorm + gamma + sigmoid gate
+        const float ssq = sum32(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+        if (tid < 32) {
+            const float r = rsqrtf(ssq * (1.0f / DV) + p.rms_eps);
+            const int64_t orow = (int64_t)u * DK + 4 * cg;
+            const float4 gm = *reinterpret_cast<const float4 *>(&s_gm[4 * cg]);
+            float4 y;
+            y.x = sigmoid(in.g01.x) * gm.x * o.x * r;
+            y.y = sigmoid(in.g01.y) * gm.y * o.y * r;
+            y.z = sigmoid(in.g23.x) * gm.z * o.z * r;
+            y.w = sigmoid(in.g23.y) * gm.w * o.w * r;
+            Act::store4(p.y, orow, y);
+            if (p.o_raw) *reinterpret_cast<float4 *>(p.o_raw + orow) = o;
+        }
+    };
+
+    // The next pair's inputs are loaded right behind this pair's state loads,
+    // at an in-range index on every path (the last pair repeats its own index
+    // and ignores the values), so that every path issues the same loads and
+    // the compiler's wait counts stay exact.
+    DecodeIn inA, inB;
+    float4 st[Sh::RPT];
+    load_in(unit, inA);
+#pragma unroll 1
+    while (true) {
+        const int n1 = unit + G;
+        issue_state(unit, st);
+        load_in(n1 < P ? n1 : unit, inB);
+        pair_body(unit, inA, st);
+        if (n1 >= P) break;
+        unit = n1;
+        const int n2 = unit + G;
+        issue_state(unit, st);
+        load_in(n2 < P ? n2 : unit, inA);
+        pair_body(unit, inB, st);
+        if (n2 >= P) break;
+        unit = n2;
     }
 }
 
@@ -426,16 +622,49 @@ hipError_t launch_decode_as(const Params &p, bool bf16, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Compute units of each device, read on first use.
+constexpr int STREAM_DEVICES = 64;
+std::atomic<int> g_stream_cus[STREAM_DEVICES];
+
+// Grid of the persistent kernel: one workgroup per compute unit, its size a
+// multiple of H; batches of at most two pairs per compute unit keep one pair
+// per workgroup.  Measured at 64 x 32 (2048 pairs, plain cache policy): 256
+// workgroups of 8 pairs 46.8 us per step, 512 of 4 48.0, 768 of 2 or 3 47.9;
+// grids that leave some workgroups one pair more than others lose the tail
+// (640: 52.0, 384: 52.0).  Prefetching the next pair's state as well (two
+// state register sets) measured slower: 49.1 us at 256 workgroups.
+template <typename Act, bool NT_LOAD, bool NT_STORE>
+hipError_t launch_stream_as(const Params &p, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int cus = dev >= 0 && dev < STREAM_DEVICES ? g_stream_cus[dev].load(std::memory_order_relaxed) : 0;
+    if (cus <= 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (cus <= 0) cus = 1;
+        if (dev >= 0 && dev < STREAM_DEVICES) g_stream_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    const int64_t pairs = (int64_t)p.num_seqs * p.H;
+    int64_t G = pairs;
+    if (pairs > 2 * (int64_t)cus) G = cus >= p.H ? (int64_t)cus / p.H * p.H : p.H;
+    hipLaunchKernelGGL((decode_stream_kernel<Act, NT_LOAD, NT_STORE>), dim3((unsigned)G), dim3(256), 0,
+                       stream, p, (int32_t)G);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-// Nontemporal state traffic wins at every size measured on MI355X.  Up to
-// the Infinity Cache size the interleaved row order is slightly faster; above
-// it the blocked order streams better (6.3 vs 6.0 TB/s at 1 GiB of state).
+// Cache policy of the state: a state that fits comfortably in the 256 MB
+// Infinity Cache (with the window and the step's other rows) stays there
+// from one step to the next under the plain policy; larger ones stream
+// better nontemporally, and above the cache size the blocked row order of
+// the one-pair-per-workgroup kernel streams best (6.3 vs 6.0 TB/s at 1 GiB).
 hipError_t launch_decode(const Params &p, bool bf16, hipStream_t stream) {
     const int64_t state_bytes = (int64_t)p.num_seqs * p.H * (DK * DV * 4);
     if (state_bytes > (int64_t(256) << 20))
         return launch_decode_as<256, true, true, true>(p, bf16, stream);
-    return launch_decode_as<256, true, true, false>(p, bf16, stream);
+    return bf16 ? launch_stream_as<BF16, false, false>(p, stream) : launch_stream_as<F32, false, false>(p, stream);
 }
 
 bool short_supported(int64_t total_tokens, int32_t num_heads) {
