@@ -344,9 +344,13 @@ def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_ptr = ws.data_ptr() if ws_bytes > 0 else None
 
+    import numpy as np
+    cu_host = np.ascontiguousarray(w.cu_seqlens, dtype=np.int32)
+    side = torch.cuda.Stream(device=dev)
+
     def launch():
-        st = L.kda_sequence(ctypes.byref(ccfg), ctypes.byref(t), w.N, cu, order.data_ptr(),
-                            w.total_tokens, ws_ptr, ws_bytes, stream.cuda_stream)
+        st = L.kda_sequence(ctypes.byref(ccfg), ctypes.byref(t), w.N, cu, cu_host.ctypes.data, order.data_ptr(),
+                            w.total_tokens, ws_ptr, ws_bytes, stream.cuda_stream, side.cuda_stream)
         if st != 0:
             raise RuntimeError("kda_sequence returned %d" % st)
     times = []

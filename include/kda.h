@@ -46,26 +46,23 @@
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
  * stream) and the call returns at once.  A kernel fault surfaces at the
- * caller's next synchronisation, as for any HIP launch.  One path (the
- * two-pass prefill of long sequences over at most 32 (sequence, head)
- * pairs) also runs part of its work on a second stream of the library's own,
- * joined to `stream` by events: that work starts after everything enqueued
- * on `stream` before the call, and everything enqueued on `stream` after the
- * call starts after it, exactly as if it ran on `stream`.  `stream` must
- * belong to the current device (the second stream is that device's).
+ * caller's next synchronisation, as for any HIP launch.  kda_sequence may
+ * also use a second stream the caller passes (see there).
  *
- * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED and KDA_ERR_DEVICE mean
- * nothing was enqueued and no buffer was touched, so the caller may run
- * another implementation instead (the pages' fused dispatch checks the return
- * value and falls back to its CPU path: "Metal (Apple GPU) backend for Kimi
- * K3", CPU fallback).  KDA_ERR_LAUNCH means the HIP runtime refused a launch;
- * for a call that enqueues several kernels, the ones before it stay enqueued.
- * The library itself never computes on the CPU.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE and
+ * KDA_ERR_SCRATCH_LIMIT mean nothing was enqueued and no buffer was touched,
+ * so the caller may run another implementation instead (the pages' fused
+ * dispatch checks the return value and falls back to its CPU path: "Metal
+ * (Apple GPU) backend for Kimi K3", CPU fallback).  KDA_ERR_LAUNCH means the
+ * HIP runtime refused a launch; for a call that enqueues several kernels, the
+ * ones before it stay enqueued.  The library itself never computes on the
+ * CPU.
  *
- * Thread safety: stateless apart from a per-device capability cache and, for
- * the path above, the per-device second stream and its events (created on
- * first use, kept until the process ends, enqueued to under a lock); calls
- * on different streams with disjoint buffers may run concurrently.
+ * Thread safety: the library keeps no streams, events or locks between
+ * calls; its only process-wide state is a per-device cache of the device
+ * kind and compute-unit count, and the static scratch of
+ * kda_lowrank_gates_noalloc.  Calls on different streams with disjoint
+ * buffers may run concurrently (the no-allocation call excepted).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -76,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 1
+#define KDA_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -168,16 +165,24 @@ typedef struct kda_tensors {
 
 /*
  * Decode: one token for each of num_seqs sequences (T = num_seqs, token row
- * n belongs to sequence n).  One kernel launch; each (sequence, head) state
- * is read once and written once.  num_seqs == 0 is a no-op that returns
- * KDA_OK after checking cfg (the tensor pointers are not inspected).
- * Equivalent to kda_sequence with every sequence of length 1.
+ * n belongs to sequence n): the whole token step of "Kimi K3 Metal Gap
+ * Analysis", §2 KDA Attention (rows Conv4 + SiLU through O projection), as
+ * "Metal (Apple GPU) backend for Kimi K3", Design notes, "Fused KDA token"
+ * runs it for one token, with the state persisting in place between calls
+ * (Design notes, zero-copy state persistence).  One kernel launch; each
+ * (sequence, head) state is read once and written once.  num_seqs == 0 is a
+ * no-op that returns KDA_OK after checking cfg (the tensor pointers are not
+ * inspected).  Equivalent to kda_sequence with every sequence of length 1.
  */
 kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
                           int32_t num_seqs, void *stream);
 
 /*
- * Prefill: num_seqs sequences packed along the token axis.
+ * Prefill: the same step over num_seqs sequences packed along the token axis,
+ * token by token in order within each sequence ("Kimi K3 Metal Gap
+ * Analysis", §2 KDA Attention; "Metal (Apple GPU) backend for Kimi K3",
+ * table "What runs where": the fused KDA row runs the step once per token,
+ * and Performance: the 13-token prompt prefill goes through it).
  *   cu_seqlens  device int32 [num_seqs + 1] token offsets, or NULL for a
  *               dense batch of num_seqs sequences of total_tokens / num_seqs
  *               tokens each (total_tokens must divide evenly).
@@ -185,12 +190,33 @@ kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
  *               non-decreasing, cu[num_seqs] = total_tokens.  The kernel
  *               clamps every range to [0, total_tokens), so a violation gives
  *               wrong results but no out-of-bounds access.
+ *   cu_seqlens_host  NULL, or a host copy of the same num_seqs + 1 offsets
+ *               (only with a device cu_seqlens).  It is checked: cu[0] = 0,
+ *               non-decreasing and cu[num_seqs] = total_tokens, else
+ *               KDA_ERR_INVALID_ARG and nothing is enqueued.  It must hold
+ *               the device array's values (not checkable).  It lets the
+ *               library plan with the lengths: ragged batches of a few
+ *               sequences then take the segmented two-pass schedule below.
+ *               Not kept after the call.
  *   seq_order   device int32 [num_seqs] or NULL: the order in which sequences
  *               are scheduled (e.g. longest first).  Must be a permutation of
  *               0..num_seqs-1; entries outside that range are skipped.
  *   total_tokens  T, the number of token rows of q, k, v, f, beta, g, y.
  *   workspace, workspace_bytes  optional device scratch (see
  *               kda_sequence_workspace_size); NULL / 0 is always allowed.
+ *   stream      the stream the call is ordered on.
+ *   side_stream NULL, or a second stream of the same device (not `stream`,
+ *               else KDA_ERR_INVALID_ARG).  The two-pass path of long
+ *               sequences over at most 32 (sequence, head) pairs then runs
+ *               the operand passes of later chunk segments and the finished
+ *               segments' RMSNorm + gate on it, beside the state passes on
+ *               `stream`.  The call joins the two with events it creates and
+ *               releases: its work starts after everything enqueued on
+ *               `stream` (and on side_stream) before the call, and
+ *               everything enqueued on `stream` after the call starts after
+ *               all of it; work enqueued on side_stream after the call may
+ *               start before the call's work on `stream` is done.  With NULL
+ *               everything runs on `stream` (same results).
  * Sequences of length 0 leave their state and window unchanged;
  * total_tokens == 0 is a no-op that returns KDA_OK after checking cfg (the
  * tensor pointers, which may then be NULL, are not inspected).  State and
@@ -199,12 +225,13 @@ kda_status kda_token_step(const kda_config *cfg, const kda_tensors *t,
  */
 kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t,
                         int32_t num_seqs, const int32_t *cu_seqlens,
-                        const int32_t *seq_order, int64_t total_tokens,
-                        void *workspace, int64_t workspace_bytes,
-                        void *stream);
+                        const int32_t *cu_seqlens_host, const int32_t *seq_order,
+                        int64_t total_tokens, void *workspace, int64_t workspace_bytes,
+                        void *stream, void *side_stream);
 
 /*
- * Bytes of device workspace with which kda_sequence runs its faster path for
+ * Bytes of device workspace with which kda_sequence (above; same passages)
+ * runs its faster path for
  * this shape (num_seqs sequences, total_tokens token rows, cfg->num_heads
  * heads, cfg->prefill_path); 0 if that path needs none.  A negative value is
  * a kda_status for bad arguments.  SPLIT uses it for its fp32 readout, which
@@ -242,7 +269,9 @@ typedef enum kda_projection {
 
 /*
  * Bytes of workspace for the fastest run of projection `which` (rank is read
- * for KDA_PROJ_LOWRANK_GATES only), or a negative kda_status.
+ * for KDA_PROJ_LOWRANK_GATES only), or a negative kda_status.  The
+ * projections are those of "Kimi K3 Metal Gap Analysis", §2 KDA Attention,
+ * rows "Decay compute" and "O projection" (below).
  */
 int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int32_t hidden,
                                       int32_t rank, int64_t tokens);
@@ -313,15 +342,19 @@ kda_status kda_output_projection(const kda_config *cfg, const void *y, const voi
                                  int32_t hidden, int64_t tokens, void *out,
                                  void *workspace, int64_t workspace_bytes, void *stream);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL).  The codes are the
+ * checked return of the fused dispatch ("Metal (Apple GPU) backend for Kimi
+ * K3", CPU fallback: a failed GPU call falls back instead of misbehaving). */
 const char *kda_status_string(int32_t status);
 
-/* KDA_VERSION of the built library. */
+/* KDA_VERSION of the built library (the interface of this header). */
 int32_t kda_version(void);
 
 /*
  * KDA_OK if the current HIP device is a gfx950 part the library was built
- * for, else KDA_ERR_DEVICE.  Cheap after the first call on a device.
+ * for, else KDA_ERR_DEVICE.  Cheap after the first call on a device.  (The
+ * GPU path is reachable only when a usable device exists: "Metal (Apple GPU)
+ * backend for Kimi K3", CPU fallback.)
  */
 kda_status kda_device_check(void);
 

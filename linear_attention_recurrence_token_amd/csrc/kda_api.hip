@@ -307,9 +307,9 @@ int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs, int
 }
 
 kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
-                        const int32_t *cu_seqlens, const int32_t *seq_order,
-                        int64_t total_tokens, void *workspace, int64_t workspace_bytes,
-                        void *stream) {
+                        const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                        const int32_t *seq_order, int64_t total_tokens, void *workspace,
+                        int64_t workspace_bytes, void *stream, void *side_stream) {
     kda_status st = check_config(cfg, t, num_seqs);
     if (st != KDA_OK) return st;
     if (total_tokens < 0) return KDA_ERR_INVALID_ARG;
@@ -320,6 +320,14 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) ||
         (seq_order && (reinterpret_cast<uintptr_t>(seq_order) & 3u)))
         return KDA_ERR_INVALID_ARG;
+    // the host copy of the offsets, when given, must describe a valid packing
+    if (cu_seqlens_host) {
+        if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
+        if (cu_seqlens_host[0] != 0 || (int64_t)cu_seqlens_host[num_seqs] != total_tokens) return KDA_ERR_INVALID_ARG;
+        for (int32_t n = 0; n < num_seqs; ++n)
+            if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERR_INVALID_ARG;
+    }
+    if (side_stream && side_stream == stream) return KDA_ERR_INVALID_ARG;
     int32_t dense_len = 0;
     if (!cu_seqlens && num_seqs > 0) {
         if (total_tokens % num_seqs != 0) return KDA_ERR_INVALID_ARG;
@@ -370,7 +378,8 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (scan_records)
-        e = kda::launch_prefill_scan(p, bf16, scan_records, scan_obuf, s);
+        e = kda::launch_prefill_scan(p, bf16, scan_records, scan_obuf, s, static_cast<hipStream_t>(side_stream),
+                                     cu_seqlens_host);
     else if (obuf)
         e = kda::launch_prefill_split(p, bf16, obuf, cols, s);
     else if (cfg->prefill_path == KDA_PREFILL_SHORT ||

@@ -72,8 +72,13 @@ hipError_t launch_split_window(const Params &p, bool bf16, hipStream_t stream);
 // of them), then the chunks of each pair in order with its state columns over
 // eight wavefronts, the readout into obuf, then launch_split_finish.  Same gate
 // support as the one-pass chunk kernel.
+// side_stream (may be null) lets long calls of few pairs run the operand
+// passes of later chunk segments beside the state passes of earlier ones;
+// cu_host (may be null) is the host copy of cu_seqlens, which lets ragged
+// batches of a few sequences do the same.
 int64_t prefill_scan_record_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads);
-hipError_t launch_prefill_scan(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream);
+hipError_t launch_prefill_scan(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream,
+                               hipStream_t side_stream, const int32_t *cu_host);
 
 // Matrix products on either side of the step (the low-rank decay and beta
 // projections, the output-gate and output projections):

@@ -23,8 +23,6 @@
 // token 7 keeping every exponential inside e^{+-|lb| C / 2}.
 #include "kda_device.hpp"
 
-#include <mutex>
-
 namespace kda {
 
 namespace {
@@ -566,54 +564,60 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
 // A pair's state pass keeps one workgroup per CU busy (its LDS), so with at
 // most 32 pairs it fills at most half of the 256 CUs, and the operand pass,
 // which has the whole GPU to itself, would otherwise run first and alone.
-// With enough chunks the chunks are cut into segments: segment s + 1's
-// operand pass runs on a second stream, on the idle CUs, while segment s's
-// state pass runs, and each state-pass launch continues from the state the
-// previous one wrote.  The two streams are ordered by events only.
+// With enough chunks, and a second stream from the caller, the chunks are
+// cut into segments: segment s + 1's operand pass runs on the second stream,
+// on the idle CUs, while segment s's state pass runs, and each state-pass
+// launch continues from the state the previous one wrote.  The two streams
+// are ordered by events that the call creates and releases.
 constexpr int SEG_MAX = 4;              // segments at most
 constexpr int SEG_CHUNKS = 128;         // chunks per segment aimed at (at least 2 segments from here)
 constexpr int64_t SEG_MAX_PAIRS = 32;   // state-pass workgroups on at most half the CUs
 
-// chunks of the longest sequence when the host knows it (dense batches, or a
-// single sequence), else 0
-int64_t scan_max_chunks(const Params &p) {
+// chunks of the longest sequence when the host knows it (dense batches, a
+// single sequence, or the caller's host copy of the offsets), else 0
+int64_t scan_max_chunks(const Params &p, const int32_t *cu_host) {
     if (!p.cu_seqlens) return ((int64_t)p.dense_len + CC - 1) / CC;
+    if (cu_host) {
+        int64_t mx = 0;
+        for (int n = 0; n < p.num_seqs; ++n) {
+            const int64_t len = (int64_t)cu_host[n + 1] - cu_host[n];
+            mx = len > mx ? len : mx;
+        }
+        return (mx + CC - 1) / CC;
+    }
     if (p.num_seqs == 1) return (p.total_tokens + CC - 1) / CC;
     return 0;
 }
 
-int scan_segments(const Params &p) {
+// ragged batches of more sequences than this finish with one epilogue launch
+// (a segment's rows are one launch per sequence)
+constexpr int SEG_MAX_RAGGED_SEQS = 8;
+
+int scan_segments(const Params &p, const int32_t *cu_host) {
     const int64_t pairs = (int64_t)p.num_seqs * p.H;
-    const int64_t nc = scan_max_chunks(p);
+    if (p.cu_seqlens && p.num_seqs > 1 && (!cu_host || p.num_seqs > SEG_MAX_RAGGED_SEQS)) return 1;
+    const int64_t nc = scan_max_chunks(p, cu_host);
     if (pairs > SEG_MAX_PAIRS || nc < SEG_CHUNKS) return 1;
     const int64_t s = nc / SEG_CHUNKS;
     return (int)(s < 2 ? 2 : (s < SEG_MAX ? s : SEG_MAX));
 }
 
-// the second stream and its events, one set per device, created on first use
-// and kept for the life of the process; a call holds the lock while it
-// enqueues, so that the events it records are the ones its waits refer to
-struct SideStream {
-    bool tried = false, ok = false;
-    hipStream_t s = nullptr;
+// events ordering the two streams of one call: created by the call, released
+// once enqueued (a recorded event lives until the device has passed it)
+struct CallEvents {
     hipEvent_t ev[2 * SEG_MAX] = {};
-};
-constexpr int SIDE_DEVICES = 64;
-std::mutex g_side_mu;
-SideStream g_side[SIDE_DEVICES];
-
-SideStream *side_stream(int dev) {   // with g_side_mu held
-    if (dev < 0 || dev >= SIDE_DEVICES) return nullptr;
-    SideStream &ss = g_side[dev];
-    if (!ss.tried) {
-        ss.tried = true;
-        ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
-        for (int i = 0; ss.ok && i < 2 * SEG_MAX; ++i)
-            ss.ok = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming) == hipSuccess;
-        if (!ss.ok) (void)hipGetLastError();
+    int n = 0;
+    hipError_t create(int count) {
+        for (n = 0; n < count; ++n) {
+            const hipError_t e = hipEventCreateWithFlags(&ev[n], hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
-    return ss.ok ? &ss : nullptr;
-}
+    ~CallEvents() {
+        for (int i = 0; i < n; ++i) (void)hipEventDestroy(ev[i]);
+    }
+};
 
 template <typename Act>
 hipError_t launch_prep(const Params &p, uint8_t *records, int64_t c_lo, int64_t c_hi, bool whole,
@@ -639,19 +643,9 @@ hipError_t launch_state_pass(const Params &p, const uint8_t *records, float *obu
 }
 
 template <typename Act>
-hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream) {
-    int nseg = scan_segments(p);
-    std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
-    SideStream *side = nullptr;
-    if (nseg > 1) {
-        int dev = -1;
-        lock.lock();
-        if (hipGetDevice(&dev) == hipSuccess) side = side_stream(dev);
-        if (!side) {
-            nseg = 1;
-            lock.unlock();
-        }
-    }
+hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream,
+                          hipStream_t side, const int32_t *cu_host) {
+    const int nseg = side ? scan_segments(p, cu_host) : 1;
     hipError_t e;
     if (nseg == 1) {
         e = launch_prep<Act>(p, records, 0, 0, true, stream);
@@ -659,25 +653,40 @@ hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *o
         if (e == hipSuccess) e = launch_split_finish(p, bf16, obuf, stream);
         return e;
     }
-    const int64_t nc = scan_max_chunks(p);
+    CallEvents events;
+    e = events.create(2 * nseg);
+    if (e != hipSuccess) return e;
+    const int64_t nc = scan_max_chunks(p, cu_host);
     auto bound = [&](int s) { return nc * s / nseg; };
-    // token rows of segment s: tokens [16 bound(s), 16 bound(s + 1)) of every
-    // sequence (all of them dense_len long, or the one sequence)
-    const int64_t len = p.cu_seqlens ? p.total_tokens : p.dense_len;
-    const int32_t nseq = p.cu_seqlens ? 1 : p.num_seqs;
+    // RMSNorm + gate of segment s: tokens [16 bound(s), 16 bound(s + 1)) of
+    // every sequence (the last segment to the end).  Dense batches and a
+    // single sequence take one launch; ragged batches one per sequence.
     auto epilogue = [&](int s, hipStream_t st) {
-        const int64_t t0 = CC * bound(s), t1 = s + 1 < nseg ? CC * bound(s + 1) : len;
-        return launch_split_epilogue(p, bf16, obuf, t0 * p.H, (t1 - t0) * p.H, len * p.H, nseq, st);
+        const int64_t t0 = CC * bound(s), t1 = s + 1 < nseg ? CC * bound(s + 1) : INT64_MAX;
+        if (!p.cu_seqlens || p.num_seqs == 1) {
+            const int64_t len = p.cu_seqlens ? p.total_tokens : p.dense_len;
+            const int32_t nseq = p.cu_seqlens ? 1 : p.num_seqs;
+            const int64_t hi = t1 < len ? t1 : len;
+            return launch_split_epilogue(p, bf16, obuf, t0 * p.H, (hi - t0) * p.H, len * p.H, nseq, st);
+        }
+        hipError_t r = hipSuccess;
+        for (int n = 0; r == hipSuccess && n < p.num_seqs; ++n) {
+            const int64_t len = (int64_t)cu_host[n + 1] - cu_host[n];
+            const int64_t lo = t0 < len ? t0 : len, hi = t1 < len ? t1 : len;
+            if (hi > lo)
+                r = launch_split_epilogue(p, bf16, obuf, ((int64_t)cu_host[n] + lo) * p.H, (hi - lo) * p.H, 0, 1, st);
+        }
+        return r;
     };
-    hipEvent_t *ev = side->ev;   // [0] start, [s] operands of s, [nseg + s] state pass of s, [2 nseg - 1] epilogues
+    hipEvent_t *ev = events.ev;   // [0] start, [s] operands of s, [nseg + s] state pass of s, [2 nseg - 1] epilogues
     // segment 0's operands on the caller's stream; the others on the side
     // stream, after it (and so after the caller's earlier work)
     e = launch_prep<Act>(p, records, 0, bound(1), false, stream);
     if (e == hipSuccess) e = hipEventRecord(ev[0], stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, ev[0], 0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[0], 0);
     for (int s = 1; e == hipSuccess && s < nseg; ++s) {
-        e = launch_prep<Act>(p, records, bound(s), bound(s + 1), false, side->s);
-        if (e == hipSuccess) e = hipEventRecord(ev[s], side->s);
+        e = launch_prep<Act>(p, records, bound(s), bound(s + 1), false, side);
+        if (e == hipSuccess) e = hipEventRecord(ev[s], side);
     }
     // the state passes in order on the caller's stream, each after its operands
     for (int s = 0; e == hipSuccess && s < nseg; ++s) {
@@ -690,10 +699,10 @@ hipError_t launch_scan_as(const Params &p, bool bf16, uint8_t *records, float *o
     // later state passes run; the last segment's and the window (which the
     // first operand pass has read) on the caller's stream, after them
     for (int s = 0; e == hipSuccess && s + 1 < nseg; ++s) {
-        e = hipStreamWaitEvent(side->s, ev[nseg + s], 0);
-        if (e == hipSuccess) e = epilogue(s, side->s);
+        e = hipStreamWaitEvent(side, ev[nseg + s], 0);
+        if (e == hipSuccess) e = epilogue(s, side);
     }
-    if (e == hipSuccess) e = hipEventRecord(ev[2 * nseg - 1], side->s);
+    if (e == hipSuccess) e = hipEventRecord(ev[2 * nseg - 1], side);
     if (e == hipSuccess) e = epilogue(nseg - 1, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(stream, ev[2 * nseg - 1], 0);
     if (e == hipSuccess) e = launch_split_window(p, bf16, stream);
@@ -706,9 +715,10 @@ int64_t prefill_scan_record_bytes(int64_t total_tokens, int32_t num_seqs, int32_
     return (total_tokens / CC + num_seqs) * num_heads * (int64_t)REC;
 }
 
-hipError_t launch_prefill_scan(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream) {
-    return bf16 ? launch_scan_as<BF16>(p, true, records, obuf, stream)
-                : launch_scan_as<F32>(p, false, records, obuf, stream);
+hipError_t launch_prefill_scan(const Params &p, bool bf16, uint8_t *records, float *obuf, hipStream_t stream,
+                               hipStream_t side_stream, const int32_t *cu_host) {
+    return bf16 ? launch_scan_as<BF16>(p, true, records, obuf, stream, side_stream, cu_host)
+                : launch_scan_as<F32>(p, false, records, obuf, stream, side_stream, cu_host);
 }
 
 }  // namespace kda

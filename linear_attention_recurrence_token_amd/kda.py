@@ -78,8 +78,8 @@ def lib() -> ctypes.CDLL:
             L.kda_token_step.argtypes = [cfgp, tp, ctypes.c_int32, ctypes.c_void_p]
             L.kda_sequence.restype = ctypes.c_int32
             L.kda_sequence.argtypes = [cfgp, tp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
-                                       ctypes.c_void_p]
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p]
             L.kda_sequence_workspace_size.restype = ctypes.c_int64
             L.kda_sequence_workspace_size.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int64]
             L.kda_status_string.restype = ctypes.c_char_p
@@ -193,16 +193,22 @@ def kda_token_step(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_
 
 
 def kda_sequence(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bias, gamma,
-                 state, conv_win, y, o_raw=None, cu_seqlens=None, seq_order=None,
-                 num_seqs: Optional[int] = None, workspace="auto", stream=None,
+                 state, conv_win, y, o_raw=None, cu_seqlens=None, cu_seqlens_host=None, seq_order=None,
+                 num_seqs: Optional[int] = None, workspace="auto", stream=None, side_stream=None,
                  check: bool = True) -> None:
     """Prefill over packed sequences (C: kda_sequence).
 
     cu_seqlens: int32 GPU tensor [N+1] of token offsets, or None for a dense
-    batch (N = state.shape[0] sequences of T / N tokens).  seq_order: optional
+    batch (N = state.shape[0] sequences of T / N tokens).  cu_seqlens_host:
+    optional host copy of the same offsets (a CPU int32 tensor or numpy
+    array; the library checks it and may plan with it).  seq_order: optional
     int32 GPU tensor [N], the scheduling order of the sequences.  workspace:
     "auto" allocates (through torch) the scratch the faster path can use, as
-    kda_sequence_workspace_size reports; None passes none; or a GPU tensor."""
+    kda_sequence_workspace_size reports; None passes none; or a GPU tensor.
+    side_stream: optional second torch stream on the same device, on which
+    the two-pass path may overlap part of its work (the call is still ordered
+    on `stream` as one unit)."""
+    import numpy as np
     import torch
     ts = dict(q=q, k=k, v=v, f=f, beta=beta, g=g, conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
               gamma=gamma, state=state, conv_win=conv_win, y=y, o_raw=o_raw)
@@ -215,6 +221,11 @@ def kda_sequence(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bi
                 continue
             if not a.is_cuda or a.dtype != torch.int32 or tuple(a.shape) != (n,) or not a.is_contiguous():
                 raise ValueError("%s must be a contiguous int32 GPU tensor of shape (%d,)" % (name, n))
+    host = None
+    if cu_seqlens_host is not None:
+        host = np.ascontiguousarray(np.asarray(cu_seqlens_host), dtype=np.int32)
+        if host.shape != (N + 1,):
+            raise ValueError("cu_seqlens_host must have shape (%d,)" % (N + 1))
     c = config.to_c()
     t = _tensors_struct(ts)
     ws_ptr, ws_bytes = None, 0
@@ -230,8 +241,10 @@ def kda_sequence(config: KdaConfig, *, q, k, v, f, beta, g, conv_w, A_log, dt_bi
             workspace = None
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    st = lib().kda_sequence(ctypes.byref(c), ctypes.byref(t), N, _ptr(cu_seqlens), _ptr(seq_order),
-                            T, ws_ptr, ws_bytes, _stream_handle(stream))
+    st = lib().kda_sequence(ctypes.byref(c), ctypes.byref(t), N, _ptr(cu_seqlens),
+                            host.ctypes.data if host is not None else None, _ptr(seq_order), T,
+                            ws_ptr, ws_bytes, _stream_handle(stream),
+                            _stream_handle(side_stream) if side_stream is not None else None)
     if st != KDA_OK:
         raise KdaError(st, "kda_sequence")
 

@@ -32,12 +32,19 @@ PATHS = {"fused": kda.KDA_PREFILL_FUSED, "split": kda.KDA_PREFILL_SPLIT, "auto":
          "chunk": kda.KDA_PREFILL_CHUNK, "short": kda.KDA_PREFILL_SHORT, "scan": kda.KDA_PREFILL_SCAN}
 
 
-def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, path="auto"):
+def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, path="auto", side_stream=False,
+                 cu_host=False):
+    """One kda_sequence call; side_stream: pass a second stream (the two-pass
+    path may then run in segments); cu_host: pass the host copy of the
+    offsets too."""
     import torch
     d = synth.to_device(w, dev, with_o_raw=with_o_raw)
     order = None if seq_order is None else torch.as_tensor(np.asarray(seq_order, np.int32), device=dev)
+    side = torch.cuda.Stream(device=dev) if side_stream else None
     kda.kda_sequence(cfg_of(w, prefill_path=PATHS[path]), **tensors(d),
-                     cu_seqlens=None if dense else d["cu_seqlens"], seq_order=order, num_seqs=w.N)
+                     cu_seqlens=None if dense else d["cu_seqlens"],
+                     cu_seqlens_host=w.cu_seqlens.astype(np.int32) if (cu_host and not dense) else None,
+                     seq_order=order, num_seqs=w.N, side_stream=side)
     torch.cuda.synchronize()
     out = {"y": _np(d["y"]), "state": _np(d["state"]), "win": d["conv_win"].cpu().numpy()}
     out["o_raw"] = _np(d["o_raw"]) if with_o_raw else None

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 1
+    assert lib.kda_version() == 2
     for st in (0, -1, -2, -3, -4, -5):
         s = kda.status_string(st)
         assert s and s != "unknown status"
@@ -70,8 +70,10 @@ def _step(lib, cfg, t, n=2):
     return lib.kda_token_step(ctypes.byref(cfg), ctypes.byref(t), n, None)
 
 
-def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8, ws=None, ws_bytes=0):
-    return lib.kda_sequence(ctypes.byref(cfg), ctypes.byref(t), n, cu, order, total, ws, ws_bytes, None)
+def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8, ws=None, ws_bytes=0, cu_host=None, stream=None,
+         side=None):
+    return lib.kda_sequence(ctypes.byref(cfg), ctypes.byref(t), n, cu, cu_host, order, total, ws, ws_bytes, stream,
+                            side)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -366,3 +368,40 @@ def test_lowrank_gates_noalloc_limit_and_no_device(lib):
     # exactly the scratch size is allowed: the call gets as far as the device check
     assert _lowrank_na(lib, tokens=32768, rank=128) == kda.KDA_ERR_DEVICE
     assert _lowrank_na(lib) == kda.KDA_ERR_DEVICE
+
+
+# --- the host copy of the offsets and the second stream -------------------------
+
+def _host(vals):
+    a = (ctypes.c_int32 * len(vals))(*vals)
+    return a, ctypes.cast(a, ctypes.c_void_p).value
+
+
+@pytest.mark.parametrize("vals,status", [
+    ([0, 3, 8], None),                      # valid: gets as far as the device check
+    ([1, 3, 8], kda.KDA_ERR_INVALID_ARG),   # cu[0] != 0
+    ([0, 5, 3], kda.KDA_ERR_INVALID_ARG),   # decreasing
+    ([0, 3, 7], kda.KDA_ERR_INVALID_ARG),   # does not end at total_tokens
+    ([0, 8, 8], None),                      # an empty last sequence is fine
+])
+def test_sequence_checks_the_host_offsets(lib, vals, status):
+    keep, ptr = _host(vals)
+    st = _seq(lib, _cfg(), _fake_tensors(), n=2, cu=(1 << 42), total=8, cu_host=ptr)
+    if status is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return
+        except ImportError:
+            pass
+        assert st == kda.KDA_ERR_DEVICE
+    else:
+        assert st == status
+
+
+def test_sequence_host_offsets_need_the_device_array_and_streams_differ(lib):
+    keep, ptr = _host([0, 4, 8])
+    # a host copy without the device array (a dense batch) is refused
+    assert _seq(lib, _cfg(), _fake_tensors(), n=2, cu=None, total=8, cu_host=ptr) == kda.KDA_ERR_INVALID_ARG
+    # the second stream may not be the call's own stream
+    assert _seq(lib, _cfg(), _fake_tensors(), n=2, total=8, stream=1 << 20, side=1 << 20) == kda.KDA_ERR_INVALID_ARG

@@ -280,22 +280,66 @@ def test_scan_segments_long_sequences(gpu, N, H, T, act, dense, path):
     w = synth.make_workload("segments", seed=300 + T, N=N, H=H, lengths=[T] * N, act_dtype=act,
                             state_std=0.02, win_std=1.0)
     note("two-pass segments %dx%dx%d %s dense=%s %s" % (N, H, T, act, dense, path))
-    a = _gpu.run_sequence(w, gpu, dense=dense, path=path)
+    a = _gpu.run_sequence(w, gpu, dense=dense, path=path, side_stream=True)
     _gpu.assert_parity(a, _gpu.oracle_sequence(w), bf16=act == "bf16", label="segments T=%d" % T)
-    b = _gpu.run_sequence(w, gpu, dense=dense, path=path)
+    b = _gpu.run_sequence(w, gpu, dense=dense, path=path, side_stream=True)
     for k in ("y", "o_raw", "state", "win"):
         np.testing.assert_array_equal(a[k], b[k])
+    # one launch per pass (no second stream): the same arithmetic
+    one = _gpu.run_sequence(w, gpu, dense=dense, path=path)
+    for k in ("y", "o_raw", "state", "win"):
+        np.testing.assert_array_equal(one[k], a[k])
     # without o_raw the readout lives in the workspace after the chunk records,
     # where the segments' RMSNorm + gate read it
-    c = _gpu.run_sequence(w, gpu, dense=dense, path=path, with_o_raw=False)
+    c = _gpu.run_sequence(w, gpu, dense=dense, path=path, with_o_raw=False, side_stream=True)
     for k in ("y", "state", "win"):
         np.testing.assert_array_equal(c[k], a[k])
     if N > 1:
         # the state passes take pairs in the scheduling order, the operand
         # passes in natural order: the result does not depend on the order
-        r = _gpu.run_sequence(w, gpu, dense=dense, path=path, seq_order=list(range(N))[::-1])
+        r = _gpu.run_sequence(w, gpu, dense=dense, path=path, seq_order=list(range(N))[::-1], side_stream=True)
         for k in ("y", "o_raw", "state", "win"):
             np.testing.assert_array_equal(r[k], a[k])
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_scan_segments_ragged_few_sequences(gpu, act):
+    # a ragged batch of three sequences (12 pairs, the longest 194 chunks):
+    # with the host copy of the offsets and a second stream the two-pass path
+    # runs in segments, each segment's RMSNorm + gate one launch per sequence;
+    # every element against the oracle, and equal to the unsegmented call
+    w = synth.make_workload("ragged segments", seed=77, N=3, H=4, lengths=[3100, 40, 2600], act_dtype=act,
+                            state_std=0.02, win_std=1.0)
+    note("two-pass segments, ragged 3 sequences x 4 heads %s" % act)
+    a = _gpu.run_sequence(w, gpu, side_stream=True, cu_host=True)
+    _gpu.assert_parity(a, _gpu.oracle_sequence(w), bf16=act == "bf16", label="ragged segments")
+    for kw in ({}, {"cu_host": True}, {"side_stream": True}):
+        b = _gpu.run_sequence(w, gpu, **kw)
+        for k in ("y", "o_raw", "state", "win"):
+            np.testing.assert_array_equal(b[k], a[k], err_msg="%s %s" % (kw, k))
+
+
+def test_scan_calls_on_two_streams(gpu):
+    # two independent two-pass calls (disjoint buffers) enqueued on two
+    # streams, each with a second stream of its own, running concurrently;
+    # both against the oracle
+    import torch
+    ws = [synth.make_workload("two streams %d" % i, seed=90 + i, N=1, H=8, lengths=[2300 + 500 * i],
+                              state_std=0.02, win_std=1.0) for i in range(2)]
+    note("two scan-path calls on two streams")
+    ds = [synth.to_device(w, gpu) for w in ws]
+    streams = [torch.cuda.Stream(device=gpu) for _ in ws]
+    sides = [torch.cuda.Stream(device=gpu) for _ in ws]
+    torch.cuda.synchronize()
+    for w, d, st, sd in zip(ws, ds, streams, sides):
+        kda.kda_sequence(_gpu.cfg_of(w, prefill_path=kda.KDA_PREFILL_SCAN), **_gpu.tensors(d),
+                         cu_seqlens=d["cu_seqlens"], cu_seqlens_host=w.cu_seqlens.astype(np.int32), num_seqs=w.N,
+                         stream=st, side_stream=sd)
+    torch.cuda.synchronize()
+    for w, d in zip(ws, ds):
+        got = {"y": _gpu._np(d["y"]), "o_raw": _gpu._np(d["o_raw"]), "state": _gpu._np(d["state"]),
+               "win": d["conv_win"].cpu().numpy()}
+        _gpu.assert_parity(got, _gpu.oracle_sequence(w), label=w.name)
 
 
 def test_empty_calls_are_noops(gpu):
