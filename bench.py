@@ -543,6 +543,93 @@ def bench_projections(torch, kda, synth, dev, idx, runs, only=None):
     return res
 
 
+def bench_layer(torch, kda, synth, dev, runs):
+    """The KDA layer around the step at 16 x 64 x 2048 (bf16, hidden 8192,
+    rank 128), timed end to end: the low-rank decay and beta products, the
+    output-gate product W_g x, the step, and the output product W_o y.  Two
+    forms: f through memory (kda_lowrank_gates, then kda_sequence) and f formed
+    in the step (kda_lowrank_factor, then kda_sequence_lowrank)."""
+    import numpy as np
+    w = synth.workload(3)
+    p = synth.projection_workload(3)
+    d = synth.to_device(w, dev, with_o_raw=False)
+    state0, win0 = d["state"].clone(), d["conv_win"].clone()
+    T, H, D, r = p.T, p.H, p.D, p.r
+    cfg = kda.KdaConfig(num_heads=H, act_dtype=kda.KDA_BF16)
+    x = torch.from_numpy(p.x).to(dev).to(torch.bfloat16)
+    wab = torch.from_numpy(np.concatenate([p.w_fa, p.w_bp])).to(dev)
+    wfb = torch.from_numpy(p.w_fb).to(dev)
+    wg = torch.from_numpy(p.w_g).to(dev).to(torch.bfloat16)
+    wo = torch.from_numpy(p.w_o).to(dev).to(torch.bfloat16)
+    out = torch.empty(T, D, device=dev, dtype=torch.bfloat16)
+    a = torch.empty(T, r, device=dev)
+    g = d["g"].view(T, H * 128)
+    stream = torch.cuda.current_stream()
+    L = kda.lib()
+    ccfg = cfg.to_c()
+    sh = stream.cuda_stream
+
+    def ws(which, rank=0):
+        n = kda.projection_workspace_size(cfg, which, D, T, rank)
+        return (torch.empty(n, dtype=torch.uint8, device=dev), n) if n > 0 else (None, 0)
+    ws_lr, n_lr = ws(kda.KDA_PROJ_LOWRANK_GATES, r)
+    ws_fa, n_fa = ws(kda.KDA_PROJ_LOWRANK_FACTOR, r)
+    ws_g, n_g = ws(kda.KDA_PROJ_GATE)
+    ws_o, n_o = ws(kda.KDA_PROJ_OUTPUT)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    t_sep = kda.kda_tensors(*[(d[n].data_ptr() if d.get(n) is not None else None) for n in kda.TENSOR_FIELDS])
+    t_lr = kda.kda_tensors(*[(d[n].data_ptr() if (d.get(n) is not None and n != "f") else None)
+                             for n in kda.TENSOR_FIELDS])
+    cu = d["cu_seqlens"].data_ptr()
+
+    def chk(st, what):
+        if st != 0:
+            raise RuntimeError("%s returned %d" % (what, st))
+    parts = {
+        "lowrank_gates": lambda: chk(L.kda_lowrank_gates(ctypes.byref(ccfg), x.data_ptr(), wab.data_ptr(),
+                                                         wfb.data_ptr(), D, r, T, d["f"].data_ptr(),
+                                                         d["beta"].data_ptr(), ptr(ws_lr), n_lr, sh), "lowrank"),
+        "lowrank_factor": lambda: chk(L.kda_lowrank_factor(ctypes.byref(ccfg), x.data_ptr(), wab.data_ptr(), D, r,
+                                                           T, a.data_ptr(), d["beta"].data_ptr(), ptr(ws_fa), n_fa,
+                                                           sh), "factor"),
+        "gate_projection": lambda: chk(L.kda_gate_projection(ctypes.byref(ccfg), x.data_ptr(), wg.data_ptr(), D, T,
+                                                             g.data_ptr(), ptr(ws_g), n_g, sh), "gate"),
+        "step": lambda: chk(L.kda_sequence(ctypes.byref(ccfg), ctypes.byref(t_sep), w.N, cu, None, None, T, None, 0,
+                                           sh, None), "sequence"),
+        "step_lowrank": lambda: chk(L.kda_sequence_lowrank(ctypes.byref(ccfg), ctypes.byref(t_lr), w.N, cu, None,
+                                                           None, T, a.data_ptr(), wfb.data_ptr(), r, sh),
+                                    "sequence_lowrank"),
+        "output_projection": lambda: chk(L.kda_output_projection(ctypes.byref(ccfg), d["y"].data_ptr(), wo.data_ptr(),
+                                                                 D, T, out.data_ptr(), ptr(ws_o), n_o, sh), "out"),
+    }
+    forms = {"f_through_memory": ["lowrank_gates", "gate_projection", "step", "output_projection"],
+             "f_in_step": ["lowrank_factor", "gate_projection", "step_lowrank", "output_projection"]}
+
+    def timed(names):
+        times = []
+        for rep in range(runs + 1):
+            d["state"].copy_(state0)
+            d["conv_win"].copy_(win0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for n in names:
+                parts[n]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+    res = {"workload": "KDA layer 16 x 64 x 2048 bf16, hidden 8192, rank 128 (synthetic weights)",
+           "token_heads": T * H, "parts_ms": {n: timed([n]) for n in parts}}
+    for form, names in forms.items():
+        ms = timed(names)
+        res[form] = {"ms": ms, "parts": names, "value": T * H / (ms * 1e-3), "unit": UNIT}
+    res["f_round_trip_bytes_removed"] = 2 * T * H * 128 * 4
+    del d, state0, win0, x, wab, wfb, wg, wo, out, a
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -604,6 +691,8 @@ def main():
             parts = args.only.split(":")
             out.update(bench_projections(torch, kda, synth, dev, int(parts[1]), args.prefill_runs,
                                          parts[2] if len(parts) > 2 else None))
+        elif args.only == "layer":
+            out.update(bench_layer(torch, kda, synth, dev, args.prefill_runs))
         elif args.only.startswith("prefill:"):
             idx = int(args.only.split(":")[1])
             r = bench_prefill(torch, kda, synth, dev, synth.workload(idx), args.prefill_runs,
@@ -711,6 +800,9 @@ def main():
             del w
 
     if args.projections != "none":
+        log("layer 16x64x2048: projections and step end to end")
+        result["layer"] = bench_layer(torch, kda, synth, dev, args.prefill_runs)
+        log("layer: %s" % result["layer"])
         result["projections"] = []
         for idx in ([1, 3] if args.projections == "default" else [1, 2, 3]):
             log("projections for workload %d" % idx)

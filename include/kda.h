@@ -230,6 +230,29 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t,
                         void *stream, void *side_stream);
 
 /*
+ * Prefill with the decay pre-activation formed inside the step from the
+ * low-rank factor: f[t, h, i] = sum_j w_fb[h * 128 + i, j] a[t, j] ("Kimi K3
+ * Metal Gap Analysis", §2 KDA Attention, row "Decay compute": the decay is
+ * formed from W_fb W_fa x), so f never goes through memory.  Everything else
+ * as kda_sequence, with t->f NULL (else KDA_ERR_INVALID_ARG) and:
+ *   a      [total_tokens, rank] fp32, device, 16-byte aligned: W_fa x of each
+ *          token row (kda_lowrank_factor); read-only
+ *   w_fb   [H * 128, rank] fp32, device, 16-byte aligned; read-only
+ *   rank   a multiple of 32 up to 128 (above: KDA_ERR_UNSUPPORTED; use
+ *          kda_lowrank_gates and kda_sequence)
+ * It runs the one-pass chunk kernel (cfg->prefill_path AUTO or CHUNK, else
+ * KDA_ERR_UNSUPPORTED), so it has the chunk form's gate rule (bounded gate,
+ * |lb| <= 7.5, else KDA_ERR_UNSUPPORTED) and needs no workspace.  f is a
+ * split-bf16 matrix-core product in the step (about 2^-16 relative error,
+ * fp32 sums): the results agree with kda_lowrank_gates + kda_sequence within
+ * the step's tolerance, not bit for bit.
+ */
+kda_status kda_sequence_lowrank(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
+                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                const int32_t *seq_order, int64_t total_tokens, const float *a,
+                                const float *w_fb, int32_t rank, void *stream);
+
+/*
  * Bytes of device workspace with which kda_sequence (above; same passages)
  * runs its faster path for
  * this shape (num_seqs sequences, total_tokens token rows, cfg->num_heads
@@ -264,7 +287,8 @@ int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs,
 typedef enum kda_projection {
     KDA_PROJ_LOWRANK_GATES = 0,  /* kda_lowrank_gates     */
     KDA_PROJ_GATE = 1,           /* kda_gate_projection   */
-    KDA_PROJ_OUTPUT = 2          /* kda_output_projection */
+    KDA_PROJ_OUTPUT = 2,         /* kda_output_projection */
+    KDA_PROJ_LOWRANK_FACTOR = 3  /* kda_lowrank_factor    */
 } kda_projection;
 
 /*
@@ -300,6 +324,20 @@ kda_status kda_lowrank_gates(const kda_config *cfg, const void *x, const float *
                              const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
                              float *f, float *beta, void *workspace, int64_t workspace_bytes,
                              void *stream);
+
+/*
+ * The first low-rank product alone, for kda_sequence_lowrank: for each token
+ * row t, a[t] = W_fa x[t] (rank values, fp32) and beta[t, h] =
+ * sigmoid(W_bp[h] . x[t]) (Gap Analysis §2, row "Decay compute"; PR table
+ * "What runs where", KDA low-rank fa, fb, bp).  Arguments as for
+ * kda_lowrank_gates, with a [tokens, rank] fp32 out in place of f; workspace
+ * optional (with the bytes kda_projection_workspace_size reports for
+ * KDA_PROJ_LOWRANK_FACTOR the weights are split into bf16 parts once and few
+ * token rows split their sums; results equal).
+ */
+kda_status kda_lowrank_factor(const kda_config *cfg, const void *x, const float *w_fa_bp, int32_t hidden,
+                              int32_t rank, int64_t tokens, float *a, float *beta, void *workspace,
+                              int64_t workspace_bytes, void *stream);
 
 /*
  * kda_lowrank_gates without a workspace, for callers that cannot allocate

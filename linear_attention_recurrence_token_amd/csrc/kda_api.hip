@@ -252,6 +252,7 @@ kda::Params make_params(const kda_config *cfg, const kda_tensors *t, int32_t num
     p.total_tokens = 0; p.num_seqs = num_seqs; p.H = cfg->num_heads; p.dense_len = 0;
     p.gate_mode = cfg->gate_mode;
     p.lb = cfg->gate_lower_bound; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
+    p.lr_a = nullptr; p.lr_wfb = nullptr; p.lr_rank = 0;
     return p;
 }
 
@@ -306,6 +307,38 @@ int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs, int
     return readout_bytes(cfg, total_tokens);
 }
 
+}  // extern "C"
+
+namespace {
+// the checks kda_sequence and kda_sequence_lowrank share, after the tensors':
+// offsets (device alignment, the host copy), the dense length, sizes
+kda_status check_packing(const kda_config *cfg, int32_t num_seqs, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, const int32_t *seq_order, int64_t total_tokens,
+                         int32_t *dense_len) {
+    if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) ||
+        (seq_order && (reinterpret_cast<uintptr_t>(seq_order) & 3u)))
+        return KDA_ERR_INVALID_ARG;
+    // the host copy of the offsets, when given, must describe a valid packing
+    if (cu_seqlens_host) {
+        if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
+        if (cu_seqlens_host[0] != 0 || (int64_t)cu_seqlens_host[num_seqs] != total_tokens) return KDA_ERR_INVALID_ARG;
+        for (int32_t n = 0; n < num_seqs; ++n)
+            if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERR_INVALID_ARG;
+    }
+    *dense_len = 0;
+    if (!cu_seqlens && num_seqs > 0) {
+        if (total_tokens % num_seqs != 0) return KDA_ERR_INVALID_ARG;
+        if (total_tokens / num_seqs > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+        *dense_len = (int32_t)(total_tokens / num_seqs);
+    }
+    // row offsets are formed in 64-bit arithmetic; keep them well inside it
+    if (total_tokens > (int64_t(1) << 40) / ((int64_t)cfg->num_heads * kda::DK)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
 kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                         const int32_t *seq_order, int64_t total_tokens, void *workspace,
@@ -317,25 +350,10 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (total_tokens == 0) return KDA_OK; // every sequence is empty; pointers are not inspected
     st = check_tensors(cfg, t, num_seqs);
     if (st != KDA_OK) return st;
-    if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) ||
-        (seq_order && (reinterpret_cast<uintptr_t>(seq_order) & 3u)))
-        return KDA_ERR_INVALID_ARG;
-    // the host copy of the offsets, when given, must describe a valid packing
-    if (cu_seqlens_host) {
-        if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
-        if (cu_seqlens_host[0] != 0 || (int64_t)cu_seqlens_host[num_seqs] != total_tokens) return KDA_ERR_INVALID_ARG;
-        for (int32_t n = 0; n < num_seqs; ++n)
-            if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERR_INVALID_ARG;
-    }
-    if (side_stream && side_stream == stream) return KDA_ERR_INVALID_ARG;
     int32_t dense_len = 0;
-    if (!cu_seqlens && num_seqs > 0) {
-        if (total_tokens % num_seqs != 0) return KDA_ERR_INVALID_ARG;
-        if (total_tokens / num_seqs > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
-        dense_len = (int32_t)(total_tokens / num_seqs);
-    }
-    // row offsets are formed in 64-bit arithmetic; keep them well inside it
-    if (total_tokens > (int64_t(1) << 40) / ((int64_t)cfg->num_heads * kda::DK)) return KDA_ERR_INVALID_ARG;
+    st = check_packing(cfg, num_seqs, cu_seqlens, cu_seqlens_host, seq_order, total_tokens, &dense_len);
+    if (st != KDA_OK) return st;
+    if (side_stream && side_stream == stream) return KDA_ERR_INVALID_ARG;
     if (workspace_bytes < 0 || (workspace && !aligned16(workspace))) return KDA_ERR_INVALID_ARG;
     // the readout buffer of the split path: o_raw, else a large enough workspace
     const int cols = split_cols_for(cfg, num_seqs, total_tokens);
@@ -393,6 +411,47 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status kda_sequence_lowrank(const kda_config *cfg, const kda_tensors *t, int32_t num_seqs,
+                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                const int32_t *seq_order, int64_t total_tokens, const float *a,
+                                const float *w_fb, int32_t rank, void *stream) {
+    kda_status st = check_config(cfg, t, num_seqs);
+    if (st != KDA_OK) return st;
+    if (total_tokens < 0 || (num_seqs == 0 && total_tokens != 0)) return KDA_ERR_INVALID_ARG;
+    if (rank < 32 || rank % 32 != 0) return KDA_ERR_INVALID_ARG;
+    if (rank > kda::LOWRANK_MAX_RANK) return KDA_ERR_UNSUPPORTED;
+    if (cfg->prefill_path != KDA_PREFILL_AUTO && cfg->prefill_path != KDA_PREFILL_CHUNK) return KDA_ERR_UNSUPPORTED;
+    if (!chunk_supported(cfg)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens == 0) return KDA_OK;
+    if (t->f) return KDA_ERR_INVALID_ARG;          // f is formed in the step
+    // the tensors' checks with a in the place of f, then w_fb like an input
+    kda_tensors tt = *t;
+    tt.f = a;
+    st = check_tensors(cfg, &tt, num_seqs);
+    if (st != KDA_OK) return st;
+    if (!w_fb || !aligned16(w_fb)) return KDA_ERR_INVALID_ARG;
+    for (const void *o : {(const void *)t->state, (const void *)t->conv_win, (const void *)t->y,
+                          (const void *)t->o_raw})
+        if (o == w_fb) return KDA_ERR_INVALID_ARG;
+    int32_t dense_len = 0;
+    st = check_packing(cfg, num_seqs, cu_seqlens, cu_seqlens_host, seq_order, total_tokens, &dense_len);
+    if (st != KDA_OK) return st;
+    st = device_ok();
+    if (st != KDA_OK) return st;
+    kda::Params p = make_params(cfg, t, num_seqs);
+    p.f = nullptr;
+    p.cu_seqlens = cu_seqlens;
+    p.seq_order = seq_order;
+    p.total_tokens = total_tokens;
+    p.dense_len = dense_len;
+    p.lr_a = a;
+    p.lr_wfb = w_fb;
+    p.lr_rank = rank;
+    const hipError_t e = kda::launch_prefill_chunk_lowrank(p, cfg->act_dtype == KDA_BF16,
+                                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int32_t hidden,
                                       int32_t rank, int64_t tokens) {
     const kda_status st = check_proj_config(cfg);
@@ -412,6 +471,17 @@ int64_t kda_projection_workspace_size(const kda_config *cfg, int32_t which, int3
         }
         const int64_t scratch = std::max(kda::proj_gemm_scratch_bytes(g1), kda::proj_gemm_scratch_bytes(g2));
         return round_up(tokens * rank * 4, WS_ALIGN) + planes + scratch;
+    }
+    if (which == KDA_PROJ_LOWRANK_FACTOR) {
+        if (rank < 32 || rank > PROJ_MAX_RANK || rank % 32 != 0 || hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
+        kda::ProjGemm g1, g2;
+        lowrank_products(cfg, nullptr, nullptr, nullptr, hidden, rank, tokens, nullptr, nullptr, nullptr, g1, g2);
+        int64_t planes = 0;
+        if (tokens >= LOWRANK_PRESPLIT_MIN_TOKENS) {
+            g1.b_presplit = true;
+            planes = lowrank_planes_bytes(cfg->num_heads, rank, hidden);
+        }
+        return planes + kda::proj_gemm_scratch_bytes(g1);
     }
     if (which == KDA_PROJ_GATE) {
         if (hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
@@ -509,6 +579,51 @@ kda_status kda_lowrank_gates_noalloc(const kda_config *cfg, const void *x, const
                                      const float *w_fb, int32_t hidden, int32_t rank, int64_t tokens,
                                      float *f, float *beta, void *stream) {
     return lowrank_gates_impl(cfg, x, w_fa_bp, w_fb, hidden, rank, tokens, f, beta, nullptr, 0, stream, true);
+}
+
+kda_status kda_lowrank_factor(const kda_config *cfg, const void *x, const float *w_fa_bp, int32_t hidden,
+                              int32_t rank, int64_t tokens, float *a, float *beta, void *workspace,
+                              int64_t workspace_bytes, void *stream) {
+    kda_status st = check_proj_config(cfg);
+    if (st != KDA_OK) return st;
+    if (hidden <= 0 || hidden > PROJ_MAX_HIDDEN || hidden % 32 != 0) return KDA_ERR_INVALID_ARG;
+    if (rank < 32 || rank > PROJ_MAX_RANK || rank % 32 != 0) return KDA_ERR_INVALID_ARG;
+    if (tokens < 0 || tokens > PROJ_MAX_TOKENS || workspace_bytes < 0) return KDA_ERR_INVALID_ARG;
+    if (tokens == 0) return KDA_OK;       // pointers are not inspected
+    if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
+    const int32_t H = cfg->num_heads;
+    const int64_t eb = cfg->act_dtype == KDA_BF16 ? 2 : 4;
+    const Span ins[] = {{x, tokens * hidden * eb}, {w_fa_bp, (int64_t)(rank + H) * hidden * 4}};
+    const Span outs[] = {{a, tokens * rank * 4}, {workspace, workspace ? workspace_bytes : 0}};
+    st = check_spans(ins, 2, outs, workspace ? 2 : 1);
+    if (st != KDA_OK) return st;
+    const Span bs = {beta, tokens * H * 4};
+    if (!beta || (reinterpret_cast<uintptr_t>(beta) & 3u)) return KDA_ERR_INVALID_ARG;
+    for (const Span &o : ins)
+        if (overlap(bs, o)) return KDA_ERR_INVALID_ARG;
+    for (int o = 0; o < (workspace ? 2 : 1); ++o)
+        if (overlap(bs, outs[o])) return KDA_ERR_INVALID_ARG;
+    kda::ProjGemm g1, g2;
+    lowrank_products(cfg, x, w_fa_bp, nullptr, hidden, rank, tokens, nullptr, beta, a, g1, g2);
+    if (!kda::proj_gemm_shape_ok(g1)) return KDA_ERR_INVALID_ARG;
+    st = device_ok();
+    if (st != KDA_OK) return st;
+    const int64_t planes = lowrank_planes_bytes(H, rank, hidden);
+    uint16_t *wparts = nullptr;
+    int64_t used = 0;
+    if (tokens >= LOWRANK_PRESPLIT_MIN_TOKENS && workspace && workspace_bytes >= planes) {
+        wparts = static_cast<uint16_t *>(workspace);
+        g1.B = wparts;
+        g1.b_presplit = true;
+        used = planes;
+    }
+    const int64_t scratch_bytes = workspace ? workspace_bytes - used : 0;
+    float *scratch_f = scratch_bytes > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + used) : nullptr;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (wparts) e = kda::launch_split_planes(w_fa_bp, wparts, (int64_t)(rank + H) * hidden, s);
+    if (e == hipSuccess) e = kda::launch_proj_gemm(g1, scratch_f, scratch_bytes, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 namespace {

@@ -31,6 +31,10 @@ struct Params {
     int32_t dense_len;           // tokens per sequence when cu_seqlens is null
     int32_t gate_mode;
     float lb, l2_eps, rms_eps;
+    // the low-rank decay form (kda_sequence_lowrank): f = W_fb a formed in the
+    // step from a [T, lr_rank] and W_fb [H * 128, lr_rank]; null otherwise
+    const float *lr_a, *lr_wfb;
+    int32_t lr_rank;
 };
 
 // Launchers (return the hipError_t of the launch).
@@ -55,6 +59,10 @@ int prefill_split_cols(int64_t units);
 // factors stay inside fp32 range.
 bool prefill_chunk_supported(int32_t gate_mode, float lb, int32_t num_heads);
 hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream);
+// the chunk kernel with f formed from the low-rank factor (p.lr_a, p.lr_wfb,
+// p.lr_rank a multiple of 32 up to LOWRANK_MAX_RANK) instead of read from p.f
+constexpr int LOWRANK_MAX_RANK = 128;
+hipError_t launch_prefill_chunk_lowrank(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_split(const Params &p, bool bf16, float *obuf, int cols_per_lane,
                                 hipStream_t stream);
 // RMSNorm + gate from a pre-norm readout buffer ([T, H, 128] fp32) into y, and

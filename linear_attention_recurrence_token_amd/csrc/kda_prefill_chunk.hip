@@ -117,7 +117,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <typename Act>
+// LR: the low-rank decay form.  f = W_fb a for the chunk's 16 tokens is one
+// more split-bf16 product per chunk (tokens x the wavefront's 16 key
+// channels, K = rank): W_fb's rows for those channels stay in registers as
+// the B operand for the workgroup's life, and each chunk's rank-r rows of a
+// pass through LDS as the A operand.  The accumulator gives lane l the
+// channel 16 w + l % 16 over tokens 4 (l / 16) .. + 3, which is the unit the
+// decay sums take, so f never goes through memory.
+template <typename Act, bool LR>
 __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     typedef BufAct<Act> BA;
     typedef typename BA::Raw2 Raw2;
@@ -160,6 +167,10 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) uint32_t s_Th[CC][TR], s_Tl[CC][TR], s_Mh[CC][TR], s_Ml[CC][TR];
     __shared__ float s_o[CC][DV + 4];      // readout of the chunk, before RMSNorm
     __shared__ float s_cw[CH][TAPS];       // conv taps of this head
+    // (LR) the chunk's rank-r rows of a split into bf16 parts, [token][k]
+    // with k padded, by chunk parity
+    constexpr int AKW = LR ? (LOWRANK_MAX_RANK + 8) / 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint32_t s_lah[LR ? 2 : 1][CC][AKW], s_lal[LR ? 2 : 1][CC][AKW];
 
     {
         const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
@@ -175,7 +186,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // lane: conv channels chq, chq + 1 of q, k, v and value channels chq, chq + 1;
     // decay: key channel dch over the tokens of quarter dq
     const int chq = 2 * lane, chk = DK + 2 * lane, chv = 2 * DK + 2 * lane;
-    const int dch = tid & (DK - 1), dq = tid >> 7;
+    // (LR: the lane of the f product's accumulator)
+    const int dch = LR ? 16 * wave + n16 : (tid & (DK - 1));
+    const int dq = LR ? g4 : (tid >> 7);
     const uint32_t foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
     const float eA = __expf(p.A_log[h * DK + dch]);
     const float dtb = p.dt_bias[h * DK + dch];
@@ -186,9 +199,57 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     Raw2 rq[RAWR], rk[RAWR], rv[RAWR], rg[TW];
     float rf[4], rb;
 
+    // (LR) W_fb's rows of this wavefront's key channels as split B operands:
+    // step m holds k = 32 m + 8 g4 + {0..7} of channel 16 w + n16, zero from
+    // the rank on; and the rank-r row piece of one token of a chunk in flight
+    // (thread: token tid / 32, k = 4 (tid % 32) .. + 3)
+    u32x4 wfh[LR ? 4 : 1], wfl[LR ? 4 : 1];
+    float4 ra = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int la_t = tid >> 5, la_k = 4 * (tid & 31);
+    if constexpr (LR) {
+        const float *wr = p.lr_wfb + ((int64_t)h * DK + 16 * wave + n16) * p.lr_rank;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int k0 = 32 * m + 8 * g4;
+            const bool live = k0 < p.lr_rank;
+            const float4 x0 = live ? ld4(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 x1 = live ? ld4(wr + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const Split2 a = split2(x0.x, x0.y), b = split2(x0.z, x0.w), c = split2(x1.x, x1.y), d = split2(x1.z, x1.w);
+            wfh[m] = u32x4{a.hi, b.hi, c.hi, d.hi};
+            wfl[m] = u32x4{a.lo, b.lo, c.lo, d.lo};
+        }
+    }
+    auto issue_lowrank = [&](int64_t c0) {
+        const int64_t end = chunk_end(c0);
+        const Rsrc aa = make_rsrc(p.lr_a + (rng.lo + c0) * (int64_t)p.lr_rank,
+                                  (uint32_t)((end - c0) * p.lr_rank * 4));
+        // columns from the rank on repeat column 0 (unused, kept in range)
+        ra = bld_f32x4(aa, (uint32_t)((la_t * p.lr_rank + (la_k < p.lr_rank ? la_k : 0)) * 4));
+    };
+    auto write_lowrank = [&](int buf) {
+        const bool live = la_k < p.lr_rank;
+        const Split2 a = split2(live ? ra.x : 0.f, live ? ra.y : 0.f);
+        const Split2 b = split2(live ? ra.z : 0.f, live ? ra.w : 0.f);
+        *reinterpret_cast<u32x2 *>(&s_lah[buf][la_t][la_k / 2]) = u32x2{a.hi, b.hi};
+        *reinterpret_cast<u32x2 *>(&s_lal[buf][la_t][la_k / 2]) = u32x2{a.lo, b.lo};
+    };
+    // f of the chunk in buffer buf for (dch, quarter dq), into rf
+    auto lowrank_f = [&](int buf) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const u32x4 ah = *reinterpret_cast<const u32x4 *>(&s_lah[buf][n16][16 * m + 4 * g4]);
+            const u32x4 al = *reinterpret_cast<const u32x4 *>(&s_lal[buf][n16][16 * m + 4 * g4]);
+            acc = mma32(ah, al, wfh[m], wfl[m], acc);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rf[u] = acc[u];
+    };
+
     // loads of a chunk at c0 >= CC (its past rows are tokens, not the window);
     // rows past the sequence end read as 0
     auto issue_inputs = [&](int64_t c0) {
+        if constexpr (LR) issue_lowrank(c0);       // first: the next half waits for it alone
         const int64_t base = c0 - PAST, end = chunk_end(c0);
         const Rsrc aq = tok_rsrc(p.q, BA::ELEM, base, end);
         const Rsrc ak = tok_rsrc(p.k, BA::ELEM, base, end);
@@ -200,9 +261,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             rk[r] = BA::load_raw2(ak, e);
             rv[r] = BA::load_raw2(av, e);
         }
-        const Rsrc af = tok_rsrc(p.f, 4, c0, end);
+        if constexpr (!LR) {
+            const Rsrc af = tok_rsrc(p.f, 4, c0, end);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
+            for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
+        }
         const Rsrc ab = make_rsrc(p.beta + (rng.lo + c0) * p.H, (uint32_t)((end - c0) * p.H * 4));
         rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
     };
@@ -456,16 +519,27 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 xv[r] = BA::load2(av, e);
             }
         }
-        const Rsrc af = tok_rsrc(p.f, 4, 0, end);
+        if constexpr (LR) {
+            issue_lowrank(0);
+        } else {
+            const Rsrc af = tok_rsrc(p.f, 4, 0, end);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
+            for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
+        }
         const Rsrc ab = make_rsrc(p.beta + rng.lo * p.H, (uint32_t)(end * p.H * 4));
         rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
+        if constexpr (LR) {
+            // f of chunk 0 from its rows of a (every wavefront's part in LDS first)
+            write_lowrank(0);
+            __syncthreads();
+            lowrank_f(0);
+        }
         prestep(xq, xk, xv, 0, 0);
         if (NC > 1) issue_inputs(CC);
     }
     __syncthreads();
     operands(0);
+    if constexpr (LR) write_lowrank(1);            // chunk 1's rows of a, read in the first half 1
     __syncthreads();
 
     f32x4 Pt, Rt;
@@ -498,6 +572,7 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // into buffers nothing reads: running them unconditionally keeps each half
     // one straight-line block for the scheduler)
     auto tokens_half1 = [&](int64_t i, int cur) {
+        if constexpr (LR) lowrank_f(cur ^ 1);      // f of chunk i + 1
         {
             float2 xq[RAWR], xk[RAWR], xv[RAWR];
 #pragma unroll
@@ -572,6 +647,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             operands(cur ^ 1);
             update(cur);
         }
+        // (LR) chunk i + 2's rows of a, loaded in half 1, for its f in the
+        // next half 1 (past the last chunk: values nothing uses)
+        if constexpr (LR) write_lowrank(cur);
         __syncthreads();
     }
 
@@ -606,10 +684,10 @@ __global__ __launch_bounds__(128) void chunk_window_kernel(Params p) {
     }
 }
 
-template <typename Act>
+template <typename Act, bool LR>
 hipError_t launch_chunk_as(const Params &p, hipStream_t stream) {
     const int64_t units = (int64_t)p.num_seqs * p.H;
-    hipLaunchKernelGGL((prefill_chunk_kernel<Act>), dim3((unsigned)units), dim3(CK_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((prefill_chunk_kernel<Act, LR>), dim3((unsigned)units), dim3(CK_THREADS), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_window_kernel<Act>), dim3((unsigned)units), dim3(128), 0, stream, p);
@@ -625,7 +703,11 @@ bool prefill_chunk_supported(int32_t gate_mode, float lb, int32_t num_heads) {
 }
 
 hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream) {
-    return bf16 ? launch_chunk_as<BF16>(p, stream) : launch_chunk_as<F32>(p, stream);
+    return bf16 ? launch_chunk_as<BF16, false>(p, stream) : launch_chunk_as<F32, false>(p, stream);
+}
+
+hipError_t launch_prefill_chunk_lowrank(const Params &p, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_chunk_as<BF16, true>(p, stream) : launch_chunk_as<F32, true>(p, stream);
 }
 
 }  // namespace kda

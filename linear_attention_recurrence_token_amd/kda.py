@@ -49,9 +49,10 @@ class kda_tensors(ctypes.Structure):
 EXPORTS = ("kda_token_step", "kda_sequence", "kda_sequence_workspace_size",
            "kda_status_string", "kda_version", "kda_device_check",
            "kda_projection_workspace_size", "kda_lowrank_gates", "kda_gate_projection",
-           "kda_output_projection", "kda_lowrank_gates_noalloc")
+           "kda_output_projection", "kda_lowrank_gates_noalloc", "kda_lowrank_factor",
+           "kda_sequence_lowrank")
 
-KDA_PROJ_LOWRANK_GATES, KDA_PROJ_GATE, KDA_PROJ_OUTPUT = 0, 1, 2
+KDA_PROJ_LOWRANK_GATES, KDA_PROJ_GATE, KDA_PROJ_OUTPUT, KDA_PROJ_LOWRANK_FACTOR = 0, 1, 2, 3
 
 
 class KdaError(RuntimeError):
@@ -97,6 +98,10 @@ def lib() -> ctypes.CDLL:
             L.kda_gate_projection.argtypes = [cfgp, vp, vp, i32, i64, vp, vp, i64, vp]
             L.kda_output_projection.restype = i32
             L.kda_output_projection.argtypes = [cfgp, vp, vp, i32, i64, vp, vp, i64, vp]
+            L.kda_lowrank_factor.restype = i32
+            L.kda_lowrank_factor.argtypes = [cfgp, vp, vp, i32, i32, i64, vp, vp, vp, i64, vp]
+            L.kda_sequence_lowrank.restype = i32
+            L.kda_sequence_lowrank.argtypes = [cfgp, tp, i32, vp, vp, vp, i64, vp, vp, i32, vp]
             L.kda_lowrank_gates_noalloc.restype = i32
             L.kda_lowrank_gates_noalloc.argtypes = [cfgp, vp, vp, vp, i32, i32, i64, vp, vp, vp]
             _lib = L
@@ -130,7 +135,7 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _check_tensors(cfg: KdaConfig, T: int, N: int, ts: dict) -> None:
+def _check_tensors(cfg: KdaConfig, T: int, N: int, ts: dict, skip=()) -> None:
     import torch
     act = torch.bfloat16 if cfg.act_dtype == KDA_BF16 else torch.float32
     H = cfg.num_heads
@@ -147,6 +152,8 @@ def _check_tensors(cfg: KdaConfig, T: int, N: int, ts: dict) -> None:
     }
     dev = None
     for name, (shape, dtype) in expect.items():
+        if name in skip:
+            continue
         t = ts.get(name)
         if t is None:
             if name == "o_raw":
@@ -343,6 +350,62 @@ def kda_lowrank_gates_noalloc(config: KdaConfig, *, x, w_fa_bp, w_fb, f, beta, s
                                          _ptr(f), _ptr(beta), _stream_handle(stream))
     if st != KDA_OK:
         raise KdaError(st, "kda_lowrank_gates_noalloc")
+
+
+def kda_lowrank_factor(config: KdaConfig, *, x, w_fa_bp, a, beta, workspace="auto", stream=None,
+                       check: bool = True) -> None:
+    """a = W_fa x and beta = sigmoid(W_bp x) (C: kda_lowrank_factor): the first
+    low-rank product alone, for kda_sequence_lowrank.  w_fa_bp [r + H, D]
+    fp32; a [T, r] and beta [T, H] fp32 out."""
+    import torch
+    T, D = int(x.shape[0]), int(x.shape[1])
+    H = config.num_heads
+    r = int(a.shape[1])
+    if check:
+        act = torch.bfloat16 if config.act_dtype == KDA_BF16 else torch.float32
+        _gpu_tensor("x", x, (T, D), act)
+        for name, t, shape in (("w_fa_bp", w_fa_bp, (r + H, D)), ("a", a, (T, r)), ("beta", beta, (T, H))):
+            _gpu_tensor(name, t, shape, torch.float32, x.device)
+    c = config.to_c()
+    ws_ptr, ws_bytes = _workspace(config, KDA_PROJ_LOWRANK_FACTOR, D, T, r, workspace, x.device)
+    st = lib().kda_lowrank_factor(ctypes.byref(c), _ptr(x), _ptr(w_fa_bp), D, r, T, _ptr(a), _ptr(beta),
+                                  ws_ptr, ws_bytes, _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_lowrank_factor")
+
+
+def kda_sequence_lowrank(config: KdaConfig, *, q, k, v, a, w_fb, beta, g, conv_w, A_log, dt_bias, gamma,
+                         state, conv_win, y, o_raw=None, cu_seqlens=None, cu_seqlens_host=None,
+                         seq_order=None, num_seqs: Optional[int] = None, stream=None,
+                         check: bool = True) -> None:
+    """Prefill with f = W_fb a formed in the step (C: kda_sequence_lowrank):
+    the tensors of kda_sequence without f, plus a [T, r] and w_fb [H * 128, r]
+    fp32 GPU tensors (r a multiple of 32 up to 128)."""
+    import numpy as np
+    import torch
+    T = int(q.shape[0])
+    N = int(state.shape[0]) if num_seqs is None else int(num_seqs)
+    H = config.num_heads
+    r = int(a.shape[1]) if a.dim() == 2 else -1
+    ts = dict(q=q, k=k, v=v, f=None, beta=beta, g=g, conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
+              gamma=gamma, state=state, conv_win=conv_win, y=y, o_raw=o_raw)
+    if check:
+        _check_tensors(config, T, N, ts, skip=("f",))
+        _gpu_tensor("a", a, (T, r), torch.float32, q.device)
+        _gpu_tensor("w_fb", w_fb, (H * DK, r), torch.float32, q.device)
+        if cu_seqlens is not None and (not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32
+                                       or tuple(cu_seqlens.shape) != (N + 1,)):
+            raise ValueError("cu_seqlens must be a contiguous int32 GPU tensor of shape (%d,)" % (N + 1))
+    host = None
+    if cu_seqlens_host is not None:
+        host = np.ascontiguousarray(np.asarray(cu_seqlens_host), dtype=np.int32)
+    c = config.to_c()
+    t = _tensors_struct(ts)
+    st = lib().kda_sequence_lowrank(ctypes.byref(c), ctypes.byref(t), N, _ptr(cu_seqlens),
+                                    host.ctypes.data if host is not None else None, _ptr(seq_order), T,
+                                    _ptr(a), _ptr(w_fb), r, _stream_handle(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_sequence_lowrank")
 
 
 def kda_gate_projection(config: KdaConfig, *, x, w_g, g, workspace="auto", stream=None,

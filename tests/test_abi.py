@@ -405,3 +405,71 @@ def test_sequence_host_offsets_need_the_device_array_and_streams_differ(lib):
     assert _seq(lib, _cfg(), _fake_tensors(), n=2, cu=None, total=8, cu_host=ptr) == kda.KDA_ERR_INVALID_ARG
     # the second stream may not be the call's own stream
     assert _seq(lib, _cfg(), _fake_tensors(), n=2, total=8, stream=1 << 20, side=1 << 20) == kda.KDA_ERR_INVALID_ARG
+
+
+# --- the step with the low-rank decay formed inside it, and its factor product ----
+
+def _seq_lr(lib, cfg, t, n=2, cu=None, total=8, a=(1 << 41), wfb=(1 << 41) + (1 << 30), rank=128):
+    return lib.kda_sequence_lowrank(ctypes.byref(cfg), ctypes.byref(t), n, cu, None, None, total, a, wfb, rank, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"rank": 48}, kda.KDA_ERR_INVALID_ARG),
+    ({"rank": 0}, kda.KDA_ERR_INVALID_ARG),
+    ({"rank": 256}, kda.KDA_ERR_UNSUPPORTED),               # above the in-step product's rank
+    ({"a": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"a": (1 << 41) + 4}, kda.KDA_ERR_INVALID_ARG),
+    ({"wfb": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"cfg": _cfg(gate_mode=kda.KDA_GATE_LITERAL)}, kda.KDA_ERR_UNSUPPORTED),
+    ({"cfg": _cfg(gate_lower_bound=-9.0)}, kda.KDA_ERR_UNSUPPORTED),
+    ({"cfg": _cfg(prefill_path=kda.KDA_PREFILL_FUSED)}, kda.KDA_ERR_UNSUPPORTED),
+    ({"cfg": _cfg(head_dim_k=64)}, kda.KDA_ERR_UNSUPPORTED),
+])
+def test_sequence_lowrank_rejects(lib, over, status):
+    t = _fake_tensors(f=None)
+    assert _seq_lr(lib, over.pop("cfg", _cfg()), t, **over) == status
+
+
+def test_sequence_lowrank_needs_f_null_and_no_device(lib):
+    # f is formed in the step: a caller f is refused
+    assert _seq_lr(lib, _cfg(), _fake_tensors()) == kda.KDA_ERR_INVALID_ARG
+    # w_fb may not be an output
+    t = _fake_tensors(f=None)
+    assert _seq_lr(lib, _cfg(), t, wfb=t.y) == kda.KDA_ERR_INVALID_ARG
+    assert _seq_lr(lib, _cfg(), _fake_tensors(f=None), total=0) == kda.KDA_OK
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return
+    except ImportError:
+        pass
+    assert _seq_lr(lib, _cfg(), _fake_tensors(f=None)) == kda.KDA_ERR_DEVICE
+
+
+def _factor(lib, cfg=None, x=1 << 40, w=(1 << 40) + (1 << 30), hidden=64, rank=32, tokens=10,
+            a=(1 << 40) + (3 << 30), beta=(1 << 40) + (4 << 30), ws=None, ws_bytes=0):
+    cfg = cfg or _cfg()
+    return lib.kda_lowrank_factor(ctypes.byref(cfg), x, w, hidden, rank, tokens, a, beta, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"hidden": 48}, kda.KDA_ERR_INVALID_ARG),
+    ({"rank": 16}, kda.KDA_ERR_INVALID_ARG),
+    ({"tokens": -1}, kda.KDA_ERR_INVALID_ARG),
+    ({"x": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"a": None}, kda.KDA_ERR_INVALID_ARG),
+    ({"a": (1 << 40) + 64}, kda.KDA_ERR_INVALID_ARG),          # a overlaps x
+    ({"beta": (1 << 40) + (3 << 30) + 64}, kda.KDA_ERR_INVALID_ARG),   # beta inside a
+    ({"ws": (1 << 40) + (3 << 30), "ws_bytes": 1 << 20}, kda.KDA_ERR_INVALID_ARG),   # workspace is a
+    ({"cfg": _cfg(head_dim_k=64)}, kda.KDA_ERR_UNSUPPORTED),
+])
+def test_lowrank_factor_rejects(lib, over, status):
+    assert _factor(lib, **over) == status
+
+
+def test_lowrank_factor_workspace_size(lib):
+    cfg = _cfg(num_heads=32)
+    few = kda.projection_workspace_size(kda.KdaConfig(num_heads=32), kda.KDA_PROJ_LOWRANK_FACTOR, 4096, 64, 128)
+    many = kda.projection_workspace_size(kda.KdaConfig(num_heads=32), kda.KDA_PROJ_LOWRANK_FACTOR, 4096, 8192, 128)
+    assert few > 0 and many >= (128 + 32) * 4096 * 4      # split-K partials; the weights' bf16 parts
+    assert _factor(lib, tokens=0, x=None, a=None, beta=None) == kda.KDA_OK
