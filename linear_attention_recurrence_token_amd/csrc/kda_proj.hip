@@ -45,12 +45,10 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // measured the fastest of 256 x 256 with 4 stages and one workgroup, 256 x 128
 // and 128 x 128.  Its limit is the rate at which tiles arrive from L2 (about
 // 17 bytes per clock per compute unit on 32768 x 8192 x 8192), not the MFMA.
-#ifndef PROJ_DMA_BM
-#define PROJ_DMA_BM 128
-#define PROJ_DMA_BN 256
-#define PROJ_DMA_NS 3
-#define PROJ_DMA_WPE 2
-#endif
+constexpr int DMA_BM = 128;      // token rows per tile
+constexpr int DMA_BN = 256;      // outputs per tile
+constexpr int DMA_NS = 3;        // K stages in LDS
+constexpr int DMA_WPE = 2;       // waves per SIMD: two workgroups of four wavefronts per compute unit
 
 constexpr int GT = 256;          // threads per workgroup
 constexpr int BK = 32;           // K columns per stage
@@ -348,7 +346,7 @@ __device__ __forceinline__ void wait_then_barrier() {
 
 
 template <int BM, int BN, int NS, typename TC>
-__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(PROJ_DMA_WPE)))
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(DMA_WPE)))
 void proj_gemm_dma_kernel(GemmArgs g) {
     static_assert(NS == 3 || NS == 4, "stages in flight");
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -490,19 +488,15 @@ __global__ __launch_bounds__(256) void proj_finalize_kernel(GemmArgs g) {
 // heads) fill three 64-wide tile columns exactly; 128 x 64 took it from 0.75
 // to 0.66 ms over 32768 rows (against 128 x 128, 128 x 192 and 256 x 64)
 template <typename TA, typename TB> struct Shapes;
-template <> struct Shapes<BF16, BF16> { static constexpr int L_BM = PROJ_DMA_BM, L_BN = PROJ_DMA_BN; };
+template <> struct Shapes<BF16, BF16> { static constexpr int L_BM = DMA_BM, L_BN = DMA_BN; };
 template <> struct Shapes<BF16, F32> { static constexpr int L_BM = 128, L_BN = 64; };
 template <> struct Shapes<F32, F32> { static constexpr int L_BM = 128, L_BN = 128; };
 template <> struct Shapes<BF16, F32P> : Shapes<BF16, F32> {};
 template <> struct Shapes<F32, F32P> : Shapes<F32, F32> {};
 constexpr int S_BM = 64, S_BN = 64;
 constexpr int64_t LARGE_MIN_M = 512;
-#ifndef PROJ_SPLIT_MIN_K
-#define PROJ_SPLIT_MIN_K 256
-#define PROJ_TARGET_WG 512
-#endif
-constexpr int SPLIT_MIN_K = PROJ_SPLIT_MIN_K;          // K columns per split at least
-constexpr int TARGET_WORKGROUPS = PROJ_TARGET_WG;     // two per compute unit
+constexpr int SPLIT_MIN_K = 256;          // K columns per split at least
+constexpr int TARGET_WORKGROUPS = 512;    // two per compute unit
 
 struct Plan {
     bool large;
@@ -548,7 +542,7 @@ hipError_t launch_typed(const GemmArgs &a, bool large, hipStream_t stream) {
     constexpr int BM = Shapes<TA, TB>::L_BM, BN = Shapes<TA, TB>::L_BN;
     if (large) {
         if constexpr (Opnd<TA>::PARTS == 1 && Opnd<TB>::PARTS == 1)
-            hipLaunchKernelGGL((proj_gemm_dma_kernel<BM, BN, PROJ_DMA_NS, TC>), dim3(total), dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((proj_gemm_dma_kernel<BM, BN, DMA_NS, TC>), dim3(total), dim3(GT), 0, stream, a);
         else
             hipLaunchKernelGGL((proj_gemm_kernel<TA, TB, TC, BM, BN>), dim3(total), dim3(GT), 0, stream, a);
     }

@@ -23,7 +23,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
-_LIB = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIB points the tests at another build of the same source (the
+# sanitizer run); it must exist, it is never built from here
+_LIB = os.environ.get("KDA_ORACLE_LIB") or os.path.join(_HERE, "libkda_oracle.so")
 
 GATE_BOUNDED, GATE_LITERAL, GATE_RAW = 0, 1, 2
 
@@ -33,6 +35,10 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile kda_oracle.c into libkda_oracle.so (gcc, OpenMP, -O2)."""
+    if os.environ.get("KDA_ORACLE_LIB"):
+        if not os.path.exists(_LIB):
+            raise FileNotFoundError(_LIB)
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
