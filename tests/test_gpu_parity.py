@@ -52,6 +52,22 @@ def test_decode_small(gpu, N, H, steps):
     _gpu.assert_parity(_gpu.run_decode(w, gpu), _gpu.oracle_decode(w), label="decode")
 
 
+@pytest.mark.parametrize("N,H,steps,act", [
+    (17, 32, 3, "f32"),     # 544 pairs on 256 workgroups: two or three pairs each
+    (20, 48, 2, "f32"),     # H does not divide 256: 240 workgroups of four pairs
+    (2, 300, 2, "bf16"),    # H above the compute units: 300 workgroups of two pairs
+    (40, 16, 3, "bf16"),    # 640 pairs: two or three each
+])
+def test_decode_persistent_grid_shapes(gpu, N, H, steps, act):
+    # batches of more than two pairs per compute unit run the persistent
+    # decode kernel, each workgroup walking several pairs of one head
+    w = synth.make_workload("decode grid", seed=700 + N + H, N=N, H=H, decode_steps=steps, act_dtype=act,
+                            state_std=0.02, win_std=1.0)
+    note("decode persistent grid N=%d H=%d steps=%d %s" % (N, H, steps, act))
+    _gpu.assert_parity(_gpu.run_decode(w, gpu), _gpu.oracle_decode(w), bf16=act == "bf16",
+                       label="decode grid %dx%d" % (N, H))
+
+
 def test_decode_bf16(gpu):
     w = synth.make_workload("decode bf16", seed=7, N=6, H=3, decode_steps=9, act_dtype="bf16",
                             state_std=0.02, win_std=1.0)
