@@ -247,10 +247,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
     const int lane = tid & 63, wave = tid >> 6;
     const int cg = tid & 31, rg = tid >> 5;
 
-    __shared__ float4 s_row[DK];
-    __shared__ float s_v[DV];
-    __shared__ float s_red[Sh::NW][4];
-    __shared__ float4 s_up[Sh::NW][32][2];
+    // per-pair values, by pair parity: a pair's writes never meet the reads of
+    // the pair before it, and the two barriers of the pair in between keep
+    // the pair two back finished
+    __shared__ float4 s_row[2][DK];
+    __shared__ float s_v[2][DV];
+    __shared__ float s_red[2][Sh::NW][4];
+    __shared__ float4 s_up[2][Sh::NW][32][2];
 
     // per-head constants, in LDS for the workgroup's life: the conv taps of
     // every channel, exp(A_log), dt_bias and gamma
@@ -265,6 +268,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
             s_gm[tid] = p.gamma[tid];
         }
     }
+    __syncthreads();                             // the per-head constants in LDS
     // thread tid < 128: q, k channel tid and the decay of key channel tid;
     // thread 128 + j: v channel j (wavefront-uniform split)
     const bool qk = tid < DK;
@@ -299,13 +303,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
         for (int m = 0; m < Sh::RPT; ++m) s[m] = ld_state<NT_LOAD>(rs, s_lane, m * ROW_STEP);
     };
     // the step of pair u from its inputs and its state registers (loads in flight)
-    auto pair_body = [&](int u, const DecodeIn &in, float4 (&s)[Sh::RPT]) {
+    auto pair_body = [&](int u, const DecodeIn &in, float4 (&s)[Sh::RPT], const int b) {
         const Rsrc rs = make_rsrc(p.state + (int64_t)u * (DK * DV), DK * DV * 4);
-        // pre-step of this pair from its prefetched inputs; the barrier keeps
-        // the previous pair's LDS reads ahead of these writes
+        // pre-step of this pair from its prefetched inputs
         float *W = p.win + (int64_t)u * (PAST * CH);
         float qq = 0.f, kk = 0.f, qkd = 0.f;
-        __syncthreads();
         // window shift: six stores by every thread (a v thread writes its
         // three values twice), so the store count is the same on every path
 #pragma unroll
@@ -318,18 +320,18 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
             const float aq = silu(c0.x * in.w0[0] + c0.y * in.w0[1] + c0.z * in.w0[2] + c0.w * in.x0);
             const float ak = silu(c1.x * in.w1[0] + c1.y * in.w1[1] + c1.z * in.w1[2] + c1.w * in.x1);
             const float al = decay(in.fa, s_eA[ch], s_dtb[ch], p.gate_mode, p.lb);
-            s_row[ch] = make_float4(al * aq, al * ak, al, ak);
+            s_row[b][ch] = make_float4(al * aq, al * ak, al, ak);
             qq = aq * aq; kk = ak * ak; qkd = aq * ak;
         } else {
             const float4 c0 = s_cw[2 * DK + ch];
-            s_v[ch] = silu(c0.x * in.w0[0] + c0.y * in.w0[1] + c0.z * in.w0[2] + c0.w * in.x0);
+            s_v[b][ch] = silu(c0.x * in.w0[0] + c0.y * in.w0[1] + c0.z * in.w0[2] + c0.w * in.x0);
         }
         qq = sum64(qq); kk = sum64(kk); qkd = sum64(qkd);
-        if (lane == 0) { s_red[wave][0] = qq; s_red[wave][1] = kk; s_red[wave][2] = qkd; }
+        if (lane == 0) { s_red[b][wave][0] = qq; s_red[b][wave][1] = kk; s_red[b][wave][2] = qkd; }
         __syncthreads();
         qq = 0.f; kk = 0.f; qkd = 0.f;
 #pragma unroll
-        for (int w = 0; w < Sh::NW; ++w) { qq += s_red[w][0]; kk += s_red[w][1]; qkd += s_red[w][2]; }
+        for (int w = 0; w < Sh::NW; ++w) { qq += s_red[b][w][0]; kk += s_red[b][w][1]; qkd += s_red[b][w][2]; }
         const float rq = rsqrtf(qq + p.l2_eps);
         const float rk = rsqrtf(kk + p.l2_eps);
         qkd *= rq * rk;
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
         float4 uu = make_float4(0.f, 0.f, 0.f, 0.f), pq = uu;
 #pragma unroll
         for (int m = 0; m < Sh::RPT; ++m) {
-            const float4 rw = s_row[rg + Sh::NRG * m];
+            const float4 rw = s_row[b][rg + Sh::NRG * m];
             uu.x += s[m].x * rw.y; uu.y += s[m].y * rw.y; uu.z += s[m].z * rw.y; uu.w += s[m].w * rw.y;
             pq.x += s[m].x * rw.x; pq.y += s[m].y * rw.x; pq.z += s[m].z * rw.x; pq.w += s[m].w * rw.x;
         }
@@ -346,12 +348,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
         uu.z += __shfl_xor(uu.z, 32); uu.w += __shfl_xor(uu.w, 32);
         pq.x += __shfl_xor(pq.x, 32); pq.y += __shfl_xor(pq.y, 32);
         pq.z += __shfl_xor(pq.z, 32); pq.w += __shfl_xor(pq.w, 32);
-        if (lane < 32) { s_up[wave][cg][0] = uu; s_up[wave][cg][1] = pq; }
+        if (lane < 32) { s_up[b][wave][cg][0] = uu; s_up[b][wave][cg][1] = pq; }
         __syncthreads();
-        uu = s_up[0][cg][0]; pq = s_up[0][cg][1];
+        uu = s_up[b][0][cg][0]; pq = s_up[b][0][cg][1];
 #pragma unroll
         for (int w = 1; w < Sh::NW; ++w) {
-            const float4 a = s_up[w][cg][0], c = s_up[w][cg][1];
+            const float4 a = s_up[b][w][cg][0], c = s_up[b][w][cg][1];
             uu.x += a.x; uu.y += a.y; uu.z += a.z; uu.w += a.w;
             pq.x += c.x; pq.y += c.y; pq.z += c.z; pq.w += c.w;
         }
@@ -359,14 +361,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
         pq.x *= rq; pq.y *= rq; pq.z *= rq; pq.w *= rq;
 
         // delta, readout, in-place update
-        const float4 vv = *reinterpret_cast<const float4 *>(&s_v[4 * cg]);
+        const float4 vv = *reinterpret_cast<const float4 *>(&s_v[b][4 * cg]);
         float4 d, o, dk;
         d.x = in.b * (vv.x - uu.x); d.y = in.b * (vv.y - uu.y); d.z = in.b * (vv.z - uu.z); d.w = in.b * (vv.w - uu.w);
         o.x = pq.x + qkd * d.x; o.y = pq.y + qkd * d.y; o.z = pq.z + qkd * d.z; o.w = pq.w + qkd * d.w;
         dk.x = d.x * rk; dk.y = d.y * rk; dk.z = d.z * rk; dk.w = d.w * rk;
 #pragma unroll
         for (int m = 0; m < Sh::RPT; ++m) {
-            const float2 ak = *reinterpret_cast<const float2 *>(&s_row[rg + Sh::NRG * m].z);
+            const float2 ak = *reinterpret_cast<const float2 *>(&s_row[b][rg + Sh::NRG * m].z);
             float4 t;
             t.x = ak.x * s[m].x + ak.y * dk.x; t.y = ak.x * s[m].y + ak.y * dk.y;
             t.z = ak.x * s[m].z + ak.y * dk.z; t.w = ak.x * s[m].w + ak.y * dk.w;
@@ -401,13 +403,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p, int32_t G)
         const int n1 = unit + G;
         issue_state(unit, st);
         load_in(n1 < P ? n1 : unit, inB);
-        pair_body(unit, inA, st);
+        pair_body(unit, inA, st, 0);
         if (n1 >= P) break;
         unit = n1;
         const int n2 = unit + G;
         issue_state(unit, st);
         load_in(n2 < P ? n2 : unit, inA);
-        pair_body(unit, inB, st);
+        pair_body(unit, inB, st, 1);
         if (n2 >= P) break;
         unit = n2;
     }
