@@ -46,11 +46,13 @@
 // vector work overlap; and the split keeps each role's registers (the state,
 // the inputs loaded ahead) apart, within the 128 that four wavefronts allow.
 // Chunk i:
-//   half 1: state: T and M of chunk i, P and R of chunk i, RMSNorm and gate of
-//           chunk i - 1; token: conv, SiLU, L2 norm and decay of chunk i + 1
-//           from registers loaded a chunk earlier, loads for chunk i + 2
-//   half 2: state: Delta, O and the state update of chunk i; token: the split
-//           operands and partial L, M of chunk i + 1
+//   half 1: state: P and R of chunk i, RMSNorm and gate of chunk i - 1, the
+//           partial L, M of chunk i + 1; token: the split operands of chunk i + 1
+//   half 2: state: Delta, O and the state update of chunk i, T and M of chunk
+//           i + 1 (wavefronts 0 and 1); token: conv, SiLU, L2 norm and decay of
+//           chunk i + 2 from registers loaded a chunk earlier, loads for chunk i + 3
+// so that the two longest stretches, the pre-step and the update, share a half
+// (the operands, T and M are therefore double-buffered, v and beta triple).
 // The state never leaves the accumulators between chunks: it feeds P and R
 // as the B operand of 16x16x32 steps directly, by ordering the sum over key
 // channels so that step m takes, in lane l, the rows the lane holds of tiles
@@ -177,20 +179,22 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     __shared__ float s_qh[CC][KP];         // q_hat of the chunk being prepared
     __shared__ float s_Gq[CC][KP];         // log-decay summed from the start of the token's quarter
     __shared__ float s_Gt[4][DK];          // log-decay summed over each quarter
-    __shared__ float s_v[2][CC][DV + 4];   // activated v            (by chunk parity)
-    __shared__ float s_beta[2][CC];        //                        (by chunk parity)
+    __shared__ float s_v[3][CC][DV + 4];   // activated v            (by chunk index mod 3)
+    __shared__ float s_beta[3][CC];        //                        (by chunk index mod 3)
     // split bf16 operands e^G . k_hat, e^G . q_hat of P and R: slot (t, m, g)
     // holds channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3} of token t
-    __shared__ __attribute__((aligned(16))) uint32_t s_kah[CC * OPR * 4], s_kal[CC * OPR * 4];
-    __shared__ __attribute__((aligned(16))) uint32_t s_qah[CC * OPR * 4], s_qal[CC * OPR * 4];
+    // (by chunk parity)
+    __shared__ __attribute__((aligned(16))) uint32_t s_kah[2][CC * OPR * 4], s_kal[2][CC * OPR * 4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_qah[2][CC * OPR * 4], s_qal[2][CC * OPR * 4];
     // [channel][token] split e^{G_C - G} . k_hat of the update (by chunk parity)
     __shared__ __attribute__((aligned(16))) uint32_t s_Eh[2][DK][ER], s_El[2][DK][ER];
     __shared__ float s_gC[2][DK];          // e^{G_C}, decay of the whole chunk (by chunk parity)
     __shared__ float s_Lp[NPART][CC][CC];  // L, M summed over one channel eighth each
     __shared__ float s_Mp[NPART][CC][CC];
     __shared__ float s_A[CC][TP];          // Diag(b) L, strictly lower
-    // (I + Diag(b) L)^{-1} and M (lower triangle with the diagonal), [row][column] split bf16
-    __shared__ __attribute__((aligned(16))) uint32_t s_Th[CC][TR], s_Tl[CC][TR], s_Mh[CC][TR], s_Ml[CC][TR];
+    // (I + Diag(b) L)^{-1} and M (lower triangle with the diagonal), [row][column]
+    // split bf16 (by chunk parity)
+    __shared__ __attribute__((aligned(16))) uint32_t s_Th[2][CC][TR], s_Tl[2][CC][TR], s_Mh[2][CC][TR], s_Ml[2][CC][TR];
     __shared__ float s_o[CC][DV + 4];      // readout of the chunk, before RMSNorm
     __shared__ float s_cw[CH][TAPS];       // conv taps of this head
     // (LR) a chunk's rank-r rows of a split into bf16 parts, [token][k] with k
@@ -217,13 +221,13 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // row 4 b + r of column c in block b, and every lane of a quad keeps the
     // finished part of column c; the rows of a block couple through quad
     // broadcasts.  Masked entries of A are exact zeros.
-    auto solve_T = [&](int buf) {
+    auto solve_T = [&](int vb, int tb) {
         {
             const int t = lane >> 2, s0 = 4 * (lane & 3);
             float4 a = ld4(&s_Lp[0][t][s0]);
 #pragma unroll
             for (int q = 1; q < NPART; ++q) a += ld4(&s_Lp[q][t][s0]);
-            const float bt = s_beta[buf][t];
+            const float bt = s_beta[vb][t];
             a.x = (s0 + 0 < t) ? bt * a.x : 0.f;
             a.y = (s0 + 1 < t) ? bt * a.y : 0.f;
             a.z = (s0 + 2 < t) ? bt * a.z : 0.f;
@@ -261,11 +265,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             Tc[4 * b + 2] = x2;
             Tc[4 * b + 3] = x3;
             const Split2 x = split2(y, 0.f);
-            reinterpret_cast<uint16_t *>(s_Th[t])[c] = (uint16_t)x.hi;
-            reinterpret_cast<uint16_t *>(s_Tl[t])[c] = (uint16_t)x.lo;
+            reinterpret_cast<uint16_t *>(s_Th[tb][t])[c] = (uint16_t)x.hi;
+            reinterpret_cast<uint16_t *>(s_Tl[tb][t])[c] = (uint16_t)x.lo;
         }
     };
-    auto reduce_M = [&]() {
+    auto reduce_M = [&](int tb) {
         const int t = lane >> 2, s0 = 4 * (lane & 3);
         float4 m = ld4(&s_Mp[0][t][s0]);
 #pragma unroll
@@ -275,8 +279,46 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         m.z = (s0 + 2 <= t) ? m.z : 0.f;
         m.w = (s0 + 3 <= t) ? m.w : 0.f;
         const Split2 a = split2(m.x, m.y), b = split2(m.z, m.w);
-        *reinterpret_cast<u32x2 *>(&s_Mh[t][s0 / 2]) = u32x2{a.hi, b.hi};
-        *reinterpret_cast<u32x2 *>(&s_Ml[t][s0 / 2]) = u32x2{a.lo, b.lo};
+        *reinterpret_cast<u32x2 *>(&s_Mh[tb][t][s0 / 2]) = u32x2{a.hi, b.hi};
+        *reinterpret_cast<u32x2 *>(&s_Ml[tb][t][s0 / 2]) = u32x2{a.lo, b.lo};
+    };
+
+    // L_ts = sum_i (e^{G_ti - r_i} k_ti)(e^{r_i - G_si} k_si), M likewise with q_t,
+    // over channel eighth rw of the prepared chunk (partial sums), r = G at the
+    // chunk middle (token 7), on fp32 MFMA; lane l: token l % 16, channels
+    // 16 rw + 4 (l / 16) + s
+    auto partial_LM = [&]() {
+        const int lc = 16 * rw + 4 * g4;
+        const int tq = n16 >> 2;
+        const float4 k4 = ld4(&s_kh[n16][lc]);
+        const float4 q4 = ld4(&s_qh[n16][lc]);
+        const float4 gq = ld4(&s_Gq[n16][lc]);
+        const float4 g7 = ld4(&s_Gq[CC / 2 - 1][lc]);   // quarter 1 up to token 7
+        const float4 c0 = ld4(&s_Gt[0][lc]);
+        const float4 c2 = ld4(&s_Gt[2][lc]);
+        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+        const float gv[4] = {gq.x, gq.y, gq.z, gq.w};
+        const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
+        const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
+        const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
+        f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // G_t - r from sums that start as close to both tokens as possible
+            const float d = tq == 0 ? gv[s] - c0v[s] - g7v[s]
+                          : tq == 1 ? gv[s] - g7v[s]
+                          : tq == 2 ? gv[s] : gv[s] + c2v[s];
+            const float ef = __expf(d), eb = __expf(-d);
+            const float b = eb * kv[s];
+            Lt = mfma4(ef * kv[s], b, Lt);
+            Mt = mfma4(ef * qv[s], b, Mt);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s_Lp[rw][4 * g4 + r][n16] = Lt[r];
+            s_Mp[rw][4 * g4 + r][n16] = Mt[r];
+        }
     };
 
     if (state_wave) {
@@ -289,7 +331,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             for (int sl = 0; sl < TW; ++sl)
                 rg[sl] = BA::load_raw2(ag, (uint32_t)((t0 + sl) * rowsz + h * DV + 2 * lane));
         };
-        // RMSNorm + gate of tokens t0, t0 + 1 of the chunk at c0 (readout in s_o, gates in rg)
+        // RMSNorm + gate of tokens t0, t0 + 1 of the chunk at c0 (readout in s_o,
+        // gates in rg); the output buffers end at the sequence end, so stores of
+        // tokens past it are dropped (no branch: the tokens' chains interleave)
         auto epilogue = [&](int64_t c0) {
             const int nve = (int)(L - c0 < CC ? L - c0 : CC);
             const Rsrc ay = tok_rsrc(p.y, BA::ELEM, c0, c0 + nve);
@@ -297,7 +341,6 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 #pragma unroll
             for (int sl = 0; sl < TW; ++sl) {
                 const int t = t0 + sl;
-                if (t >= nve) break;               // wavefront-uniform
                 const float2 o = ld2(&s_o[t][chq]);
                 const float r = rsqrtf(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
                 const uint32_t e = (uint32_t)(t * rowsz + h * DV + chq);
@@ -323,21 +366,25 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         __syncthreads();                           // conv taps in LDS
         if constexpr (LR) __syncthreads();         // chunk 0's rows of a in LDS
         __syncthreads();                           // chunk 0 prepared
-        __syncthreads();                           // chunk 0's operands
+        partial_LM();                              // L, M of chunk 0
+        __syncthreads();                           // chunk 0's operands, L and M
+        if (rw == 0) solve_T(0, 0);
+        else if (rw == 1) reduce_M(0);
+        __syncthreads();                           // T, M of chunk 0; chunk 1 prepared
 
         f32x4 Pt, Rt;
         // P, R of the current chunk: step m covers state rows 32 m .. 32 m + 31
         // (tiles 2 m, 2 m + 1)
-        auto products_PR = [&]() {
+        auto products_PR = [&](int pb) {
             Pt = f32x4{0.f, 0.f, 0.f, 0.f};
             Rt = Pt;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int w = (n16 * OPR + m * 4 + g4) * 4;
-                const u32x4 kah = *reinterpret_cast<const u32x4 *>(&s_kah[w]);
-                const u32x4 kal = *reinterpret_cast<const u32x4 *>(&s_kal[w]);
-                const u32x4 qah = *reinterpret_cast<const u32x4 *>(&s_qah[w]);
-                const u32x4 qal = *reinterpret_cast<const u32x4 *>(&s_qal[w]);
+                const u32x4 kah = *reinterpret_cast<const u32x4 *>(&s_kah[pb][w]);
+                const u32x4 kal = *reinterpret_cast<const u32x4 *>(&s_kal[pb][w]);
+                const u32x4 qah = *reinterpret_cast<const u32x4 *>(&s_qah[pb][w]);
+                const u32x4 qal = *reinterpret_cast<const u32x4 *>(&s_qal[pb][w]);
                 const Split2 x0 = split2(st[2 * m][0], st[2 * m][1]);
                 const Split2 x1 = split2(st[2 * m][2], st[2 * m][3]);
                 const Split2 x2 = split2(st[2 * m + 1][0], st[2 * m + 1][1]);
@@ -348,18 +395,18 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             }
         };
         // Delta, O and the state update of the current chunk
-        auto update = [&](int cur) {
+        auto update = [&](int vb, int cur) {
             // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
             f32x4 Wt;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g4 + r;
-                Wt[r] = s_beta[cur][t] * (s_v[cur][t][col0 + n16] - Pt[r]);
+                Wt[r] = s_beta[vb][t] * (s_v[vb][t][col0 + n16] - Pt[r]);
             }
-            const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[n16][2 * g4]);
-            const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[n16][2 * g4]);
-            const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[n16][2 * g4]);
-            const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[n16][2 * g4]);
+            const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[cur][n16][2 * g4]);
+            const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[cur][n16][2 * g4]);
+            const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[cur][n16][2 * g4]);
+            const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[cur][n16][2 * g4]);
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
             u32x2 wh, wl, dh, dl;
             split4(Wt, wh, wl);
@@ -389,19 +436,26 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             for (int rt = 0; rt < 8; ++rt) st[rt] = mma_hihi(eh[rt], dh, st[rt]);
         };
 
+        int vb = 0;                                // chunk i's index mod 3
 #pragma unroll 1
         for (int64_t i = 0; i < NC; ++i) {
             const int cur = (int)(i & 1);
-            // ================= half 1
-            if (rw == 0) solve_T(cur);
-            else if (rw == 1) reduce_M();
-            products_PR();
+            const int vb1 = vb == 2 ? 0 : vb + 1;
+            // ================= half 1: P, R of chunk i; epilogue of chunk i - 1;
+            // partial L, M of chunk i + 1
+            products_PR(cur);
             if (i >= 1) epilogue((i - 1) * CC);
             issue_gate(i * CC);
+            if (i + 1 < NC) partial_LM();
             __syncthreads();
-            // ================= half 2
-            update(cur);
+            // ================= half 2: update of chunk i; T and M of chunk i + 1
+            update(vb, cur);
+            if (i + 1 < NC) {
+                if (rw == 0) solve_T(vb1, cur ^ 1);
+                else if (rw == 1) reduce_M(cur ^ 1);
+            }
             __syncthreads();
+            vb = vb1;
         }
         epilogue((NC - 1) * CC);
 #pragma unroll
@@ -423,6 +477,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 
     // registers loaded a chunk ahead: raw inputs of the next chunk to pre-step
     Raw2 rq[RAWR], rk[RAWR], rv[RAWR];
+    // conv taps of this lane's channels, kept in registers (their LDS reads
+    // would queue behind the state wavefronts' operand reads every chunk)
+    float4 wq0, wq1, wk0, wk1, wv0, wv1;
     float rf[4], rb;
 
     // (LR) W_fb's rows of this wavefront's key channels as split B operands:
@@ -497,46 +554,44 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     };
 
     // conv + SiLU + L2 norm of this wavefront's tokens of the chunk at c0 (zeros
-    // past the end), decay sums of (dch, quarter dq); v, beta to buffer buf
+    // past the end), decay sums of (dch, quarter dq); v, beta to buffer vb
     auto prestep = [&](const float2 (&xq)[RAWR], const float2 (&xk)[RAWR], const float2 (&xv)[RAWR],
-                       int64_t c0, int buf) {
+                       int64_t c0, int vb) {
         const int nv = (int)(L - c0 < CC ? L - c0 : CC);
-        const float4 wq0 = ld4(s_cw[chq]), wq1 = ld4(s_cw[chq + 1]);
-        const float4 wk0 = ld4(s_cw[chk]), wk1 = ld4(s_cw[chk + 1]);
-        const float4 wv0 = ld4(s_cw[chv]), wv1 = ld4(s_cw[chv + 1]);
 #pragma unroll
         for (int sl = 0; sl < TW; ++sl) {
+            // (no branch on the token: the two tokens' chains interleave; a
+            // token past the end is computed and then replaced by zeros)
             const int t = t0 + sl;
-            float2 qh = make_float2(0.f, 0.f), kh = qh, vh = qh;
-            if (t < nv) {                          // wavefront-uniform
-                const float aq0 = silu(cconv4(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
-                const float aq1 = silu(cconv4(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
-                const float ak0 = silu(cconv4(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
-                const float ak1 = silu(cconv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
-                vh.x = silu(cconv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
-                vh.y = silu(cconv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
-                const float nq = rsqrtf(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
-                const float nk = rsqrtf(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
-                qh = make_float2(aq0 * nq, aq1 * nq);
-                kh = make_float2(ak0 * nk, ak1 * nk);
-            }
+            const bool live = t < nv;
+            const float aq0 = silu(cconv4(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
+            const float aq1 = silu(cconv4(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
+            const float ak0 = silu(cconv4(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
+            const float ak1 = silu(cconv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
+            const float av0 = silu(cconv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
+            const float av1 = silu(cconv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
+            const float nq = rsqrtf(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
+            const float nk = rsqrtf(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
+            const float2 qh = live ? make_float2(aq0 * nq, aq1 * nq) : make_float2(0.f, 0.f);
+            const float2 kh = live ? make_float2(ak0 * nk, ak1 * nk) : make_float2(0.f, 0.f);
+            const float2 vh = live ? make_float2(av0, av1) : make_float2(0.f, 0.f);
             *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
             *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
-            *reinterpret_cast<float2 *>(&s_v[buf][t][chq]) = vh;
+            *reinterpret_cast<float2 *>(&s_v[vb][t][chq]) = vh;
         }
-        if (lane < TW) s_beta[buf][t0 + lane] = (t0 + lane < nv) ? rb : 0.f;
+        if (lane < TW) s_beta[vb][t0 + lane] = (t0 + lane < nv) ? rb : 0.f;
         float G = 0.f;                             // held constant past the last token
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = 4 * dq + u;
-            if (t < nv) G += p.lb * sigmoid(eA * (rf[u] + dtb));
+            const float gk = p.lb * sigmoid(eA * (rf[u] + dtb));
+            G += (t < nv) ? gk : 0.f;
             s_Gq[t][dch] = G;
         }
         s_Gt[dq][dch] = G;
     };
 
-    // split operands of the prepared chunk (into buffer buf) and the partial
-    // L, M over channel eighth rw
+    // split operands of the prepared chunk (into buffer buf)
     auto operands = [&](int buf) {
         {
             // lane: channels chq, chq + 1 of this wavefront's tokens (quarter rw / 2)
@@ -564,8 +619,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 const Split2 ka = split2(eg0 * kh.x, eg1 * kh.y);
                 const Split2 qa = split2(eg0 * qh.x, eg1 * qh.y);
                 const int w = (t * OPR + m * 4 + gg) * 4 + e / 2;
-                s_kah[w] = ka.hi; s_kal[w] = ka.lo;
-                s_qah[w] = qa.hi; s_qal[w] = qa.lo;
+                s_kah[buf][w] = ka.hi; s_kal[buf][w] = ka.lo;
+                s_qah[buf][w] = qa.hi; s_qal[buf][w] = qa.lo;
                 // G_C - G_t = (rest of this quarter) + (later quarters)
                 E0[sl] = __expf(gq_end.x - gq.x + after.x) * kh.x;
                 E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
@@ -580,43 +635,12 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 *reinterpret_cast<float2 *>(&s_gC[buf][chq]) = make_float2(__expf(gc0), __expf(gc1));
             }
         }
-        // L_ts = sum_i (e^{G_ti - r_i} k_ti)(e^{r_i - G_si} k_si), M likewise with q_t,
-        // r = G at the chunk middle (token 7), on fp32 MFMA; lane l: token l % 16,
-        // channels 16 rw + 4 (l / 16) + s
-        const int lc = 16 * rw + 4 * g4;
-        const int tq = n16 >> 2;
-        const float4 k4 = ld4(&s_kh[n16][lc]);
-        const float4 q4 = ld4(&s_qh[n16][lc]);
-        const float4 gq = ld4(&s_Gq[n16][lc]);
-        const float4 g7 = ld4(&s_Gq[CC / 2 - 1][lc]);   // quarter 1 up to token 7
-        const float4 c0 = ld4(&s_Gt[0][lc]);
-        const float4 c2 = ld4(&s_Gt[2][lc]);
-        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
-        const float gv[4] = {gq.x, gq.y, gq.z, gq.w};
-        const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
-        const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
-        const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
-        f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            // G_t - r from sums that start as close to both tokens as possible
-            const float d = tq == 0 ? gv[s] - c0v[s] - g7v[s]
-                          : tq == 1 ? gv[s] - g7v[s]
-                          : tq == 2 ? gv[s] : gv[s] + c2v[s];
-            const float ef = __expf(d), eb = __expf(-d);
-            const float b = eb * kv[s];
-            Lt = mfma4(ef * kv[s], b, Lt);
-            Mt = mfma4(ef * qv[s], b, Mt);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s_Lp[rw][4 * g4 + r][n16] = Lt[r];
-            s_Mp[rw][4 * g4 + r][n16] = Mt[r];
-        }
     };
 
     __syncthreads();                               // conv taps in LDS
+    wq0 = ld4(s_cw[chq]); wq1 = ld4(s_cw[chq + 1]);
+    wk0 = ld4(s_cw[chk]); wk1 = ld4(s_cw[chk + 1]);
+    wv0 = ld4(s_cw[chv]); wv1 = ld4(s_cw[chv + 1]);
     // ---- chunk 0 (its past rows come from the carried window)
     {
         const int64_t end = chunk_end(0);
@@ -660,18 +684,37 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     }
     __syncthreads();                               // chunk 0 prepared
     operands(0);
-    if constexpr (LR) write_lowrank();             // chunk 1's rows of a, read in the first half 1
-    __syncthreads();                               // chunk 0's operands
+    if constexpr (LR) write_lowrank();             // chunk 1's rows of a
+    __syncthreads();                               // chunk 0's operands, L and M
+    // ---- chunk 1 (its rows were loaded with chunk 0's)
+    if (NC > 1) {
+        if constexpr (LR) lowrank_f();             // f of chunk 1
+        float2 xq[RAWR], xk[RAWR], xv[RAWR];
+#pragma unroll
+        for (int r = 0; r < RAWR; ++r) {
+            xq[r] = BA::unpack2(rq[r]);
+            xk[r] = BA::unpack2(rk[r]);
+            xv[r] = BA::unpack2(rv[r]);
+        }
+        prestep(xq, xk, xv, CC, 1);
+        if (NC > 2) issue_inputs(2 * CC);
+    }
+    __syncthreads();                               // T, M of chunk 0; chunk 1 prepared
 
-    // (past the last chunk the pre-step and the operands run on masked tokens
-    // into buffers nothing reads: running them unconditionally keeps each half
-    // one straight-line block for the scheduler)
+    // (the work of chunks past the last is skipped; the branches are uniform)
+    int vb = 0;                                    // chunk i's index mod 3
 #pragma unroll 1
     for (int64_t i = 0; i < NC; ++i) {
         const int cur = (int)(i & 1);
-        // ================= half 1: pre-step of chunk i + 1, loads for chunk i + 2
-        if constexpr (LR) lowrank_f();             // f of chunk i + 1
-        {
+        const int vb1 = vb == 2 ? 0 : vb + 1, vb2 = vb1 == 2 ? 0 : vb1 + 1;
+        // ================= half 1: operands of chunk i + 1; (LR) chunk i + 2's
+        // rows of a, loaded a half earlier
+        if (i + 1 < NC) operands(cur ^ 1);
+        if constexpr (LR) write_lowrank();
+        __syncthreads();
+        // ================= half 2: pre-step of chunk i + 2, loads for chunk i + 3
+        if (i + 2 < NC) {
+            if constexpr (LR) lowrank_f();         // f of chunk i + 2
             float2 xq[RAWR], xk[RAWR], xv[RAWR];
 #pragma unroll
             for (int r = 0; r < RAWR; ++r) {
@@ -679,16 +722,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 xk[r] = BA::unpack2(rk[r]);
                 xv[r] = BA::unpack2(rv[r]);
             }
-            prestep(xq, xk, xv, (i + 1) * CC, cur ^ 1);
+            prestep(xq, xk, xv, (i + 2) * CC, vb2);
         }
-        if (i + 2 < NC) issue_inputs((i + 2) * CC);
+        if (i + 3 < NC) issue_inputs((i + 3) * CC);
         __syncthreads();
-        // ================= half 2: operands of chunk i + 1
-        operands(cur ^ 1);
-        // (LR) chunk i + 2's rows of a, loaded in half 1, for its f in the
-        // next half 1 (past the last chunk: values nothing uses)
-        if constexpr (LR) write_lowrank();
-        __syncthreads();
+        vb = vb1;
     }
 }
 
