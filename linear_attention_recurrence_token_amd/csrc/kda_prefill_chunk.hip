@@ -71,6 +71,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CK_THREADS = 1024;   // 16 wavefronts: 8 state, 8 token
+constexpr int LR_THREADS = 512;    // the low-rank form's kernel: 8 wavefronts
 constexpr int CC = 16;             // tokens per chunk
 constexpr int TW = CC / 8;         // tokens per wavefront in the token-wise work
 constexpr int RAWR = PAST + TW;    // raw rows behind those tokens
@@ -121,6 +122,14 @@ __device__ __forceinline__ f32x4 mma_hihi(u32x2 ah, u32x2 bh, f32x4 c) {
     typedef bf16x4 B4;
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, ah), __builtin_bit_cast(B4, bh), c, 0, 0, 0);
 }
+// c + a b with both operands split, over K = 16 as three 16x16x16 steps (the
+// low-rank form's kernel)
+__device__ __forceinline__ f32x4 mma16(u32x2 ah, u32x2 al, u32x2 bh, u32x2 bl, f32x4 c) {
+    typedef bf16x4 B4;
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, al), __builtin_bit_cast(B4, bh), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, ah), __builtin_bit_cast(B4, bl), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, ah), __builtin_bit_cast(B4, bh), c, 0, 0, 0);
+}
 // the four rows 4 g + r of an accumulator tile as the split B operand of a 16x16x16 step
 __device__ __forceinline__ void split4(f32x4 d, u32x2 &h, u32x2 &l) {
     const Split2 a = split2(d[0], d[1]), b = split2(d[2], d[3]);
@@ -142,14 +151,7 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// LR: the low-rank decay form.  f = W_fb a for the chunk's 16 tokens is one
-// more split-bf16 product per chunk (tokens x the token wavefront's 16 key
-// channels, K = rank): W_fb's rows for those channels stay in registers as
-// the B operand for the workgroup's life, and each chunk's rank-r rows of a
-// pass through LDS as the A operand.  The accumulator gives lane l the
-// channel 16 u + l % 16 over tokens 4 (l / 16) .. + 3, which is the unit the
-// decay sums take, so f never goes through memory.
-template <typename Act, bool LR>
+template <typename Act>
 __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     typedef BufAct<Act> BA;
     typedef typename BA::Raw2 Raw2;
@@ -197,10 +199,6 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) uint32_t s_Th[2][CC][TR], s_Tl[2][CC][TR], s_Mh[2][CC][TR], s_Ml[2][CC][TR];
     __shared__ float s_o[CC][DV + 4];      // readout of the chunk, before RMSNorm
     __shared__ float s_cw[CH][TAPS];       // conv taps of this head
-    // (LR) a chunk's rank-r rows of a split into bf16 parts, [token][k] with k
-    // padded: written at the end of a half 2, read in the next half 1
-    constexpr int AKW = LR ? (LOWRANK_MAX_RANK + 8) / 2 : 1;
-    __shared__ __attribute__((aligned(16))) uint32_t s_lah[CC][AKW], s_lal[CC][AKW];
 
     {
         const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
@@ -364,7 +362,6 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 st[rt][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
 
         __syncthreads();                           // conv taps in LDS
-        if constexpr (LR) __syncthreads();         // chunk 0's rows of a in LDS
         __syncthreads();                           // chunk 0 prepared
         partial_LM();                              // L, M of chunk 0
         __syncthreads();                           // chunk 0's operands, L and M
@@ -468,71 +465,25 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 
     // =========================================================== token role
     // decay: key channel dch over the tokens of quarter dq
-    // (LR: the lane of the f product's accumulator)
-    const int dch = LR ? 16 * rw + n16 : (rtid & (DK - 1));
-    const int dq = LR ? g4 : (rtid >> 7);
+    const int dch = rtid & (DK - 1);
+    const int dq = rtid >> 7;
     const uint32_t foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
     const float eA = __expf(p.A_log[h * DK + dch]);
     const float dtb = p.dt_bias[h * DK + dch];
 
     // registers loaded a chunk ahead: raw inputs of the next chunk to pre-step
     Raw2 rq[RAWR], rk[RAWR], rv[RAWR];
+    auto unpack_q = [&](int r) { return BA::unpack2(rq[r]); };
+    auto unpack_k = [&](int r) { return BA::unpack2(rk[r]); };
+    auto unpack_v = [&](int r) { return BA::unpack2(rv[r]); };
     // conv taps of this lane's channels, kept in registers (their LDS reads
     // would queue behind the state wavefronts' operand reads every chunk)
     float4 wq0, wq1, wk0, wk1, wv0, wv1;
     float rf[4], rb;
 
-    // (LR) W_fb's rows of this wavefront's key channels as split B operands:
-    // step m holds k = 32 m + 8 g4 + {0..7} of channel 16 u + n16, zero from
-    // the rank on; and the rank-r row piece of one token of a chunk in flight
-    // (thread: token rtid / 32, k = 4 (rtid % 32) .. + 3)
-    u32x4 wfh[LR ? 4 : 1], wfl[LR ? 4 : 1];
-    float4 ra = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int la_t = rtid >> 5, la_k = 4 * (rtid & 31);
-    if constexpr (LR) {
-        const float *wr = p.lr_wfb + ((int64_t)h * DK + 16 * rw + n16) * p.lr_rank;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int k0 = 32 * m + 8 * g4;
-            const bool live = k0 < p.lr_rank;
-            const float4 x0 = live ? ld4(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float4 x1 = live ? ld4(wr + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            const Split2 a = split2(x0.x, x0.y), b = split2(x0.z, x0.w), c = split2(x1.x, x1.y), d = split2(x1.z, x1.w);
-            wfh[m] = u32x4{a.hi, b.hi, c.hi, d.hi};
-            wfl[m] = u32x4{a.lo, b.lo, c.lo, d.lo};
-        }
-    }
-    auto issue_lowrank = [&](int64_t c0) {
-        const int64_t end = chunk_end(c0);
-        const Rsrc aa = make_rsrc(p.lr_a + (rng.lo + c0) * (int64_t)p.lr_rank,
-                                  (uint32_t)((end - c0) * p.lr_rank * 4));
-        // columns from the rank on repeat column 0 (unused, kept in range)
-        ra = bld_f32x4(aa, (uint32_t)((la_t * p.lr_rank + (la_k < p.lr_rank ? la_k : 0)) * 4));
-    };
-    auto write_lowrank = [&]() {
-        const bool live = la_k < p.lr_rank;
-        const Split2 a = split2(live ? ra.x : 0.f, live ? ra.y : 0.f);
-        const Split2 b = split2(live ? ra.z : 0.f, live ? ra.w : 0.f);
-        *reinterpret_cast<u32x2 *>(&s_lah[la_t][la_k / 2]) = u32x2{a.hi, b.hi};
-        *reinterpret_cast<u32x2 *>(&s_lal[la_t][la_k / 2]) = u32x2{a.lo, b.lo};
-    };
-    // f of the chunk whose rows are in LDS for (dch, quarter dq), into rf
-    auto lowrank_f = [&]() {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const u32x4 ah = *reinterpret_cast<const u32x4 *>(&s_lah[n16][16 * m + 4 * g4]);
-            const u32x4 al = *reinterpret_cast<const u32x4 *>(&s_lal[n16][16 * m + 4 * g4]);
-            acc = mma32(ah, al, wfh[m], wfl[m], acc);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) rf[u] = acc[u];
-    };
-
     // loads of a chunk at c0 >= CC (its past rows are tokens, not the window);
     // rows past the sequence end read as 0
     auto issue_inputs = [&](int64_t c0) {
-        if constexpr (LR) issue_lowrank(c0);       // first: the next half waits for it alone
         const int64_t base = c0 - PAST, end = chunk_end(c0);
         const Rsrc aq = tok_rsrc(p.q, BA::ELEM, base, end);
         const Rsrc ak = tok_rsrc(p.k, BA::ELEM, base, end);
@@ -544,7 +495,7 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             rk[r] = BA::load_raw2(ak, e);
             rv[r] = BA::load_raw2(av, e);
         }
-        if constexpr (!LR) {
+        {
             const Rsrc af = tok_rsrc(p.f, 4, c0, end);
 #pragma unroll
             for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
@@ -555,38 +506,47 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 
     // conv + SiLU + L2 norm of this wavefront's tokens of the chunk at c0 (zeros
     // past the end), decay sums of (dch, quarter dq); v, beta to buffer vb
-    auto prestep = [&](const float2 (&xq)[RAWR], const float2 (&xk)[RAWR], const float2 (&xv)[RAWR],
-                       int64_t c0, int vb) {
+    // (gq, gk, gv: row r of the raw window behind the tokens, as float2)
+    auto prestep = [&](auto gq, auto gk, auto gv, int64_t c0, int vb) {
         const int nv = (int)(L - c0 < CC ? L - c0 : CC);
+        // conv + SiLU of one of q, k, v for this wavefront's two tokens
+        auto act = [&](auto g, const float4 &w0, const float4 &w1, float (&a)[TW][2]) {
+            float2 x[RAWR];
+#pragma unroll
+            for (int r = 0; r < RAWR; ++r) x[r] = g(r);
+#pragma unroll
+            for (int sl = 0; sl < TW; ++sl) {
+                a[sl][0] = silu(cconv4(w0, x[sl].x, x[sl + 1].x, x[sl + 2].x, x[sl + 3].x));
+                a[sl][1] = silu(cconv4(w1, x[sl].y, x[sl + 1].y, x[sl + 2].y, x[sl + 3].y));
+            }
+        };
+        float aq[TW][2], ak[TW][2], av[TW][2];
+        act(gq, wq0, wq1, aq);
+        act(gk, wk0, wk1, ak);
+        act(gv, wv0, wv1, av);
 #pragma unroll
         for (int sl = 0; sl < TW; ++sl) {
             // (no branch on the token: the two tokens' chains interleave; a
             // token past the end is computed and then replaced by zeros)
             const int t = t0 + sl;
             const bool live = t < nv;
-            const float aq0 = silu(cconv4(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
-            const float aq1 = silu(cconv4(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
-            const float ak0 = silu(cconv4(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
-            const float ak1 = silu(cconv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
-            const float av0 = silu(cconv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
-            const float av1 = silu(cconv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
-            const float nq = rsqrtf(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
-            const float nk = rsqrtf(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
-            const float2 qh = live ? make_float2(aq0 * nq, aq1 * nq) : make_float2(0.f, 0.f);
-            const float2 kh = live ? make_float2(ak0 * nk, ak1 * nk) : make_float2(0.f, 0.f);
-            const float2 vh = live ? make_float2(av0, av1) : make_float2(0.f, 0.f);
+            const float nq = rsqrtf(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + p.l2_eps);
+            const float nk = rsqrtf(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + p.l2_eps);
+            const float2 qh = live ? make_float2(aq[sl][0] * nq, aq[sl][1] * nq) : make_float2(0.f, 0.f);
+            const float2 kh = live ? make_float2(ak[sl][0] * nk, ak[sl][1] * nk) : make_float2(0.f, 0.f);
+            const float2 vh = live ? make_float2(av[sl][0], av[sl][1]) : make_float2(0.f, 0.f);
             *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
             *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
             *reinterpret_cast<float2 *>(&s_v[vb][t][chq]) = vh;
         }
         if (lane < TW) s_beta[vb][t0 + lane] = (t0 + lane < nv) ? rb : 0.f;
         float G = 0.f;                             // held constant past the last token
+        const int rem = nv - 4 * dq;               // tokens of quarter dq within the sequence
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int t = 4 * dq + u;
             const float gk = p.lb * sigmoid(eA * (rf[u] + dtb));
-            G += (t < nv) ? gk : 0.f;
-            s_Gq[t][dch] = G;
+            G += (u < rem) ? gk : 0.f;
+            s_Gq[4 * dq + u][dch] = G;
         }
         s_Gt[dq][dch] = G;
     };
@@ -664,39 +624,22 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 xv[r] = BA::load2(av, e);
             }
         }
-        if constexpr (LR) {
-            issue_lowrank(0);
-        } else {
+        {
             const Rsrc af = tok_rsrc(p.f, 4, 0, end);
 #pragma unroll
             for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
         }
         const Rsrc ab = make_rsrc(p.beta + rng.lo * p.H, (uint32_t)(end * p.H * 4));
         rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
-        if constexpr (LR) {
-            // f of chunk 0 from its rows of a (every wavefront's part in LDS first)
-            write_lowrank();
-            __syncthreads();
-            lowrank_f();
-        }
-        prestep(xq, xk, xv, 0, 0);
+        prestep([&](int r) { return xq[r]; }, [&](int r) { return xk[r]; }, [&](int r) { return xv[r]; }, 0, 0);
         if (NC > 1) issue_inputs(CC);
     }
     __syncthreads();                               // chunk 0 prepared
     operands(0);
-    if constexpr (LR) write_lowrank();             // chunk 1's rows of a
     __syncthreads();                               // chunk 0's operands, L and M
     // ---- chunk 1 (its rows were loaded with chunk 0's)
     if (NC > 1) {
-        if constexpr (LR) lowrank_f();             // f of chunk 1
-        float2 xq[RAWR], xk[RAWR], xv[RAWR];
-#pragma unroll
-        for (int r = 0; r < RAWR; ++r) {
-            xq[r] = BA::unpack2(rq[r]);
-            xk[r] = BA::unpack2(rk[r]);
-            xv[r] = BA::unpack2(rv[r]);
-        }
-        prestep(xq, xk, xv, CC, 1);
+        prestep(unpack_q, unpack_k, unpack_v, CC, 1);
         if (NC > 2) issue_inputs(2 * CC);
     }
     __syncthreads();                               // T, M of chunk 0; chunk 1 prepared
@@ -707,14 +650,467 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     for (int64_t i = 0; i < NC; ++i) {
         const int cur = (int)(i & 1);
         const int vb1 = vb == 2 ? 0 : vb + 1, vb2 = vb1 == 2 ? 0 : vb1 + 1;
-        // ================= half 1: operands of chunk i + 1; (LR) chunk i + 2's
-        // rows of a, loaded a half earlier
+        // ================= half 1: operands of chunk i + 1
         if (i + 1 < NC) operands(cur ^ 1);
-        if constexpr (LR) write_lowrank();
         __syncthreads();
         // ================= half 2: pre-step of chunk i + 2, loads for chunk i + 3
         if (i + 2 < NC) {
-            if constexpr (LR) lowrank_f();         // f of chunk i + 2
+            prestep(unpack_q, unpack_k, unpack_v, (i + 2) * CC, vb2);
+        }
+        if (i + 3 < NC) issue_inputs((i + 3) * CC);
+        __syncthreads();
+        vb = vb1;
+    }
+}
+
+// The low-rank decay form (kda_sequence_lowrank) runs on this kernel: one
+// role, 8 wavefronts (512 threads), each owning 16 state columns and two tokens
+// of the token-wise work, as the 16-wavefront kernel's roles do together.  Its
+// W_fb operand (32 registers per lane) does not fit beside either role of the
+// 16-wavefront kernel within the 128 registers that four wavefronts per SIMD
+// allow.  f = W_fb a for the chunk's 16 tokens is one more split-bf16 product
+// per chunk (tokens x the wavefront's 16 key channels, K = rank): W_fb's rows
+// for those channels stay in registers as the B operand for the workgroup's
+// life, and each chunk's rank-r rows of a pass through LDS as the A operand.
+// The accumulator gives lane l the channel 16 w + l % 16 over tokens
+// 4 (l / 16) .. + 3, which is the unit the decay sums take, so f never goes
+// through memory.
+template <typename Act>
+__global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) {
+    typedef BufAct<Act> BA;
+    typedef typename BA::Raw2 Raw2;
+    const int slot_n = blockIdx.x / p.H;
+    const int h = blockIdx.x - slot_n * p.H;
+    int n = slot_n;
+    if (p.seq_order) {
+        n = p.seq_order[slot_n];
+        if (n < 0 || n >= p.num_seqs) return;
+    }
+    const Range rng = seq_range(p, n);
+    if (rng.len <= 0) return;
+    const int64_t L = rng.len;
+    const int64_t NC = (L + CC - 1) / CC;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int64_t unit = (int64_t)n * p.H + h;
+    const int64_t rowsz = (int64_t)p.H * DK;       // elements per token row of q, k, v, f, g, y
+    const int t0 = TW * wave;                       // this wavefront's tokens in the token-wise work
+
+    __shared__ float s_kh[CC][KP];         // k_hat of the chunk being prepared
+    __shared__ float s_qh[CC][KP];         // q_hat of the chunk being prepared
+    __shared__ float s_Gq[CC][KP];         // log-decay summed from the start of the token's quarter
+    __shared__ float s_Gt[4][DK];          // log-decay summed over each quarter
+    __shared__ float s_v[2][CC][DV + 4];   // activated v            (by chunk parity)
+    __shared__ float s_beta[2][CC];        //                        (by chunk parity)
+    // split bf16 operands e^G . k_hat, e^G . q_hat of P and R: slot (t, m, g)
+    // holds channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3} of token t
+    __shared__ __attribute__((aligned(16))) uint32_t s_kah[CC * OPR * 4], s_kal[CC * OPR * 4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_qah[CC * OPR * 4], s_qal[CC * OPR * 4];
+    // [channel][token] split e^{G_C - G} . k_hat of the update (by chunk parity)
+    __shared__ __attribute__((aligned(16))) uint32_t s_Eh[2][DK][ER], s_El[2][DK][ER];
+    __shared__ float s_gC[2][DK];          // e^{G_C}, decay of the whole chunk (by chunk parity)
+    __shared__ float s_Lp[NPART][CC][CC];  // L, M summed over one channel eighth each
+    __shared__ float s_Mp[NPART][CC][CC];
+    __shared__ float s_A[CC][TP];          // Diag(b) L, strictly lower
+    // (I + Diag(b) L)^{-1} and M (lower triangle with the diagonal), [row][column] split bf16
+    __shared__ __attribute__((aligned(16))) uint32_t s_Th[CC][TR], s_Tl[CC][TR], s_Mh[CC][TR], s_Ml[CC][TR];
+    __shared__ float s_o[CC][DV + 4];      // readout of the chunk, before RMSNorm
+    __shared__ float s_cw[CH][TAPS];       // conv taps of this head
+    // the chunk's rank-r rows of a split into bf16 parts, [token][k] with k
+    // padded, by chunk parity
+    constexpr int AKW = (LOWRANK_MAX_RANK + 8) / 2;
+    __shared__ __attribute__((aligned(16))) uint32_t s_lah[2][CC][AKW], s_lal[2][CC][AKW];
+
+    {
+        const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+        for (int c = tid; c < CH; c += LR_THREADS) st4(s_cw[c], ld4(cw + c * TAPS));
+    }
+
+    auto tok_rsrc = [&](const void *t, uint32_t elem, int64_t base, int64_t end) -> Rsrc {
+        return make_rsrc(static_cast<const char *>(t) + (rng.lo + base) * rowsz * elem,
+                         (uint32_t)((end - base) * rowsz * elem));
+    };
+    auto chunk_end = [&](int64_t c0) -> int64_t { return (c0 + CC < L) ? c0 + CC : L; };
+
+    // lane: conv channels chq, chq + 1 of q, k, v and value channels chq, chq + 1;
+    // decay: key channel dch over the tokens of quarter dq
+    const int chq = 2 * lane, chk = DK + 2 * lane, chv = 2 * DK + 2 * lane;
+    // (the lane of the f product's accumulator)
+    const int dch = 16 * wave + n16;
+    const int dq = g4;
+    const float eA = __expf(p.A_log[h * DK + dch]);
+    const float dtb = p.dt_bias[h * DK + dch];
+    const float2 gm = ld2(p.gamma + 2 * lane);
+
+    // registers loaded a chunk ahead: raw inputs of the next chunk to pre-step,
+    // and the gate pre-activations of the chunk whose epilogue comes next
+    Raw2 rq[RAWR], rk[RAWR], rv[RAWR], rg[TW];
+    float rf[4], rb;
+
+    // W_fb's rows of this wavefront's key channels as split B operands:
+    // step m holds k = 32 m + 8 g4 + {0..7} of channel 16 w + n16, zero from
+    // the rank on; and the rank-r row piece of one token of a chunk in flight
+    // (thread: token tid / 32, k = 4 (tid % 32) .. + 3)
+    u32x4 wfh[4], wfl[4];
+    float4 ra = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int la_t = tid >> 5, la_k = 4 * (tid & 31);
+    {
+        const float *wr = p.lr_wfb + ((int64_t)h * DK + 16 * wave + n16) * p.lr_rank;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int k0 = 32 * m + 8 * g4;
+            const bool live = k0 < p.lr_rank;
+            const float4 x0 = live ? ld4(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 x1 = live ? ld4(wr + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const Split2 a = split2(x0.x, x0.y), b = split2(x0.z, x0.w), c = split2(x1.x, x1.y), d = split2(x1.z, x1.w);
+            wfh[m] = u32x4{a.hi, b.hi, c.hi, d.hi};
+            wfl[m] = u32x4{a.lo, b.lo, c.lo, d.lo};
+        }
+    }
+    auto issue_lowrank = [&](int64_t c0) {
+        const int64_t end = chunk_end(c0);
+        const Rsrc aa = make_rsrc(p.lr_a + (rng.lo + c0) * (int64_t)p.lr_rank,
+                                  (uint32_t)((end - c0) * p.lr_rank * 4));
+        // columns from the rank on repeat column 0 (unused, kept in range)
+        ra = bld_f32x4(aa, (uint32_t)((la_t * p.lr_rank + (la_k < p.lr_rank ? la_k : 0)) * 4));
+    };
+    auto write_lowrank = [&](int buf) {
+        const bool live = la_k < p.lr_rank;
+        const Split2 a = split2(live ? ra.x : 0.f, live ? ra.y : 0.f);
+        const Split2 b = split2(live ? ra.z : 0.f, live ? ra.w : 0.f);
+        *reinterpret_cast<u32x2 *>(&s_lah[buf][la_t][la_k / 2]) = u32x2{a.hi, b.hi};
+        *reinterpret_cast<u32x2 *>(&s_lal[buf][la_t][la_k / 2]) = u32x2{a.lo, b.lo};
+    };
+    // f of the chunk in buffer buf for (dch, quarter dq), into rf
+    auto lowrank_f = [&](int buf) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const u32x4 ah = *reinterpret_cast<const u32x4 *>(&s_lah[buf][n16][16 * m + 4 * g4]);
+            const u32x4 al = *reinterpret_cast<const u32x4 *>(&s_lal[buf][n16][16 * m + 4 * g4]);
+            acc = mma32(ah, al, wfh[m], wfl[m], acc);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rf[u] = acc[u];
+    };
+
+    // loads of a chunk at c0 >= CC (its past rows are tokens, not the window);
+    // rows past the sequence end read as 0
+    auto issue_inputs = [&](int64_t c0) {
+        issue_lowrank(c0);                         // first: the next half waits for it alone
+        const int64_t base = c0 - PAST, end = chunk_end(c0);
+        const Rsrc aq = tok_rsrc(p.q, BA::ELEM, base, end);
+        const Rsrc ak = tok_rsrc(p.k, BA::ELEM, base, end);
+        const Rsrc av = tok_rsrc(p.v, BA::ELEM, base, end);
+#pragma unroll
+        for (int r = 0; r < RAWR; ++r) {
+            const uint32_t e = (uint32_t)((t0 + r) * rowsz + h * DK + 2 * lane);
+            rq[r] = BA::load_raw2(aq, e);
+            rk[r] = BA::load_raw2(ak, e);
+            rv[r] = BA::load_raw2(av, e);
+        }
+        const Rsrc ab = make_rsrc(p.beta + (rng.lo + c0) * p.H, (uint32_t)((end - c0) * p.H * 4));
+        rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
+    };
+    auto issue_gate = [&](int64_t c0) {
+        const Rsrc ag = tok_rsrc(p.g, BA::ELEM, c0, chunk_end(c0));
+#pragma unroll
+        for (int sl = 0; sl < TW; ++sl)
+            rg[sl] = BA::load_raw2(ag, (uint32_t)((t0 + sl) * rowsz + h * DV + 2 * lane));
+    };
+
+    // conv + SiLU + L2 norm of this wavefront's tokens of the chunk at c0 (zeros
+    // past the end), decay sums of (dch, quarter dq); v, beta to buffer buf
+    auto prestep = [&](const float2 (&xq)[RAWR], const float2 (&xk)[RAWR], const float2 (&xv)[RAWR],
+                       int64_t c0, int buf) {
+        const int nv = (int)(L - c0 < CC ? L - c0 : CC);
+        const float4 wq0 = ld4(s_cw[chq]), wq1 = ld4(s_cw[chq + 1]);
+        const float4 wk0 = ld4(s_cw[chk]), wk1 = ld4(s_cw[chk + 1]);
+        const float4 wv0 = ld4(s_cw[chv]), wv1 = ld4(s_cw[chv + 1]);
+#pragma unroll
+        for (int sl = 0; sl < TW; ++sl) {
+            const int t = t0 + sl;
+            float2 qh = make_float2(0.f, 0.f), kh = qh, vh = qh;
+            if (t < nv) {                          // wavefront-uniform
+                const float aq0 = silu(cconv4(wq0, xq[sl].x, xq[sl + 1].x, xq[sl + 2].x, xq[sl + 3].x));
+                const float aq1 = silu(cconv4(wq1, xq[sl].y, xq[sl + 1].y, xq[sl + 2].y, xq[sl + 3].y));
+                const float ak0 = silu(cconv4(wk0, xk[sl].x, xk[sl + 1].x, xk[sl + 2].x, xk[sl + 3].x));
+                const float ak1 = silu(cconv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
+                vh.x = silu(cconv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
+                vh.y = silu(cconv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
+                const float nq = rsqrtf(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
+                const float nk = rsqrtf(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
+                qh = make_float2(aq0 * nq, aq1 * nq);
+                kh = make_float2(ak0 * nk, ak1 * nk);
+            }
+            *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
+            *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
+            *reinterpret_cast<float2 *>(&s_v[buf][t][chq]) = vh;
+        }
+        if (lane < TW) s_beta[buf][t0 + lane] = (t0 + lane < nv) ? rb : 0.f;
+        float G = 0.f;                             // held constant past the last token
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = 4 * dq + u;
+            if (t < nv) G += p.lb * sigmoid(eA * (rf[u] + dtb));
+            s_Gq[t][dch] = G;
+        }
+        s_Gt[dq][dch] = G;
+    };
+
+    // split operands of the prepared chunk (into buffer buf) and the partial
+    // L, M over channel eighth `wave`
+    auto operands = [&](int buf) {
+        {
+            // lane: channels chq, chq + 1 of this wavefront's tokens (quarter wave / 2)
+            const int qt = t0 >> 2;
+            const float2 gt0 = ld2(&s_Gt[0][chq]), gt1 = ld2(&s_Gt[1][chq]);
+            const float2 gt2 = ld2(&s_Gt[2][chq]), gt3 = ld2(&s_Gt[3][chq]);
+            // sums of the quarters before and after this one
+            float2 before = make_float2(0.f, 0.f), after = make_float2(0.f, 0.f);
+            if (qt > 0) { before.x += gt0.x; before.y += gt0.y; }
+            if (qt > 1) { before.x += gt1.x; before.y += gt1.y; }
+            if (qt > 2) { before.x += gt2.x; before.y += gt2.y; }
+            if (qt < 1) { after.x += gt1.x; after.y += gt1.y; }
+            if (qt < 2) { after.x += gt2.x; after.y += gt2.y; }
+            if (qt < 3) { after.x += gt3.x; after.y += gt3.y; }
+            const float2 gq_end = ld2(&s_Gt[qt][chq]);
+            const int m = chq >> 5, gg = (chq & 15) >> 2, e = ((chq & 31) >> 4) * 4 + (chq & 3);
+            float E0[TW], E1[TW];
+#pragma unroll
+            for (int sl = 0; sl < TW; ++sl) {
+                const int t = t0 + sl;
+                const float2 gq = ld2(&s_Gq[t][chq]);
+                const float2 kh = ld2(&s_kh[t][chq]);
+                const float2 qh = ld2(&s_qh[t][chq]);
+                const float eg0 = __expf(before.x + gq.x), eg1 = __expf(before.y + gq.y);
+                const Split2 ka = split2(eg0 * kh.x, eg1 * kh.y);
+                const Split2 qa = split2(eg0 * qh.x, eg1 * qh.y);
+                const int w = (t * OPR + m * 4 + gg) * 4 + e / 2;
+                s_kah[w] = ka.hi; s_kal[w] = ka.lo;
+                s_qah[w] = qa.hi; s_qal[w] = qa.lo;
+                // G_C - G_t = (rest of this quarter) + (later quarters)
+                E0[sl] = __expf(gq_end.x - gq.x + after.x) * kh.x;
+                E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
+            }
+            const Split2 a0 = split2(E0[0], E0[1]), a1 = split2(E1[0], E1[1]);
+            reinterpret_cast<uint32_t *>(s_Eh[buf][chq])[wave] = a0.hi;
+            reinterpret_cast<uint32_t *>(s_El[buf][chq])[wave] = a0.lo;
+            reinterpret_cast<uint32_t *>(s_Eh[buf][chq + 1])[wave] = a1.hi;
+            reinterpret_cast<uint32_t *>(s_El[buf][chq + 1])[wave] = a1.lo;
+            if (wave == 0) {
+                const float gc0 = gt0.x + gt1.x + gt2.x + gt3.x, gc1 = gt0.y + gt1.y + gt2.y + gt3.y;
+                *reinterpret_cast<float2 *>(&s_gC[buf][chq]) = make_float2(__expf(gc0), __expf(gc1));
+            }
+        }
+        // L_ts = sum_i (e^{G_ti - r_i} k_ti)(e^{r_i - G_si} k_si), M likewise with q_t,
+        // r = G at the chunk middle (token 7), on fp32 MFMA; lane l: token l % 16,
+        // channels 16 wave + 4 (l / 16) + s
+        const int cb = 16 * wave + 4 * g4;
+        const int tq = n16 >> 2;
+        const float4 k4 = ld4(&s_kh[n16][cb]);
+        const float4 q4 = ld4(&s_qh[n16][cb]);
+        const float4 gq = ld4(&s_Gq[n16][cb]);
+        const float4 g7 = ld4(&s_Gq[CC / 2 - 1][cb]);   // quarter 1 up to token 7
+        const float4 c0 = ld4(&s_Gt[0][cb]);
+        const float4 c2 = ld4(&s_Gt[2][cb]);
+        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+        const float gv[4] = {gq.x, gq.y, gq.z, gq.w};
+        const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
+        const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
+        const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
+        f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // G_t - r from sums that start as close to both tokens as possible
+            const float d = tq == 0 ? gv[s] - c0v[s] - g7v[s]
+                          : tq == 1 ? gv[s] - g7v[s]
+                          : tq == 2 ? gv[s] : gv[s] + c2v[s];
+            const float ef = __expf(d), eb = __expf(-d);
+            const float b = eb * kv[s];
+            Lt = mfma4(ef * kv[s], b, Lt);
+            Mt = mfma4(ef * qv[s], b, Mt);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s_Lp[wave][4 * g4 + r][n16] = Lt[r];
+            s_Mp[wave][4 * g4 + r][n16] = Mt[r];
+        }
+    };
+
+    // T = (I + A)^{-1}, A = Diag(b) L strictly lower, by forward substitution
+    // in blocks of 4 rows on one wavefront: lane (c = l / 4, r = l % 4) builds
+    // row 4 b + r of column c in block b, and every lane of a quad keeps the
+    // finished part of column c; the rows of a block couple through quad
+    // broadcasts.  Masked entries of A are exact zeros.
+    auto solve_T = [&](int buf) {
+        {
+            const int t = lane >> 2, s0 = 4 * (lane & 3);
+            float4 a = ld4(&s_Lp[0][t][s0]);
+#pragma unroll
+            for (int q = 1; q < NPART; ++q) a += ld4(&s_Lp[q][t][s0]);
+            const float bt = s_beta[buf][t];
+            a.x = (s0 + 0 < t) ? bt * a.x : 0.f;
+            a.y = (s0 + 1 < t) ? bt * a.y : 0.f;
+            a.z = (s0 + 2 < t) ? bt * a.z : 0.f;
+            a.w = (s0 + 3 < t) ? bt * a.w : 0.f;
+            st4(&s_A[t][s0], a);
+        }
+        wave_lds_sync();
+        const int c = lane >> 2, r = lane & 3;
+        float Tc[CC];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int t = 4 * b + r;
+            // y = e_c(t) - sum over the finished rows s < 4 b of A[t][s] T[s][c]
+            float acc[4] = {(t == c) ? 1.0f : 0.0f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < b; ++s4) {
+                const float4 a = ld4(&s_A[t][4 * s4]);
+                acc[0] = fmaf(-a.x, Tc[4 * s4 + 0], acc[0]);
+                acc[1] = fmaf(-a.y, Tc[4 * s4 + 1], acc[1]);
+                acc[2] = fmaf(-a.z, Tc[4 * s4 + 2], acc[2]);
+                acc[3] = fmaf(-a.w, Tc[4 * s4 + 3], acc[3]);
+            }
+            float y = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            // inside the block: row r subtracts A[t][4 b + r'] times finished row r' < r
+            const float4 ab = ld4(&s_A[t][4 * b]);
+            const float x0 = dpp<0x00>(y);
+            y = fmaf(-ab.x, x0, y);
+            const float x1 = dpp<0x55>(y);
+            y = fmaf(-ab.y, x1, y);
+            const float x2 = dpp<0xAA>(y);
+            y = fmaf(-ab.z, x2, y);
+            const float x3 = dpp<0xFF>(y);
+            Tc[4 * b + 0] = x0;
+            Tc[4 * b + 1] = x1;
+            Tc[4 * b + 2] = x2;
+            Tc[4 * b + 3] = x3;
+            const Split2 x = split2(y, 0.f);
+            reinterpret_cast<uint16_t *>(s_Th[t])[c] = (uint16_t)x.hi;
+            reinterpret_cast<uint16_t *>(s_Tl[t])[c] = (uint16_t)x.lo;
+        }
+    };
+    auto reduce_M = [&]() {
+        const int t = lane >> 2, s0 = 4 * (lane & 3);
+        float4 m = ld4(&s_Mp[0][t][s0]);
+#pragma unroll
+        for (int q = 1; q < NPART; ++q) m += ld4(&s_Mp[q][t][s0]);
+        m.x = (s0 + 0 <= t) ? m.x : 0.f;
+        m.y = (s0 + 1 <= t) ? m.y : 0.f;
+        m.z = (s0 + 2 <= t) ? m.z : 0.f;
+        m.w = (s0 + 3 <= t) ? m.w : 0.f;
+        const Split2 a = split2(m.x, m.y), b = split2(m.z, m.w);
+        *reinterpret_cast<u32x2 *>(&s_Mh[t][s0 / 2]) = u32x2{a.hi, b.hi};
+        *reinterpret_cast<u32x2 *>(&s_Ml[t][s0 / 2]) = u32x2{a.lo, b.lo};
+    };
+
+    // RMSNorm + gate of this wavefront's tokens of the chunk at c0 (readout in s_o, gates in rg)
+    auto epilogue = [&](int64_t c0) {
+        const int nve = (int)(L - c0 < CC ? L - c0 : CC);
+        const Rsrc ay = tok_rsrc(p.y, BA::ELEM, c0, c0 + nve);
+        const Rsrc ao = tok_rsrc(p.o_raw, 4, c0, c0 + nve);
+#pragma unroll
+        for (int sl = 0; sl < TW; ++sl) {
+            const int t = t0 + sl;
+            if (t >= nve) break;                   // wavefront-uniform
+            const float2 o = ld2(&s_o[t][chq]);
+            const float r = rsqrtf(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
+            const uint32_t e = (uint32_t)(t * rowsz + h * DV + chq);
+            const float2 gg = BA::unpack2(rg[sl]);
+            float2 y;
+            y.x = sigmoid(gg.x) * gm.x * o.x * r;
+            y.y = sigmoid(gg.y) * gm.y * o.y * r;
+            BA::store2(ay, e, y);
+            if (p.o_raw) bst_f32x2(ao, o, e * 4);
+        }
+    };
+
+    // ---- state into the accumulator tiles (lane offset: row 4 g4 + r,
+    // column col0 + n16; row tile rt as the scalar offset)
+    const int col0 = 16 * wave;
+    const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
+    f32x4 st[8];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            st[rt][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
+
+    __syncthreads();                               // conv taps in LDS
+    // ---- chunk 0 (its past rows come from the carried window)
+    {
+        const int64_t end = chunk_end(0);
+        const Rsrc aq = tok_rsrc(p.q, BA::ELEM, 0, end);
+        const Rsrc ak = tok_rsrc(p.k, BA::ELEM, 0, end);
+        const Rsrc av = tok_rsrc(p.v, BA::ELEM, 0, end);
+        const float *W = p.win + unit * (PAST * CH);
+        float2 xq[RAWR], xk[RAWR], xv[RAWR];
+#pragma unroll
+        for (int r = 0; r < RAWR; ++r) {
+            const int jj = t0 - PAST + r;
+            if (jj < 0) {
+                const float *wr = W + (jj + PAST) * CH;
+                xq[r] = ld2(wr + chq);
+                xk[r] = ld2(wr + chk);
+                xv[r] = ld2(wr + chv);
+            } else {
+                const uint32_t e = (uint32_t)(jj * rowsz + h * DK + 2 * lane);
+                xq[r] = BA::load2(aq, e);
+                xk[r] = BA::load2(ak, e);
+                xv[r] = BA::load2(av, e);
+            }
+        }
+        issue_lowrank(0);
+        const Rsrc ab = make_rsrc(p.beta + rng.lo * p.H, (uint32_t)(end * p.H * 4));
+        rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
+        // f of chunk 0 from its rows of a (every wavefront's part in LDS first)
+        write_lowrank(0);
+        __syncthreads();
+        lowrank_f(0);
+        prestep(xq, xk, xv, 0, 0);
+        if (NC > 1) issue_inputs(CC);
+    }
+    __syncthreads();
+    operands(0);
+    write_lowrank(1);                              // chunk 1's rows of a, read in the first half 1
+    __syncthreads();
+
+    f32x4 Pt, Rt;
+    // P, R of the current chunk: step m covers state rows 32 m .. 32 m + 31
+    // (tiles 2 m, 2 m + 1)
+    auto products_PR = [&]() {
+        Pt = f32x4{0.f, 0.f, 0.f, 0.f};
+        Rt = Pt;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int w = (n16 * OPR + m * 4 + g4) * 4;
+            const u32x4 kah = *reinterpret_cast<const u32x4 *>(&s_kah[w]);
+            const u32x4 kal = *reinterpret_cast<const u32x4 *>(&s_kal[w]);
+            const u32x4 qah = *reinterpret_cast<const u32x4 *>(&s_qah[w]);
+            const u32x4 qal = *reinterpret_cast<const u32x4 *>(&s_qal[w]);
+            const Split2 x0 = split2(st[2 * m][0], st[2 * m][1]);
+            const Split2 x1 = split2(st[2 * m][2], st[2 * m][3]);
+            const Split2 x2 = split2(st[2 * m + 1][0], st[2 * m + 1][1]);
+            const Split2 x3 = split2(st[2 * m + 1][2], st[2 * m + 1][3]);
+            const u32x4 sh = {x0.hi, x1.hi, x2.hi, x3.hi}, sl = {x0.lo, x1.lo, x2.lo, x3.lo};
+            Pt = mma32(kah, kal, sh, sl, Pt);
+            Rt = mma32(qah, qal, sh, sl, Rt);
+        }
+    };
+    // token-wise work of half 1: pre-step of chunk i + 1, epilogue of chunk
+    // i - 1, loads for chunk i + 2 (the epilogue waits for its gate loads
+    // before the next chunk's loads are issued: the memory counter drains in
+    // order)
+    // (past the last chunk the pre-step and the operands run on masked tokens
+    // into buffers nothing reads: running them unconditionally keeps each half
+    // one straight-line block for the scheduler)
+    auto tokens_half1 = [&](int64_t i, int cur) {
+        lowrank_f(cur ^ 1);                        // f of chunk i + 1
+        {
             float2 xq[RAWR], xk[RAWR], xv[RAWR];
 #pragma unroll
             for (int r = 0; r < RAWR; ++r) {
@@ -722,12 +1118,84 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 xk[r] = BA::unpack2(rk[r]);
                 xv[r] = BA::unpack2(rv[r]);
             }
-            prestep(xq, xk, xv, (i + 2) * CC, vb2);
+            prestep(xq, xk, xv, (i + 1) * CC, cur ^ 1);
         }
-        if (i + 3 < NC) issue_inputs((i + 3) * CC);
+        if (i >= 1) epilogue((i - 1) * CC);
+        if (i + 2 < NC) issue_inputs((i + 2) * CC);
+        issue_gate(i * CC);
+    };
+    // Delta, O and the state update of the current chunk
+    auto update = [&](int cur) {
+        // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
+        f32x4 Wt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g4 + r;
+            Wt[r] = s_beta[cur][t] * (s_v[cur][t][col0 + n16] - Pt[r]);
+        }
+        const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[n16][2 * g4]);
+        const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[n16][2 * g4]);
+        const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[n16][2 * g4]);
+        const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[n16][2 * g4]);
+        u32x2 wh, wl, dh, dl;
+        split4(Wt, wh, wl);
+        const f32x4 Dt = mma16(th, tl, wh, wl, f32x4{0.f, 0.f, 0.f, 0.f});
+        split4(Dt, dh, dl);
+        const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_o[4 * g4 + r][col0 + n16] = Ot[r];
+        // S <- Diag(e^{G_C}) S + E^T Delta
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const float4 dc = ld4(&s_gC[cur][16 * rt + 4 * g4]);
+            const u32x2 eh = *reinterpret_cast<const u32x2 *>(&s_Eh[cur][16 * rt + n16][2 * g4]);
+            const u32x2 el = *reinterpret_cast<const u32x2 *>(&s_El[cur][16 * rt + n16][2 * g4]);
+            st[rt][0] *= dc.x;
+            st[rt][1] *= dc.y;
+            st[rt][2] *= dc.z;
+            st[rt][3] *= dc.w;
+            st[rt] = mma16(eh, el, dh, dl, st[rt]);
+        }
+    };
+
+    // The two wavefronts that share a SIMD (w and w + 4) take the matrix work
+    // and the vector work of each half in opposite orders, so that one's
+    // MFMAs run while the other issues vector instructions.
+    const bool mfma_first = wave < 4;
+#pragma unroll 1
+    for (int64_t i = 0; i < NC; ++i) {
+        const int cur = (int)(i & 1);
+        // ================= half 1
+        if (wave == 0) solve_T(cur);
+        else if (wave == 1) reduce_M();
+        if (mfma_first) {
+            products_PR();
+            tokens_half1(i, cur);
+        } else {
+            tokens_half1(i, cur);
+            products_PR();
+        }
         __syncthreads();
-        vb = vb1;
+        // ================= half 2
+        if (mfma_first) {
+            update(cur);
+            operands(cur ^ 1);
+        } else {
+            operands(cur ^ 1);
+            update(cur);
+        }
+        // chunk i + 2's rows of a, loaded in half 1, for its f in the
+        // next half 1 (past the last chunk: values nothing uses)
+        write_lowrank(cur);
+        __syncthreads();
     }
+
+    epilogue((NC - 1) * CC);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            bst_f32(rs_state, st[rt][r], ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
 }
 
 // window out (same as after the column-split path): every thread reads all
@@ -753,10 +1221,13 @@ __global__ __launch_bounds__(128) void chunk_window_kernel(Params p) {
     }
 }
 
-template <typename Act, bool LR>
-hipError_t launch_chunk_as(const Params &p, hipStream_t stream) {
+template <typename Act>
+hipError_t launch_chunk_as(const Params &p, bool lowrank, hipStream_t stream) {
     const int64_t units = (int64_t)p.num_seqs * p.H;
-    hipLaunchKernelGGL((prefill_chunk_kernel<Act, LR>), dim3((unsigned)units), dim3(CK_THREADS), 0, stream, p);
+    if (lowrank)
+        hipLaunchKernelGGL((prefill_chunk_lr_kernel<Act>), dim3((unsigned)units), dim3(LR_THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_chunk_kernel<Act>), dim3((unsigned)units), dim3(CK_THREADS), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_window_kernel<Act>), dim3((unsigned)units), dim3(128), 0, stream, p);
@@ -772,11 +1243,11 @@ bool prefill_chunk_supported(int32_t gate_mode, float lb, int32_t num_heads) {
 }
 
 hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream) {
-    return bf16 ? launch_chunk_as<BF16, false>(p, stream) : launch_chunk_as<F32, false>(p, stream);
+    return bf16 ? launch_chunk_as<BF16>(p, false, stream) : launch_chunk_as<F32>(p, false, stream);
 }
 
 hipError_t launch_prefill_chunk_lowrank(const Params &p, bool bf16, hipStream_t stream) {
-    return bf16 ? launch_chunk_as<BF16, true>(p, stream) : launch_chunk_as<F32, true>(p, stream);
+    return bf16 ? launch_chunk_as<BF16>(p, true, stream) : launch_chunk_as<F32>(p, true, stream);
 }
 
 }  // namespace kda
