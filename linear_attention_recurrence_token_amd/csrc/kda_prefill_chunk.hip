@@ -41,10 +41,11 @@
 //   token wavefronts 8 + u (u = 0..7) do the token-wise work of tokens 2 u,
 //     2 u + 1 (conv, SiLU, L2 norm, the split operands) and the decay sums and
 //     partial L, M of channel eighth u.
-// A wavefront issues vector instructions at about a third of its SIMD's rate,
-// so each SIMD holds four wavefronts: two of each role, whose matrix and
-// vector work overlap; and the split keeps each role's registers (the state,
-// the inputs loaded ahead) apart, within the 128 that four wavefronts allow.
+// A wavefront issues vector instructions at no more than about half its
+// SIMD's rate, and the step's chains stall it far more often, so each SIMD
+// holds four wavefronts: two of each role, whose matrix and vector work
+// overlap; and the split keeps each role's registers (the state, the inputs
+// loaded ahead) apart, within the 128 that four wavefronts allow.
 // Chunk i:
 //   half 1: state: P and R of chunk i, RMSNorm and gate of chunk i - 1, the
 //           partial L, M of chunk i + 1; token: the split operands of chunk i + 1
