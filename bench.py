@@ -72,7 +72,7 @@ CHUNK = 16
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_token_amd", "csrc")
 COMMON_SOURCES = ["kda_api.hip", "kda_device.hpp", "kda_internal.hpp", "../../include/kda.h"]
 PATH_SOURCES = {"decode": ["kda_decode.hip"], "short": ["kda_decode.hip"],
-                "chunk": ["kda_prefill_chunk.hip"], "scan": ["kda_prefill_scan.hip", "kda_prefill_split.hip"],
+                "chunk": ["kda_prefill_chunk.hip"], "chunk_short": ["kda_prefill_chunk.hip"], "scan": ["kda_prefill_scan.hip", "kda_prefill_split.hip"],
                 "split": ["kda_prefill_split.hip"], "fused": ["kda_prefill.hip", "kda_prefill_split.hip"],
                 "proj": ["kda_proj.hip"]}
 
@@ -368,17 +368,20 @@ def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=
             times.append(e0.elapsed_time(e1))
     ms = float(np.median(times))
     th = int(lens.sum()) * w.H
-    # the kernel the automatic choice runs (the library's rule: the short-
-    # sequence kernel under 8 tokens per sequence on average; else, for the
-    # bounded gate with |lower bound| <= 7.5, the two-pass chunk path for at
-    # most 64 pairs averaging 128 tokens or more (given its workspace) and the
-    # one-pass chunk kernel otherwise; else split / fused)
-    short = w.total_tokens < 8 * w.N
-    chunk = (cfg.gate_mode == kda.KDA_GATE_BOUNDED and -7.5 <= cfg.gate_lower_bound <= 0.0
-             and not short)
+    # the kernel the automatic choice runs (the library's rule: for the
+    # bounded gate with |lower bound| <= 7.5, the short-sequence kernel under 4
+    # tokens per sequence on average, the two-pass chunk path for at most 64
+    # pairs averaging 128 tokens or more (given its workspace), the chunk
+    # kernel without a pipeline up to 16 tokens on average (64 from 512
+    # pairs on) and the one-pass chunk kernel otherwise; for the other gates
+    # the short-sequence kernel under 8 tokens, else split / fused)
+    chunk_gate = cfg.gate_mode == kda.KDA_GATE_BOUNDED and -7.5 <= cfg.gate_lower_bound <= 0.0
+    short = w.total_tokens < (4 if chunk_gate else 8) * w.N
+    chunk = chunk_gate and not short
     scan = chunk and w.N * w.H <= 64 and w.total_tokens >= 128 * w.N and ws_bytes > 0
-    path = ("short" if short else ("scan" if scan else ("chunk" if chunk else
-                                                        ("split" if ws_bytes > 0 else "fused"))))
+    chunk_short = chunk and not scan and w.total_tokens <= (64 if w.N * w.H >= 512 else 16) * w.N
+    path = ("short" if short else ("scan" if scan else ("chunk_short" if chunk_short else (
+        "chunk" if chunk else ("split" if ws_bytes > 0 else "fused")))))
     traffic = committed_traffic(path, traffic_key) if traffic_key else None
     # algorithmic HBM bytes: state in+out and window in+out per pair, and per
     # token.head q, k, v, g, y (activation dtype) with f (fp32) and beta
@@ -411,7 +414,8 @@ def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic}
     if traffic_key:
-        busy = committed_sq_busy(traffic_key, {"chunk": "prefill_chunk_kernel", "scan": "scan_kernel"}.get(path, path))
+        busy = committed_sq_busy(traffic_key, {"chunk": "prefill_chunk_kernel", "scan": "scan_kernel",
+                                               "chunk_short": "prefill_chunk_short_kernel"}.get(path, path))
         if busy:
             out["roofline"]["sq_busy"] = busy
     if want_check:
@@ -677,7 +681,6 @@ def main():
     torch.cuda.set_device(dev)
     if kda.device_check() != 0:
         raise SystemExit("libkda: the current device is not a gfx950 part")
-    smi_before = rocm_smi_snapshot()
 
     N, H = 64, 32
     steps, warmup = max(1, args.steps), max(0, args.warmup)
@@ -713,6 +716,9 @@ def main():
             out["copy_calibration_bytes_each_way"] = nbytes
         print(json.dumps(out), flush=True)
         return
+    # (not in the profiling runs above: under a counter-collecting profiler
+    # the rocm-smi child would start with the profiler's library preloaded)
+    smi_before = rocm_smi_snapshot()
     log("decode %dx%d: generating %d steps of inputs" % (N, H, steps))
     check = not args.no_cpu_baseline
     dec = bench_decode(torch, kda, synth, dev, N, H, steps, warmup, check_seqs=(0, N - 1) if check else ())

@@ -101,11 +101,14 @@ typedef enum kda_gate_mode {
 } kda_gate_mode;
 
 /* Which prefill kernel kda_sequence runs.  All compute the same function
- * within the fp32 tolerance.  AUTO takes SHORT when the sequences hold fewer
- * than 8 tokens on average (total_tokens < 8 * num_seqs); otherwise, where
- * the gate allows the chunk form, SCAN for at most 64 (sequence, head) pairs
- * averaging 128 tokens or more when the workspace is large enough, else
- * CHUNK; otherwise SPLIT for few pairs and FUSED for many.  SPLIT
+ * within the fp32 tolerance.  Where the gate allows the chunk form, AUTO
+ * takes SHORT when the sequences hold fewer than 4 tokens on average
+ * (total_tokens < 4 * num_seqs); else SCAN for at most 64 (sequence, head)
+ * pairs averaging 128 tokens or more when the workspace is large enough;
+ * else CHUNK_SHORT for sequences averaging at most 16 tokens, or at most 64
+ * tokens from 512 pairs on; else CHUNK.  With the other gates AUTO takes
+ * SHORT below 8 tokens on average, else SPLIT for few pairs and FUSED for
+ * many.  SPLIT
  * spreads each pair's state columns over several workgroups (for few pairs,
  * e.g. one long sequence) and needs an fp32 buffer for the pre-norm readout:
  * o_raw, or else a workspace of the size kda_sequence_workspace_size reports.
@@ -130,7 +133,12 @@ typedef enum kda_prefill_path {
                                    long sequences.  Same gate rule as CHUNK;
                                    needs the workspace kda_sequence_workspace_size
                                    reports (less the readout part when o_raw
-                                   is given), else KDA_ERR_INVALID_ARG       */
+                                   is given), else KDA_ERR_INVALID_ARG       */,
+    KDA_PREFILL_CHUNK_SHORT = 6 /* CHUNK for sequences of a few chunks: each
+                                   pair's chunks in turn without a pipeline,
+                                   two workgroups per compute unit so that one
+                                   pair's state load and store overlap another
+                                   pair's arithmetic.  Same gate rule as CHUNK */
 } kda_prefill_path;
 
 typedef struct kda_config {

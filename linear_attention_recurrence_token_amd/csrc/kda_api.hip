@@ -77,7 +77,7 @@ kda_status check_config(const kda_config *cfg, const kda_tensors *t, int32_t num
     if (cfg->gate_mode < KDA_GATE_BOUNDED || cfg->gate_mode > KDA_GATE_RAW) return KDA_ERR_INVALID_ARG;
     if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return KDA_ERR_INVALID_ARG;
     if (cfg->gate_lower_bound != cfg->gate_lower_bound) return KDA_ERR_INVALID_ARG;
-    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_SCAN)
+    if (cfg->prefill_path < KDA_PREFILL_AUTO || cfg->prefill_path > KDA_PREFILL_CHUNK_SHORT)
         return KDA_ERR_INVALID_ARG;
     if (cfg->head_dim_k != kda::DK || cfg->head_dim_v != kda::DV || cfg->conv_taps != kda::TAPS)
         return KDA_ERR_UNSUPPORTED;
@@ -89,19 +89,37 @@ bool chunk_supported(const kda_config *cfg) {
 }
 
 // Sequences shorter than this on average run the short-sequence kernel under
-// AUTO: below about half a chunk the chunkwise kernel's fixed cost per
-// (sequence, head) outweighs its cheaper arithmetic (measured at 64 x 32:
-// the token-loop kernels are faster up to 4 tokens, even at 8, the chunk
-// kernel faster from 13 on).
-constexpr int64_t CHUNK_MIN_AVG_TOKENS = 8;
+// AUTO (the token-loop kernels' cost grows with the tokens, the chunk
+// kernels' barely below a chunk).  Measured at 64 x 32: with the chunk forms'
+// gate the token loop is faster up to 3 tokens, level at 4 (fp32) and slower
+// from 6 (fp32) or 4 (bf16) on; with the other gates the token loops are the
+// only kernels, the short one faster than the fused one below 8 tokens.
+constexpr int64_t CHUNK_MIN_AVG_TOKENS = 4;
+constexpr int64_t SHORT_MAX_AVG_TOKENS_OTHER_GATES = 8;
 
-bool auto_short(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
-    return total_tokens < CHUNK_MIN_AVG_TOKENS * (int64_t)num_seqs &&
-           kda::short_supported(total_tokens, num_heads);
+bool auto_short(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    const int64_t lim = chunk_supported(cfg) ? CHUNK_MIN_AVG_TOKENS : SHORT_MAX_AVG_TOKENS_OTHER_GATES;
+    return total_tokens < lim * (int64_t)num_seqs && kda::short_supported(total_tokens, cfg->num_heads);
 }
 
 bool auto_chunk(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     return chunk_supported(cfg) && total_tokens >= CHUNK_MIN_AVG_TOKENS * (int64_t)num_seqs;
+}
+
+// The chunk kernel without a pipeline (two workgroups per compute unit, so
+// one pair's state round trip overlaps another's arithmetic) against the
+// pipelined one, measured: faster up to 16 tokens per sequence at any batch
+// (level at 256 pairs), up to 64 tokens from 512 pairs on (64 x 32 fp32: 86
+// vs 106 us at 13 tokens, 241 vs 253 at 64, level at 96, slower from 128;
+// 16 x 64 bf16: 104 vs 115 us at 64, level at 128; 8 x 32: slower from 32).
+constexpr int64_t CHUNK_SHORT_MAX_AVG_TOKENS = 16;
+constexpr int64_t CHUNK_SHORT_MAX_AVG_TOKENS_MANY = 64;
+constexpr int64_t CHUNK_SHORT_MANY_UNITS = 512;
+
+bool auto_chunk_short(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    const int64_t units = (int64_t)num_seqs * cfg->num_heads;
+    const int64_t lim = units >= CHUNK_SHORT_MANY_UNITS ? CHUNK_SHORT_MAX_AVG_TOKENS_MANY : CHUNK_SHORT_MAX_AVG_TOKENS;
+    return auto_chunk(cfg, num_seqs, total_tokens) && total_tokens <= lim * (int64_t)num_seqs;
 }
 
 // The two-pass chunk path pays for writing and reading every chunk's operands
@@ -129,18 +147,19 @@ int64_t readout_bytes(const kda_config *cfg, int64_t total_tokens) {
 }
 
 // columns per lane of the split prefill for this shape, 0 = another kernel.
-// Automatic choice: the short-sequence kernel when the sequences average
-// under 8 tokens; else the chunkwise kernel wherever the gate allows it (it
-// is the fastest at every batch size); else the split kernel for few
-// (sequence, head) pairs, else the fused kernel.
+// Automatic choice: the short-sequence kernel below the averages above; else
+// the chunkwise kernels wherever the gate allows them (they are the fastest
+// at every batch size); else the split kernel for few (sequence, head) pairs,
+// else the fused kernel.
 int split_cols_for(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     const int64_t units = (int64_t)num_seqs * cfg->num_heads;
     if (cfg->prefill_path == KDA_PREFILL_FUSED || cfg->prefill_path == KDA_PREFILL_CHUNK ||
-        cfg->prefill_path == KDA_PREFILL_SHORT || cfg->prefill_path == KDA_PREFILL_SCAN)
+        cfg->prefill_path == KDA_PREFILL_SHORT || cfg->prefill_path == KDA_PREFILL_SCAN ||
+        cfg->prefill_path == KDA_PREFILL_CHUNK_SHORT)
         return 0;
     const int c = kda::prefill_split_cols(units);
     if (cfg->prefill_path == KDA_PREFILL_SPLIT) return c ? c : 4;
-    if (auto_short(num_seqs, total_tokens, cfg->num_heads) || auto_chunk(cfg, num_seqs, total_tokens)) return 0;
+    if (auto_short(cfg, num_seqs, total_tokens) || auto_chunk(cfg, num_seqs, total_tokens)) return 0;
     return c;
 }
 
@@ -382,7 +401,9 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
             return KDA_ERR_INVALID_ARG;
         }
     }
-    if (cfg->prefill_path == KDA_PREFILL_CHUNK && !chunk_supported(cfg)) return KDA_ERR_UNSUPPORTED;
+    if ((cfg->prefill_path == KDA_PREFILL_CHUNK || cfg->prefill_path == KDA_PREFILL_CHUNK_SHORT) &&
+        !chunk_supported(cfg))
+        return KDA_ERR_UNSUPPORTED;
     if (cfg->prefill_path == KDA_PREFILL_SHORT && !kda::short_supported(total_tokens, cfg->num_heads))
         return KDA_ERR_UNSUPPORTED;
     st = device_ok();
@@ -401,8 +422,11 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
     else if (obuf)
         e = kda::launch_prefill_split(p, bf16, obuf, cols, s);
     else if (cfg->prefill_path == KDA_PREFILL_SHORT ||
-             (cfg->prefill_path == KDA_PREFILL_AUTO && auto_short(num_seqs, total_tokens, cfg->num_heads)))
+             (cfg->prefill_path == KDA_PREFILL_AUTO && auto_short(cfg, num_seqs, total_tokens)))
         e = kda::launch_short(p, bf16, s);
+    else if (cfg->prefill_path == KDA_PREFILL_CHUNK_SHORT ||
+             (cfg->prefill_path == KDA_PREFILL_AUTO && auto_chunk_short(cfg, num_seqs, total_tokens)))
+        e = kda::launch_prefill_chunk_short(p, bf16, s);
     else if (cfg->prefill_path == KDA_PREFILL_CHUNK ||
              (cfg->prefill_path == KDA_PREFILL_AUTO && auto_chunk(cfg, num_seqs, total_tokens)))
         e = kda::launch_prefill_chunk(p, bf16, s);

@@ -63,6 +63,9 @@ hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream);
 // p.lr_rank a multiple of 32 up to LOWRANK_MAX_RANK) instead of read from p.f
 constexpr int LOWRANK_MAX_RANK = 128;
 hipError_t launch_prefill_chunk_lowrank(const Params &p, bool bf16, hipStream_t stream);
+// the chunk form for sequences of a few chunks: no pipeline across chunks, two
+// workgroups per compute unit (same gate support as launch_prefill_chunk)
+hipError_t launch_prefill_chunk_short(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_split(const Params &p, bool bf16, float *obuf, int cols_per_lane,
                                 hipStream_t stream);
 // RMSNorm + gate from a pre-norm readout buffer ([T, H, 128] fp32) into y, and

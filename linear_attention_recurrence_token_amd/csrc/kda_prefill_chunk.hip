@@ -145,6 +145,27 @@ __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast
 __device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
 __device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
 
+// G_t - r, the log-decay of a token of quarter tq relative to the chunk
+// middle, from the sums that start as close to the token as possible: the
+// token's own sum from its quarter's start (g), minus quarter 0 (c0) and the
+// part of quarter 1 up to token 7 (g7) for quarter 0, minus g7 for quarter 1,
+// plus quarter 2 (c2) for quarter 3.  The terms are chosen by coefficients 0
+// or 1 per lane rather than by branches (x - 1 y and x + 0 y round exactly as
+// x - y and x).
+struct MidCoef {
+    float a0, a1, a3;
+};
+// (formed anew at each use from an opaque copy of the lane's token, rather
+// than kept in registers across a chunk loop)
+__device__ __forceinline__ MidCoef mid_coef(int t) {
+    asm volatile("" : "+v"(t));
+    const int tq = t >> 2;
+    return {tq == 0 ? 1.f : 0.f, tq <= 1 ? 1.f : 0.f, tq == 3 ? 1.f : 0.f};
+}
+__device__ __forceinline__ float rel_mid(MidCoef m, float g, float c0, float g7, float c2) {
+    return fmaf(m.a3, c2, fmaf(-m.a1, g7, fmaf(-m.a0, c0, g)));
+}
+
 // LDS writes of this wavefront visible to its other lanes (no other wavefront)
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1199,6 +1220,533 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
             bst_f32(rs_state, st[rt][r], ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
 }
 
+// Sequences of a few chunks.  The kernels above hold one workgroup per
+// compute unit (1024 threads and 147 KB of LDS, or 512 threads at 256
+// registers), so a pair's state load and store never overlap another pair's
+// work; in a batch of short sequences that round trip (128 KiB per pair) is
+// most of the bytes.  This kernel takes a pair's chunks one after the other,
+// without a pipeline: 8 wavefronts (512 threads), one buffer of everything,
+// 79 KB of LDS and at most 128 registers, so that two workgroups share a
+// compute unit and one's loads and stores run beside the other's arithmetic.
+// Wavefront w does the token-wise work of tokens 2 w, 2 w + 1 (as the token
+// role above) and holds rows 64 (w % 2) .. + 63 of state columns 32 (w / 2)
+// .. + 31: the two wavefronts of a column block add their partial P and R
+// through LDS, and every state load and store covers 128 contiguous bytes of
+// a row.  It writes the conv window out itself.  Per chunk, four workgroup
+// barriers apart:
+//   1. the chunk's loads (the first chunk: the carried window into LDS, the
+//      state last); conv, SiLU, L2 norm and the decay sums of tokens 2 w,
+//      2 w + 1 and of a channel quarter
+//   2. the split operands; partial L (wavefronts 0-3, one key-channel quarter
+//      each) or M (wavefronts 4-7)
+//   3. T (wavefront 0) and M (wavefront 1); P and R over the wavefront's rows
+//   4. the other half's P and R added; Delta, O, the state update, the sums
+//      of O^2 over the wavefront's readout columns
+//   then the RMSNorm and gate of the chunk and its stores.
+constexpr int CS_THREADS = 512;
+constexpr int CS_PART = 4;         // partial L, M over channel quarters
+
+template <typename Act> __device__ __forceinline__ void bst_one(Rsrc r, uint32_t i, float x);
+template <> __device__ __forceinline__ void bst_one<F32>(Rsrc r, uint32_t i, float x) { bst_f32(r, x, i * 4); }
+template <> __device__ __forceinline__ void bst_one<BF16>(Rsrc r, uint32_t i, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(x, 0.f) & 0xffffu), r, i * 2, 0, 0);
+}
+
+template <typename Act>
+__global__ __launch_bounds__(CS_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void prefill_chunk_short_kernel(Params p) {
+    typedef BufAct<Act> BA;
+    const int slot_n = blockIdx.x / p.H;
+    const int h = blockIdx.x - slot_n * p.H;
+    int n = slot_n;
+    if (p.seq_order) {
+        n = p.seq_order[slot_n];
+        if (n < 0 || n >= p.num_seqs) return;
+    }
+    const Range rng = seq_range(p, n);
+    if (rng.len <= 0) return;
+    const int64_t L = rng.len;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // in a scalar register
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int t0 = TW * wave;                       // tokens of this wavefront's token-wise work
+    // its state block: rows 64 hb .. 64 hb + 63 of columns 32 cb .. 32 cb + 31
+    const int cb = wave >> 1, hb = wave & 1;
+    const int64_t unit = (int64_t)n * p.H + h;
+    const int64_t rowsz = (int64_t)p.H * DK;       // elements per token row of q, k, v, f, g, y
+
+    // k_hat, q_hat and the log-decay summed from the start of the token's
+    // quarter; after the operands are formed from them, the partial P and R
+    // that the two wavefronts of a column block exchange
+    __shared__ __attribute__((aligned(16))) float s_pre[3][CC][KP];
+    float (*s_kh)[KP] = s_pre[0];
+    float (*s_qh)[KP] = s_pre[1];
+    float (*s_Gq)[KP] = s_pre[2];
+    float *s_xP = &s_pre[0][0][0];            // [wavefront][column tile][16][16]
+    float *s_xR = s_xP + 8 * 2 * 256;         // [wavefront][16][16]
+    static_assert(8 * 3 * 256 <= 3 * CC * KP, "exchange area");
+    __shared__ float s_Gt[4][DK];          // log-decay summed over each quarter
+    __shared__ float s_v[CC][DV + 4];      // activated v
+    __shared__ float s_beta[CC];
+    // split bf16 operands e^G . k_hat, e^G . q_hat of P and R: slot (t, m, g)
+    // holds channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3} of token t
+    __shared__ __attribute__((aligned(16))) uint32_t s_kah[CC * OPR * 4], s_kal[CC * OPR * 4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_qah[CC * OPR * 4], s_qal[CC * OPR * 4];
+    // [channel][token] split e^{G_C - G} . k_hat of the update
+    __shared__ __attribute__((aligned(16))) uint32_t s_Eh[DK][ER], s_El[DK][ER];
+    __shared__ float s_gC[DK];             // e^{G_C}, decay of the whole chunk
+    __shared__ float s_Lp[CS_PART][CC][CC];   // L, M summed over one channel quarter each
+    __shared__ float s_Mp[CS_PART][CC][CC];
+    __shared__ float s_A[CC][TP];          // Diag(b) L, strictly lower
+    // (I + Diag(b) L)^{-1} and M (lower triangle with the diagonal), [row][column] split bf16
+    __shared__ __attribute__((aligned(16))) uint32_t s_Th[CC][TR], s_Tl[CC][TR], s_Mh[CC][TR], s_Ml[CC][TR];
+    __shared__ __attribute__((aligned(16))) float s_ss[8][CC];   // sums of O^2 over each wavefront's columns
+    __shared__ __attribute__((aligned(16))) float s_win[PAST][CH];  // the carried conv window
+
+    // the state in the accumulator tiles: in tile 4 ct + rl, lane (g4, n16)
+    // holds row 64 hb + 16 rl + 4 g4 + r, column 32 cb + 2 n16 + ct in element
+    // r.  The two column tiles interleave, so a lane's two columns are
+    // adjacent and each load or store of a row covers 128 contiguous bytes
+    // (a wavefront owning 16 columns would touch 64-byte halves of lines).
+    // Loaded with the first chunk.
+    const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
+    f32x4 st[8];
+    auto st_off = [&](int rl, int r) -> uint32_t {
+        return (uint32_t)(((64 * hb + 16 * rl + 4 * g4 + r) * DV + 32 * cb + 2 * n16) * 4);
+    };
+
+    // one chunk; the first is its own copy, which also loads the state (after
+    // the chunk's inputs: loads complete in order, so the pre-step waits for
+    // the inputs alone and the state arrives during it)
+    auto chunk = [&](int64_t c0, auto first) {
+        // the lane's indices anew each chunk (an opaque copy of the thread
+        // index): otherwise every address derived from them is kept live
+        // across the loop, beyond the registers two workgroups per compute
+        // unit allow
+        int ti = tid;
+        asm volatile("" : "+v"(ti));
+        const int lane = ti & 63;
+        const int n16 = lane & 15, g4 = lane >> 4;
+        auto tok_rsrc = [&](const void *t, uint32_t elem, int64_t base, int64_t end) -> Rsrc {
+            return make_rsrc(static_cast<const char *>(t) + (rng.lo + base) * rowsz * elem,
+                             (uint32_t)((end - base) * rowsz * elem));
+        };
+        // lane: conv channels chq, chq + 1 of q, k, v (and value channels chq, chq + 1);
+        // decay: key channel dch over the tokens of quarter dq
+        const int chq = 2 * lane, chk = DK + 2 * lane, chv = 2 * DK + 2 * lane;
+        const int dch = ti & (DK - 1), dq = ti >> 7;
+        const uint32_t foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
+        const float eA = __expf(p.A_log[h * DK + dch]);
+        const float dtb = p.dt_bias[h * DK + dch];
+        const int jo = 32 * cb + 2 * n16 + hb;   // the column whose readout this lane forms
+        const float gmc = p.gamma[jo];
+        // conv taps of this head, read per chunk (cache hits) rather than held
+        // across the loop
+        const Rsrc rs_cw = make_rsrc(p.conv_w + (int64_t)h * (CH * TAPS), CH * TAPS * 4);
+
+        // T = (I + A)^{-1} by forward substitution, as in the kernel above
+        auto solve_T = [&]() {
+            {
+                const int t = lane >> 2, s0 = 4 * (lane & 3);
+                float4 a = ld4(&s_Lp[0][t][s0]);
+#pragma unroll
+                for (int q = 1; q < CS_PART; ++q) a += ld4(&s_Lp[q][t][s0]);
+                const float bt = s_beta[t];
+                a.x = (s0 + 0 < t) ? bt * a.x : 0.f;
+                a.y = (s0 + 1 < t) ? bt * a.y : 0.f;
+                a.z = (s0 + 2 < t) ? bt * a.z : 0.f;
+                a.w = (s0 + 3 < t) ? bt * a.w : 0.f;
+                st4(&s_A[t][s0], a);
+            }
+            wave_lds_sync();
+            const int c = lane >> 2, r = lane & 3;
+            float Tc[CC];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int t = 4 * b + r;
+                float acc[4] = {(t == c) ? 1.0f : 0.0f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < b; ++s4) {
+                    const float4 a = ld4(&s_A[t][4 * s4]);
+                    acc[0] = fmaf(-a.x, Tc[4 * s4 + 0], acc[0]);
+                    acc[1] = fmaf(-a.y, Tc[4 * s4 + 1], acc[1]);
+                    acc[2] = fmaf(-a.z, Tc[4 * s4 + 2], acc[2]);
+                    acc[3] = fmaf(-a.w, Tc[4 * s4 + 3], acc[3]);
+                }
+                float y = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                const float4 ab = ld4(&s_A[t][4 * b]);
+                const float x0 = dpp<0x00>(y);
+                y = fmaf(-ab.x, x0, y);
+                const float x1 = dpp<0x55>(y);
+                y = fmaf(-ab.y, x1, y);
+                const float x2 = dpp<0xAA>(y);
+                y = fmaf(-ab.z, x2, y);
+                const float x3 = dpp<0xFF>(y);
+                Tc[4 * b + 0] = x0;
+                Tc[4 * b + 1] = x1;
+                Tc[4 * b + 2] = x2;
+                Tc[4 * b + 3] = x3;
+                const Split2 x = split2(y, 0.f);
+                reinterpret_cast<uint16_t *>(s_Th[t])[c] = (uint16_t)x.hi;
+                reinterpret_cast<uint16_t *>(s_Tl[t])[c] = (uint16_t)x.lo;
+            }
+        };
+        auto reduce_M = [&]() {
+            const int t = lane >> 2, s0 = 4 * (lane & 3);
+            float4 m = ld4(&s_Mp[0][t][s0]);
+#pragma unroll
+            for (int q = 1; q < CS_PART; ++q) m += ld4(&s_Mp[q][t][s0]);
+            m.x = (s0 + 0 <= t) ? m.x : 0.f;
+            m.y = (s0 + 1 <= t) ? m.y : 0.f;
+            m.z = (s0 + 2 <= t) ? m.z : 0.f;
+            m.w = (s0 + 3 <= t) ? m.w : 0.f;
+            const Split2 a = split2(m.x, m.y), b = split2(m.z, m.w);
+            *reinterpret_cast<u32x2 *>(&s_Mh[t][s0 / 2]) = u32x2{a.hi, b.hi};
+            *reinterpret_cast<u32x2 *>(&s_Ml[t][s0 / 2]) = u32x2{a.lo, b.lo};
+        };
+        // wavefronts 0-3: L over key channels 32 j .. 32 j + 31 (j = w); 4-7: M
+        // over the same quarter (j = w - 4); lane l: token l % 16 and channels
+        // 32 j + 8 (l / 16) + {0..7}; factors e^{+-(G - r)}, r the log-decay at
+        // the chunk middle, as in the kernel above
+        auto partial_LM = [&]() {
+            const int j = wave & 3;
+            const bool is_M = wave >= 4;              // wavefront-uniform
+            const MidCoef mc = mid_coef(n16);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int lc = 32 * j + 8 * g4 + 4 * hh;
+                const float4 k4 = ld4(&s_kh[n16][lc]);
+                const float4 a4 = is_M ? ld4(&s_qh[n16][lc]) : k4;
+                const float4 gq = ld4(&s_Gq[n16][lc]);
+                const float4 g7 = ld4(&s_Gq[CC / 2 - 1][lc]);
+                const float4 c0 = ld4(&s_Gt[0][lc]);
+                const float4 c2 = ld4(&s_Gt[2][lc]);
+                const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+                const float gv[4] = {gq.x, gq.y, gq.z, gq.w};
+                const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
+                const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
+                const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float d = rel_mid(mc, gv[s], c0v[s], g7v[s], c2v[s]);
+                    acc = mfma4(__expf(d) * av[s], __expf(-d) * kv[s], acc);
+                }
+            }
+            float (*dst)[CC] = is_M ? s_Mp[j] : s_Lp[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[4 * g4 + r][n16] = acc[r];
+        };
+        // split operands of the chunk (lane: channels chq, chq + 1 of tokens t0, t0 + 1)
+        auto operands = [&]() {
+            const int qt = t0 >> 2;
+            const float2 gt0 = ld2(&s_Gt[0][chq]), gt1 = ld2(&s_Gt[1][chq]);
+            const float2 gt2 = ld2(&s_Gt[2][chq]), gt3 = ld2(&s_Gt[3][chq]);
+            float2 before = make_float2(0.f, 0.f), after = make_float2(0.f, 0.f);
+            if (qt > 0) { before.x += gt0.x; before.y += gt0.y; }
+            if (qt > 1) { before.x += gt1.x; before.y += gt1.y; }
+            if (qt > 2) { before.x += gt2.x; before.y += gt2.y; }
+            if (qt < 1) { after.x += gt1.x; after.y += gt1.y; }
+            if (qt < 2) { after.x += gt2.x; after.y += gt2.y; }
+            if (qt < 3) { after.x += gt3.x; after.y += gt3.y; }
+            const float2 gq_end = ld2(&s_Gt[qt][chq]);
+            const int m = chq >> 5, gg = (chq & 15) >> 2, e = ((chq & 31) >> 4) * 4 + (chq & 3);
+            float E0[TW], E1[TW];
+#pragma unroll
+            for (int sl = 0; sl < TW; ++sl) {
+                const int t = t0 + sl;
+                const float2 gq = ld2(&s_Gq[t][chq]);
+                const float2 kh = ld2(&s_kh[t][chq]);
+                const float2 qh = ld2(&s_qh[t][chq]);
+                const float eg0 = __expf(before.x + gq.x), eg1 = __expf(before.y + gq.y);
+                const Split2 ka = split2(eg0 * kh.x, eg1 * kh.y);
+                const Split2 qa = split2(eg0 * qh.x, eg1 * qh.y);
+                const int w = (t * OPR + m * 4 + gg) * 4 + e / 2;
+                s_kah[w] = ka.hi; s_kal[w] = ka.lo;
+                s_qah[w] = qa.hi; s_qal[w] = qa.lo;
+                E0[sl] = __expf(gq_end.x - gq.x + after.x) * kh.x;
+                E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
+            }
+            const Split2 a0 = split2(E0[0], E0[1]), a1 = split2(E1[0], E1[1]);
+            reinterpret_cast<uint32_t *>(s_Eh[chq])[wave] = a0.hi;
+            reinterpret_cast<uint32_t *>(s_El[chq])[wave] = a0.lo;
+            reinterpret_cast<uint32_t *>(s_Eh[chq + 1])[wave] = a1.hi;
+            reinterpret_cast<uint32_t *>(s_El[chq + 1])[wave] = a1.lo;
+            if (wave == 0) {
+                const float gc0 = gt0.x + gt1.x + gt2.x + gt3.x, gc1 = gt0.y + gt1.y + gt2.y + gt3.y;
+                *reinterpret_cast<float2 *>(&s_gC[chq]) = make_float2(__expf(gc0), __expf(gc1));
+            }
+        };
+
+        const int64_t end = (c0 + CC < L) ? c0 + CC : L;
+        const int nv = (int)(end - c0);
+        // ================= 1: loads; conv, SiLU, L2 norm, decay sums
+        // (rows before the sequence start come from the carried window, rows
+        // past its end read as 0)
+        // raw rows behind this wavefront's tokens: rows of the sequence (past
+        // its end they read as 0) and, in the first chunk, rows of the carried
+        // window, which are copied to LDS first (a token row's load is then
+        // sent out of range and reads as 0, without a branch on the row)
+        typename BA::Raw2 xq[RAWR], xk[RAWR], xv[RAWR];
+        float rf[4], gg[4], rb;
+        float4 wt[6];                              // conv taps of channels chq, chq + 1 of q, k, v
+        float wn[PAST];
+        const float *W = p.win + unit * (PAST * CH);
+        if constexpr (decltype(first)::value) {
+            if (tid < CH) {
+#pragma unroll
+                for (int r = 0; r < PAST; ++r) wn[r] = W[r * CH + tid];
+            }
+        }
+        {
+#pragma unroll
+            for (int i = 0; i < 6; ++i)
+                wt[i] = bld_f32x4(rs_cw, ((i >> 1) * DK + chq + (i & 1)) * TAPS * 4);
+            const int64_t base = c0 == 0 ? 0 : c0 - PAST;
+            const Rsrc aq = tok_rsrc(p.q, BA::ELEM, base, end);
+            const Rsrc ak = tok_rsrc(p.k, BA::ELEM, base, end);
+            const Rsrc av = tok_rsrc(p.v, BA::ELEM, base, end);
+#pragma unroll
+            for (int r = 0; r < RAWR; ++r) {
+                const int64_t jj = c0 + t0 - PAST + r;
+                const uint32_t e = jj < 0 ? 0x40000000u : (uint32_t)((jj - base) * rowsz + h * DK + 2 * lane);
+                xq[r] = BA::load_raw2(aq, e);
+                xk[r] = BA::load_raw2(ak, e);
+                xv[r] = BA::load_raw2(av, e);
+            }
+            const Rsrc af = tok_rsrc(p.f, 4, c0, end);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rf[u] = bld_f32(af, foff, (uint32_t)(u * rowsz * 4));
+            const Rsrc ab = make_rsrc(p.beta + (rng.lo + c0) * p.H, (uint32_t)((end - c0) * p.H * 4));
+            rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
+            const Rsrc ag = tok_rsrc(p.g, BA::ELEM, c0, end);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                gg[r] = bld_one<Act>(ag, (uint32_t)((4 * g4 + r) * rowsz + h * DV + jo));
+        }
+        if constexpr (decltype(first)::value) {
+#pragma unroll
+            for (int rl = 0; rl < 4; ++rl)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float2 x = bld_f32x2(rs_state, st_off(rl, r));
+                    st[rl][r] = x.x;
+                    st[4 + rl][r] = x.y;
+                }
+            if (tid < CH) {
+#pragma unroll
+                for (int r = 0; r < PAST; ++r) s_win[r][tid] = wn[r];
+            }
+            __syncthreads();
+        }
+        {
+            auto act = [&](const typename BA::Raw2 (&raw)[RAWR], int ch, const float4 &w0, const float4 &w1,
+                           float (&a)[TW][2]) {
+                float2 x[RAWR];
+#pragma unroll
+                for (int r = 0; r < RAWR; ++r) {
+                    x[r] = BA::unpack2(raw[r]);
+                    if constexpr (decltype(first)::value) {
+                        if (t0 - PAST + r < 0) x[r] = ld2(&s_win[t0 + r][ch]);   // wavefront-uniform
+                    }
+                }
+#pragma unroll
+                for (int sl = 0; sl < TW; ++sl) {
+                    a[sl][0] = silu(cconv4(w0, x[sl].x, x[sl + 1].x, x[sl + 2].x, x[sl + 3].x));
+                    a[sl][1] = silu(cconv4(w1, x[sl].y, x[sl + 1].y, x[sl + 2].y, x[sl + 3].y));
+                }
+            };
+            float aq[TW][2], ak[TW][2], av[TW][2];
+            act(xq, chq, wt[0], wt[1], aq);
+            act(xk, chk, wt[2], wt[3], ak);
+            act(xv, chv, wt[4], wt[5], av);
+#pragma unroll
+            for (int sl = 0; sl < TW; ++sl) {
+                const int t = t0 + sl;
+                const bool live = t < nv;
+                const float nq = rsqrtf(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + p.l2_eps);
+                const float nk = rsqrtf(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + p.l2_eps);
+                const float2 qh = live ? make_float2(aq[sl][0] * nq, aq[sl][1] * nq) : make_float2(0.f, 0.f);
+                const float2 kh = live ? make_float2(ak[sl][0] * nk, ak[sl][1] * nk) : make_float2(0.f, 0.f);
+                const float2 vh = live ? make_float2(av[sl][0], av[sl][1]) : make_float2(0.f, 0.f);
+                *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
+                *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
+                *reinterpret_cast<float2 *>(&s_v[t][chq]) = vh;
+            }
+            if (lane < TW) s_beta[t0 + lane] = (t0 + lane < nv) ? rb : 0.f;
+            float G = 0.f;                         // held constant past the last token
+            const int rem = nv - 4 * dq;           // tokens of quarter dq within the sequence
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float gk = p.lb * sigmoid(eA * (rf[u] + dtb));
+                G += (u < rem) ? gk : 0.f;
+                s_Gq[4 * dq + u][dch] = G;
+            }
+            s_Gt[dq][dch] = G;
+        }
+        __syncthreads();
+        // ================= 2: split operands; partial L or M
+        operands();
+        partial_LM();
+        __syncthreads();
+        // ================= 3: T, M; P and R over this wavefront's 64 rows
+        // (step m covers its row tiles 2 m, 2 m + 1: key channels from 64 hb +
+        // 32 m, operand slot 2 hb + m), handed to the other wavefront of the
+        // column block: both P tiles, and the R tile whose readout it forms
+        if (wave == 0) solve_T();
+        else if (wave == 1) reduce_M();
+        f32x4 Pt[2], Rt[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) Pt[ct] = Rt[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int w = (n16 * OPR + (2 * hb + m) * 4 + g4) * 4;
+            const u32x4 kah = *reinterpret_cast<const u32x4 *>(&s_kah[w]);
+            const u32x4 kal = *reinterpret_cast<const u32x4 *>(&s_kal[w]);
+            const u32x4 qah = *reinterpret_cast<const u32x4 *>(&s_qah[w]);
+            const u32x4 qal = *reinterpret_cast<const u32x4 *>(&s_qal[w]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const f32x4 &a = st[4 * ct + 2 * m], &b = st[4 * ct + 2 * m + 1];
+                const Split2 x0 = split2(a[0], a[1]), x1 = split2(a[2], a[3]);
+                const Split2 x2 = split2(b[0], b[1]), x3 = split2(b[2], b[3]);
+                const u32x4 sh = {x0.hi, x1.hi, x2.hi, x3.hi}, sl = {x0.lo, x1.lo, x2.lo, x3.lo};
+                Pt[ct] = mma32(kah, kal, sh, sl, Pt[ct]);
+                Rt[ct] = mma32(qah, qal, sh, sl, Rt[ct]);
+            }
+        }
+        {
+            // lane (g4, n16): rows 4 g4 + r of the 16 x 16 tiles
+            float *xp = s_xP + wave * 512 + g4 * 64 + n16;
+            float *xr = s_xR + wave * 256 + g4 * 64 + n16;
+            const f32x4 &ro = hb ? Rt[0] : Rt[1];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                xp[16 * r] = Pt[0][r];
+                xp[256 + 16 * r] = Pt[1][r];
+                xr[16 * r] = ro[r];
+            }
+        }
+        __syncthreads();
+        f32x4 Rs;                                   // R of this lane's readout column, whole
+        {
+            const int pw = wave ^ 1;
+            const float *xp = s_xP + pw * 512 + g4 * 64 + n16;
+            const float *xr = s_xR + pw * 256 + g4 * 64 + n16;
+            const f32x4 &ri = hb ? Rt[1] : Rt[0];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Pt[0][r] += xp[16 * r];
+                Pt[1][r] += xp[256 + 16 * r];
+                Rs[r] = ri[r] + xr[16 * r];
+            }
+        }
+        // ================= 4: Delta, O, the state update; sums of O^2
+        f32x4 Ot;
+        {
+            // W = Diag(b) (V - P) for both column tiles (columns 32 cb + 2 n16 + ct)
+            f32x4 Wt[2];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                const float2 v2 = ld2(&s_v[t][32 * cb + 2 * n16]);
+                const float bt = s_beta[t];
+                Wt[0][r] = bt * (v2.x - Pt[0][r]);
+                Wt[1][r] = bt * (v2.y - Pt[1][r]);
+            }
+            const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[n16][2 * g4]);
+            const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[n16][2 * g4]);
+            const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[n16][2 * g4]);
+            const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[n16][2 * g4]);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            u32x2 dh[2], dl[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                u32x2 wh, wl;
+                split4(Wt[ct], wh, wl);
+                const f32x4 Dt = mma_cross(th, tl, wh, wl, zero) + mma_hihi(th, wh, zero);
+                split4(Dt, dh[ct], dl[ct]);
+            }
+            // O = R + M Delta for the readout column tile (ct = hb)
+            const u32x2 &doh = hb ? dh[1] : dh[0], &dol = hb ? dl[1] : dl[0];
+            Ot = mma_cross(mh, ml, doh, dol, Rs) + mma_hihi(mh, doh, zero);
+            // rows 4 g4 + r: the sum over this wavefront's 16 readout columns,
+            // written by lane n16 = r
+            float ss[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ss[r] = sum16(Ot[r] * Ot[r]);
+            if (n16 < 4) s_ss[wave][4 * g4 + n16] = n16 == 0 ? ss[0] : n16 == 1 ? ss[1] : n16 == 2 ? ss[2] : ss[3];
+            // S <- Diag(e^{G_C}) S + E^T Delta on this wavefront's rows (key
+            // channels 64 hb + 16 rl + ..): the cross-term steps of all eight
+            // tiles, then their hi * hi steps (the empty asm keeps that order,
+            // so seven steps separate each pair)
+            u32x2 eh[4];
+#pragma unroll
+            for (int rl = 0; rl < 4; ++rl) {
+                const int row = 64 * hb + 16 * rl;
+                const float4 dc = ld4(&s_gC[row + 4 * g4]);
+                eh[rl] = *reinterpret_cast<const u32x2 *>(&s_Eh[row + n16][2 * g4]);
+                const u32x2 el = *reinterpret_cast<const u32x2 *>(&s_El[row + n16][2 * g4]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    f32x4 &x = st[4 * ct + rl];
+                    x[0] *= dc.x;
+                    x[1] *= dc.y;
+                    x[2] *= dc.z;
+                    x[3] *= dc.w;
+                    x = mma_cross(eh[rl], el, dh[ct], dl[ct], x);
+                }
+            }
+            asm volatile("" : "+v"(st[0]), "+v"(st[1]), "+v"(st[2]), "+v"(st[3]),
+                              "+v"(st[4]), "+v"(st[5]), "+v"(st[6]), "+v"(st[7]));
+#pragma unroll
+            for (int rl = 0; rl < 4; ++rl)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) st[4 * ct + rl] = mma_hihi(eh[rl], dh[ct], st[4 * ct + rl]);
+        }
+        __syncthreads();
+        // ================= RMSNorm + gate of tokens 4 g4 + r, column jo
+        // (the output buffers end at the sequence end: later tokens are dropped)
+        {
+            float4 s = ld4(&s_ss[0][4 * g4]);
+#pragma unroll
+            for (int w = 1; w < 8; ++w) s += ld4(&s_ss[w][4 * g4]);
+            const float sv[4] = {s.x, s.y, s.z, s.w};
+            const Rsrc ay = tok_rsrc(p.y, BA::ELEM, c0, end);
+            const Rsrc ao = tok_rsrc(p.o_raw, 4, c0, end);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float rr = rsqrtf(sv[r] * (1.0f / DV) + p.rms_eps);
+                const uint32_t e = (uint32_t)((4 * g4 + r) * rowsz + h * DV + jo);
+                bst_one<Act>(ay, e, sigmoid(gg[r]) * gmc * Ot[r] * rr);
+                if (p.o_raw) bst_f32(ao, Ot[r], e * 4);
+            }
+        }
+    };
+    chunk(0, std::true_type{});
+#pragma unroll 1
+    for (int64_t c0 = CC; c0 < L; c0 += CC) chunk(c0, std::false_type{});
+#pragma unroll
+    for (int rl = 0; rl < 4; ++rl)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bst_f32x2(rs_state, make_float2(st[rl][r], st[4 + rl][r]), st_off(rl, r));
+    // the conv window out: the last PAST raw rows of (window, tokens), the
+    // window's rows from its copy in LDS
+    if (tid < CH) {
+        float *W = p.win + unit * (PAST * CH);
+        const void *src = tid < DK ? p.q : (tid < 2 * DK ? p.k : p.v);
+#pragma unroll
+        for (int r = 0; r < PAST; ++r) {
+            const int64_t j = L - PAST + r;
+            W[r * CH + tid] = j >= 0 ? Act::load1(src, ((rng.lo + j) * p.H + h) * DK + (tid & (DK - 1)))
+                                     : s_win[j + PAST][tid];
+        }
+    }
+}
+
 // window out (same as after the column-split path): every thread reads all
 // sources of its channels before writing them
 template <typename Act>
@@ -1245,6 +1793,15 @@ bool prefill_chunk_supported(int32_t gate_mode, float lb, int32_t num_heads) {
 
 hipError_t launch_prefill_chunk(const Params &p, bool bf16, hipStream_t stream) {
     return bf16 ? launch_chunk_as<BF16>(p, false, stream) : launch_chunk_as<F32>(p, false, stream);
+}
+
+hipError_t launch_prefill_chunk_short(const Params &p, bool bf16, hipStream_t stream) {
+    const int64_t units = (int64_t)p.num_seqs * p.H;
+    if (bf16)
+        hipLaunchKernelGGL((prefill_chunk_short_kernel<BF16>), dim3((unsigned)units), dim3(CS_THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_chunk_short_kernel<F32>), dim3((unsigned)units), dim3(CS_THREADS), 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_chunk_lowrank(const Params &p, bool bf16, hipStream_t stream) {

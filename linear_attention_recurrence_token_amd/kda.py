@@ -25,6 +25,7 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_BOUNDED, KDA_GATE_LITERAL, KDA_GATE_RAW = 0, 1, 2
 KDA_PREFILL_AUTO, KDA_PREFILL_FUSED, KDA_PREFILL_SPLIT, KDA_PREFILL_CHUNK, KDA_PREFILL_SHORT = 0, 1, 2, 3, 4
 KDA_PREFILL_SCAN = 5
+KDA_PREFILL_CHUNK_SHORT = 6
 DK = DV = 128
 TAPS = 4
 CH = 2 * DK + DV

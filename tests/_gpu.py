@@ -29,7 +29,8 @@ def tensors(d):
 
 
 PATHS = {"fused": kda.KDA_PREFILL_FUSED, "split": kda.KDA_PREFILL_SPLIT, "auto": kda.KDA_PREFILL_AUTO,
-         "chunk": kda.KDA_PREFILL_CHUNK, "short": kda.KDA_PREFILL_SHORT, "scan": kda.KDA_PREFILL_SCAN}
+         "chunk": kda.KDA_PREFILL_CHUNK, "short": kda.KDA_PREFILL_SHORT, "scan": kda.KDA_PREFILL_SCAN,
+         "chunk_short": kda.KDA_PREFILL_CHUNK_SHORT}
 
 
 def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, path="auto", side_stream=False,

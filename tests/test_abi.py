@@ -87,7 +87,7 @@ def _seq(lib, cfg, t, n=2, cu=None, order=None, total=8, ws=None, ws_bytes=0, cu
     ({"l2_eps": -1.0}, kda.KDA_ERR_INVALID_ARG),
     ({"rms_eps": float("nan")}, kda.KDA_ERR_INVALID_ARG),
     ({"gate_lower_bound": float("nan")}, kda.KDA_ERR_INVALID_ARG),
-    ({"prefill_path": 6}, kda.KDA_ERR_INVALID_ARG),
+    ({"prefill_path": 7}, kda.KDA_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected(lib, over, status):
     t = _fake_tensors()
@@ -145,6 +145,7 @@ def test_workspace_size_and_checks(lib):
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=1)), 2, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=3)), 2, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=4)), 2, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=6)), 2, 100) == 0
     # the two-pass chunk path: records (35 KiB per chunk slot and head; a
     # sequence of len tokens takes at most len // 16 + 1 slots), then the readout
     rec = lambda T, N, H: ((T // 16 + N) * H * 35840 + 255) // 256 * 256
@@ -213,6 +214,8 @@ def test_path_support_checked_before_the_device(lib):
     assert _seq(lib, _cfg(prefill_path=3, gate_mode=kda.KDA_GATE_RAW), t) == kda.KDA_ERR_UNSUPPORTED
     assert _seq(lib, _cfg(prefill_path=3, gate_lower_bound=-8.0), t) == kda.KDA_ERR_UNSUPPORTED
     assert _seq(lib, _cfg(prefill_path=5, gate_mode=kda.KDA_GATE_LITERAL), t) == kda.KDA_ERR_UNSUPPORTED
+    assert _seq(lib, _cfg(prefill_path=6, gate_mode=kda.KDA_GATE_RAW), t) == kda.KDA_ERR_UNSUPPORTED
+    assert _seq(lib, _cfg(prefill_path=6, gate_lower_bound=-8.0), t) == kda.KDA_ERR_UNSUPPORTED
     # the two-pass path without the workspace it needs
     assert _seq(lib, _cfg(prefill_path=5), t, ws=1 << 41, ws_bytes=1 << 10) == kda.KDA_ERR_INVALID_ARG
     assert _seq(lib, _cfg(prefill_path=5), t) == kda.KDA_ERR_INVALID_ARG

@@ -15,7 +15,7 @@ from tests import _gpu
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ["fused", "split", "chunk", "short", "scan"]
+PATHS = ["fused", "split", "chunk", "short", "scan", "chunk_short"]
 
 
 def note(msg):

@@ -26,7 +26,7 @@ def note(msg):
 
 # ---------------------------------------------------------------- small sizes
 
-PATHS = pytest.mark.parametrize("path", ["fused", "split", "chunk", "short", "scan"])
+PATHS = pytest.mark.parametrize("path", ["fused", "split", "chunk", "short", "scan", "chunk_short"])
 PATHS_ANY_GATE = pytest.mark.parametrize("path", ["fused", "split", "short"])
 
 
@@ -115,7 +115,7 @@ def test_ragged_edges(gpu, act, path):
                        bf16=(act == "bf16"), label="ragged")
 
 
-@pytest.mark.parametrize("path", ["auto", "fused", "split", "chunk", "short", "scan"])
+@pytest.mark.parametrize("path", ["auto", "fused", "split", "chunk", "short", "scan", "chunk_short"])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_many_short_sequences(gpu, act, path):
     # lengths 1..16 over many sequences: below, at and around one chunk, and
@@ -128,22 +128,23 @@ def test_many_short_sequences(gpu, act, path):
                        bf16=act == "bf16", label="short %s" % path)
 
 
+@pytest.mark.parametrize("path", ["chunk", "chunk_short"])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
-def test_chunk_many_pairs_short_average(gpu, act):
+def test_chunk_many_pairs_short_average(gpu, act, path):
     # more (sequence, head) pairs than CUs and few tokens on average: the
     # chunk path's workgroups loop over several pairs each; lengths 0..40
     # (empty ones included) give one to three chunks per pair
     w = synth.make_workload("many pairs", seed=35, N=150, H=2,
                             lengths=lambda rng: rng.integers(0, 41, size=150), act_dtype=act,
                             state_std=0.02, win_std=1.0, fresh_prob=0.3)
-    note("chunk path, 150 x 2 pairs, lengths U[0,40], %s" % act)
+    note("%s path, 150 x 2 pairs, lengths U[0,40], %s" % (path, act))
     order = np.argsort(-w.lengths, kind="stable")
     for seq_order in (None, order):
-        _gpu.assert_parity(_gpu.run_sequence(w, gpu, path="chunk", seq_order=seq_order),
+        _gpu.assert_parity(_gpu.run_sequence(w, gpu, path=path, seq_order=seq_order),
                            _gpu.oracle_sequence(w), bf16=act == "bf16", label="many pairs")
 
 
-@pytest.mark.parametrize("path", ["auto", "chunk", "short"])
+@pytest.mark.parametrize("path", ["auto", "chunk", "short", "chunk_short"])
 def test_short_average_with_long_sequences(gpu, path):
     # a batch that is short on average (the chunk path's single-buffered
     # variant) but holds a few sequences of several chunks
@@ -175,7 +176,7 @@ def test_bounded_gate_other_bounds(gpu, lb, path):
     w = synth.make_workload("lb", seed=70, N=2, H=2, lengths=[29, 12], lower_bound=lb,
                             decay=(lo, 0.999), state_std=0.02, win_std=1.0)
     assert np.all(np.isfinite(w.f))
-    if path in ("chunk", "scan") and lb < -7.5:
+    if path in ("chunk", "scan", "chunk_short") and lb < -7.5:
         # the chunkwise forms need |lb| <= 7.5 and say so
         with pytest.raises(kda.KdaError) as ei:
             _gpu.run_sequence(w, gpu, path=path)
@@ -211,7 +212,7 @@ def test_decode_large_state(gpu):
 
 # ---------------------------------------------------------------- invariances
 
-@pytest.mark.parametrize("other", ["split", "chunk", "short", "scan"])
+@pytest.mark.parametrize("other", ["split", "chunk", "short", "scan", "chunk_short"])
 def test_prefill_paths_agree(gpu, other):
     w = synth.workload(3, scale={"N": 3, "H": 5, "T": 131})
     note("%s vs fused prefill" % other)
@@ -223,7 +224,7 @@ def test_prefill_paths_agree(gpu, other):
     np.testing.assert_array_equal(a["win"], b["win"])
 
 
-@pytest.mark.parametrize("path", ["chunk", "scan"])
+@pytest.mark.parametrize("path", ["chunk", "scan", "chunk_short"])
 def test_chunk_path_rejects_unbounded_gates(gpu, path):
     w = synth.make_workload("raw", seed=5, N=1, H=2, lengths=[20], gate_mode=synth.GATE_RAW)
     with pytest.raises(kda.KdaError) as ei:
@@ -493,7 +494,7 @@ def test_full_ragged_prefill_256x32(gpu):
     _gpu.assert_parity(got, _gpu.oracle_sequence(synth.subset(w, seqs, heads)), bf16=True, label=w.name)
 
 
-@pytest.mark.parametrize("path", ["auto", "fused", "chunk", "short"])
+@pytest.mark.parametrize("path", ["auto", "fused", "chunk", "short", "chunk_short"])
 def test_full_short_prefill_64x32x13(gpu, path):
     # the short multi-token case: 13 tokens per sequence over a decode-sized
     # batch, state and window carried in; the oracle covers every pair

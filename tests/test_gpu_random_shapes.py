@@ -31,8 +31,8 @@ def _case(seed):
                                              decode_steps=int(rng.integers(1, 6)), **common), {}
     N = int(rng.integers(1, 24))
     lengths = [int(rng.choice(LENGTHS)) if rng.random() < 0.6 else int(rng.integers(0, 700)) for _ in range(N)]
-    path = str(rng.choice(["auto", "fused", "split", "chunk", "short", "scan"]))
-    if path in ("chunk", "scan") and gate != synth.GATE_BOUNDED:
+    path = str(rng.choice(["auto", "fused", "split", "chunk", "short", "scan", "chunk_short"]))
+    if path in ("chunk", "scan", "chunk_short") and gate != synth.GATE_BOUNDED:
         path = "auto"          # the chunkwise forms take the bounded gate only
     fresh = 0.3 if rng.random() < 0.3 else None
     w = synth.make_workload("random prefill", N=N, lengths=lengths, fresh_prob=fresh, **common)
