@@ -1267,10 +1267,14 @@ void prefill_chunk_short_kernel(Params p) {
     if (rng.len <= 0) return;
     const int64_t L = rng.len;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // in a scalar register
-    const int n16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // in a scalar register
+    // the lane index, formed where it is used (from the lane count): a copy
+    // kept for the workgroup's life costs a register the kernel does not have
+    auto lane_id = []() -> int {
+        int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        asm volatile("" : "+v"(l));
+        return l;
+    };
     const int t0 = TW * wave;                       // tokens of this wavefront's token-wise work
     // its state block: rows 64 hb .. 64 hb + 63 of columns 32 cb .. 32 cb + 31
     const int cb = wave >> 1, hb = wave & 1;
@@ -1291,19 +1295,28 @@ void prefill_chunk_short_kernel(Params p) {
     __shared__ float s_v[CC][DV + 4];      // activated v
     __shared__ float s_beta[CC];
     // split bf16 operands e^G . k_hat, e^G . q_hat of P and R: slot (t, m, g)
-    // holds channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3} of token t
-    __shared__ __attribute__((aligned(16))) uint32_t s_kah[CC * OPR * 4], s_kal[CC * OPR * 4];
-    __shared__ __attribute__((aligned(16))) uint32_t s_qah[CC * OPR * 4], s_qal[CC * OPR * 4];
+    // holds channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3} of token
+    // t; before the first chunk's operands, the carried conv window
+    __shared__ __attribute__((aligned(16))) uint32_t s_ops[4][CC * OPR * 4];
+    uint32_t *s_kah = s_ops[0], *s_kal = s_ops[1], *s_qah = s_ops[2], *s_qal = s_ops[3];
+    float (*s_win)[CH] = reinterpret_cast<float (*)[CH]>(&s_ops[0][0]);
+    static_assert(PAST * CH <= 4 * CC * OPR * 4, "window copy");
     // [channel][token] split e^{G_C - G} . k_hat of the update
     __shared__ __attribute__((aligned(16))) uint32_t s_Eh[DK][ER], s_El[DK][ER];
     __shared__ float s_gC[DK];             // e^{G_C}, decay of the whole chunk
-    __shared__ float s_Lp[CS_PART][CC][CC];   // L, M summed over one channel quarter each
-    __shared__ float s_Mp[CS_PART][CC][CC];
-    __shared__ float s_A[CC][TP];          // Diag(b) L, strictly lower
+    // L, M summed over one channel quarter each; Diag(b) L (strictly lower)
+    // over the partial L, which wavefront 0 reads before it writes; the sums
+    // of O^2 over each wavefront's readout columns over the partial M (no
+    // longer read by then)
+    __shared__ __attribute__((aligned(16))) float s_LM[2][CS_PART][CC][CC];
+    float (*s_Lp)[CC][CC] = s_LM[0];
+    float (*s_Mp)[CC][CC] = s_LM[1];
+    float (*s_A)[TP] = reinterpret_cast<float (*)[TP]>(&s_LM[0][0][0][0]);
+    float (*s_ss)[CC] = reinterpret_cast<float (*)[CC]>(&s_LM[1][0][0][0]);
+    static_assert(CC * TP <= CS_PART * CC * CC && 8 * CC <= CS_PART * CC * CC, "aliases");
     // (I + Diag(b) L)^{-1} and M (lower triangle with the diagonal), [row][column] split bf16
     __shared__ __attribute__((aligned(16))) uint32_t s_Th[CC][TR], s_Tl[CC][TR], s_Mh[CC][TR], s_Ml[CC][TR];
-    __shared__ __attribute__((aligned(16))) float s_ss[8][CC];   // sums of O^2 over each wavefront's columns
-    __shared__ __attribute__((aligned(16))) float s_win[PAST][CH];  // the carried conv window
+    __shared__ __attribute__((aligned(16))) float s_cw[CH][TAPS];   // conv taps of this head
 
     // the state in the accumulator tiles: in tile 4 ct + rl, lane (g4, n16)
     // holds row 64 hb + 16 rl + 4 g4 + r, column 32 cb + 2 n16 + ct in element
@@ -1313,20 +1326,19 @@ void prefill_chunk_short_kernel(Params p) {
     // Loaded with the first chunk.
     const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
     f32x4 st[8];
-    auto st_off = [&](int rl, int r) -> uint32_t {
-        return (uint32_t)(((64 * hb + 16 * rl + 4 * g4 + r) * DV + 32 * cb + 2 * n16) * 4);
+    auto st_off = [&](int l, int rl, int r) -> uint32_t {
+        return (uint32_t)(((64 * hb + 16 * rl + 4 * (l >> 4) + r) * DV + 32 * cb + 2 * (l & 15)) * 4);
     };
 
     // one chunk; the first is its own copy, which also loads the state (after
     // the chunk's inputs: loads complete in order, so the pre-step waits for
     // the inputs alone and the state arrives during it)
     auto chunk = [&](int64_t c0, auto first) {
-        // the lane's indices anew each chunk (an opaque copy of the thread
-        // index): otherwise every address derived from them is kept live
-        // across the loop, beyond the registers two workgroups per compute
-        // unit allow
-        int ti = tid;
-        asm volatile("" : "+v"(ti));
+        // the lane's indices anew each chunk (from the lane count, opaque to
+        // the compiler): otherwise every address derived from them is kept
+        // live across the loop, beyond the registers two workgroups per
+        // compute unit allow
+        const int ti = wave * 64 + lane_id();
         const int lane = ti & 63;
         const int n16 = lane & 15, g4 = lane >> 4;
         auto tok_rsrc = [&](const void *t, uint32_t elem, int64_t base, int64_t end) -> Rsrc {
@@ -1342,9 +1354,6 @@ void prefill_chunk_short_kernel(Params p) {
         const float dtb = p.dt_bias[h * DK + dch];
         const int jo = 32 * cb + 2 * n16 + hb;   // the column whose readout this lane forms
         const float gmc = p.gamma[jo];
-        // conv taps of this head, read per chunk (cache hits) rather than held
-        // across the loop
-        const Rsrc rs_cw = make_rsrc(p.conv_w + (int64_t)h * (CH * TAPS), CH * TAPS * 4);
 
         // T = (I + A)^{-1} by forward substitution, as in the kernel above
         auto solve_T = [&]() {
@@ -1492,19 +1501,18 @@ void prefill_chunk_short_kernel(Params p) {
         // sent out of range and reads as 0, without a branch on the row)
         typename BA::Raw2 xq[RAWR], xk[RAWR], xv[RAWR];
         float rf[4], gg[4], rb;
-        float4 wt[6];                              // conv taps of channels chq, chq + 1 of q, k, v
         float wn[PAST];
-        const float *W = p.win + unit * (PAST * CH);
+        float4 cw4;                                // the head's conv taps, for LDS
         if constexpr (decltype(first)::value) {
-            if (tid < CH) {
+            if (ti < CH) {
+                const Rsrc rs_cw = make_rsrc(p.conv_w + (int64_t)h * (CH * TAPS), CH * TAPS * 4);
+                const Rsrc rs_w = make_rsrc(p.win + unit * (PAST * CH), PAST * CH * 4);
+                cw4 = bld_f32x4(rs_cw, (uint32_t)(ti * TAPS * 4));
 #pragma unroll
-                for (int r = 0; r < PAST; ++r) wn[r] = W[r * CH + tid];
+                for (int r = 0; r < PAST; ++r) wn[r] = bld_f32(rs_w, (uint32_t)((r * CH + ti) * 4));
             }
         }
         {
-#pragma unroll
-            for (int i = 0; i < 6; ++i)
-                wt[i] = bld_f32x4(rs_cw, ((i >> 1) * DK + chq + (i & 1)) * TAPS * 4);
             const int64_t base = c0 == 0 ? 0 : c0 - PAST;
             const Rsrc aq = tok_rsrc(p.q, BA::ELEM, base, end);
             const Rsrc ak = tok_rsrc(p.k, BA::ELEM, base, end);
@@ -1532,19 +1540,25 @@ void prefill_chunk_short_kernel(Params p) {
             for (int rl = 0; rl < 4; ++rl)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float2 x = bld_f32x2(rs_state, st_off(rl, r));
+                    const float2 x = bld_f32x2(rs_state, st_off(lane, rl, r));
                     st[rl][r] = x.x;
                     st[4 + rl][r] = x.y;
                 }
-            if (tid < CH) {
+            if (ti < CH) {
 #pragma unroll
-                for (int r = 0; r < PAST; ++r) s_win[r][tid] = wn[r];
+                for (int r = 0; r < PAST; ++r) s_win[r][ti] = wn[r];
+                st4(s_cw[ti], cw4);
             }
             __syncthreads();
         }
         {
-            auto act = [&](const typename BA::Raw2 (&raw)[RAWR], int ch, const float4 &w0, const float4 &w1,
-                           float (&a)[TW][2]) {
+            // (the conv window out: the sequence's last PAST raw rows, written
+            // in the last chunk by the wavefront whose tokens they are, rows
+            // before the chunk by wavefront 0; every read of the carried window
+            // lies before the first chunk's barrier)
+            const Rsrc rs_win = make_rsrc(p.win + unit * (PAST * CH), PAST * CH * 4);
+            auto act = [&](const typename BA::Raw2 (&raw)[RAWR], int ch, float (&a)[TW][2]) {
+                const float4 w0 = ld4(s_cw[ch]), w1 = ld4(s_cw[ch + 1]);
                 float2 x[RAWR];
 #pragma unroll
                 for (int r = 0; r < RAWR; ++r) {
@@ -1552,6 +1566,9 @@ void prefill_chunk_short_kernel(Params p) {
                     if constexpr (decltype(first)::value) {
                         if (t0 - PAST + r < 0) x[r] = ld2(&s_win[t0 + r][ch]);   // wavefront-uniform
                     }
+                    const int64_t j = c0 + t0 - PAST + r;
+                    if ((r >= PAST || wave == 0) && j >= L - PAST && j < L)    // wavefront-uniform
+                        bst_f32x2(rs_win, x[r], (uint32_t)(((j - (L - PAST)) * CH + ch) * 4));
                 }
 #pragma unroll
                 for (int sl = 0; sl < TW; ++sl) {
@@ -1560,9 +1577,9 @@ void prefill_chunk_short_kernel(Params p) {
                 }
             };
             float aq[TW][2], ak[TW][2], av[TW][2];
-            act(xq, chq, wt[0], wt[1], aq);
-            act(xk, chk, wt[2], wt[3], ak);
-            act(xv, chv, wt[4], wt[5], av);
+            act(xq, chq, aq);
+            act(xk, chk, ak);
+            act(xv, chv, av);
 #pragma unroll
             for (int sl = 0; sl < TW; ++sl) {
                 const int t = t0 + sl;
@@ -1729,22 +1746,11 @@ void prefill_chunk_short_kernel(Params p) {
     chunk(0, std::true_type{});
 #pragma unroll 1
     for (int64_t c0 = CC; c0 < L; c0 += CC) chunk(c0, std::false_type{});
+    const int lane = lane_id();
 #pragma unroll
     for (int rl = 0; rl < 4; ++rl)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bst_f32x2(rs_state, make_float2(st[rl][r], st[4 + rl][r]), st_off(rl, r));
-    // the conv window out: the last PAST raw rows of (window, tokens), the
-    // window's rows from its copy in LDS
-    if (tid < CH) {
-        float *W = p.win + unit * (PAST * CH);
-        const void *src = tid < DK ? p.q : (tid < 2 * DK ? p.k : p.v);
-#pragma unroll
-        for (int r = 0; r < PAST; ++r) {
-            const int64_t j = L - PAST + r;
-            W[r * CH + tid] = j >= 0 ? Act::load1(src, ((rng.lo + j) * p.H + h) * DK + (tid & (DK - 1)))
-                                     : s_win[j + PAST][tid];
-        }
-    }
+        for (int r = 0; r < 4; ++r) bst_f32x2(rs_state, make_float2(st[rl][r], st[4 + rl][r]), st_off(lane, rl, r));
 }
 
 // window out (same as after the column-split path): every thread reads all
