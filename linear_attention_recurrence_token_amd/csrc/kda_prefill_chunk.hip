@@ -1246,10 +1246,18 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
 constexpr int CS_THREADS = 512;
 constexpr int CS_PART = 4;         // partial L, M over channel quarters
 
-template <typename Act> __device__ __forceinline__ void bst_one(Rsrc r, uint32_t i, float x);
-template <> __device__ __forceinline__ void bst_one<F32>(Rsrc r, uint32_t i, float x) { bst_f32(r, x, i * 4); }
-template <> __device__ __forceinline__ void bst_one<BF16>(Rsrc r, uint32_t i, float x) {
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(x, 0.f) & 0xffffu), r, i * 2, 0, 0);
+// four consecutive activations (element index i, a multiple of 4) through a buffer
+template <typename Act> __device__ __forceinline__ float4 bld4(Rsrc r, uint32_t i);
+template <> __device__ __forceinline__ float4 bld4<F32>(Rsrc r, uint32_t i) { return bld_f32x4(r, i * 4); }
+template <> __device__ __forceinline__ float4 bld4<BF16>(Rsrc r, uint32_t i) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, i * 2, 0, 0);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+template <typename Act> __device__ __forceinline__ void bst4(Rsrc r, uint32_t i, float4 x);
+template <> __device__ __forceinline__ void bst4<F32>(Rsrc r, uint32_t i, float4 x) { bst_f32x4_at(r, x, i * 4); }
+template <> __device__ __forceinline__ void bst4<BF16>(Rsrc r, uint32_t i, float4 x) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)}, r, i * 2, 0, 0);
 }
 
 template <typename Act>
@@ -1301,6 +1309,10 @@ void prefill_chunk_short_kernel(Params p) {
     uint32_t *s_kah = s_ops[0], *s_kal = s_ops[1], *s_qah = s_ops[2], *s_qal = s_ops[3];
     float (*s_win)[CH] = reinterpret_cast<float (*)[CH]>(&s_ops[0][0]);
     static_assert(PAST * CH <= 4 * CC * OPR * 4, "window copy");
+    // after the products, each wavefront's readout tile [token][n16], for the
+    // stores of whole column runs
+    float (*s_ox)[CC][16] = reinterpret_cast<float (*)[CC][16]>(&s_ops[0][0]);
+    static_assert(8 * CC * 16 <= 4 * CC * OPR * 4, "readout exchange");
     // [channel][token] split e^{G_C - G} . k_hat of the update
     __shared__ __attribute__((aligned(16))) uint32_t s_Eh[DK][ER], s_El[DK][ER];
     __shared__ float s_gC[DK];             // e^{G_C}, decay of the whole chunk
@@ -1352,8 +1364,8 @@ void prefill_chunk_short_kernel(Params p) {
         const uint32_t foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
         const float eA = __expf(p.A_log[h * DK + dch]);
         const float dtb = p.dt_bias[h * DK + dch];
-        const int jo = 32 * cb + 2 * n16 + hb;   // the column whose readout this lane forms
-        const float gmc = p.gamma[jo];
+        // the epilogue's lane: token 8 hb + lane / 8, columns jq .. jq + 3
+        const int te = 8 * hb + (lane >> 3), jq = 32 * cb + 4 * (lane & 7);
 
         // T = (I + A)^{-1} by forward substitution, as in the kernel above
         auto solve_T = [&]() {
@@ -1500,7 +1512,8 @@ void prefill_chunk_short_kernel(Params p) {
         // window, which are copied to LDS first (a token row's load is then
         // sent out of range and reads as 0, without a branch on the row)
         typename BA::Raw2 xq[RAWR], xk[RAWR], xv[RAWR];
-        float rf[4], gg[4], rb;
+        float rf[4], rb;
+        float4 gg;                                 // gates of the epilogue's token and columns
         float wn[PAST];
         float4 cw4;                                // the head's conv taps, for LDS
         if constexpr (decltype(first)::value) {
@@ -1531,9 +1544,7 @@ void prefill_chunk_short_kernel(Params p) {
             const Rsrc ab = make_rsrc(p.beta + (rng.lo + c0) * p.H, (uint32_t)((end - c0) * p.H * 4));
             rb = bld_f32(ab, (uint32_t)(((t0 + (lane & (TW - 1))) * p.H + h) * 4));
             const Rsrc ag = tok_rsrc(p.g, BA::ELEM, c0, end);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                gg[r] = bld_one<Act>(ag, (uint32_t)((4 * g4 + r) * rowsz + h * DV + jo));
+            gg = bld4<Act>(ag, (uint32_t)(te * rowsz + h * DV + jq));
         }
         if constexpr (decltype(first)::value) {
 #pragma unroll
@@ -1696,6 +1707,8 @@ void prefill_chunk_short_kernel(Params p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) ss[r] = sum16(Ot[r] * Ot[r]);
             if (n16 < 4) s_ss[wave][4 * g4 + n16] = n16 == 0 ? ss[0] : n16 == 1 ? ss[1] : n16 == 2 ? ss[2] : ss[3];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_ox[wave][4 * g4 + r][n16] = Ot[r];
             // S <- Diag(e^{G_C}) S + E^T Delta on this wavefront's rows (key
             // channels 64 hb + 16 rl + ..): the cross-term steps of all eight
             // tiles, then their hi * hi steps (the empty asm keeps that order,
@@ -1725,22 +1738,23 @@ void prefill_chunk_short_kernel(Params p) {
                 for (int ct = 0; ct < 2; ++ct) st[4 * ct + rl] = mma_hihi(eh[rl], dh[ct], st[4 * ct + rl]);
         }
         __syncthreads();
-        // ================= RMSNorm + gate of tokens 4 g4 + r, column jo
-        // (the output buffers end at the sequence end: later tokens are dropped)
+        // ================= RMSNorm + gate of token te, columns jq .. jq + 3
+        // (columns 32 cb + 2 n16 + ct of the two tiles interleave; the output
+        // buffers end at the sequence end: later tokens are dropped)
         {
-            float4 s = ld4(&s_ss[0][4 * g4]);
+            float s = s_ss[0][te];
 #pragma unroll
-            for (int w = 1; w < 8; ++w) s += ld4(&s_ss[w][4 * g4]);
-            const float sv[4] = {s.x, s.y, s.z, s.w};
-            const Rsrc ay = tok_rsrc(p.y, BA::ELEM, c0, end);
-            const Rsrc ao = tok_rsrc(p.o_raw, 4, c0, end);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float rr = rsqrtf(sv[r] * (1.0f / DV) + p.rms_eps);
-                const uint32_t e = (uint32_t)((4 * g4 + r) * rowsz + h * DV + jo);
-                bst_one<Act>(ay, e, sigmoid(gg[r]) * gmc * Ot[r] * rr);
-                if (p.o_raw) bst_f32(ao, Ot[r], e * 4);
-            }
+            for (int w = 1; w < 8; ++w) s += s_ss[w][te];
+            const float rr = rsqrtf(s * (1.0f / DV) + p.rms_eps);
+            const float2 o0 = ld2(&s_ox[2 * cb][te][2 * (lane & 7)]);
+            const float2 o1 = ld2(&s_ox[2 * cb + 1][te][2 * (lane & 7)]);
+            const float4 o = make_float4(o0.x, o1.x, o0.y, o1.y);
+            const float4 gm = ld4(p.gamma + jq);
+            const float4 y = make_float4(sigmoid(gg.x) * gm.x * o.x * rr, sigmoid(gg.y) * gm.y * o.y * rr,
+                                         sigmoid(gg.z) * gm.z * o.z * rr, sigmoid(gg.w) * gm.w * o.w * rr);
+            const uint32_t e = (uint32_t)(te * rowsz + h * DV + jq);
+            bst4<Act>(tok_rsrc(p.y, BA::ELEM, c0, end), e, y);
+            if (p.o_raw) bst4<F32>(tok_rsrc(p.o_raw, 4, c0, end), e, o);
         }
     };
     chunk(0, std::true_type{});
