@@ -309,7 +309,6 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // 16 rw + 4 (l / 16) + s
     auto partial_LM = [&]() {
         const int lc = 16 * rw + 4 * g4;
-        const int tq = n16 >> 2;
         const float4 k4 = ld4(&s_kh[n16][lc]);
         const float4 q4 = ld4(&s_qh[n16][lc]);
         const float4 gq = ld4(&s_Gq[n16][lc]);
@@ -322,13 +321,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
         const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
         const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
+        const MidCoef mc = mid_coef(n16);
         f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            // G_t - r from sums that start as close to both tokens as possible
-            const float d = tq == 0 ? gv[s] - c0v[s] - g7v[s]
-                          : tq == 1 ? gv[s] - g7v[s]
-                          : tq == 2 ? gv[s] : gv[s] + c2v[s];
+            const float d = rel_mid(mc, gv[s], c0v[s], g7v[s], c2v[s]);
             const float ef = __expf(d), eb = __expf(-d);
             const float b = eb * kv[s];
             Lt = mfma4(ef * kv[s], b, Lt);
