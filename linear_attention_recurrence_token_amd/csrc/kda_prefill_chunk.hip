@@ -190,7 +190,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     const int64_t NC = (L + CC - 1) / CC;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // in a scalar register
     const int n16 = lane & 15, g4 = lane >> 4;
     const bool state_wave = wave < 8;               // the role (wavefront-uniform)
     const int rw = wave & 7;                        // wavefront index within the role
