@@ -75,12 +75,26 @@ __device__ __forceinline__ int64_t slot_base(const Params &p, int n) {
     return c / CC + n;
 }
 
+// four consecutive activations at byte offset o of a buffer (reads 0 out of range)
+template <typename Act> __device__ __forceinline__ float4 ld_act4(Rsrc r, uint32_t o);
+template <> __device__ __forceinline__ float4 ld_act4<F32>(Rsrc r, uint32_t o) { return bld_f32x4(r, o); }
+template <> __device__ __forceinline__ float4 ld_act4<BF16>(Rsrc r, uint32_t o) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
 // ---------------------------------------------------------------- pass 1
 constexpr int PREP_THREADS = 256;
 constexpr int XP = CH + 4;              // raw / activated row length in LDS
 constexpr int FP = DK + 4;              // L, M factor rows: 16-byte aligned, and the 16
                                         // rows a 16-lane group reads at one column on distinct banks
-constexpr int RAW_PER = ((CC + PAST) * CH + PREP_THREADS - 1) / PREP_THREADS;   // raw loads per thread
+// raw rows: a thread loads 4 channels of one row of q, k or v at a time, the
+// workgroup RAW_GRP rows of a tensor per pass
+constexpr int RAW_ROWS = CC + PAST;
+constexpr int RAW_GRP = PREP_THREADS / (DK / 4);
+constexpr int RAW_PASSES = (RAW_ROWS + RAW_GRP - 1) / RAW_GRP;
+constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every range here: reads 0
 
 // LDS of the operand pass: the raw / activated rows, later the L, M factor
 // rows in the same bytes; the conv taps, later the decay sums in the same bytes
@@ -133,30 +147,39 @@ void scan_prep_kernel(Params p, uint8_t *records, int32_t seg_lo) {
     __shared__ float s_A[CC][CC], s_b[CC];
 
     const int64_t rowsz = (int64_t)p.H * DK;
-    const float *W = p.win + ((int64_t)n * p.H + h) * (PAST * CH);
-    // every global load of the chunk first (they are independent), then LDS
-    float xr[RAW_PER], fv[CC];
+    // every global load of the chunk first (they are independent), then LDS.
+    // Raw rows c0 - 3 .. c0 + 15: a row before the sequence comes from the
+    // carried window, a row past its end reads 0; both loads are issued for
+    // every row, one of them out of its buffer's range (reading 0), so the
+    // pair adds up to the row without a branch.
+    const int64_t rb0 = c0 - PAST < 0 ? 0 : c0 - PAST;   // first token row loaded
+    const int64_t rend = rng.len < c0 + CC ? rng.len : c0 + CC;
+    const Rsrc r_win = make_rsrc(p.win + ((int64_t)n * p.H + h) * (PAST * CH), PAST * CH * 4);
+    const int rg = tid / (DK / 4), c4 = 4 * (tid % (DK / 4));
+    float4 xr[3][RAW_PASSES];
 #pragma unroll
-    for (int u = 0; u < RAW_PER; ++u) {
-        const int idx = tid + u * PREP_THREADS;
-        const int r = idx / CH, ch = idx - r * CH;
-        const int64_t j = c0 - PAST + r;
-        float x = 0.f;
-        if (idx < (CC + PAST) * CH) {
-            if (j < 0) {
-                x = W[(j + PAST) * CH + ch];
-            } else if (j < rng.len) {
-                const void *src = ch < DK ? p.q : (ch < 2 * DK ? p.k : p.v);
-                x = Act::load1(src, (rng.lo + j) * rowsz + (int64_t)h * DK + (ch & (DK - 1)));
-            }
+    for (int ten = 0; ten < 3; ++ten) {
+        const void *src = ten == 0 ? p.q : (ten == 1 ? p.k : p.v);
+        const Rsrc r_tok = make_rsrc(static_cast<const char *>(src) + (rng.lo + rb0) * rowsz * BufAct<Act>::ELEM,
+                                     (uint32_t)((rend - rb0) * rowsz * BufAct<Act>::ELEM));
+#pragma unroll
+        for (int u = 0; u < RAW_PASSES; ++u) {
+            const int r = rg + RAW_GRP * u;
+            const int64_t j = c0 - PAST + r;
+            const bool live = r < RAW_ROWS;
+            const uint32_t to = (live && j >= 0) ? (uint32_t)(((j - rb0) * rowsz + (int64_t)h * DK + c4) * BufAct<Act>::ELEM) : OOB;
+            const uint32_t wo = (live && j < 0) ? (uint32_t)(((j + PAST) * CH + ten * DK + c4) * 4) : OOB;
+            const float4 a = ld_act4<Act>(r_tok, to), b = bld_f32x4(r_win, wo);
+            xr[ten][u] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
         }
-        xr[u] = x;
     }
+    float fv[CC];
     float eA = 0.f, dtb = 0.f, bt = 0.f;
     if (tid < DK) {
+        // (rows past the sequence end read 0)
+        const Rsrc r_f = make_rsrc(p.f + (rng.lo + c0) * rowsz, (uint32_t)(nv * rowsz * 4));
 #pragma unroll
-        for (int t = 0; t < CC; ++t)
-            fv[t] = t < nv ? p.f[(rng.lo + c0 + t) * rowsz + h * DK + tid] : 0.f;
+        for (int t = 0; t < CC; ++t) fv[t] = bld_f32(r_f, (uint32_t)((h * DK + tid) * 4), (uint32_t)(t * rowsz * 4));
         eA = p.A_log[h * DK + tid];
         dtb = p.dt_bias[h * DK + tid];
     } else if (tid < DK + CC) {
@@ -170,11 +193,12 @@ void scan_prep_kernel(Params p, uint8_t *records, int32_t seg_lo) {
     *reinterpret_cast<float4 *>(s_cw[tid]) = cw0;
     if (tid < CH - PREP_THREADS) *reinterpret_cast<float4 *>(s_cw[PREP_THREADS + tid]) = cw1;
 #pragma unroll
-    for (int u = 0; u < RAW_PER; ++u) {
-        const int idx = tid + u * PREP_THREADS;
-        const int r = idx / CH, ch = idx - r * CH;
-        if (idx < (CC + PAST) * CH) s_x[r][ch] = xr[u];
-    }
+    for (int ten = 0; ten < 3; ++ten)
+#pragma unroll
+        for (int u = 0; u < RAW_PASSES; ++u) {
+            const int r = rg + RAW_GRP * u;
+            if (r < RAW_ROWS) *reinterpret_cast<float4 *>(&s_x[r][ten * DK + c4]) = xr[ten][u];
+        }
     __syncthreads();
     // conv + SiLU (tokens past the end give zeros); each thread keeps its
     // results in registers until every tap has been read
