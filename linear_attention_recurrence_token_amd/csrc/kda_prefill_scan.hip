@@ -389,10 +389,18 @@ __device__ __forceinline__ f32x4 mma16(u32x2 ah, u32x2 al, u32x2 bh, u32x2 bl, f
 
 // wait until at most N of this wavefront's loads are outstanding and its LDS
 // reads are complete, then the workgroup barrier (no fence: that would wait
-// for the loads still in flight)
+// for the loads still in flight).  The wait is the builtin, which the
+// compiler's own wait counting sees: it then knows the record loads older
+// than the last N have landed and adds no wait for them before the record's
+// LDS reads (behind a wait in inline asm it waited for every load in flight
+// once per loop trip).  The barrier is asm with a memory clobber, so that no
+// LDS access moves across it.
 template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    static_assert(N < 64, "vmcnt has 6 bits");
+    // s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8 (0)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+    asm volatile("s_barrier" ::: "memory");
 }
 // LDS writes complete, then the workgroup barrier (loads may stay in flight)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -552,8 +560,10 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
         }
     };
     // chunk c: its record landed everywhere (and every wavefront is done with
-    // chunk c - 1's buffer), the record RING - 1 chunks ahead into that
-    // buffer, then the chunk
+    // chunk c - 1's buffer), the chunk, then the record RING - 1 chunks ahead
+    // into that buffer.  (Issued before the chunk, those loads made the
+    // compiler wait for every load in flight before the chunk's record reads
+    // once per loop trip: it cannot tell the buffers' loads apart there.)
     auto step = [&](int64_t c, const uint8_t *cur, uint8_t *prev) {
         if (c >= NC) return;
         const int64_t after = NC - 1 - c < RING - 2 ? NC - 1 - c : RING - 2;
@@ -563,8 +573,8 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
             wait_then_barrier<LOADS_PER_WAVE>();
         else
             wait_then_barrier<0>();
-        if (c + RING - 1 < NC) rec_issue(rec_rsrc(c + RING - 1), prev, wave, lane);
         chunk(c, cur);
+        if (c + RING - 1 < NC) rec_issue(rec_rsrc(c + RING - 1), prev, wave, lane);
     };
     rec_issue(rec_rsrc(c_lo), sR0, wave, lane);
     if (NC > c_lo + 1) rec_issue(rec_rsrc(c_lo + 1), sR1, wave, lane);
