@@ -338,10 +338,15 @@ __device__ __forceinline__ void dma_issue(Rsrc r, uint8_t *stage, int wave, int 
 
 // wait until at most N of this wavefront's global loads are outstanding and
 // its LDS reads are complete, then the workgroup barrier (no memory fence:
-// that would wait for every load in flight)
+// that would wait for every load in flight).  The wait is the builtin, which
+// the compiler's own wait counting sees; the barrier is asm with a memory
+// clobber, so that no LDS access moves across it.
 template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    static_assert(N < 64, "vmcnt has 6 bits");
+    // s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8 (0)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+    asm volatile("s_barrier" ::: "memory");
 }
 
 
@@ -408,8 +413,11 @@ void proj_gemm_dma_kernel(GemmArgs g) {
         }
     };
     // one K stage: its loads done everywhere (and every wavefront's reads of
-    // the previous stage complete), the loads NS - 1 stages ahead into the
-    // buffer the previous stage used, then the products
+    // the previous stage complete), the products, then the loads NS - 1
+    // stages ahead into the buffer the previous stage used.  (Issued before
+    // the products, those loads made the compiler wait for every load in
+    // flight before the stage's LDS reads once per loop trip: it cannot tell
+    // the stage buffers' loads apart there.)
     auto stage = [&](int s, const uint8_t *a, const uint8_t *b, uint8_t *na, uint8_t *nb) {
         if (s >= nst) return;
         // outstanding after stage s: stages s + 1 .. min(s + NS - 2, nst - 1)
@@ -420,8 +428,8 @@ void proj_gemm_dma_kernel(GemmArgs g) {
             wait_then_barrier<LOADS>();
         else
             wait_then_barrier<0>();
-        if (s + NS - 1 < nst) issue(s + NS - 1, na, nb);
         compute(a, b);
+        if (s + NS - 1 < nst) issue(s + NS - 1, na, nb);
     };
 
     issue(0, sA0, sB0);
