@@ -80,6 +80,7 @@ constexpr int KP = DK + 4;         // padded fp32 LDS rows (rows read as float4 
 constexpr int TP = CC + 4;
 constexpr int OPR = 17;            // 16-byte slots per token row of the P / R operands (one pad slot)
 constexpr int ER = (CC + 4) / 2;   // u32 per channel row of E (16 tokens as bf16, padded)
+constexpr int EIR = CC + 4;        // u32 per channel row of E with hi and lo interleaved (padded)
 constexpr int TR = (CC + 4) / 2;   // u32 per row of T and M (bf16, padded)
 constexpr int NPART = 8;           // partial L, M over channel eighths
 constexpr float CHUNK_MAX_HALF_LOG_DECAY = 60.0f;
@@ -95,6 +96,31 @@ __device__ __forceinline__ Split2 split2(float x0, float x1) {
     const f32x2 x = {x0, x1};
     const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
     const f32x2 r = {x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u)};
+    return {hb, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
+}
+// The split of values that are not needed afterwards: lo = x - hi as the bf16
+// dot product of the packed hi parts with the pair (-1, 0) or (0, -1),
+// accumulated onto x itself.  That is one instruction per value in place of a
+// shift or mask and a subtraction, and exact: x - hi is representable in fp32
+// (checked bit for bit against the subtraction over 2^22 values of every
+// exponent, denormals included).  The two pairs come in scalar registers the
+// compiler cannot see through: as an immediate it encodes the pair (-1, 0) as
+// the inline constant -1.0, which the instruction reads as the fp32 pattern,
+// that is as the pair (0, -1).
+struct NegOne {
+    uint32_t lo, hi;   // (-1, 0) and (0, -1) as bf16 pairs
+};
+__device__ __forceinline__ NegOne neg_one_pairs() {
+    uint32_t a = 0x0000bf80u, b = 0xbf800000u;
+    asm volatile("" : "+s"(a), "+s"(b));
+    return {a, b};
+}
+__device__ __forceinline__ Split2 split2_dead(float x0, float x1, NegOne n) {
+    const f32x2 x = {x0, x1};
+    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    const bf16x2 h = __builtin_bit_cast(bf16x2, hb);
+    const f32x2 r = {__builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, n.lo), x0, false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, n.hi), x1, false)};
     return {hb, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
 }
 // c + a b with both operands split (16x16x32 and 16x16x16 bf16 steps)
@@ -123,6 +149,14 @@ __device__ __forceinline__ f32x4 mma_hihi(u32x2 ah, u32x2 bh, f32x4 c) {
     typedef bf16x4 B4;
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(B4, ah), __builtin_bit_cast(B4, bh), c, 0, 0, 0);
 }
+// The same cross-term step with a given as {a_lo, a_hi} in one 16-byte group,
+// as the interleaved E rows hold it (the group goes to the matrix core as
+// read, with no register moves to assemble it)
+__device__ __forceinline__ f32x4 mma_cross_packed(u32x4 a, u32x2 bh, u32x2 bl, f32x4 c) {
+    typedef bf16x8 B8;
+    const u32x4 b = {bh.x, bh.y, bl.x, bl.y};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(B8, a), __builtin_bit_cast(B8, b), c, 0, 0, 0);
+}
 // c + a b with both operands split, over K = 16 as three 16x16x16 steps (the
 // low-rank form's kernel)
 __device__ __forceinline__ f32x4 mma16(u32x2 ah, u32x2 al, u32x2 bh, u32x2 bl, f32x4 c) {
@@ -134,6 +168,12 @@ __device__ __forceinline__ f32x4 mma16(u32x2 ah, u32x2 al, u32x2 bh, u32x2 bl, f
 // the four rows 4 g + r of an accumulator tile as the split B operand of a 16x16x16 step
 __device__ __forceinline__ void split4(f32x4 d, u32x2 &h, u32x2 &l) {
     const Split2 a = split2(d[0], d[1]), b = split2(d[2], d[3]);
+    h = u32x2{a.hi, b.hi};
+    l = u32x2{a.lo, b.lo};
+}
+// (the same for a tile not needed afterwards)
+__device__ __forceinline__ void split4_dead(f32x4 d, u32x2 &h, u32x2 &l, NegOne n) {
+    const Split2 a = split2_dead(d[0], d[1], n), b = split2_dead(d[2], d[3], n);
     h = u32x2{a.hi, b.hi};
     l = u32x2{a.lo, b.lo};
 }
@@ -166,6 +206,21 @@ __device__ __forceinline__ float rel_mid(MidCoef m, float g, float c0, float g7,
     return fmaf(m.a3, c2, fmaf(-m.a1, g7, fmaf(-m.a0, c0, g)));
 }
 
+// the lane index, formed where it is used (from the lane count) and opaque to
+// the compiler, so that addresses derived from it are not hoisted out of a
+// chunk loop and kept (or spilled) for the workgroup's life
+__device__ __forceinline__ int opaque_lane() {
+    int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
+// 1/sqrt(x) by the hardware instruction, without the scaling the library adds
+// for denormal arguments: the same result for every x from the smallest normal
+// float up (x is a sum of squares plus eps here, so only an eps below that
+// bound, with an all but zero vector, can reach the difference)
+__device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
 // LDS writes of this wavefront visible to its other lanes (no other wavefront)
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -194,6 +249,7 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // in a scalar register
     const int n16 = lane & 15, g4 = lane >> 4;
     const bool state_wave = wave < 8;               // the role (wavefront-uniform)
+    const NegOne neg1 = neg_one_pairs();
     const int rw = wave & 7;                        // wavefront index within the role
     const int rtid = tid & (CK_THREADS / 2 - 1);    // thread index within the role
     const int t0 = TW * rw;                         // tokens of this wavefront's token-wise work
@@ -211,8 +267,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // (by chunk parity)
     __shared__ __attribute__((aligned(16))) uint32_t s_kah[2][CC * OPR * 4], s_kal[2][CC * OPR * 4];
     __shared__ __attribute__((aligned(16))) uint32_t s_qah[2][CC * OPR * 4], s_qal[2][CC * OPR * 4];
-    // [channel][token] split e^{G_C - G} . k_hat of the update (by chunk parity)
-    __shared__ __attribute__((aligned(16))) uint32_t s_Eh[2][DK][ER], s_El[2][DK][ER];
+    // [channel][token] split e^{G_C - G} . k_hat of the update (by chunk parity):
+    // for tokens 4 g .. 4 g + 3, u32 4 g and 4 g + 1 hold the lo parts and
+    // 4 g + 2 and 4 g + 3 the hi parts, so that one 16-byte read is the A
+    // operand of a cross-term step as it stands
+    __shared__ __attribute__((aligned(16))) uint32_t s_E[2][DK][EIR];
     __shared__ float s_gC[2][DK];          // e^{G_C}, decay of the whole chunk (by chunk parity)
     __shared__ float s_Lp[NPART][CC][CC];  // L, M summed over one channel eighth each
     __shared__ float s_Mp[NPART][CC][CC];
@@ -291,7 +350,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         }
     };
     auto reduce_M = [&](int tb) {
-        const int t = lane >> 2, s0 = 4 * (lane & 3);
+        const int l = opaque_lane();
+        const int t = l >> 2, s0 = 4 * (l & 3);
         float4 m = ld4(&s_Mp[0][t][s0]);
 #pragma unroll
         for (int q = 1; q < NPART; ++q) m += ld4(&s_Mp[q][t][s0]);
@@ -360,7 +420,7 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             for (int sl = 0; sl < TW; ++sl) {
                 const int t = t0 + sl;
                 const float2 o = ld2(&s_o[t][chq]);
-                const float r = rsqrtf(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
+                const float r = rsq(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
                 const uint32_t e = (uint32_t)(t * rowsz + h * DV + chq);
                 const float2 gg = BA::unpack2(rg[sl]);
                 float2 y;
@@ -426,9 +486,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[cur][n16][2 * g4]);
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
             u32x2 wh, wl, dh, dl;
-            split4(Wt, wh, wl);
+            split4_dead(Wt, wh, wl, neg1);
             const f32x4 Dt = mma_cross(th, tl, wh, wl, zero) + mma_hihi(th, wh, zero);
-            split4(Dt, dh, dl);
+            split4_dead(Dt, dh, dl, neg1);
             const f32x4 Ot = mma_cross(mh, ml, dh, dl, Rt) + mma_hihi(mh, dh, zero);
 #pragma unroll
             for (int r = 0; r < 4; ++r) s_o[4 * g4 + r][col0 + n16] = Ot[r];
@@ -439,13 +499,13 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
                 const float4 dc = ld4(&s_gC[cur][16 * rt + 4 * g4]);
-                eh[rt] = *reinterpret_cast<const u32x2 *>(&s_Eh[cur][16 * rt + n16][2 * g4]);
-                const u32x2 el = *reinterpret_cast<const u32x2 *>(&s_El[cur][16 * rt + n16][2 * g4]);
+                const u32x4 e = *reinterpret_cast<const u32x4 *>(&s_E[cur][16 * rt + n16][4 * g4]);
+                eh[rt] = u32x2{e.z, e.w};
                 st[rt][0] *= dc.x;
                 st[rt][1] *= dc.y;
                 st[rt][2] *= dc.z;
                 st[rt][3] *= dc.w;
-                st[rt] = mma_cross(eh[rt], el, dh, dl, st[rt]);
+                st[rt] = mma_cross_packed(e, dh, dl, st[rt]);
             }
             asm volatile("" : "+v"(st[0]), "+v"(st[1]), "+v"(st[2]), "+v"(st[3]),
                               "+v"(st[4]), "+v"(st[5]), "+v"(st[6]), "+v"(st[7]));
@@ -544,31 +604,40 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         act(gq, wq0, wq1, aq);
         act(gk, wk0, wk1, ak);
         act(gv, wv0, wv1, av);
+        // the L2 norms and the stores; a token past the end is computed and
+        // then replaced by zeros, and the decay sum held constant past the last
+        // token (only in a chunk the sequence ends inside: the condition is
+        // wavefront-uniform, so a full chunk takes the branch without selects)
+        auto finish = [&](auto masked) {
 #pragma unroll
-        for (int sl = 0; sl < TW; ++sl) {
-            // (no branch on the token: the two tokens' chains interleave; a
-            // token past the end is computed and then replaced by zeros)
-            const int t = t0 + sl;
-            const bool live = t < nv;
-            const float nq = rsqrtf(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + p.l2_eps);
-            const float nk = rsqrtf(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + p.l2_eps);
-            const float2 qh = live ? make_float2(aq[sl][0] * nq, aq[sl][1] * nq) : make_float2(0.f, 0.f);
-            const float2 kh = live ? make_float2(ak[sl][0] * nk, ak[sl][1] * nk) : make_float2(0.f, 0.f);
-            const float2 vh = live ? make_float2(av[sl][0], av[sl][1]) : make_float2(0.f, 0.f);
-            *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
-            *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
-            *reinterpret_cast<float2 *>(&s_v[vb][t][chq]) = vh;
-        }
-        if (lane < TW) s_beta[vb][t0 + lane] = (t0 + lane < nv) ? rb : 0.f;
-        float G = 0.f;                             // held constant past the last token
-        const int rem = nv - 4 * dq;               // tokens of quarter dq within the sequence
+            for (int sl = 0; sl < TW; ++sl) {
+                // (no branch on the token: the two tokens' chains interleave)
+                const int t = t0 + sl;
+                const float nq = rsq(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + p.l2_eps);
+                const float nk = rsq(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + p.l2_eps);
+                float2 qh = make_float2(aq[sl][0] * nq, aq[sl][1] * nq);
+                float2 kh = make_float2(ak[sl][0] * nk, ak[sl][1] * nk);
+                float2 vh = make_float2(av[sl][0], av[sl][1]);
+                if (masked && t >= nv) qh = kh = vh = make_float2(0.f, 0.f);
+                *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
+                *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
+                *reinterpret_cast<float2 *>(&s_v[vb][t][chq]) = vh;
+            }
+            if (lane < TW) s_beta[vb][t0 + lane] = (!masked || t0 + lane < nv) ? rb : 0.f;
+            float G = 0.f;
+            const int rem = nv - 4 * dq;           // tokens of quarter dq within the sequence
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float gk = p.lb * sigmoid(eA * (rf[u] + dtb));
-            G += (u < rem) ? gk : 0.f;
-            s_Gq[4 * dq + u][dch] = G;
-        }
-        s_Gt[dq][dch] = G;
+            for (int u = 0; u < 4; ++u) {
+                const float gk = p.lb * sigmoid(eA * (rf[u] + dtb));
+                G += (!masked || u < rem) ? gk : 0.f;
+                s_Gq[4 * dq + u][dch] = G;
+            }
+            s_Gt[dq][dch] = G;
+        };
+        if (nv == CC)
+            finish(false);
+        else
+            finish(true);
     };
 
     // split operands of the prepared chunk (into buffer buf)
@@ -578,14 +647,27 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             const int qt = t0 >> 2;
             const float2 gt0 = ld2(&s_Gt[0][chq]), gt1 = ld2(&s_Gt[1][chq]);
             const float2 gt2 = ld2(&s_Gt[2][chq]), gt3 = ld2(&s_Gt[3][chq]);
-            // sums of the quarters before and after this one
-            float2 before = make_float2(0.f, 0.f), after = make_float2(0.f, 0.f);
-            if (qt > 0) { before.x += gt0.x; before.y += gt0.y; }
-            if (qt > 1) { before.x += gt1.x; before.y += gt1.y; }
-            if (qt > 2) { before.x += gt2.x; before.y += gt2.y; }
-            if (qt < 1) { after.x += gt1.x; after.y += gt1.y; }
-            if (qt < 2) { after.x += gt2.x; after.y += gt2.y; }
-            if (qt < 3) { after.x += gt3.x; after.y += gt3.y; }
+            // sums of the quarters before and after this one (qt is
+            // wavefront-uniform: one scalar branch, no per-lane selects)
+            float2 before, after;
+            switch (qt) {
+            case 0:
+                before = make_float2(0.f, 0.f);
+                after = make_float2((gt1.x + gt2.x) + gt3.x, (gt1.y + gt2.y) + gt3.y);
+                break;
+            case 1:
+                before = gt0;
+                after = make_float2(gt2.x + gt3.x, gt2.y + gt3.y);
+                break;
+            case 2:
+                before = make_float2(gt0.x + gt1.x, gt0.y + gt1.y);
+                after = gt3;
+                break;
+            default:
+                before = make_float2((gt0.x + gt1.x) + gt2.x, (gt0.y + gt1.y) + gt2.y);
+                after = make_float2(0.f, 0.f);
+                break;
+            }
             const float2 gq_end = ld2(&s_Gt[qt][chq]);
             const int m = chq >> 5, gg = (chq & 15) >> 2, e = ((chq & 31) >> 4) * 4 + (chq & 3);
             float E0[TW], E1[TW];
@@ -596,8 +678,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 const float2 kh = ld2(&s_kh[t][chq]);
                 const float2 qh = ld2(&s_qh[t][chq]);
                 const float eg0 = __expf(before.x + gq.x), eg1 = __expf(before.y + gq.y);
-                const Split2 ka = split2(eg0 * kh.x, eg1 * kh.y);
-                const Split2 qa = split2(eg0 * qh.x, eg1 * qh.y);
+                const Split2 ka = split2_dead(eg0 * kh.x, eg1 * kh.y, neg1);
+                const Split2 qa = split2_dead(eg0 * qh.x, eg1 * qh.y, neg1);
                 const int w = (t * OPR + m * 4 + gg) * 4 + e / 2;
                 s_kah[buf][w] = ka.hi; s_kal[buf][w] = ka.lo;
                 s_qah[buf][w] = qa.hi; s_qal[buf][w] = qa.lo;
@@ -605,11 +687,12 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 E0[sl] = __expf(gq_end.x - gq.x + after.x) * kh.x;
                 E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
             }
-            const Split2 a0 = split2(E0[0], E0[1]), a1 = split2(E1[0], E1[1]);
-            reinterpret_cast<uint32_t *>(s_Eh[buf][chq])[rw] = a0.hi;
-            reinterpret_cast<uint32_t *>(s_El[buf][chq])[rw] = a0.lo;
-            reinterpret_cast<uint32_t *>(s_Eh[buf][chq + 1])[rw] = a1.hi;
-            reinterpret_cast<uint32_t *>(s_El[buf][chq + 1])[rw] = a1.lo;
+            const Split2 a0 = split2_dead(E0[0], E0[1], neg1), a1 = split2_dead(E1[0], E1[1], neg1);
+            const int eo = 4 * (rw >> 1) + (rw & 1);   // tokens t0, t0 + 1 in their group of four
+            s_E[buf][chq][eo] = a0.lo;
+            s_E[buf][chq][eo + 2] = a0.hi;
+            s_E[buf][chq + 1][eo] = a1.lo;
+            s_E[buf][chq + 1][eo + 2] = a1.hi;
             if (rw == 0) {
                 const float gc0 = gt0.x + gt1.x + gt2.x + gt3.x, gc1 = gt0.y + gt1.y + gt2.y + gt3.y;
                 *reinterpret_cast<float2 *>(&s_gC[buf][chq]) = make_float2(__expf(gc0), __expf(gc1));
@@ -860,8 +943,8 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
                 const float ak1 = silu(cconv4(wk1, xk[sl].y, xk[sl + 1].y, xk[sl + 2].y, xk[sl + 3].y));
                 vh.x = silu(cconv4(wv0, xv[sl].x, xv[sl + 1].x, xv[sl + 2].x, xv[sl + 3].x));
                 vh.y = silu(cconv4(wv1, xv[sl].y, xv[sl + 1].y, xv[sl + 2].y, xv[sl + 3].y));
-                const float nq = rsqrtf(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
-                const float nk = rsqrtf(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
+                const float nq = rsq(sum64(aq0 * aq0 + aq1 * aq1) + p.l2_eps);
+                const float nk = rsq(sum64(ak0 * ak0 + ak1 * ak1) + p.l2_eps);
                 qh = make_float2(aq0 * nq, aq1 * nq);
                 kh = make_float2(ak0 * nk, ak1 * nk);
             }
@@ -888,14 +971,27 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
             const int qt = t0 >> 2;
             const float2 gt0 = ld2(&s_Gt[0][chq]), gt1 = ld2(&s_Gt[1][chq]);
             const float2 gt2 = ld2(&s_Gt[2][chq]), gt3 = ld2(&s_Gt[3][chq]);
-            // sums of the quarters before and after this one
-            float2 before = make_float2(0.f, 0.f), after = make_float2(0.f, 0.f);
-            if (qt > 0) { before.x += gt0.x; before.y += gt0.y; }
-            if (qt > 1) { before.x += gt1.x; before.y += gt1.y; }
-            if (qt > 2) { before.x += gt2.x; before.y += gt2.y; }
-            if (qt < 1) { after.x += gt1.x; after.y += gt1.y; }
-            if (qt < 2) { after.x += gt2.x; after.y += gt2.y; }
-            if (qt < 3) { after.x += gt3.x; after.y += gt3.y; }
+            // sums of the quarters before and after this one (qt is
+            // wavefront-uniform: one scalar branch, no per-lane selects)
+            float2 before, after;
+            switch (qt) {
+            case 0:
+                before = make_float2(0.f, 0.f);
+                after = make_float2((gt1.x + gt2.x) + gt3.x, (gt1.y + gt2.y) + gt3.y);
+                break;
+            case 1:
+                before = gt0;
+                after = make_float2(gt2.x + gt3.x, gt2.y + gt3.y);
+                break;
+            case 2:
+                before = make_float2(gt0.x + gt1.x, gt0.y + gt1.y);
+                after = gt3;
+                break;
+            default:
+                before = make_float2((gt0.x + gt1.x) + gt2.x, (gt0.y + gt1.y) + gt2.y);
+                after = make_float2(0.f, 0.f);
+                break;
+            }
             const float2 gq_end = ld2(&s_Gt[qt][chq]);
             const int m = chq >> 5, gg = (chq & 15) >> 2, e = ((chq & 31) >> 4) * 4 + (chq & 3);
             float E0[TW], E1[TW];
@@ -1038,7 +1134,7 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
             const int t = t0 + sl;
             if (t >= nve) break;                   // wavefront-uniform
             const float2 o = ld2(&s_o[t][chq]);
-            const float r = rsqrtf(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
+            const float r = rsq(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
             const uint32_t e = (uint32_t)(t * rowsz + h * DV + chq);
             const float2 gg = BA::unpack2(rg[sl]);
             float2 y;
@@ -1274,13 +1370,7 @@ void prefill_chunk_short_kernel(Params p) {
     const int64_t L = rng.len;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // in a scalar register
-    // the lane index, formed where it is used (from the lane count): a copy
-    // kept for the workgroup's life costs a register the kernel does not have
-    auto lane_id = []() -> int {
-        int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-        asm volatile("" : "+v"(l));
-        return l;
-    };
+    auto lane_id = opaque_lane;
     const int t0 = TW * wave;                       // tokens of this wavefront's token-wise work
     // its state block: rows 64 hb .. 64 hb + 63 of columns 32 cb .. 32 cb + 31
     const int cb = wave >> 1, hb = wave & 1;
@@ -1311,8 +1401,10 @@ void prefill_chunk_short_kernel(Params p) {
     // stores of whole column runs
     float (*s_ox)[CC][16] = reinterpret_cast<float (*)[CC][16]>(&s_ops[0][0]);
     static_assert(8 * CC * 16 <= 4 * CC * OPR * 4, "readout exchange");
-    // [channel][token] split e^{G_C - G} . k_hat of the update
-    __shared__ __attribute__((aligned(16))) uint32_t s_Eh[DK][ER], s_El[DK][ER];
+    // [channel][token] split e^{G_C - G} . k_hat of the update, hi and lo
+    // interleaved by groups of four tokens (u32 4 g, 4 g + 1: lo; 4 g + 2,
+    // 4 g + 3: hi), one 16-byte read per cross-term operand
+    __shared__ __attribute__((aligned(16))) uint32_t s_E[DK][EIR];
     __shared__ float s_gC[DK];             // e^{G_C}, decay of the whole chunk
     // L, M summed over one channel quarter each; Diag(b) L (strictly lower)
     // over the partial L, which wavefront 0 reads before it writes; the sums
@@ -1490,10 +1582,11 @@ void prefill_chunk_short_kernel(Params p) {
                 E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
             }
             const Split2 a0 = split2(E0[0], E0[1]), a1 = split2(E1[0], E1[1]);
-            reinterpret_cast<uint32_t *>(s_Eh[chq])[wave] = a0.hi;
-            reinterpret_cast<uint32_t *>(s_El[chq])[wave] = a0.lo;
-            reinterpret_cast<uint32_t *>(s_Eh[chq + 1])[wave] = a1.hi;
-            reinterpret_cast<uint32_t *>(s_El[chq + 1])[wave] = a1.lo;
+            const int eo = 4 * (wave >> 1) + (wave & 1);   // this wavefront's two tokens in their group of four
+            s_E[chq][eo] = a0.lo;
+            s_E[chq][eo + 2] = a0.hi;
+            s_E[chq + 1][eo] = a1.lo;
+            s_E[chq + 1][eo + 2] = a1.hi;
             if (wave == 0) {
                 const float gc0 = gt0.x + gt1.x + gt2.x + gt3.x, gc1 = gt0.y + gt1.y + gt2.y + gt3.y;
                 *reinterpret_cast<float2 *>(&s_gC[chq]) = make_float2(__expf(gc0), __expf(gc1));
@@ -1593,8 +1686,8 @@ void prefill_chunk_short_kernel(Params p) {
             for (int sl = 0; sl < TW; ++sl) {
                 const int t = t0 + sl;
                 const bool live = t < nv;
-                const float nq = rsqrtf(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + p.l2_eps);
-                const float nk = rsqrtf(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + p.l2_eps);
+                const float nq = rsq(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + p.l2_eps);
+                const float nk = rsq(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + p.l2_eps);
                 const float2 qh = live ? make_float2(aq[sl][0] * nq, aq[sl][1] * nq) : make_float2(0.f, 0.f);
                 const float2 kh = live ? make_float2(ak[sl][0] * nk, ak[sl][1] * nk) : make_float2(0.f, 0.f);
                 const float2 vh = live ? make_float2(av[sl][0], av[sl][1]) : make_float2(0.f, 0.f);
@@ -1716,8 +1809,8 @@ void prefill_chunk_short_kernel(Params p) {
             for (int rl = 0; rl < 4; ++rl) {
                 const int row = 64 * hb + 16 * rl;
                 const float4 dc = ld4(&s_gC[row + 4 * g4]);
-                eh[rl] = *reinterpret_cast<const u32x2 *>(&s_Eh[row + n16][2 * g4]);
-                const u32x2 el = *reinterpret_cast<const u32x2 *>(&s_El[row + n16][2 * g4]);
+                const u32x4 e = *reinterpret_cast<const u32x4 *>(&s_E[row + n16][4 * g4]);
+                eh[rl] = u32x2{e.z, e.w};
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     f32x4 &x = st[4 * ct + rl];
@@ -1725,7 +1818,7 @@ void prefill_chunk_short_kernel(Params p) {
                     x[1] *= dc.y;
                     x[2] *= dc.z;
                     x[3] *= dc.w;
-                    x = mma_cross(eh[rl], el, dh[ct], dl[ct], x);
+                    x = mma_cross_packed(e, dh[ct], dl[ct], x);
                 }
             }
             asm volatile("" : "+v"(st[0]), "+v"(st[1]), "+v"(st[2]), "+v"(st[3]),
@@ -1743,7 +1836,7 @@ void prefill_chunk_short_kernel(Params p) {
             float s = s_ss[0][te];
 #pragma unroll
             for (int w = 1; w < 8; ++w) s += s_ss[w][te];
-            const float rr = rsqrtf(s * (1.0f / DV) + p.rms_eps);
+            const float rr = rsq(s * (1.0f / DV) + p.rms_eps);
             const float2 o0 = ld2(&s_ox[2 * cb][te][2 * (lane & 7)]);
             const float2 o1 = ld2(&s_ox[2 * cb + 1][te][2 * (lane & 7)]);
             const float4 o = make_float4(o0.x, o1.x, o0.y, o1.y);
