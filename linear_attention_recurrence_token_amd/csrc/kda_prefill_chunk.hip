@@ -17,13 +17,12 @@
 //     S_C = Diag(e^{G_C}) S_0 + E^T Delta,  E_s = e^{G_C - G_s} . k_s.
 //
 // Arithmetic.  On gfx950 fp32 MFMA holds the SIMD's vector ALU for its whole
-// duration, while bf16 MFMA runs beside it at 16x the rate.  The products with
-// the state (P, R, the update) and Delta, O therefore run on bf16 MFMA with
-// every operand split as x = hi + lo, hi = bf16(x), lo = bf16(x - hi), and
-// a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi: relative error about 2^-16 per
-// product, accumulated in fp32, the state itself kept in fp32.  L and M (two
-// 16x16 products per chunk) stay on fp32 MFMA; T = (I + Diag(b) L)^{-1} is
-// solved by forward substitution in fp32.
+// duration, while bf16 MFMA runs beside it at 16x the rate.  Every product
+// (P, R, the update, Delta, O, and the partial L and M) therefore runs on bf16
+// MFMA with each operand split as x = hi + lo, hi = bf16(x), lo = bf16(x - hi),
+// and a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi: relative error about 2^-16 per
+// product, accumulated in fp32, the state itself kept in fp32.
+// T = (I + Diag(b) L)^{-1} is solved by forward substitution in fp32.
 //
 // Exponent ranges: L and M use factors e^{G_t - r} and e^{r - G_s} with r the
 // log-decay at the chunk middle, so every factor lies within e^{+-|lb| C / 2};
@@ -84,10 +83,6 @@ constexpr int EIR = CC + 4;        // u32 per channel row of E with hi and lo in
 constexpr int TR = (CC + 4) / 2;   // u32 per row of T and M (bf16, padded)
 constexpr int NPART = 8;           // partial L, M over channel eighths
 constexpr float CHUNK_MAX_HALF_LOG_DECAY = 60.0f;
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 struct Split2 {
     uint32_t hi, lo;   // bf16 pairs, first value in the low half
@@ -366,8 +361,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 
     // L_ts = sum_i (e^{G_ti - r_i} k_ti)(e^{r_i - G_si} k_si), M likewise with q_t,
     // over channel eighth rw of the prepared chunk (partial sums), r = G at the
-    // chunk middle (token 7), on fp32 MFMA; lane l: token l % 16, channels
-    // 16 rw + 4 (l / 16) + s
+    // chunk middle (token 7), as split bf16 products; lane l: token l % 16,
+    // channels 16 rw + 4 (l / 16) + s
     auto partial_LM = [&]() {
         const int lc = 16 * rw + 4 * g4;
         const float4 k4 = ld4(&s_kh[n16][lc]);
@@ -383,15 +378,25 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
         const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
         const MidCoef mc = mid_coef(n16);
-        f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
+        float fl[4], fm[4], fb[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const float d = rel_mid(mc, gv[s], c0v[s], g7v[s], c2v[s]);
             const float ef = __expf(d), eb = __expf(-d);
-            const float b = eb * kv[s];
-            Lt = mfma4(ef * kv[s], b, Lt);
-            Mt = mfma4(ef * qv[s], b, Mt);
+            fl[s] = ef * kv[s];
+            fm[s] = ef * qv[s];
+            fb[s] = eb * kv[s];
         }
+        // one K = 16 step covers the lane's four channels s: the factors split
+        // into bf16 parts, three 16x16x16 steps per product (the same form
+        // throughout, so no step reads another form's result)
+        const Split2 l0 = split2_dead(fl[0], fl[1], neg1), l1 = split2_dead(fl[2], fl[3], neg1);
+        const Split2 m0 = split2_dead(fm[0], fm[1], neg1), m1 = split2_dead(fm[2], fm[3], neg1);
+        const Split2 b0 = split2_dead(fb[0], fb[1], neg1), b1 = split2_dead(fb[2], fb[3], neg1);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const u32x2 bh = {b0.hi, b1.hi}, bl = {b0.lo, b1.lo};
+        const f32x4 Lt = mma16(u32x2{l0.hi, l1.hi}, u32x2{l0.lo, l1.lo}, bh, bl, zero);
+        const f32x4 Mt = mma16(u32x2{m0.hi, m1.hi}, u32x2{m0.lo, m1.lo}, bh, bl, zero);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             s_Lp[rw][4 * g4 + r][n16] = Lt[r];
@@ -800,6 +805,7 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
     const int64_t unit = (int64_t)n * p.H + h;
     const int64_t rowsz = (int64_t)p.H * DK;       // elements per token row of q, k, v, f, g, y
     const int t0 = TW * wave;                       // this wavefront's tokens in the token-wise work
+    const NegOne neg1 = neg_one_pairs();
 
     __shared__ float s_kh[CC][KP];         // k_hat of the chunk being prepared
     __shared__ float s_qh[CC][KP];         // q_hat of the chunk being prepared
@@ -1022,8 +1028,8 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
             }
         }
         // L_ts = sum_i (e^{G_ti - r_i} k_ti)(e^{r_i - G_si} k_si), M likewise with q_t,
-        // r = G at the chunk middle (token 7), on fp32 MFMA; lane l: token l % 16,
-        // channels 16 wave + 4 (l / 16) + s
+        // r = G at the chunk middle (token 7), as split bf16 products over the
+        // wavefront's 16 channels; lane l: token l % 16, channels 16 wave + 4 (l / 16) + s
         const int cb = 16 * wave + 4 * g4;
         const int tq = n16 >> 2;
         const float4 k4 = ld4(&s_kh[n16][cb]);
@@ -1038,7 +1044,7 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
         const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
         const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
         const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
-        f32x4 Lt = {0.f, 0.f, 0.f, 0.f}, Mt = Lt;
+        float fl[4], fm[4], fb[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             // G_t - r from sums that start as close to both tokens as possible
@@ -1046,10 +1052,18 @@ __global__ __launch_bounds__(LR_THREADS) void prefill_chunk_lr_kernel(Params p) 
                           : tq == 1 ? gv[s] - g7v[s]
                           : tq == 2 ? gv[s] : gv[s] + c2v[s];
             const float ef = __expf(d), eb = __expf(-d);
-            const float b = eb * kv[s];
-            Lt = mfma4(ef * kv[s], b, Lt);
-            Mt = mfma4(ef * qv[s], b, Mt);
+            fl[s] = ef * kv[s];
+            fm[s] = ef * qv[s];
+            fb[s] = eb * kv[s];
         }
+        // (one K = 16 step per part: three 16x16x16 steps per product)
+        const Split2 l0 = split2_dead(fl[0], fl[1], neg1), l1 = split2_dead(fl[2], fl[3], neg1);
+        const Split2 m0 = split2_dead(fm[0], fm[1], neg1), m1 = split2_dead(fm[2], fm[3], neg1);
+        const Split2 b0 = split2_dead(fb[0], fb[1], neg1), b1 = split2_dead(fb[2], fb[3], neg1);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const u32x2 bh = {b0.hi, b1.hi}, bl = {b0.lo, b1.lo};
+        const f32x4 Lt = mma16(u32x2{l0.hi, l1.hi}, u32x2{l0.lo, l1.lo}, bh, bl, zero);
+        const f32x4 Mt = mma16(u32x2{m0.hi, m1.hi}, u32x2{m0.lo, m1.lo}, bh, bl, zero);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             s_Lp[wave][4 * g4 + r][n16] = Lt[r];
@@ -1371,6 +1385,7 @@ void prefill_chunk_short_kernel(Params p) {
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // in a scalar register
     auto lane_id = opaque_lane;
+    const NegOne neg1 = neg_one_pairs();
     const int t0 = TW * wave;                       // tokens of this wavefront's token-wise work
     // its state block: rows 64 hb .. 64 hb + 63 of columns 32 cb .. 32 cb + 31
     const int cb = wave >> 1, hb = wave & 1;
@@ -1520,7 +1535,9 @@ void prefill_chunk_short_kernel(Params p) {
         // wavefronts 0-3: L over key channels 32 j .. 32 j + 31 (j = w); 4-7: M
         // over the same quarter (j = w - 4); lane l: token l % 16 and channels
         // 32 j + 8 (l / 16) + {0..7}; factors e^{+-(G - r)}, r the log-decay at
-        // the chunk middle, as in the kernel above
+        // the chunk middle, as in the kernel above; split bf16 products, one
+        // K = 16 step per half hh of the lane's channels (three 16x16x16 steps
+        // each, accumulated in one form)
         auto partial_LM = [&]() {
             const int j = wave & 3;
             const bool is_M = wave >= 4;              // wavefront-uniform
@@ -1541,11 +1558,16 @@ void prefill_chunk_short_kernel(Params p) {
                 const float g7v[4] = {g7.x, g7.y, g7.z, g7.w};
                 const float c0v[4] = {c0.x, c0.y, c0.z, c0.w};
                 const float c2v[4] = {c2.x, c2.y, c2.z, c2.w};
+                float fa[4], fb[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const float d = rel_mid(mc, gv[s], c0v[s], g7v[s], c2v[s]);
-                    acc = mfma4(__expf(d) * av[s], __expf(-d) * kv[s], acc);
+                    fa[s] = __expf(d) * av[s];
+                    fb[s] = __expf(-d) * kv[s];
                 }
+                const Split2 a0 = split2_dead(fa[0], fa[1], neg1), a1 = split2_dead(fa[2], fa[3], neg1);
+                const Split2 b0 = split2_dead(fb[0], fb[1], neg1), b1 = split2_dead(fb[2], fb[3], neg1);
+                acc = mma16(u32x2{a0.hi, a1.hi}, u32x2{a0.lo, a1.lo}, u32x2{b0.hi, b1.hi}, u32x2{b0.lo, b1.lo}, acc);
             }
             float (*dst)[CC] = is_M ? s_Mp[j] : s_Lp[j];
 #pragma unroll
@@ -1556,13 +1578,27 @@ void prefill_chunk_short_kernel(Params p) {
             const int qt = t0 >> 2;
             const float2 gt0 = ld2(&s_Gt[0][chq]), gt1 = ld2(&s_Gt[1][chq]);
             const float2 gt2 = ld2(&s_Gt[2][chq]), gt3 = ld2(&s_Gt[3][chq]);
-            float2 before = make_float2(0.f, 0.f), after = make_float2(0.f, 0.f);
-            if (qt > 0) { before.x += gt0.x; before.y += gt0.y; }
-            if (qt > 1) { before.x += gt1.x; before.y += gt1.y; }
-            if (qt > 2) { before.x += gt2.x; before.y += gt2.y; }
-            if (qt < 1) { after.x += gt1.x; after.y += gt1.y; }
-            if (qt < 2) { after.x += gt2.x; after.y += gt2.y; }
-            if (qt < 3) { after.x += gt3.x; after.y += gt3.y; }
+            // sums of the quarters before and after this one (qt is
+            // wavefront-uniform: one scalar branch, no per-lane selects)
+            float2 before, after;
+            switch (qt) {
+            case 0:
+                before = make_float2(0.f, 0.f);
+                after = make_float2((gt1.x + gt2.x) + gt3.x, (gt1.y + gt2.y) + gt3.y);
+                break;
+            case 1:
+                before = gt0;
+                after = make_float2(gt2.x + gt3.x, gt2.y + gt3.y);
+                break;
+            case 2:
+                before = make_float2(gt0.x + gt1.x, gt0.y + gt1.y);
+                after = gt3;
+                break;
+            default:
+                before = make_float2((gt0.x + gt1.x) + gt2.x, (gt0.y + gt1.y) + gt2.y);
+                after = make_float2(0.f, 0.f);
+                break;
+            }
             const float2 gq_end = ld2(&s_Gt[qt][chq]);
             const int m = chq >> 5, gg = (chq & 15) >> 2, e = ((chq & 31) >> 4) * 4 + (chq & 3);
             float E0[TW], E1[TW];
