@@ -329,6 +329,25 @@ def prefill_samples(w):
     return seqs[:4], heads
 
 
+# The GPU's clock ramps up over the first ~20 ms of sustained load (16 x 64 x
+# 2048 bf16 back to back: 2.40, 2.35, 2.24, 2.13, 2.06, 2.01 ms for the first
+# calls, then 1.82-1.90 ms from about the tenth).  Prefill and layer calls
+# therefore run untimed until WARM_MS of GPU time have passed (at least one
+# call), and only then are `runs` calls timed: the steady state a serving loop
+# runs in, as the 1000-step decode timing is.
+WARM_MS = 60.0
+
+
+def warm_up(one_call):
+    """Call one_call() (which returns its GPU milliseconds) until WARM_MS have
+    passed; returns the number of calls."""
+    total, calls = 0.0, 0
+    while calls == 0 or total < WARM_MS:
+        total += one_call()
+        calls += 1
+    return calls
+
+
 def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=True):
     import numpy as np
     d = synth.to_device(w, dev, with_o_raw=False)
@@ -355,8 +374,7 @@ def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=
                             w.total_tokens, ws_ptr, ws_bytes, stream.cuda_stream, side.cuda_stream)
         if st != 0:
             raise RuntimeError("kda_sequence returned %d" % st)
-    times = []
-    for r in range(runs + 1):
+    def one_call():
         d["state"].copy_(state0)
         d["conv_win"].copy_(win0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -364,8 +382,9 @@ def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=
         launch()
         e1.record(stream)
         torch.cuda.synchronize()
-        if r:
-            times.append(e0.elapsed_time(e1))
+        return e0.elapsed_time(e1)
+    warm_calls = warm_up(one_call)
+    times = [one_call() for _ in range(runs)]
     ms = float(np.median(times))
     th = int(lens.sum()) * w.H
     # the kernel the automatic choice runs (the library's rule: for the
@@ -390,6 +409,7 @@ def bench_prefill(torch, kda, synth, dev, w, runs, traffic_key=None, want_check=
     hbm_bytes = w.N * w.H * (2 * DK * DV * 4 + 2 * 3 * 384 * 4) + th * per_token
     recur_tf = th * RECUR_FLOPS / (ms * 1e-3) / 1e12
     out = {"workload": w.name, "path": path, "token_heads": th, "ms": ms, "runs": runs,
+           "warmup_calls": warm_calls, "ms_each": [round(x, 4) for x in times],
            "value": th / (ms * 1e-3), "unit": UNIT,
            "ns_per_token_per_chain": ms * 1e6 / int(lens.max()),
            "hbm_GBps_algorithmic": hbm_bytes / (ms * 1e-3) / 1e9,
@@ -612,8 +632,7 @@ def bench_layer(torch, kda, synth, dev, runs):
              "f_in_step": ["lowrank_factor", "gate_projection", "step_lowrank", "output_projection"]}
 
     def timed(names):
-        times = []
-        for rep in range(runs + 1):
+        def one_call():
             d["state"].copy_(state0)
             d["conv_win"].copy_(win0)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -622,9 +641,9 @@ def bench_layer(torch, kda, synth, dev, runs):
                 parts[n]()
             e1.record(stream)
             torch.cuda.synchronize()
-            if rep:
-                times.append(e0.elapsed_time(e1))
-        return float(np.median(times))
+            return e0.elapsed_time(e1)
+        warm_up(one_call)
+        return float(np.median([one_call() for _ in range(runs)]))
     res = {"workload": "KDA layer 16 x 64 x 2048 bf16, hidden 8192, rank 128 (synthetic weights)",
            "token_heads": T * H, "parts_ms": {n: timed([n]) for n in parts}}
     for form, names in forms.items():
@@ -637,12 +656,15 @@ def bench_layer(torch, kda, synth, dev, runs):
 
 
 def main():
+    global WARM_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prefill", choices=["none", "default", "all"], default="default")
     ap.add_argument("--prefill-runs", type=int, default=5)
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="untimed GPU milliseconds before each prefill / layer timing (0: one call)")
     ap.add_argument("--projections", choices=["none", "default", "all"], default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU leg: no oracle baseline and no parity check of the timed runs")
@@ -658,6 +680,7 @@ def main():
                     help="print the source key of a path's kernels (decode, chunk, scan, short, split, "
                          "fused, proj), as the traffic summaries record it, and exit")
     args = ap.parse_args()
+    WARM_MS = max(0.0, args.warm_ms)
 
     if args.source_key:
         print(source_key(args.source_key))
