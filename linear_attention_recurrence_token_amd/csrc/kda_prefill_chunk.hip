@@ -260,8 +260,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // split bf16 operands e^G . k_hat, e^G . q_hat of P and R: slot (t, m, g)
     // holds channels 32 m + 4 g + {0..3} and 32 m + 16 + 4 g + {0..3} of token t
     // (by chunk parity)
-    __shared__ __attribute__((aligned(16))) uint32_t s_kah[2][CC * OPR * 4], s_kal[2][CC * OPR * 4];
-    __shared__ __attribute__((aligned(16))) uint32_t s_qah[2][CC * OPR * 4], s_qal[2][CC * OPR * 4];
+    // (one array: k hi, k lo, q hi, q lo by the second index, so that a lane's
+    // 16 reads of them per chunk share one address register)
+    __shared__ __attribute__((aligned(16))) uint32_t s_pr[2][4][CC * OPR * 4];
     // [channel][token] split e^{G_C - G} . k_hat of the update (by chunk parity):
     // for tokens 4 g .. 4 g + 3, u32 4 g and 4 g + 1 hold the lo parts and
     // 4 g + 2 and 4 g + 3 the hi parts, so that one 16-byte read is the A
@@ -273,7 +274,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     __shared__ float s_A[CC][TP];          // Diag(b) L, strictly lower
     // (I + Diag(b) L)^{-1} and M (lower triangle with the diagonal), [row][column]
     // split bf16 (by chunk parity)
-    __shared__ __attribute__((aligned(16))) uint32_t s_Th[2][CC][TR], s_Tl[2][CC][TR], s_Mh[2][CC][TR], s_Ml[2][CC][TR];
+    // (one array: T hi, T lo, M hi, M lo by the second index)
+    __shared__ __attribute__((aligned(16))) uint32_t s_tm[2][4][CC][TR];
     __shared__ float s_o[CC][DV + 4];      // readout of the chunk, before RMSNorm
     __shared__ float s_cw[CH][TAPS];       // conv taps of this head
 
@@ -340,8 +342,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             Tc[4 * b + 2] = x2;
             Tc[4 * b + 3] = x3;
             const Split2 x = split2(y, 0.f);
-            reinterpret_cast<uint16_t *>(s_Th[tb][t])[c] = (uint16_t)x.hi;
-            reinterpret_cast<uint16_t *>(s_Tl[tb][t])[c] = (uint16_t)x.lo;
+            reinterpret_cast<uint16_t *>(s_tm[tb][0][t])[c] = (uint16_t)x.hi;
+            reinterpret_cast<uint16_t *>(s_tm[tb][1][t])[c] = (uint16_t)x.lo;
         }
     };
     auto reduce_M = [&](int tb) {
@@ -355,8 +357,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         m.z = (s0 + 2 <= t) ? m.z : 0.f;
         m.w = (s0 + 3 <= t) ? m.w : 0.f;
         const Split2 a = split2(m.x, m.y), b = split2(m.z, m.w);
-        *reinterpret_cast<u32x2 *>(&s_Mh[tb][t][s0 / 2]) = u32x2{a.hi, b.hi};
-        *reinterpret_cast<u32x2 *>(&s_Ml[tb][t][s0 / 2]) = u32x2{a.lo, b.lo};
+        *reinterpret_cast<u32x2 *>(&s_tm[tb][2][t][s0 / 2]) = u32x2{a.hi, b.hi};
+        *reinterpret_cast<u32x2 *>(&s_tm[tb][3][t][s0 / 2]) = u32x2{a.lo, b.lo};
     };
 
     // L_ts = sum_i (e^{G_ti - r_i} k_ti)(e^{r_i - G_si} k_si), M likewise with q_t,
@@ -463,10 +465,10 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int w = (n16 * OPR + m * 4 + g4) * 4;
-                const u32x4 kah = *reinterpret_cast<const u32x4 *>(&s_kah[pb][w]);
-                const u32x4 kal = *reinterpret_cast<const u32x4 *>(&s_kal[pb][w]);
-                const u32x4 qah = *reinterpret_cast<const u32x4 *>(&s_qah[pb][w]);
-                const u32x4 qal = *reinterpret_cast<const u32x4 *>(&s_qal[pb][w]);
+                const u32x4 kah = *reinterpret_cast<const u32x4 *>(&s_pr[pb][0][w]);
+                const u32x4 kal = *reinterpret_cast<const u32x4 *>(&s_pr[pb][1][w]);
+                const u32x4 qah = *reinterpret_cast<const u32x4 *>(&s_pr[pb][2][w]);
+                const u32x4 qal = *reinterpret_cast<const u32x4 *>(&s_pr[pb][3][w]);
                 const Split2 x0 = split2(st[2 * m][0], st[2 * m][1]);
                 const Split2 x1 = split2(st[2 * m][2], st[2 * m][3]);
                 const Split2 x2 = split2(st[2 * m + 1][0], st[2 * m + 1][1]);
@@ -485,10 +487,10 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 const int t = 4 * g4 + r;
                 Wt[r] = s_beta[vb][t] * (s_v[vb][t][col0 + n16] - Pt[r]);
             }
-            const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_Th[cur][n16][2 * g4]);
-            const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_Tl[cur][n16][2 * g4]);
-            const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_Mh[cur][n16][2 * g4]);
-            const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_Ml[cur][n16][2 * g4]);
+            const u32x2 th = *reinterpret_cast<const u32x2 *>(&s_tm[cur][0][n16][2 * g4]);
+            const u32x2 tl = *reinterpret_cast<const u32x2 *>(&s_tm[cur][1][n16][2 * g4]);
+            const u32x2 mh = *reinterpret_cast<const u32x2 *>(&s_tm[cur][2][n16][2 * g4]);
+            const u32x2 ml = *reinterpret_cast<const u32x2 *>(&s_tm[cur][3][n16][2 * g4]);
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
             u32x2 wh, wl, dh, dl;
             split4_dead(Wt, wh, wl, neg1);
@@ -553,8 +555,10 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     const int dch = rtid & (DK - 1);
     const int dq = rtid >> 7;
     const uint32_t foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
-    const float eA = __expf(p.A_log[h * DK + dch]);
-    const float dtb = p.dt_bias[h * DK + dch];
+    // sigmoid(exp(A_log) (f + dt_bias)) = 1 / (1 + 2^(nA f + nAd)), with nA =
+    // -log2(e) exp(A_log) and nAd = nA dt_bias formed once
+    const float nA = -1.4426950408889634f * __expf(p.A_log[h * DK + dch]);
+    const float nAd = nA * p.dt_bias[h * DK + dch];
 
     // registers loaded a chunk ahead: raw inputs of the next chunk to pre-step
     Raw2 rq[RAWR], rk[RAWR], rv[RAWR];
@@ -633,7 +637,7 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             const int rem = nv - 4 * dq;           // tokens of quarter dq within the sequence
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float gk = p.lb * sigmoid(eA * (rf[u] + dtb));
+                const float gk = p.lb * fast_rcp(1.0f + __builtin_amdgcn_exp2f(fmaf(nA, rf[u], nAd)));
                 G += (!masked || u < rem) ? gk : 0.f;
                 s_Gq[4 * dq + u][dch] = G;
             }
@@ -686,8 +690,8 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 const Split2 ka = split2_dead(eg0 * kh.x, eg1 * kh.y, neg1);
                 const Split2 qa = split2_dead(eg0 * qh.x, eg1 * qh.y, neg1);
                 const int w = (t * OPR + m * 4 + gg) * 4 + e / 2;
-                s_kah[buf][w] = ka.hi; s_kal[buf][w] = ka.lo;
-                s_qah[buf][w] = qa.hi; s_qal[buf][w] = qa.lo;
+                s_pr[buf][0][w] = ka.hi; s_pr[buf][1][w] = ka.lo;
+                s_pr[buf][2][w] = qa.hi; s_pr[buf][3][w] = qa.lo;
                 // G_C - G_t = (rest of this quarter) + (later quarters)
                 E0[sl] = __expf(gq_end.x - gq.x + after.x) * kh.x;
                 E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
