@@ -482,16 +482,36 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
         // partial P, R over this wavefront's key rows: steps m = 2 rh, 2 rh + 1
         // (rows 32 m .. 32 m + 31, tiles 2 (m - 2 rh), + 1); the three parts of
         // each split product accumulate in one chain
+        // (LDS reads complete in order: the products' operands are read first,
+        // then the chunk's other record fields that the chain after the
+        // exchange needs, so that their latency runs under the products; the
+        // scheduling barriers keep that order)
         const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
         f32x4 Pp = z4, Rp = z4;
+        u32x4 ka_h[2], ka_l[2], qa_h[2], qa_l[2];
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-            const int m = 2 * rh + mm;
-            const int so = ((m * 4 + g4) * CC + n16) * 16;
-            const u32x4 kah = *reinterpret_cast<const u32x4 *>(R + R_KA + so);
-            const u32x4 kal = *reinterpret_cast<const u32x4 *>(R + R_KA + 4096 + so);
-            const u32x4 qah = *reinterpret_cast<const u32x4 *>(R + R_QA + so);
-            const u32x4 qal = *reinterpret_cast<const u32x4 *>(R + R_QA + 4096 + so);
+            const int so = (((2 * rh + mm) * 4 + g4) * CC + n16) * 16;
+            ka_h[mm] = *reinterpret_cast<const u32x4 *>(R + R_KA + so);
+            ka_l[mm] = *reinterpret_cast<const u32x4 *>(R + R_KA + 4096 + so);
+            qa_h[mm] = *reinterpret_cast<const u32x4 *>(R + R_QA + so);
+            qa_l[mm] = *reinterpret_cast<const u32x4 *>(R + R_QA + 4096 + so);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // beta, v, T and M of the chunk, behind the products' operands
+        const float4 bt = *reinterpret_cast<const float4 *>(R + R_B + 16 * g4);   // beta of tokens 4 g4 + r
+        float vt[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vt[r] = reinterpret_cast<const float *>(R + R_V)[(4 * g4 + r) * DK + col0 + n16];
+        const int to = (n16 * CC + 4 * g4) * 2;
+        const u32x2 th = *reinterpret_cast<const u32x2 *>(R + R_T + to);
+        const u32x2 tl = *reinterpret_cast<const u32x2 *>(R + R_T + 512 + to);
+        const u32x2 mh = *reinterpret_cast<const u32x2 *>(R + R_M + to);
+        const u32x2 ml = *reinterpret_cast<const u32x2 *>(R + R_M + 512 + to);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            const u32x4 kah = ka_h[mm], kal = ka_l[mm], qah = qa_h[mm], qal = qa_l[mm];
             const Split2 x0 = split2(st[2 * mm][0], st[2 * mm][1]);
             const Split2 x1 = split2(st[2 * mm][2], st[2 * mm][3]);
             const Split2 x2 = split2(st[2 * mm + 1][0], st[2 * mm + 1][1]);
@@ -510,6 +530,18 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
             sX[wave][1][r][lane] = Rp[r];
         }
         lds_barrier();
+        // the update's operands from the record, read before the chain of W,
+        // Delta and O, which they then wait under
+        float4 dc[4];
+        u32x2 eh[4], el[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rt = 4 * rh + j;
+            dc[j] = *reinterpret_cast<const float4 *>(R + R_GC + (16 * rt + 4 * g4) * 4);
+            const int eo = ((16 * rt + n16) * CC + 4 * g4) * 2;
+            eh[j] = *reinterpret_cast<const u32x2 *>(R + R_E + eo);
+            el[j] = *reinterpret_cast<const u32x2 *>(R + R_E + 4096 + eo);
+        }
         // whole P, R: the lower row half's part plus the upper's, in that order
         // in both wavefronts, so that both form the same Delta
         f32x4 Pt, Rt;
@@ -520,23 +552,12 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
             Rt[r] = rh == 0 ? Rp[r] + ro : ro + Rp[r];
         }
         // W = Diag(b) (V - P) (rows 4 g4 + r); Delta = T W; O = R + M Delta
-        f32x4 Wt;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g4 + r;
-            Wt[r] = reinterpret_cast<const float *>(R + R_B)[t] *
-                    (reinterpret_cast<const float *>(R + R_V)[t * DK + col0 + n16] - Pt[r]);
-        }
-        const int to = (n16 * CC + 4 * g4) * 2;
-        const u32x2 th = *reinterpret_cast<const u32x2 *>(R + R_T + to);
-        const u32x2 tl = *reinterpret_cast<const u32x2 *>(R + R_T + 512 + to);
+        const f32x4 Wt = {bt.x * (vt[0] - Pt[0]), bt.y * (vt[1] - Pt[1]), bt.z * (vt[2] - Pt[2]), bt.w * (vt[3] - Pt[3])};
         u32x2 wh, wl, dh, dl;
         split4(Wt, wh, wl);
         const f32x4 Dt = mma16(th, tl, wh, wl, f32x4{0.f, 0.f, 0.f, 0.f});
         split4(Dt, dh, dl);
         if (rh == 0) {
-            const u32x2 mh = *reinterpret_cast<const u32x2 *>(R + R_M + to);
-            const u32x2 ml = *reinterpret_cast<const u32x2 *>(R + R_M + 512 + to);
             const f32x4 Ot = mma16(mh, ml, dh, dl, Rt);
             const int64_t nv = rng.len - c * CC < CC ? rng.len - c * CC : CC;
             const Rsrc ro = make_rsrc(obuf + (rng.lo + c * CC) * rowsz + (int64_t)h * DV + col0,
@@ -547,16 +568,11 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(Params p, const u
         // S <- Diag(e^{G_C}) S + E^T Delta on this wavefront's rows
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int rt = 4 * rh + j;
-            const float4 dc = *reinterpret_cast<const float4 *>(R + R_GC + (16 * rt + 4 * g4) * 4);
-            const int eo = ((16 * rt + n16) * CC + 4 * g4) * 2;
-            const u32x2 eh = *reinterpret_cast<const u32x2 *>(R + R_E + eo);
-            const u32x2 el = *reinterpret_cast<const u32x2 *>(R + R_E + 4096 + eo);
-            st[j][0] *= dc.x;
-            st[j][1] *= dc.y;
-            st[j][2] *= dc.z;
-            st[j][3] *= dc.w;
-            st[j] = mma16(eh, el, dh, dl, st[j]);
+            st[j][0] *= dc[j].x;
+            st[j][1] *= dc[j].y;
+            st[j][2] *= dc[j].z;
+            st[j][3] *= dc[j].w;
+            st[j] = mma16(eh[j], el[j], dh, dl, st[j]);
         }
     };
     // chunk c: its record landed everywhere (and every wavefront is done with
