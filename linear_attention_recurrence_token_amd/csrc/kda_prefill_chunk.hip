@@ -253,8 +253,10 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 
     __shared__ float s_kh[CC][KP];         // k_hat of the chunk being prepared
     __shared__ float s_qh[CC][KP];         // q_hat of the chunk being prepared
-    __shared__ float s_Gq[CC][KP];         // log-decay summed from the start of the token's quarter
-    __shared__ float s_Gt[4][DK];          // log-decay summed over each quarter
+    // (the log-decay sums in base 2: log2(alpha) = log2(e) gk, so that each
+    // factor e^{G...} below is one exp2)
+    __shared__ float s_Gq[CC][KP];         // log2-decay summed from the start of the token's quarter
+    __shared__ float s_Gt[4][DK];          // log2-decay summed over each quarter
     __shared__ float s_v[3][CC][DV + 4];   // activated v            (by chunk index mod 3)
     __shared__ float s_beta[3][CC];        //                        (by chunk index mod 3)
     // split bf16 operands e^G . k_hat, e^G . q_hat of P and R: slot (t, m, g)
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const float d = rel_mid(mc, gv[s], c0v[s], g7v[s], c2v[s]);
-            const float ef = __expf(d), eb = __expf(-d);
+            const float ef = __builtin_amdgcn_exp2f(d), eb = __builtin_amdgcn_exp2f(-d);
             fl[s] = ef * kv[s];
             fm[s] = ef * qv[s];
             fb[s] = eb * kv[s];
@@ -568,6 +570,9 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // conv taps of this lane's channels, kept in registers (their LDS reads
     // would queue behind the state wavefronts' operand reads every chunk)
     float4 wq0, wq1, wk0, wk1, wv0, wv1;
+    constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+    const float l2_eps2 = p.l2_eps * (LOG2E * LOG2E);   // eps for the activations times log2(e)
+    const float lb2 = p.lb * LOG2E;                     // the decay's bound in base 2
     float rf[4], rb;
 
     // loads of a chunk at c0 >= CC (its past rows are tokens, not the window);
@@ -598,15 +603,20 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // (gq, gk, gv: row r of the raw window behind the tokens, as float2)
     auto prestep = [&](auto gq, auto gk, auto gv, int64_t c0, int vb) {
         const int nv = (int)(L - c0 < CC ? L - c0 : CC);
-        // conv + SiLU of one of q, k, v for this wavefront's two tokens
+        // conv + SiLU of one of q, k, v for this wavefront's two tokens, times
+        // log2(e): the taps in registers carry that factor, so that
+        // e^{-conv} is one exp2 of the scaled sum (the factor drops out of
+        // the L2 norms of q and k with eps scaled by log2(e)^2, and v is
+        // scaled back)
+        auto silu2 = [](float y) { return y * fast_rcp(1.0f + __builtin_amdgcn_exp2f(-y)); };
         auto act = [&](auto g, const float4 &w0, const float4 &w1, float (&a)[TW][2]) {
             float2 x[RAWR];
 #pragma unroll
             for (int r = 0; r < RAWR; ++r) x[r] = g(r);
 #pragma unroll
             for (int sl = 0; sl < TW; ++sl) {
-                a[sl][0] = silu(cconv4(w0, x[sl].x, x[sl + 1].x, x[sl + 2].x, x[sl + 3].x));
-                a[sl][1] = silu(cconv4(w1, x[sl].y, x[sl + 1].y, x[sl + 2].y, x[sl + 3].y));
+                a[sl][0] = silu2(cconv4(w0, x[sl].x, x[sl + 1].x, x[sl + 2].x, x[sl + 3].x));
+                a[sl][1] = silu2(cconv4(w1, x[sl].y, x[sl + 1].y, x[sl + 2].y, x[sl + 3].y));
             }
         };
         float aq[TW][2], ak[TW][2], av[TW][2];
@@ -622,11 +632,11 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             for (int sl = 0; sl < TW; ++sl) {
                 // (no branch on the token: the two tokens' chains interleave)
                 const int t = t0 + sl;
-                const float nq = rsq(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + p.l2_eps);
-                const float nk = rsq(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + p.l2_eps);
+                const float nq = rsq(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + l2_eps2);
+                const float nk = rsq(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + l2_eps2);
                 float2 qh = make_float2(aq[sl][0] * nq, aq[sl][1] * nq);
                 float2 kh = make_float2(ak[sl][0] * nk, ak[sl][1] * nk);
-                float2 vh = make_float2(av[sl][0], av[sl][1]);
+                float2 vh = make_float2(av[sl][0] * LN2, av[sl][1] * LN2);
                 if (masked && t >= nv) qh = kh = vh = make_float2(0.f, 0.f);
                 *reinterpret_cast<float2 *>(&s_qh[t][chq]) = qh;
                 *reinterpret_cast<float2 *>(&s_kh[t][chq]) = kh;
@@ -637,7 +647,7 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             const int rem = nv - 4 * dq;           // tokens of quarter dq within the sequence
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float gk = p.lb * fast_rcp(1.0f + __builtin_amdgcn_exp2f(fmaf(nA, rf[u], nAd)));
+                const float gk = lb2 * fast_rcp(1.0f + __builtin_amdgcn_exp2f(fmaf(nA, rf[u], nAd)));
                 G += (!masked || u < rem) ? gk : 0.f;
                 s_Gq[4 * dq + u][dch] = G;
             }
@@ -686,15 +696,15 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
                 const float2 gq = ld2(&s_Gq[t][chq]);
                 const float2 kh = ld2(&s_kh[t][chq]);
                 const float2 qh = ld2(&s_qh[t][chq]);
-                const float eg0 = __expf(before.x + gq.x), eg1 = __expf(before.y + gq.y);
+                const float eg0 = __builtin_amdgcn_exp2f(before.x + gq.x), eg1 = __builtin_amdgcn_exp2f(before.y + gq.y);
                 const Split2 ka = split2_dead(eg0 * kh.x, eg1 * kh.y, neg1);
                 const Split2 qa = split2_dead(eg0 * qh.x, eg1 * qh.y, neg1);
                 const int w = (t * OPR + m * 4 + gg) * 4 + e / 2;
                 s_pr[buf][0][w] = ka.hi; s_pr[buf][1][w] = ka.lo;
                 s_pr[buf][2][w] = qa.hi; s_pr[buf][3][w] = qa.lo;
                 // G_C - G_t = (rest of this quarter) + (later quarters)
-                E0[sl] = __expf(gq_end.x - gq.x + after.x) * kh.x;
-                E1[sl] = __expf(gq_end.y - gq.y + after.y) * kh.y;
+                E0[sl] = __builtin_amdgcn_exp2f(gq_end.x - gq.x + after.x) * kh.x;
+                E1[sl] = __builtin_amdgcn_exp2f(gq_end.y - gq.y + after.y) * kh.y;
             }
             const Split2 a0 = split2_dead(E0[0], E0[1], neg1), a1 = split2_dead(E1[0], E1[1], neg1);
             const int eo = 4 * (rw >> 1) + (rw & 1);   // tokens t0, t0 + 1 in their group of four
@@ -704,15 +714,17 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             s_E[buf][chq + 1][eo + 2] = a1.hi;
             if (rw == 0) {
                 const float gc0 = gt0.x + gt1.x + gt2.x + gt3.x, gc1 = gt0.y + gt1.y + gt2.y + gt3.y;
-                *reinterpret_cast<float2 *>(&s_gC[buf][chq]) = make_float2(__expf(gc0), __expf(gc1));
+                *reinterpret_cast<float2 *>(&s_gC[buf][chq]) =
+                    make_float2(__builtin_amdgcn_exp2f(gc0), __builtin_amdgcn_exp2f(gc1));
             }
         }
     };
 
     __syncthreads();                               // conv taps in LDS
-    wq0 = ld4(s_cw[chq]); wq1 = ld4(s_cw[chq + 1]);
-    wk0 = ld4(s_cw[chk]); wk1 = ld4(s_cw[chk + 1]);
-    wv0 = ld4(s_cw[chv]); wv1 = ld4(s_cw[chv + 1]);
+    // the taps times log2(e) (see the pre-step)
+    wq0 = ld4(s_cw[chq]) * LOG2E; wq1 = ld4(s_cw[chq + 1]) * LOG2E;
+    wk0 = ld4(s_cw[chk]) * LOG2E; wk1 = ld4(s_cw[chk + 1]) * LOG2E;
+    wv0 = ld4(s_cw[chv]) * LOG2E; wv1 = ld4(s_cw[chv + 1]) * LOG2E;
     // ---- chunk 0 (its past rows come from the carried window)
     {
         const int64_t end = chunk_end(0);
