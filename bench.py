@@ -55,14 +55,13 @@ FP32_TOL, BF16_TOL = 1e-4, 2e-2
 # Matrix-core flops the chunkwise kernels issue per 16-token chunk of one
 # (sequence, head) pair, every split product counted as its three bf16
 # products (16x16x32 step: 16384 flops, 16x16x16 step: 8192):
-#   one-pass kernel, 8 wavefronts: P and R 24 x 16x16x32, Delta, O 2 x 3 and the
-#   state update 8 x 3 16x16x16 steps each -> 8 x (24 x 16384 + 30 x 8192);
+#   one-pass kernel, 8 wavefronts: P and R 24 x 16x16x32, Delta, O 2 x 3, the
+#   state update 8 x 3 and the partial L, M 2 x 3 16x16x16 steps each ->
+#   8 x (24 x 16384 + 36 x 8192);
 #   two-pass state pass, 16 wavefronts (two row halves of 8 column blocks): P, R
 #   12 x 16x16x32, Delta 3 and the update 4 x 3 16x16x16 each, O 3 x 16x16x16
-#   on the 8 lower halves.
-# (The one-pass kernel also issues L and M on fp32 MFMA: 8 x 8 16x16x4 steps
-# = 131072 flops per chunk, not counted.)
-CHUNK_MFMA_FLOPS = {"chunk": 8 * (24 * 16384 + 30 * 8192),
+#   on the 8 lower halves (its L and M are formed in the operand pass).
+CHUNK_MFMA_FLOPS = {"chunk": 8 * (24 * 16384 + 36 * 8192),
                     "scan": 16 * (12 * 16384 + 15 * 8192) + 8 * 3 * 8192}
 CHUNK = 16
 
