@@ -216,6 +216,24 @@ __device__ __forceinline__ int opaque_lane() {
 // bound, with an all but zero vector, can reach the difference)
 __device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// The sums over the 64 lanes of two values at once, in every lane: the two
+// share the cross-row lane swaps.  After the sums within rows of 16 lanes, the
+// first swap and add leave a's pair sums (rows 0 + 1, 2 + 3) in rows 0 and 2
+// and b's in rows 1 and 3; the second, a's total in rows 0 and 2 and b's in
+// rows 1 and 3; the third hands every row both (each total is formed once, in
+// one order, so all lanes hold the same bits).
+__device__ __forceinline__ void sum64x2(float &a, float &b) {
+    a = sum16(a);
+    b = sum16(b);
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const float c = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    s = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+    const float e = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    s = __builtin_amdgcn_permlane16_swap(__float_as_uint(e), __float_as_uint(e), false, false);
+    a = __uint_as_float(s[0]);
+    b = __uint_as_float(s[1]);
+}
+
 // LDS writes of this wavefront visible to its other lanes (no other wavefront)
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -425,11 +443,15 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             const int nve = (int)(L - c0 < CC ? L - c0 : CC);
             const Rsrc ay = tok_rsrc(p.y, BA::ELEM, c0, c0 + nve);
             const Rsrc ao = tok_rsrc(p.o_raw, 4, c0, c0 + nve);
+            static_assert(TW == 2, "two tokens a wavefront: their sums share the lane swaps");
+            const float2 o0 = ld2(&s_o[t0][chq]), o1 = ld2(&s_o[t0 + 1][chq]);
+            float ss[TW] = {o0.x * o0.x + o0.y * o0.y, o1.x * o1.x + o1.y * o1.y};
+            sum64x2(ss[0], ss[1]);
 #pragma unroll
             for (int sl = 0; sl < TW; ++sl) {
                 const int t = t0 + sl;
-                const float2 o = ld2(&s_o[t][chq]);
-                const float r = rsq(sum64(o.x * o.x + o.y * o.y) * (1.0f / DV) + p.rms_eps);
+                const float2 o = sl == 0 ? o0 : o1;
+                const float r = rsq(ss[sl] * (1.0f / DV) + p.rms_eps);
                 const uint32_t e = (uint32_t)(t * rowsz + h * DV + chq);
                 const float2 gg = BA::unpack2(rg[sl]);
                 float2 y;
@@ -628,12 +650,21 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         // token (only in a chunk the sequence ends inside: the condition is
         // wavefront-uniform, so a full chunk takes the branch without selects)
         auto finish = [&](auto masked) {
+            // squared norms of q and k of the two tokens (pairs share lane swaps)
+            float sq[TW], sk[TW];
+#pragma unroll
+            for (int sl = 0; sl < TW; ++sl) {
+                sq[sl] = aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1];
+                sk[sl] = ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1];
+            }
+            sum64x2(sq[0], sk[0]);
+            sum64x2(sq[1], sk[1]);
 #pragma unroll
             for (int sl = 0; sl < TW; ++sl) {
                 // (no branch on the token: the two tokens' chains interleave)
                 const int t = t0 + sl;
-                const float nq = rsq(sum64(aq[sl][0] * aq[sl][0] + aq[sl][1] * aq[sl][1]) + l2_eps2);
-                const float nk = rsq(sum64(ak[sl][0] * ak[sl][0] + ak[sl][1] * ak[sl][1]) + l2_eps2);
+                const float nq = rsq(sq[sl] + l2_eps2);
+                const float nk = rsq(sk[sl] + l2_eps2);
                 float2 qh = make_float2(aq[sl][0] * nq, aq[sl][1] * nq);
                 float2 kh = make_float2(ak[sl][0] * nk, ak[sl][1] * nk);
                 float2 vh = make_float2(av[sl][0] * LN2, av[sl][1] * LN2);
