@@ -67,6 +67,11 @@ __device__ __forceinline__ Split2 split2(float x0, float x1) {
     return {hb, pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u))};
 }
 
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+
 // record slot of chunk c of sequence n: slots floor(cu[n] / 16) + n + c never
 // collide (a sequence of len tokens has at most floor(len / 16) + 1 chunks)
 __device__ __forceinline__ int64_t slot_base(const Params &p, int n) {
@@ -87,8 +92,6 @@ template <> __device__ __forceinline__ float4 ld_act4<BF16>(Rsrc r, uint32_t o) 
 // ---------------------------------------------------------------- pass 1
 constexpr int PREP_THREADS = 256;
 constexpr int XP = CH + 4;              // raw / activated row length in LDS
-constexpr int FP = DK + 4;              // L, M factor rows: 16-byte aligned, and the 16
-                                        // rows a 16-lane group reads at one column on distinct banks
 // raw rows: a thread loads 4 channels of one row of q, k or v at a time, the
 // workgroup RAW_GRP rows of a tensor per pass
 constexpr int RAW_ROWS = CC + PAST;
@@ -96,10 +99,10 @@ constexpr int RAW_GRP = PREP_THREADS / (DK / 4);
 constexpr int RAW_PASSES = (RAW_ROWS + RAW_GRP - 1) / RAW_GRP;
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every range here: reads 0
 
-// LDS of the operand pass: the raw / activated rows, later the L, M factor
-// rows in the same bytes; the conv taps, later the decay sums in the same bytes
-constexpr int X_BYTES = (CC + PAST) * XP * 4, F_BYTES = 3 * CC * FP * 4;
-constexpr int R1_BYTES = X_BYTES > F_BYTES ? X_BYTES : F_BYTES;
+// LDS of the operand pass: the raw / activated rows, later each wavefront's
+// partial L, M in the same bytes; the conv taps, later the decay sums in the
+// same bytes
+constexpr int R1_BYTES = (CC + PAST) * XP * 4;
 constexpr int G_BYTES = CC * DK * 4, CW_BYTES = CH * TAPS * 4;
 constexpr int R2_BYTES = G_BYTES > CW_BYTES ? G_BYTES : CW_BYTES;
 
@@ -136,10 +139,10 @@ void scan_prep_kernel(Params p, uint8_t *records, int32_t seg_lo) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[R1_BYTES + R2_BYTES];
     // raw rows c0 - 3 .. c0 + 15, then activated rows 3 .. 18
     float(*s_x)[XP] = reinterpret_cast<float(*)[XP]>(smem);
-    // L, M factors (after the last read of s_x)
-    float(*s_kl)[FP] = reinterpret_cast<float(*)[FP]>(smem);
-    float(*s_ql)[FP] = reinterpret_cast<float(*)[FP]>(smem + CC * FP * 4);
-    float(*s_kr)[FP] = reinterpret_cast<float(*)[FP]>(smem + 2 * CC * FP * 4);
+    // each wavefront's partial L, M (after the last read of s_x)
+    float(*s_part)[2][CC * CC] = reinterpret_cast<float(*)[2][CC * CC]>(smem);
+    static_assert(PREP_THREADS / 64 * 2 * CC * CC * 4 <= R1_BYTES, "partials in the raw rows' bytes");
+    f32x4 lp, mp;
     float(*s_cw)[TAPS] = reinterpret_cast<float(*)[TAPS]>(smem + R1_BYTES);
     // log-decay summed from the chunk start (after the conv's last read of s_cw)
     float(*s_G)[DK] = reinterpret_cast<float(*)[DK]>(smem + R1_BYTES);
@@ -289,7 +292,7 @@ void scan_prep_kernel(Params p, uint8_t *records, int32_t seg_lo) {
     }
     __syncthreads();                           // s_x is dead from here on
     {
-        float ka[8], qa[8];
+        float ka[8], qa[8], fl[8], fm[8], fr[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int i = 32 * st_m + 16 * (e >> 2) + 4 * st_g + (e & 3);
@@ -298,10 +301,26 @@ void scan_prep_kernel(Params p, uint8_t *records, int32_t seg_lo) {
             ka[e] = eg * sk[e];
             qa[e] = eg * sq[e];
             const float ef = __expf(G - r), eb = __expf(r - G);
-            s_kl[st_t][i] = ef * sk[e];
-            s_ql[st_t][i] = ef * sq[e];
-            s_kr[st_t][i] = eb * sk[e];
+            fl[e] = ef * sk[e];
+            fm[e] = ef * sq[e];
+            fr[e] = eb * sk[e];
         }
+        // the partial L, M over this wavefront's 32 channels as one 16x16x32
+        // step per split part: lane l holds token l % 16 and eight channels as
+        // k = 8 (l / 16) + e, both for the rows (fl, fm) and for the columns
+        // (fr), so the lane's own factors are the operands
+        u32x4 lh, ll, mh, ml, rh, rl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const Split2 a = split2(fl[2 * e], fl[2 * e + 1]), b = split2(fm[2 * e], fm[2 * e + 1]);
+            const Split2 c = split2(fr[2 * e], fr[2 * e + 1]);
+            lh[e] = a.hi; ll[e] = a.lo;
+            mh[e] = b.hi; ml[e] = b.lo;
+            rh[e] = c.hi; rl[e] = c.lo;
+        }
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        lp = mfma32(lh, rh, mfma32(lh, rl, mfma32(ll, rh, z4)));
+        mp = mfma32(mh, rh, mfma32(mh, rl, mfma32(ml, rh, z4)));
         const int so = (((st_m * 4 + st_g) * CC) + st_t) * 16;
         u32x4 kh4, kl4, qh4, ql4;
 #pragma unroll
@@ -318,20 +337,26 @@ void scan_prep_kernel(Params p, uint8_t *records, int32_t seg_lo) {
         *reinterpret_cast<u32x4 *>(rec + R_QA + 4096 + so) = ql4;
     }
     __syncthreads();
+    // the four wavefronts' partials (lane l: rows 4 (l / 16) + r of column
+    // l % 16) through LDS, in the bytes the raw rows used
+    {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s_part[st_m][0][(4 * st_g + r) * CC + st_t] = lp[r];
+            s_part[st_m][1][(4 * st_g + r) * CC + st_t] = mp[r];
+        }
+    }
+    __syncthreads();
     // L (strictly lower, times beta: the matrix A of the solve) and M (lower
-    // with the diagonal): one (t, s) pair per thread
+    // with the diagonal): one (t, s) pair per thread, the partials added in
+    // wavefront order
     {
         const int t = tid >> 4, s = tid & 15;
-        float l = 0.f, mm = 0.f;
-        if (s <= t) {
-#pragma unroll 8
-            for (int i = 0; i < DK; i += 4) {
-                const float4 a = *reinterpret_cast<const float4 *>(&s_kl[t][i]);
-                const float4 q = *reinterpret_cast<const float4 *>(&s_ql[t][i]);
-                const float4 b = *reinterpret_cast<const float4 *>(&s_kr[s][i]);
-                l = fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, fmaf(a.w, b.w, l))));
-                mm = fmaf(q.x, b.x, fmaf(q.y, b.y, fmaf(q.z, b.z, fmaf(q.w, b.w, mm))));
-            }
+        float l = s_part[0][0][tid], mm = s_part[0][1][tid];
+#pragma unroll
+        for (int w = 1; w < PREP_THREADS / 64; ++w) {
+            l += s_part[w][0][tid];
+            mm += s_part[w][1][tid];
         }
         s_A[t][s] = s < t ? s_b[t] * l : 0.f;
         split_store(rec, R_M, 512, t * CC + s, s <= t ? mm : 0.f);
@@ -362,10 +387,6 @@ constexpr int SCAN_GROUPS = DV / (16 * SCAN_COLS);
 constexpr int XCDS = 8;
 constexpr int RING = 4;                 // record buffers per workgroup (3 loading while 1 is used)
 
-__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                   c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
                                                      c, 0, 0, 0);
