@@ -35,11 +35,13 @@
 // chunks and the same two workgroup barriers per chunk:
 //   state wavefronts w = 0..7 own state columns 16 w .. 16 w + 15 as 8 MFMA
 //     accumulator tiles (lane l holds S[16 rt + 4 (l / 16) + r][16 w + l % 16]
-//     in element r of tile rt) and do the matrix work, the solve for T and M
-//     (wavefronts 0 and 1) and the RMSNorm epilogue of tokens 2 w, 2 w + 1;
+//     in element r of tile rt) and do the matrix work: P, R, the update, the
+//     partial L, M over key channels 16 w .. 16 w + 15, the solve for T and the
+//     sum of M (wavefronts 0 and 1), and the RMSNorm epilogue of tokens 2 w,
+//     2 w + 1;
 //   token wavefronts 8 + u (u = 0..7) do the token-wise work of tokens 2 u,
-//     2 u + 1 (conv, SiLU, L2 norm, the split operands) and the decay sums and
-//     partial L, M of channel eighth u.
+//     2 u + 1 (conv, SiLU, L2 norm, the split operands) and the decay sums of
+//     (channel, quarter) pairs 64 u .. 64 u + 63.
 // A wavefront issues vector instructions at no more than about half its
 // SIMD's rate, and the step's chains stall it far more often, so each SIMD
 // holds four wavefronts: two of each role, whose matrix and vector work
