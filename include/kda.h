@@ -267,12 +267,18 @@ kda_status kda_sequence_lowrank(const kda_config *cfg, const kda_tensors *t, int
  * heads, cfg->prefill_path); 0 if that path needs none.  A negative value is
  * a kda_status for bad arguments.  SPLIT uses it for its fp32 readout, which
  * o_raw replaces when given; SCAN for every chunk's operands (about 2.2 KiB
- * per token and head) followed by the readout (not needed with o_raw).  With
+ * per token and head) followed by the readout (not needed with o_raw).
+ * CHUNK (and AUTO where it takes CHUNK) asks for 256 bytes: a counter of
+ * (sequence, head) pairs, which the call zeroes on `stream` before its kernel
+ * runs.  With it the kernel runs one workgroup per compute unit, each taking
+ * pairs in the scheduling order until none are left, so that compute units
+ * running at different clocks share the work evenly; without it, one
+ * workgroup per pair.  The results are the same bit for bit.  With
  * a smaller or NULL workspace kda_sequence falls back under
  * KDA_PREFILL_AUTO (to CHUNK or FUSED) and fails with KDA_ERR_INVALID_ARG
  * under KDA_PREFILL_SPLIT and KDA_PREFILL_SCAN.  Caller-owned, 16-byte
  * aligned, no initialisation needed, not kept after the call; its contents
- * are scratch.
+ * are scratch (two calls in flight at once need a workspace each).
  */
 int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                     int64_t total_tokens);

@@ -136,6 +136,25 @@ bool scan_shape(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
            total_tokens >= SCAN_MIN_AVG_TOKENS * (int64_t)num_seqs;
 }
 
+// The one-pass chunk kernel's pair counter: with it the kernel runs one
+// workgroup per compute unit, each taking pairs in the scheduling order until
+// none are left, which evens out compute units (and chiplets) that run at
+// different clocks; its workspace is this one counter.
+constexpr int64_t TICKET_BYTES = 256;
+
+// the path kda_sequence takes is the one-pass chunk kernel (given no
+// workspace large enough for the two-pass one)
+bool chunk_path(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    if (cfg->prefill_path == KDA_PREFILL_CHUNK) return chunk_supported(cfg);
+    return cfg->prefill_path == KDA_PREFILL_AUTO && !auto_short(cfg, num_seqs, total_tokens) &&
+           !auto_chunk_short(cfg, num_seqs, total_tokens) && auto_chunk(cfg, num_seqs, total_tokens);
+}
+
+// the counter's tickets (pairs plus one per workgroup) stay within int32
+bool tickets_fit(const kda_config *cfg, int32_t num_seqs) {
+    return (int64_t)num_seqs * cfg->num_heads < (int64_t(1) << 30);
+}
+
 // workspace of the two-pass path: the chunk records, then (without o_raw)
 // the fp32 readout
 int64_t scan_record_bytes(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
@@ -272,6 +291,7 @@ kda::Params make_params(const kda_config *cfg, const kda_tensors *t, int32_t num
     p.gate_mode = cfg->gate_mode;
     p.lb = cfg->gate_lower_bound; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
     p.lr_a = nullptr; p.lr_wfb = nullptr; p.lr_rank = 0;
+    p.tickets = nullptr;
     return p;
 }
 
@@ -322,7 +342,8 @@ int64_t kda_sequence_workspace_size(const kda_config *cfg, int32_t num_seqs, int
     if (cfg->prefill_path == KDA_PREFILL_SCAN ||
         (cfg->prefill_path == KDA_PREFILL_AUTO && scan_shape(cfg, num_seqs, total_tokens)))
         return scan_record_bytes(cfg, num_seqs, total_tokens) + readout_bytes(cfg, total_tokens);
-    if (split_cols_for(cfg, num_seqs, total_tokens) == 0) return 0;
+    if (split_cols_for(cfg, num_seqs, total_tokens) == 0)
+        return chunk_path(cfg, num_seqs, total_tokens) && tickets_fit(cfg, num_seqs) ? TICKET_BYTES : 0;
     return readout_bytes(cfg, total_tokens);
 }
 
@@ -428,8 +449,11 @@ kda_status kda_sequence(const kda_config *cfg, const kda_tensors *t, int32_t num
              (cfg->prefill_path == KDA_PREFILL_AUTO && auto_chunk_short(cfg, num_seqs, total_tokens)))
         e = kda::launch_prefill_chunk_short(p, bf16, s);
     else if (cfg->prefill_path == KDA_PREFILL_CHUNK ||
-             (cfg->prefill_path == KDA_PREFILL_AUTO && auto_chunk(cfg, num_seqs, total_tokens)))
+             (cfg->prefill_path == KDA_PREFILL_AUTO && auto_chunk(cfg, num_seqs, total_tokens))) {
+        if (workspace && workspace_bytes >= TICKET_BYTES && tickets_fit(cfg, num_seqs))
+            p.tickets = static_cast<int32_t *>(workspace);
         e = kda::launch_prefill_chunk(p, bf16, s);
+    }
     else
         e = kda::launch_prefill(p, bf16, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;

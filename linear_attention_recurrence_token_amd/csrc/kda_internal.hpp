@@ -35,6 +35,9 @@ struct Params {
     // step from a [T, lr_rank] and W_fb [H * 128, lr_rank]; null otherwise
     const float *lr_a, *lr_wfb;
     int32_t lr_rank;
+    // the chunk kernel's pair counter (one int32, zeroed by its launcher);
+    // null = one (sequence, head) pair per workgroup
+    int32_t *tickets;
 };
 
 // Launchers (return the hipError_t of the launch).

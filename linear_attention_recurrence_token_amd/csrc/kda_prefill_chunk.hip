@@ -31,7 +31,7 @@
 // selection, never multiplied.)  Other gate forms take the recurrent path.
 //
 // Layout and schedule.  One 1024-thread workgroup (16 wavefronts, four per
-// SIMD) per (sequence, head), in two roles, each with its own loop over the
+// SIMD) per (sequence, head) at a time, in two roles, each with its own loop over the
 // chunks and the same two workgroup barriers per chunk:
 //   state wavefronts w = 0..7 own state columns 16 w .. 16 w + 15 as 8 MFMA
 //     accumulator tiles (lane l holds S[16 rt + 4 (l / 16) + r][16 w + l % 16]
@@ -59,6 +59,15 @@
 // as the B operand of 16x16x32 steps directly, by ordering the sum over key
 // channels so that step m takes, in lane l, the rows the lane holds of tiles
 // 2 m and 2 m + 1; the A operands are stored in LDS in that order.
+// Pairs in turn.  Given a pair counter, the grid is one workgroup per compute
+// unit and each workgroup takes pairs from the counter until none are left:
+// faster compute units (chiplets run at different clocks) take more pairs,
+// and a pair's start overlaps the previous one's end, since the token role
+// begins the next pair's chunk 0 (its taps, loads and pre-step) while the
+// state role finishes the last RMSNorm and stores the state (chunk 0 writes
+// none of the LDS that this tail reads).
+#include <atomic>
+
 #include "kda_device.hpp"
 
 namespace kda {
@@ -247,17 +256,32 @@ template <typename Act>
 __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     typedef BufAct<Act> BA;
     typedef typename BA::Raw2 Raw2;
-    const int slot_n = blockIdx.x / p.H;
-    const int h = blockIdx.x - slot_n * p.H;
-    int n = slot_n;
-    if (p.seq_order) {
-        n = p.seq_order[slot_n];
-        if (n < 0 || n >= p.num_seqs) return;
+    // the (sequence, head) pair in hand: ticket tk of the scheduling order is
+    // head tk % H of the sequence in slot tk / H.  Workgroup b starts with
+    // ticket b; with a pair counter (p.tickets) it asks the counter for its
+    // next ticket while it works on a pair (tickets past the grid's own, in
+    // the order workgroups ask), so that compute units that run faster take
+    // more of the pairs
+    const int64_t tickets_total = (int64_t)p.num_seqs * p.H;
+    int64_t tk = blockIdx.x;
+    int h, n;
+    Range rng;
+    int64_t L, NC, unit;
+    auto take = [&](int64_t t, int nn, Range r) {
+        tk = t;
+        h = (int)(t % p.H);
+        n = nn;
+        rng = r;
+        L = r.len;
+        NC = (L + CC - 1) / CC;
+        unit = (int64_t)n * p.H + h;
+    };
+    {
+        const int slot = (int)(tk / p.H);
+        const int nn = p.seq_order ? p.seq_order[slot] : slot;
+        const bool ok = nn >= 0 && nn < p.num_seqs;   // entries out of range are skipped
+        take(tk, ok ? nn : 0, ok ? seq_range(p, nn) : Range{0, 0});
     }
-    const Range rng = seq_range(p, n);
-    if (rng.len <= 0) return;
-    const int64_t L = rng.len;
-    const int64_t NC = (L + CC - 1) / CC;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -268,7 +292,6 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     const int rw = wave & 7;                        // wavefront index within the role
     const int rtid = tid & (CK_THREADS / 2 - 1);    // thread index within the role
     const int t0 = TW * rw;                         // tokens of this wavefront's token-wise work
-    const int64_t unit = (int64_t)n * p.H + h;
     const int64_t rowsz = (int64_t)p.H * DK;       // elements per token row of q, k, v, f, g, y
 
     __shared__ float s_kh[CC][KP];         // k_hat of the chunk being prepared
@@ -299,12 +322,22 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
     // (one array: T hi, T lo, M hi, M lo by the second index)
     __shared__ __attribute__((aligned(16))) uint32_t s_tm[2][4][CC][TR];
     __shared__ float s_o[CC][DV + 4];      // readout of the chunk, before RMSNorm
-    __shared__ float s_cw[CH][TAPS];       // conv taps of this head
+    __shared__ long long s_nx[4];          // the next pair: ticket, sequence, first token, length
 
-    {
-        const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
-        for (int c = tid; c < CH; c += CK_THREADS) st4(s_cw[c], ld4(cw + c * TAPS));
-    }
+    // the next pair as published in s_nx (false: no pairs left)
+    auto next_pair = [&]() -> bool {
+        long long v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const long long x = s_nx[i];
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)x >> 32));
+            v[i] = (long long)(((unsigned long long)hi << 32) | lo);
+        }
+        if (v[0] >= tickets_total) return false;
+        take(v[0], (int)v[1], Range{v[2], v[3]});
+        return true;
+    };
 
     auto tok_rsrc = [&](const void *t, uint32_t elem, int64_t base, int64_t end) -> Rsrc {
         return make_rsrc(static_cast<const char *>(t) + (rng.lo + base) * rowsz * elem,
@@ -464,23 +497,30 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             }
         };
 
-        // ---- state into the accumulator tiles (lane offset: row 4 g4 + r,
-        // column col0 + n16; row tile rt as the scalar offset)
-        const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
+        // the state in the accumulator tiles (lane offset: row 4 g4 + r, column
+        // col0 + n16; row tile rt as the scalar offset)
         f32x4 st[8];
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                st[rt][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
-
-        __syncthreads();                           // conv taps in LDS
-        __syncthreads();                           // chunk 0 prepared
-        partial_LM();                              // L, M of chunk 0
-        __syncthreads();                           // chunk 0's operands, L and M
-        if (rw == 0) solve_T(0, 0);
-        else if (rw == 1) reduce_M(0);
-        __syncthreads();                           // T, M of chunk 0; chunk 1 prepared
+        // lane 0 of wavefront 2 asks the counter for the next ticket at the
+        // start of a pair, looks up its sequence after the first barrier and
+        // publishes it with the sequence's token range before the third (the
+        // others read s_nx after the pair, before their next barrier)
+        const bool asker = p.tickets && rw == 2 && lane == 0;
+        int32_t nx_a = 0, nx_n = -1;
+        auto ask = [&]() { nx_a = __hip_atomic_fetch_add(p.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        auto look_up = [&]() {
+            const int64_t t = (int64_t)gridDim.x + nx_a;
+            const int slot = (int)(t / p.H);
+            nx_n = t >= tickets_total ? -1 : (p.seq_order ? p.seq_order[slot] : slot);
+        };
+        auto publish = [&]() {
+            const int64_t t = (int64_t)gridDim.x + nx_a;
+            const bool ok = t < tickets_total && nx_n >= 0 && nx_n < p.num_seqs;
+            const Range r = ok ? seq_range(p, nx_n) : Range{0, 0};
+            s_nx[0] = t;
+            s_nx[1] = ok ? nx_n : 0;
+            s_nx[2] = r.lo;
+            s_nx[3] = r.len;
+        };
 
         f32x4 Pt, Rt;
         // P, R of the current chunk: step m covers state rows 32 m .. 32 m + 31
@@ -546,6 +586,25 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
             for (int rt = 0; rt < 8; ++rt) st[rt] = mma_hihi(eh[rt], dh, st[rt]);
         };
 
+#pragma unroll 1
+        for (;;) {
+        if (L > 0) {
+        const Rsrc rs_state = make_rsrc(p.state + unit * (DK * DV), DK * DV * 4);
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st[rt][r] = bld_f32(rs_state, ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
+        if (asker) ask();
+        __syncthreads();                           // chunk 0 prepared
+        partial_LM();                              // L, M of chunk 0
+        if (asker) look_up();
+        __syncthreads();                           // chunk 0's operands, L and M
+        if (rw == 0) solve_T(0, 0);
+        else if (rw == 1) reduce_M(0);
+        else if (asker) publish();
+        __syncthreads();                           // T, M of chunk 0; chunk 1 prepared
+
         int vb = 0;                                // chunk i's index mod 3
 #pragma unroll 1
         for (int64_t i = 0; i < NC; ++i) {
@@ -573,18 +632,28 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 bst_f32(rs_state, st[rt][r], ((4 * g4 + r) * DV + col0 + n16) * 4, rt * 16 * DV * 4);
-        return;
+        } else if (p.tickets) {
+            // an empty pair: its successor is asked for at once
+            __syncthreads();                       // s_nx read by all
+            if (asker) {
+                ask();
+                look_up();
+                publish();
+            }
+            __syncthreads();                       // s_nx written
+        }
+        if (!p.tickets || !next_pair()) return;
+        }
     }
 
     // =========================================================== token role
     // decay: key channel dch over the tokens of quarter dq
     const int dch = rtid & (DK - 1);
     const int dq = rtid >> 7;
-    const uint32_t foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
+    uint32_t foff;
     // sigmoid(exp(A_log) (f + dt_bias)) = 1 / (1 + 2^(nA f + nAd)), with nA =
-    // -log2(e) exp(A_log) and nAd = nA dt_bias formed once
-    const float nA = -1.4426950408889634f * __expf(p.A_log[h * DK + dch]);
-    const float nAd = nA * p.dt_bias[h * DK + dch];
+    // -log2(e) exp(A_log) and nAd = nA dt_bias formed once a pair
+    float nA, nAd;
 
     // registers loaded a chunk ahead: raw inputs of the next chunk to pre-step
     Raw2 rq[RAWR], rk[RAWR], rv[RAWR];
@@ -753,11 +822,19 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         }
     };
 
-    __syncthreads();                               // conv taps in LDS
-    // the taps times log2(e) (see the pre-step)
-    wq0 = ld4(s_cw[chq]) * LOG2E; wq1 = ld4(s_cw[chq + 1]) * LOG2E;
-    wk0 = ld4(s_cw[chk]) * LOG2E; wk1 = ld4(s_cw[chk + 1]) * LOG2E;
-    wv0 = ld4(s_cw[chv]) * LOG2E; wv1 = ld4(s_cw[chv + 1]) * LOG2E;
+#pragma unroll 1
+    for (;;) {
+    if (L > 0) {
+    // this head's taps times log2(e) (see the pre-step) and decay constants
+    {
+        const float *cw = p.conv_w + (int64_t)h * (CH * TAPS);
+        wq0 = ld4(cw + chq * TAPS) * LOG2E; wq1 = ld4(cw + (chq + 1) * TAPS) * LOG2E;
+        wk0 = ld4(cw + chk * TAPS) * LOG2E; wk1 = ld4(cw + (chk + 1) * TAPS) * LOG2E;
+        wv0 = ld4(cw + chv * TAPS) * LOG2E; wv1 = ld4(cw + (chv + 1) * TAPS) * LOG2E;
+        foff = (uint32_t)((4 * dq * rowsz + h * DK + dch) * 4);
+        nA = -1.4426950408889634f * __expf(p.A_log[h * DK + dch]);
+        nAd = nA * p.dt_bias[h * DK + dch];
+    }
     // ---- chunk 0 (its past rows come from the carried window)
     {
         const int64_t end = chunk_end(0);
@@ -817,6 +894,12 @@ __global__ __launch_bounds__(CK_THREADS) void prefill_chunk_kernel(Params p) {
         if (i + 3 < NC) issue_inputs((i + 3) * CC);
         __syncthreads();
         vb = vb1;
+    }
+    } else if (p.tickets) {
+        __syncthreads();                           // s_nx read by all
+        __syncthreads();                           // s_nx written
+    }
+    if (!p.tickets || !next_pair()) return;
     }
 }
 
@@ -1966,13 +2049,48 @@ __global__ __launch_bounds__(128) void chunk_window_kernel(Params p) {
     }
 }
 
+// zeroes the pair counter before a launch that takes tickets from it (a
+// kernel, not a memset, so that the call can be captured in a graph)
+__global__ void ticket_reset_kernel(int32_t *c) {
+    if (threadIdx.x == 0) *c = 0;
+}
+
+// Compute units of each device, read on first use.
+constexpr int CHUNK_DEVICES = 64;
+std::atomic<int> g_chunk_cus[CHUNK_DEVICES];
+
+hipError_t device_cus(int &cus) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    cus = dev >= 0 && dev < CHUNK_DEVICES ? g_chunk_cus[dev].load(std::memory_order_relaxed) : 0;
+    if (cus <= 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (cus <= 0) cus = 1;
+        if (dev >= 0 && dev < CHUNK_DEVICES) g_chunk_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    return hipSuccess;
+}
+
+// With a pair counter the 16-wavefront kernel runs one workgroup per compute
+// unit (its LDS allows no more) and each takes pairs until none are left;
+// without one, one workgroup per pair.
 template <typename Act>
 hipError_t launch_chunk_as(const Params &p, bool lowrank, hipStream_t stream) {
     const int64_t units = (int64_t)p.num_seqs * p.H;
-    if (lowrank)
+    if (lowrank) {
         hipLaunchKernelGGL((prefill_chunk_lr_kernel<Act>), dim3((unsigned)units), dim3(LR_THREADS), 0, stream, p);
-    else
+    } else if (p.tickets) {
+        int cus = 0;
+        hipError_t e = device_cus(cus);
+        if (e != hipSuccess) return e;
+        const int64_t G = units < cus ? units : cus;
+        hipLaunchKernelGGL(ticket_reset_kernel, dim3(1), dim3(64), 0, stream, p.tickets);
+        hipLaunchKernelGGL((prefill_chunk_kernel<Act>), dim3((unsigned)G), dim3(CK_THREADS), 0, stream, p);
+    } else {
         hipLaunchKernelGGL((prefill_chunk_kernel<Act>), dim3((unsigned)units), dim3(CK_THREADS), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_window_kernel<Act>), dim3((unsigned)units), dim3(128), 0, stream, p);

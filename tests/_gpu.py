@@ -34,10 +34,10 @@ PATHS = {"fused": kda.KDA_PREFILL_FUSED, "split": kda.KDA_PREFILL_SPLIT, "auto":
 
 
 def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, path="auto", side_stream=False,
-                 cu_host=False):
+                 cu_host=False, workspace="auto"):
     """One kda_sequence call; side_stream: pass a second stream (the two-pass
     path may then run in segments); cu_host: pass the host copy of the
-    offsets too."""
+    offsets too; workspace: "auto" (the size the library asks for) or None."""
     import torch
     d = synth.to_device(w, dev, with_o_raw=with_o_raw)
     order = None if seq_order is None else torch.as_tensor(np.asarray(seq_order, np.int32), device=dev)
@@ -45,7 +45,7 @@ def run_sequence(w, dev, *, with_o_raw=True, seq_order=None, dense=False, path="
     kda.kda_sequence(cfg_of(w, prefill_path=PATHS[path]), **tensors(d),
                      cu_seqlens=None if dense else d["cu_seqlens"],
                      cu_seqlens_host=w.cu_seqlens.astype(np.int32) if (cu_host and not dense) else None,
-                     seq_order=order, num_seqs=w.N, side_stream=side)
+                     seq_order=order, num_seqs=w.N, side_stream=side, workspace=workspace)
     torch.cuda.synchronize()
     out = {"y": _np(d["y"]), "state": _np(d["state"]), "win": d["conv_win"].cpu().numpy()}
     out["o_raw"] = _np(d["o_raw"]) if with_o_raw else None

@@ -133,9 +133,11 @@ def test_beta_needs_only_word_alignment(lib):
 
 
 def test_workspace_size_and_checks(lib):
-    # bounded gate: AUTO takes the chunkwise kernel, or the short-sequence
-    # kernel when the sequences are very short on average; neither needs one
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 100) == 0
+    # bounded gate: AUTO takes the chunkwise kernel, which asks for its pair
+    # counter (256 bytes), or for short sequences on average the chunk kernel
+    # without a pipeline or the short-sequence kernel, which need none
+    TICKETS = 256
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 100) == TICKETS
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 14) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 16) == 0
     # other gates, few (sequence, head) pairs: the split path wants one fp32
@@ -143,7 +145,7 @@ def test_workspace_size_and_checks(lib):
     lit = dict(gate_mode=kda.KDA_GATE_LITERAL)
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(**lit)), 2, 100) == 100 * 4 * 128 * 4
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=1)), 2, 100) == 0
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=3)), 2, 100) == 0
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=3)), 2, 100) == TICKETS
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=4)), 2, 100) == 0
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=6)), 2, 100) == 0
     # the two-pass chunk path: records (35 KiB per chunk slot and head; a
@@ -153,8 +155,8 @@ def test_workspace_size_and_checks(lib):
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(prefill_path=5)), 2, 100) == rec(100, 2, 4) + out(100, 4)
     # AUTO takes it for at most 64 pairs (here 8) averaging at least 128 tokens
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 256) == rec(256, 2, 4) + out(256, 4)
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 254) == 0
-    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 2, 8192) == 0   # 128 pairs
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg()), 2, 254) == TICKETS
+    assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64)), 2, 8192) == TICKETS   # 128 pairs
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=32)), 2, 8192) == \
         rec(8192, 2, 32) + out(8192, 32)
     assert lib.kda_sequence_workspace_size(ctypes.byref(_cfg(num_heads=64, **lit)), 16, 100) == 0

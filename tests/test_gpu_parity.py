@@ -144,6 +144,41 @@ def test_chunk_many_pairs_short_average(gpu, act, path):
                            _gpu.oracle_sequence(w), bf16=act == "bf16", label="many pairs")
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_chunk_pair_counter(gpu, act):
+    # the one-pass chunk kernel with its pair counter (the workspace the
+    # library asks for: one workgroup per compute unit, each taking pairs
+    # until none are left) against one pair per workgroup (no workspace):
+    # 400 pairs, so most workgroups take two, with empty sequences among them
+    # and, in the last order, two entries out of range (skipped, leaving
+    # those sequences' state as it was); every pair's
+    # arithmetic is the same either way, so the results agree bit for bit
+    N, H = 100, 4
+    w = synth.make_workload("pair counter", seed=37, N=N, H=H,
+                            lengths=lambda rng: rng.choice([0, 1, 15, 16, 17, 40, 97], size=N), act_dtype=act,
+                            state_std=0.02, win_std=1.0, fresh_prob=0.3)
+    assert kda.sequence_workspace_size(_gpu.cfg_of(w, prefill_path=kda.KDA_PREFILL_CHUNK), N, w.total_tokens) == 256
+    order = np.argsort(-w.lengths, kind="stable").astype(np.int32)
+    bad = order.copy()
+    bad[3], bad[50] = -1, N + 7
+    ref = _gpu.oracle_sequence(w)
+    for label, seq_order in (("natural order", None), ("longest first", order), ("two entries out of range", bad)):
+        note("chunk path with and without its pair counter, 100 x 4 pairs, %s, %s" % (label, act))
+        a = _gpu.run_sequence(w, gpu, path="chunk", seq_order=seq_order)
+        b = _gpu.run_sequence(w, gpu, path="chunk", seq_order=seq_order, workspace=None)
+        for k in ("y", "o_raw", "state", "win"):
+            np.testing.assert_array_equal(a[k], b[k], err_msg="%s %s" % (label, k))
+        if seq_order is bad:
+            skipped = [int(order[3]), int(order[50])]
+            kept = [n for n in range(N) if n not in skipped]
+            np.testing.assert_array_equal(a["state"][skipped], w.state0[skipped].astype(np.float32))
+            sub = synth.subset(w, kept, list(range(H)))
+            got = {"state": a["state"][kept], "win": a["win"][kept]}
+            _gpu.assert_parity(got, _gpu.oracle_sequence(sub), keys=("state",), label=label)
+        else:
+            _gpu.assert_parity(a, ref, bf16=act == "bf16", label=label)
+
+
 @pytest.mark.parametrize("path", ["auto", "chunk", "short", "chunk_short"])
 def test_short_average_with_long_sequences(gpu, path):
     # a batch that is short on average (the chunk path's single-buffered
