@@ -601,6 +601,8 @@ def bench_layer(torch, kda, synth, dev, runs):
     ws_fa, n_fa = ws(kda.KDA_PROJ_LOWRANK_FACTOR, r)
     ws_g, n_g = ws(kda.KDA_PROJ_GATE)
     ws_o, n_o = ws(kda.KDA_PROJ_OUTPUT)
+    n_sq = kda.sequence_workspace_size(cfg, w.N, T)
+    ws_sq = torch.empty(n_sq, dtype=torch.uint8, device=dev) if n_sq > 0 else None
     ptr = lambda t: t.data_ptr() if t is not None else None
     t_sep = kda.kda_tensors(*[(d[n].data_ptr() if d.get(n) is not None else None) for n in kda.TENSOR_FIELDS])
     t_lr = kda.kda_tensors(*[(d[n].data_ptr() if (d.get(n) is not None and n != "f") else None)
@@ -619,8 +621,8 @@ def bench_layer(torch, kda, synth, dev, runs):
                                                            sh), "factor"),
         "gate_projection": lambda: chk(L.kda_gate_projection(ctypes.byref(ccfg), x.data_ptr(), wg.data_ptr(), D, T,
                                                              g.data_ptr(), ptr(ws_g), n_g, sh), "gate"),
-        "step": lambda: chk(L.kda_sequence(ctypes.byref(ccfg), ctypes.byref(t_sep), w.N, cu, None, None, T, None, 0,
-                                           sh, None), "sequence"),
+        "step": lambda: chk(L.kda_sequence(ctypes.byref(ccfg), ctypes.byref(t_sep), w.N, cu, None, None, T,
+                                           ptr(ws_sq), n_sq, sh, None), "sequence"),
         "step_lowrank": lambda: chk(L.kda_sequence_lowrank(ctypes.byref(ccfg), ctypes.byref(t_lr), w.N, cu, None,
                                                            None, T, a.data_ptr(), wfb.data_ptr(), r, sh),
                                     "sequence_lowrank"),
