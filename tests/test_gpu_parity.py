@@ -179,6 +179,58 @@ def test_chunk_pair_counter(gpu, act):
             _gpu.assert_parity(a, ref, bf16=act == "bf16", label=label)
 
 
+def test_chunk_pair_counter_in_a_graph(gpu):
+    # the call captured in a HIP graph: its counter is zeroed by a kernel in
+    # the graph, so every replay (with eager work and synchronisations
+    # between them) must give the eager call's results bit for bit
+    import torch
+    N, H = 70, 4
+    w = synth.make_workload("graph", seed=39, N=N, H=H,
+                            lengths=lambda rng: rng.choice([0, 5, 16, 33, 80], size=N), act_dtype="bf16",
+                            state_std=0.02, win_std=1.0, fresh_prob=0.3)
+    d = synth.to_device(w, gpu, with_o_raw=True)
+    s0, w0 = d["state"].clone(), d["conv_win"].clone()
+    cfg = _gpu.cfg_of(w, prefill_path=kda.KDA_PREFILL_CHUNK)
+    ws = torch.empty(kda.sequence_workspace_size(cfg, N, w.total_tokens), dtype=torch.uint8, device=gpu)
+    assert ws.numel() == 256
+    order = torch.as_tensor(np.argsort(-w.lengths, kind="stable").astype(np.int32), device=gpu)
+
+    def call():
+        kda.kda_sequence(cfg, **_gpu.tensors(d), cu_seqlens=d["cu_seqlens"], seq_order=order, num_seqs=N,
+                         workspace=ws, check=False)
+
+    def reset():
+        d["state"].copy_(s0)
+        d["conv_win"].copy_(w0)
+        d["y"].zero_()
+        d["o_raw"].zero_()
+
+    def snap():
+        return {k: d[k].float().cpu().numpy().copy() for k in ("y", "o_raw", "state", "conv_win")}
+
+    note("chunk path with its pair counter, eager then captured, 70 x 4 pairs")
+    call()
+    torch.cuda.synchronize()
+    ref = snap()
+    _gpu.assert_parity({"y": ref["y"].astype(np.float64), "o_raw": ref["o_raw"].astype(np.float64),
+                        "state": ref["state"].astype(np.float64), "win": ref["conv_win"]},
+                       _gpu.oracle_sequence(w), bf16=True, label="eager")
+    reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snap()
+        for k in ref:
+            np.testing.assert_array_equal(got[k], ref[k], err_msg="replay %d %s" % (rep, k))
+
+
 @pytest.mark.parametrize("path", ["auto", "chunk", "short", "chunk_short"])
 def test_short_average_with_long_sequences(gpu, path):
     # a batch that is short on average (the chunk path's single-buffered
